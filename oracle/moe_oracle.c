@@ -1,0 +1,390 @@
+/*
+ * CPU oracle of the MoE SwiGLU feed-forward forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain definition that the
+ * HIP path is checked against. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the product path never does.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Every sum is accumulated in fp64 and no intermediate result is rounded:
+ * inputs are read exactly as stored (fp32, or bf16 widened by this file's
+ * own converter) and the results are fp64.
+ *
+ * Sources (page title, section):
+ *  - "APEX-1 Mathematical Reference - Part 3", section 12.2 (SwiGLU formula),
+ *    12.3 (SiLU), 13.2 (MoE = shared experts + sum_k g_k Expert_{e_k},
+ *    router r = x W_router + b, top-K, softmax over the selected scores).
+ *  - "A working MoE layer in PyTorch" (moe-from-scratch): fp32 softmax over
+ *    all experts, top-K, renormalise; sorted dispatch with bincount.
+ *  - "StableLatentMoE and QuantileBalancer": sigmoid scores + bias select
+ *    the top-(K+1), the last is dropped, weights are the uncorrected sigmoid
+ *    scores (renormalised only on request) times a routed scaling factor;
+ *    stable argsort dispatch with counts and cumulative ends; latent
+ *    down-projection M->L, routed experts in L, optional RMSNorm in L,
+ *    up-projection L->M, output = shared + routed.
+ *  - "10 - Mixture of Experts" (APEX-1 docs): shared experts see every token
+ *    and are added to the routed sum; an expert with no tokens is skipped.
+ *
+ * Readings where the pages are silent (listed with the rest in the design
+ * notes): equal scores rank the lower expert id first; slots are ordered by
+ * descending score; the balance bias enters the softmax-over-selected
+ * weights (it is part of the ranked logits) but not the sigmoid weights;
+ * RMSNorm is R / sqrt(mean(R^2) + eps) * gamma.
+ *
+ * Parity pins live in the test suite: the SiLU table of section 12.3, the
+ * derivable part of the section 12.5 worked example, the router example of
+ * section 13.5, the dispatch example of the StableLatentMoE page, closed-form
+ * identities and a dense, masked brute force on tiny inputs.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F64 2 /* only for the y_rows argument of or_combine */
+
+#define OR_ROUTE_TOPK_SOFTMAX 0  /* rank r = xW + b, softmax over the K picked */
+#define OR_ROUTE_SOFTMAX_TOPK 1  /* p = softmax(r) over E, top-K, renormalise  */
+#define OR_ROUTE_SIGMOID_BIAS 2  /* s = sigmoid(xW); rank s + b; g = s (raw)   */
+
+typedef struct {
+  int64_t T;
+  int32_t d, d_ff, E, K, d_shared, latent;
+  int32_t act;
+  int32_t route;
+  int32_t renormalize, has_rmsnorm;
+  double routed_scale, rms_eps;
+} or_layer;
+
+typedef struct {
+  const void *x;          /* [T, d]                act                */
+  const float *w_router;  /* [E, d]                fp32               */
+  const float *bias;      /* [E] or NULL           fp32               */
+  const void *w_gate;     /* [E, d_ff, d_e]        act (out x in)     */
+  const void *w_up;       /* [E, d_ff, d_e]        act                */
+  const void *w_down;     /* [E, d_e, d_ff]        act                */
+  const void *ws_gate;    /* [d_shared, d]         act (may be NULL)  */
+  const void *ws_up;      /* [d_shared, d]         act                */
+  const void *ws_down;    /* [d, d_shared]         act                */
+  const void *w_lat_down; /* [L, d]                act (latent only)  */
+  const void *w_lat_up;   /* [d, L]                act                */
+  const float *rms_gamma; /* [L]                   fp32               */
+} or_tensors;
+
+/* ------------------------------------------------------------ scalars */
+
+double or_bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Logistic sigmoid, 1 / (1 + e^-x)   (Math. Reference Part 3, 12.3). */
+double or_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + e^-x)   (Math. Reference Part 3, 12.3). */
+double or_silu(double x) { return x / (1.0 + exp(-x)); }
+
+static double ld(const void *p, int act, int64_t i) {
+  if (act == OR_BF16) return or_bf16_to_double(((const uint16_t *)p)[i]);
+  if (act == OR_F64) return ((const double *)p)[i];
+  return (double)((const float *)p)[i];
+}
+
+/* sum_i w[off + i] * v[i] over n entries, fp64 accumulation. */
+static double dot(const void *w, int act, int64_t off, const double *v, int n) {
+  double s = 0.0;
+  if (act == OR_BF16) {
+    const uint16_t *p = (const uint16_t *)w + off;
+    for (int i = 0; i < n; ++i) s += or_bf16_to_double(p[i]) * v[i];
+  } else {
+    const float *p = (const float *)w + off;
+    for (int i = 0; i < n; ++i) s += (double)p[i] * v[i];
+  }
+  return s;
+}
+
+/* ------------------------------------------------------------ routing */
+
+/* Rank by repeatedly taking the largest remaining score; on equal scores the
+ * earlier (lower) expert id is taken first. Writes the first n_pick ids. */
+static void rank_top(const double *score, int E, int n_pick, int *taken, int32_t *out) {
+  for (int e = 0; e < E; ++e) taken[e] = 0;
+  for (int r = 0; r < n_pick; ++r) {
+    int best = -1;
+    for (int e = 0; e < E; ++e)
+      if (!taken[e] && (best < 0 || score[e] > score[best])) best = e;
+    taken[best] = 1;
+    out[r] = best;
+  }
+}
+
+/* Route one token (Math. Reference Part 3, 13.2; moe-from-scratch router;
+ * StableLatentMoE "FP32 router and training-only QB update").
+ * xv: the token's d inputs. Outputs idx[K], g[K], *gap, top[K+1] (may be NULL).
+ * If force_idx is given, it replaces the selection (weights still computed
+ * from this token's scores). */
+static void route_one(const or_layer *L, const or_tensors *W, const double *xv,
+                      const int32_t *force_idx, int32_t *idx, double *g, double *gap,
+                      double *top) {
+  const int E = L->E, K = L->K, d = L->d;
+  double *r = (double *)malloc(sizeof(double) * (size_t)E * 3);
+  double *rank_score = r + E, *raw = r + 2 * E;
+  int *taken = (int *)malloc(sizeof(int) * (size_t)E);
+  int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+  for (int e = 0; e < E; ++e) {
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) s += (double)W->w_router[(int64_t)e * d + i] * xv[i];
+    r[e] = s;
+  }
+  if (L->route == OR_ROUTE_SIGMOID_BIAS) {
+    for (int e = 0; e < E; ++e) {
+      raw[e] = or_sigmoid(r[e]);
+      rank_score[e] = raw[e] + (W->bias ? (double)W->bias[e] : 0.0);
+    }
+  } else {
+    for (int e = 0; e < E; ++e) rank_score[e] = r[e] + (W->bias ? (double)W->bias[e] : 0.0);
+    if (L->route == OR_ROUTE_SOFTMAX_TOPK) {
+      double m = rank_score[0], z = 0.0;
+      for (int e = 1; e < E; ++e) m = rank_score[e] > m ? rank_score[e] : m;
+      for (int e = 0; e < E; ++e) { rank_score[e] = exp(rank_score[e] - m); z += rank_score[e]; }
+      for (int e = 0; e < E; ++e) rank_score[e] /= z;
+    }
+  }
+  const int n_pick = K + 1 <= E ? K + 1 : E;
+  rank_top(rank_score, E, n_pick, taken, sel);
+  if (gap) *gap = (K < E) ? rank_score[sel[K - 1]] - rank_score[sel[K]] : INFINITY;
+  if (top)
+    for (int r2 = 0; r2 <= K; ++r2) top[r2] = r2 < n_pick ? rank_score[sel[r2]] : -INFINITY;
+  if (force_idx)
+    for (int k = 0; k < K; ++k) sel[k] = force_idx[k];
+  for (int k = 0; k < K; ++k) idx[k] = sel[k];
+
+  if (L->route == OR_ROUTE_TOPK_SOFTMAX) {
+    /* softmax over the K selected biased logits */
+    double m = rank_score[sel[0]], z = 0.0;
+    for (int k = 1; k < K; ++k) m = rank_score[sel[k]] > m ? rank_score[sel[k]] : m;
+    for (int k = 0; k < K; ++k) { g[k] = exp(rank_score[sel[k]] - m); z += g[k]; }
+    for (int k = 0; k < K; ++k) g[k] /= z;
+  } else if (L->route == OR_ROUTE_SOFTMAX_TOPK) {
+    /* probabilities of the selected experts, divided by their sum */
+    double z = 0.0;
+    for (int k = 0; k < K; ++k) { g[k] = rank_score[sel[k]]; z += g[k]; }
+    for (int k = 0; k < K; ++k) g[k] /= z;
+  } else {
+    /* uncorrected sigmoid scores; renormalised only on request */
+    double z = 0.0;
+    for (int k = 0; k < K; ++k) { g[k] = raw[sel[k]]; z += g[k]; }
+    if (L->renormalize)
+      for (int k = 0; k < K; ++k) g[k] /= z;
+  }
+  for (int k = 0; k < K; ++k) g[k] *= L->routed_scale;
+  free(sel);
+  free(taken);
+  free(r);
+}
+
+static void load_row(const void *x, int act, int64_t row, int n, double *out) {
+  for (int i = 0; i < n; ++i) out[i] = ld(x, act, row * (int64_t)n + i);
+}
+
+static int check_layer(const or_layer *L) {
+  if (!L || L->T < 0 || L->d <= 0 || L->E <= 0 || L->K <= 0 || L->K > L->E) return -2;
+  if (L->route < 0 || L->route > 2 || (L->act != OR_F32 && L->act != OR_BF16)) return -3;
+  return 0;
+}
+
+int or_route(const or_layer *L, const or_tensors *W, const int64_t *tokens, int64_t n,
+             int32_t *idx, double *g, double *gap, double *top_scores) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < n; ++j) {
+    double *xv = (double *)malloc(sizeof(double) * (size_t)L->d);
+    load_row(W->x, L->act, tokens ? tokens[j] : j, L->d, xv);
+    route_one(L, W, xv, NULL, idx + j * L->K, g + j * L->K, gap ? gap + j : NULL,
+              top_scores ? top_scores + j * (L->K + 1) : NULL);
+    free(xv);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------ SwiGLU */
+
+/* y += scale * W_down (SiLU(W_gate v) * (W_up v))   (Math. Reference Part 3,
+ * 12.2), one expert, weights stored out x in: gate/up [f, n], down [n, f]. */
+static void swiglu_acc(const void *wg, const void *wu, const void *wd, int act,
+                       int64_t base_gu, int64_t base_d, int n, int f, const double *v,
+                       double scale, double *y, double *h) {
+  for (int j = 0; j < f; ++j) {
+    double a = dot(wg, act, base_gu + (int64_t)j * n, v, n);
+    double u = dot(wu, act, base_gu + (int64_t)j * n, v, n);
+    h[j] = or_silu(a) * u;
+  }
+  for (int i = 0; i < n; ++i) y[i] += scale * dot(wd, act, base_d + (int64_t)i * f, h, f);
+}
+
+/* Whole layer for one token, fp64 (Math. Reference Part 3, 13.2; latent
+ * variant per StableLatentMoE "Return to model width"). */
+static void forward_one(const or_layer *L, const or_tensors *W, int64_t t,
+                        const int32_t *force_idx, double *y, int32_t *idx, double *g,
+                        double *gap) {
+  const int d = L->d, f = L->d_ff, K = L->K;
+  const int de = L->latent ? L->latent : d;
+  int hmax = f > L->d_shared ? f : L->d_shared;
+  double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+  double *zv = (double *)malloc(sizeof(double) * (size_t)de);
+  double *rv = (double *)calloc((size_t)de, sizeof(double));
+  double *h = (double *)malloc(sizeof(double) * (size_t)(hmax > 0 ? hmax : 1));
+  load_row(W->x, L->act, t, d, xv);
+  route_one(L, W, xv, force_idx, idx, g, gap, NULL);
+
+  /* routed input: x itself, or its latent projection z = W_lat_down x */
+  if (L->latent)
+    for (int l = 0; l < de; ++l) zv[l] = dot(W->w_lat_down, L->act, (int64_t)l * d, xv, d);
+  else
+    memcpy(zv, xv, sizeof(double) * (size_t)d);
+
+  for (int k = 0; k < K; ++k) {
+    const int64_t e = idx[k];
+    swiglu_acc(W->w_gate, W->w_up, W->w_down, L->act, e * (int64_t)f * de,
+               e * (int64_t)de * f, de, f, zv, g[k], rv, h);
+  }
+
+  for (int i = 0; i < d; ++i) y[i] = 0.0;
+  if (L->latent) {
+    if (L->has_rmsnorm) {
+      double ms = 0.0;
+      for (int l = 0; l < de; ++l) ms += rv[l] * rv[l];
+      ms /= de;
+      const double inv = 1.0 / sqrt(ms + L->rms_eps);
+      for (int l = 0; l < de; ++l)
+        rv[l] = rv[l] * inv * (W->rms_gamma ? (double)W->rms_gamma[l] : 1.0);
+    }
+    for (int i = 0; i < d; ++i) y[i] = dot(W->w_lat_up, L->act, (int64_t)i * de, rv, de);
+  } else {
+    for (int i = 0; i < d; ++i) y[i] = rv[i];
+  }
+  if (L->d_shared > 0)
+    swiglu_acc(W->ws_gate, W->ws_up, W->ws_down, L->act, 0, 0, d, L->d_shared, xv, 1.0, y, h);
+  free(h);
+  free(rv);
+  free(zv);
+  free(xv);
+}
+
+int or_forward(const or_layer *L, const or_tensors *W, const int64_t *tokens, int64_t n,
+               const int32_t *idx_override, double *out, int32_t *idx, double *g,
+               double *gap) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t j = 0; j < n; ++j) {
+    forward_one(L, W, tokens ? tokens[j] : j, idx_override ? idx_override + j * L->K : NULL,
+                out + j * L->d, idx + j * L->K, g + j * L->K, gap ? gap + j : NULL);
+  }
+  return 0;
+}
+
+/* Expert FFN on given rows: out[p] = scale[p] * FFN_{expert[p]}(rows[p]), at
+ * the routed width d_e. Used to check the grouped expert stage alone. */
+int or_expert_rows(const or_layer *L, const or_tensors *W, const void *rows,
+                   const int32_t *expert, const float *scale, int64_t n, double *out) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  const int f = L->d_ff, de = L->latent ? L->latent : L->d;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t p = 0; p < n; ++p) {
+    double *v = (double *)malloc(sizeof(double) * (size_t)de);
+    double *h = (double *)malloc(sizeof(double) * (size_t)f);
+    load_row(rows, L->act, p, de, v);
+    for (int i = 0; i < de; ++i) out[p * de + i] = 0.0;
+    const int64_t e = expert[p];
+    swiglu_acc(W->w_gate, W->w_up, W->w_down, L->act, e * (int64_t)f * de,
+               e * (int64_t)de * f, de, f, v, scale ? (double)scale[p] : 1.0, out + p * de, h);
+    free(h);
+    free(v);
+  }
+  return 0;
+}
+
+/* Combine for given tokens: out[t] = shared(x_t) + routed(t), where the routed
+ * part is sum_k y_rows[inv[t*K + k]] (fixed expert-slot order), passed through
+ * the latent RMSNorm and up-projection when the layer is latent. y_rows is
+ * [T*K, d_e] in y_dtype (OR_F32, OR_BF16 or OR_F64). */
+int or_combine(const or_layer *L, const or_tensors *W, const void *y_rows, int y_dtype,
+               const int32_t *inv, const int64_t *tokens, int64_t n, double *out) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  const int d = L->d, K = L->K, de = L->latent ? L->latent : d;
+  const int hs = L->d_shared > 0 ? L->d_shared : 1;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t t = tokens ? tokens[j] : j;
+    double *rv = (double *)calloc((size_t)de, sizeof(double));
+    double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *h = (double *)malloc(sizeof(double) * (size_t)hs);
+    double *y = out + j * d;
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = inv[t * K + k];
+      for (int l = 0; l < de; ++l) rv[l] += ld(y_rows, y_dtype, p * de + l);
+    }
+    if (L->latent) {
+      if (L->has_rmsnorm) {
+        double ms = 0.0;
+        for (int l = 0; l < de; ++l) ms += rv[l] * rv[l];
+        ms /= de;
+        const double s = 1.0 / sqrt(ms + L->rms_eps);
+        for (int l = 0; l < de; ++l) rv[l] = rv[l] * s * (W->rms_gamma ? (double)W->rms_gamma[l] : 1.0);
+      }
+      for (int i = 0; i < d; ++i) y[i] = dot(W->w_lat_up, L->act, (int64_t)i * de, rv, de);
+    } else {
+      for (int i = 0; i < d; ++i) y[i] = rv[i];
+    }
+    if (L->d_shared > 0) {
+      load_row(W->x, L->act, t, d, xv);
+      swiglu_acc(W->ws_gate, W->ws_up, W->ws_down, L->act, 0, 0, d, L->d_shared, xv, 1.0, y, h);
+    }
+    free(h);
+    free(xv);
+    free(rv);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------ dispatch */
+
+/* Stable counting sort of the T*K (token, slot) assignments by expert id
+ * (StableLatentMoE, "Dispatch is a stable permutation"): counts per expert,
+ * exclusive offsets (offsets[E] = T*K), then each slot in increasing t*K + k
+ * order is placed at offsets[e] + (number of earlier slots with expert e).
+ * perm[pos] = t*K + k, sorted_token[pos] = t, inv[t*K + k] = pos,
+ * sorted_w[pos] = g[t*K + k]. Any output pointer except counts may be NULL. */
+int or_dispatch(int64_t T, int32_t K, int32_t E, const int32_t *idx, const float *g,
+                int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *sorted_token,
+                int32_t *inv, float *sorted_w) {
+  if (T < 0 || K <= 0 || E <= 0 || !counts) return -1;
+  const int64_t n = T * K;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t s = 0; s < n; ++s) {
+    if (idx[s] < 0 || idx[s] >= E) return -2;
+    counts[idx[s]]++;
+  }
+  int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  next[0] = 0;
+  for (int e = 0; e < E; ++e) next[e + 1] = next[e] + counts[e];
+  if (offsets)
+    for (int e = 0; e <= E; ++e) offsets[e] = next[e];
+  for (int64_t s = 0; s < n; ++s) {
+    const int32_t pos = next[idx[s]]++;
+    if (perm) perm[pos] = (int32_t)s;
+    if (sorted_token) sorted_token[pos] = (int32_t)(s / K);
+    if (inv) inv[s] = pos;
+    if (sorted_w && g) sorted_w[pos] = g[s];
+  }
+  free(next);
+  return 0;
+}
