@@ -1,0 +1,234 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Mixture-of-Experts SwiGLU
+ * feed-forward forward pass (libmoe.so).
+ *
+ * The layer (APEX-1 Mathematical Reference - Part 3, section 13.2):
+ *
+ *   MoE(x) = sum_s Expert_s(x)  +  sum_k g_k * Expert_{e_k}(x)
+ *            (shared, always on)   (routed, top-K selected)
+ *
+ *   Expert(x) = W_down (SiLU(W_gate x) * (W_up x))        (section 12.2)
+ *
+ * computed as: fp32 router -> top-K and weights -> stable sorted dispatch of
+ * the T*K (token, slot) assignments by expert -> grouped SwiGLU GEMMs over
+ * contiguous expert slices -> atomic-free combine through the inverse
+ * permutation, plus the shared experts.
+ *
+ * Conventions that hold for every entry point:
+ *  - Pointers to tensors are DEVICE pointers to caller-owned memory. The
+ *    library never allocates, frees or keeps a pointer after it returns.
+ *    Descriptor structs are host memory, read during the call only.
+ *  - Matrices are row-major and dense. Weights are stored "out x in", as a
+ *    linear layer stores them: W_gate[e] is [d_ff, d_e], so W_gate x is a
+ *    product with the transpose of the page's d x d_ff matrix.
+ *  - act_dtype (MOE_F32 or MOE_BF16) is the type of x, of every expert,
+ *    shared and latent weight, of the routed rows and of out. The router
+ *    weight, the balance bias, the routing weights g and the RMSNorm gain
+ *    are always fp32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream). No call synchronises with the host: outputs are valid once
+ *    the stream has reached that point.
+ *  - Return value: MOE_OK, or a negative moe_status. Arguments are checked
+ *    on the host before anything is launched; a failed check launches
+ *    nothing. MOE_ERR_HIP reports a launch failure.
+ *  - T = 0 is valid and launches nothing. Experts that receive no tokens
+ *    cost nothing (APEX-1 docs "10 - Mixture of Experts", BUG-08: an expert
+ *    may get 0, 1 or many tokens).
+ *  - Inputs must be finite; NaN / Inf behaviour is unspecified.
+ *  - The library has no mutable global state; calls on different streams
+ *    with disjoint outputs and workspaces may run concurrently.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,      /* a required pointer is NULL                      */
+  MOE_ERR_SHAPE = -2,     /* T < 0, a width <= 0 or not a multiple of 8,
+                             K < 1, K > E, K > 16, E > 1024, or a size that
+                             overflows the 32-bit row indices               */
+  MOE_ERR_MODE = -3,      /* unknown dtype / route mode, or a mode
+                             combination this layer does not define         */
+  MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_workspace_size()     */
+  MOE_ERR_HIP = -5        /* a kernel launch failed                          */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Router rules.
+ * MOE_ROUTE_TOPK_SOFTMAX (APEX-1 Math. Reference Part 3, 13.2):
+ *   r = x W_router^T + b; pick the K largest r; g = softmax over those K.
+ * MOE_ROUTE_SOFTMAX_TOPK ("A working MoE layer in PyTorch", the MoELayer
+ *   forward): p = softmax(x W_router^T + b) over all E in fp32; pick the K
+ *   largest p; g = p / (sum of the K picked). Equal to the rule above in
+ *   exact arithmetic; gap and top scores are reported in probability space.
+ * MOE_ROUTE_SIGMOID_BIAS ("StableLatentMoE and QuantileBalancer", section
+ *   "FP32 router and training-only QB update" and "Flatten routing and
+ *   recover original token order"): s = sigmoid(x W_router^T); c = s + b;
+ *   pick the top K+1 of c and drop the last; g = s of the K picked (the
+ *   uncorrected scores), divided by their sum only if renormalize is set.
+ * In every rule g is finally multiplied by routed_scale. Equal scores rank
+ * the lower expert id first; slots are ordered by descending score. */
+typedef enum moe_route_mode {
+  MOE_ROUTE_TOPK_SOFTMAX = 0,
+  MOE_ROUTE_SOFTMAX_TOPK = 1,
+  MOE_ROUTE_SIGMOID_BIAS = 2
+} moe_route_mode;
+
+/* Shape and mode of one layer. d_e = latent ? latent : d_model is the width
+ * the routed experts run at. */
+typedef struct moe_desc {
+  int64_t T;           /* tokens (batch x sequence, flattened)               */
+  int32_t d_model;     /* d (M for the latent layer)                         */
+  int32_t d_ff;        /* per-expert intermediate width (I for latent)        */
+  int32_t n_experts;   /* E, 1..1024                                          */
+  int32_t top_k;       /* K, 1..min(E, 16)                                    */
+  int32_t d_shared;    /* n_shared x shared width (shared FFNs concatenated
+                          along the intermediate axis), 0 = no shared expert  */
+  int32_t latent;      /* 0, or L: routed path runs at width L between a
+                          down-projection M->L and an up-projection L->M
+                          ("StableLatentMoE", "Construction separates shared
+                          and routed capacities")                             */
+  int32_t act_dtype;   /* moe_dtype                                           */
+  int32_t route_mode;  /* moe_route_mode                                      */
+  int32_t renormalize; /* MOE_ROUTE_SIGMOID_BIAS only: 1 = divide g by sum    */
+  int32_t has_rmsnorm; /* latent only: RMSNorm of the routed sum in L          */
+  float routed_scale;  /* multiplies every g (1.0 when unused)                */
+  float rms_eps;       /* RMSNorm: R / sqrt(mean(R^2) + eps) * gamma          */
+} moe_desc;
+
+/* Weights of one layer (device pointers, caller-owned). */
+typedef struct moe_weights {
+  const float *w_router;  /* [E, d_model] fp32                                */
+  const float *bias;      /* [E] fp32 balance bias, or NULL for zeros          */
+  const void *w_gate;     /* [E, d_ff, d_e]  act                               */
+  const void *w_up;       /* [E, d_ff, d_e]  act                               */
+  const void *w_down;     /* [E, d_e, d_ff]  act                               */
+  const void *ws_gate;    /* [d_shared, d_model] act (NULL if d_shared == 0)   */
+  const void *ws_up;      /* [d_shared, d_model] act                           */
+  const void *ws_down;    /* [d_model, d_shared] act                           */
+  const void *w_lat_down; /* [L, d_model] act (latent only)                    */
+  const void *w_lat_up;   /* [d_model, L] act (latent only)                    */
+  const float *rms_gamma; /* [L] fp32, or NULL for ones (latent + rmsnorm)     */
+} moe_weights;
+
+/* Optional timing probe for moe_forward: if stage >= 0, ev_begin and ev_end
+ * (hipEvent_t, created by the caller) are recorded on the stream right
+ * before the first and right after the last kernel of that stage. */
+typedef enum moe_stage {
+  MOE_STAGE_ROUTE = 0,         /* router GEMM + selection + weights          */
+  MOE_STAGE_DISPATCH = 1,      /* histogram, scan, stable scatter            */
+  MOE_STAGE_LATENT_DOWN = 2,   /* z = x W_lat_down^T (latent only)           */
+  MOE_STAGE_EXPERT_GATE_UP = 3,/* grouped GEMM 1 with SiLU(gate) * up        */
+  MOE_STAGE_EXPERT_DOWN = 4,   /* grouped GEMM 2 times the routing weight    */
+  MOE_STAGE_SHARED_GATE_UP = 5,/* shared SwiGLU, first GEMM                  */
+  MOE_STAGE_COMBINE = 6,       /* shared down GEMM + routed combine (or the
+                                  latent combine, RMSNorm and up-projection) */
+  MOE_STAGE_COUNT = 7
+} moe_stage;
+
+typedef struct moe_probe {
+  int32_t stage;   /* moe_stage, or -1 for none */
+  void *ev_begin;  /* hipEvent_t */
+  void *ev_end;    /* hipEvent_t */
+} moe_probe;
+
+/* Text of a status code (static storage). */
+MOE_API const char *moe_strerror(int status);
+
+/* Name of a moe_stage (static storage), or "?" for an unknown value. */
+MOE_API const char *moe_stage_name(int stage);
+
+/* Device workspace, in bytes, that moe_forward needs for this layer
+ * (moe_dispatch, moe_expert_ffn and moe_combine need no more than this).
+ * Writes *bytes; returns MOE_OK or a shape/mode error. */
+MOE_API int moe_workspace_size(const moe_desc *desc, size_t *bytes);
+
+/* Router (Math. Reference Part 3, 13.2 "Router" and "Top-K selection";
+ * the three rules of moe_route_mode). For every token t:
+ *   idx[t*K + k]  int32, expert of slot k (descending ranking score)
+ *   g[t*K + k]    fp32 routing weight
+ *   gap[t]        fp32, K-th minus (K+1)-th ranking score (+inf if K == E);
+ *                 NULL to skip
+ *   top_scores[t*(K+1) + r]  fp32, the K+1 largest ranking scores (the
+ *                 (K+1)-th is -inf if K == E); NULL to skip. For the sigmoid
+ *                 rule these are the bias-corrected scores whose last entry
+ *                 is each token's balancing threshold ("QuantileBalancer").
+ * The router GEMM is fp32 whatever act_dtype is ("StableLatentMoE", FP32
+ * router with autocast disabled). x is [T, d_model] act. */
+MOE_API int moe_route(const moe_desc *desc, const moe_weights *w, const void *x, int32_t *idx,
+              float *g, float *gap, float *top_scores, void *stream);
+
+/* Sorted dispatch ("StableLatentMoE and QuantileBalancer", section "Dispatch
+ * is a stable permutation, not token duplication in model state"): the T*K
+ * assignments idx (as moe_route writes them) are sorted by expert id,
+ * stably in t*K + k order:
+ *   counts[e]          int32 [E], assignments of expert e
+ *   offsets[e]         int32 [E+1], exclusive prefix sum (offsets[E] = T*K)
+ *   perm[p]            int32 [T*K], flat slot t*K + k at sorted position p
+ *   sorted_token[p]    int32 [T*K], = perm[p] / K
+ *   inv[t*K + k]       int32 [T*K], sorted position of slot (t, k)
+ *   sorted_w[p]        fp32 [T*K], g[perm[p]] (NULL to skip; g may then be
+ *                      NULL)
+ *   rows_sorted[p, :]  act [T*K, d_e], = rows[sorted_token[p], :] (NULL to
+ *                      skip; rows may then be NULL). rows is x, or the latent
+ *                      z = x W_lat_down^T for a latent layer.
+ * Expert ids outside [0, E) are a caller error: such slots are dropped from
+ * every output (no out-of-bounds access), leaving those outputs incomplete.
+ * ws must hold moe_workspace_size() bytes. */
+MOE_API int moe_dispatch(const moe_desc *desc, const int32_t *idx, const float *g, const void *rows,
+                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *sorted_token,
+                 int32_t *inv, float *sorted_w, void *rows_sorted, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Grouped expert SwiGLU over contiguous expert slices (Math. Reference
+ * Part 3, 12.2; "StableLatentMoE", "The actual grouped GEMM"; "A working MoE
+ * layer in PyTorch", per-expert contiguous slices). For every sorted
+ * position p in [offsets[e], offsets[e+1]):
+ *   y_sorted[p, :] = row_scale[p] * W_down[e] (SiLU(W_gate[e] a_p) * (W_up[e] a_p))
+ * with a_p = rows[row_index[p], :] if row_index is given (the gather is
+ * fused into the GEMM's operand load), else rows[p, :]. rows is act
+ * [*, d_e]; row_scale fp32 [T*K] or NULL for 1; y_sorted act [T*K, d_e].
+ * The intermediate SiLU(gate) * up is rounded to act_dtype. */
+MOE_API int moe_expert_ffn(const moe_desc *desc, const moe_weights *w, const void *rows,
+                   const int32_t *row_index, const int32_t *offsets, const float *row_scale,
+                   void *y_sorted, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine + shared experts (Math. Reference Part 3, 13.2; "StableLatentMoE",
+ * "Return to model width"). For every token t, with R_t = sum over k = 0..K-1
+ * (in that order, fp32) of y_sorted[inv[t*K + k], :]:
+ *   out[t, :] = Shared(x_t) + R_t                                (latent = 0)
+ *   out[t, :] = Shared(x_t) + W_lat_up RMSNorm(R_t)              (latent)
+ * Shared is the SwiGLU FFN of width d_shared (absent if 0). No atomics: each
+ * output row is written once. x [T, d_model] act; y_sorted act [T*K, d_e];
+ * out act [T, d_model]. */
+MOE_API int moe_combine(const moe_desc *desc, const moe_weights *w, const void *x, const void *y_sorted,
+                const int32_t *inv, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole forward pass: route, dispatch, (latent down-projection), grouped
+ * expert SwiGLU, shared experts and combine. out act [T, d_model].
+ * counts: int32 [E] expert loads, or NULL.
+ * n_near_ties: int32 [1], number of tokens whose K-th and (K+1)-th ranking
+ *   scores (as this call computed them) differ by less than 1e-5, or NULL.
+ * probe: optional timing probe, or NULL. */
+MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *x, void *out,
+                int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
+                const moe_probe *probe, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,483 @@
+// C ABI of libmoe.so: argument checks, workspace layout and the launch
+// sequence of each entry point. Every step of the layer runs in this
+// library's HIP kernels; the host only validates and enqueues.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr float kTieEps = 1e-5f;
+constexpr int kMaxLatent = 16384;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+  size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, ntie;
+  size_t z, h, y, hsh, r;
+  size_t total;
+  int64_t max_tiles;
+};
+
+int64_t grouped_tile_bound(int64_t rows, int64_t E, int bm) {
+  return rows / bm + (rows < E ? rows : E) + 1;
+}
+
+Layout layout_of(const moe_desc *d) {
+  Layout L{};
+  const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
+  const size_t es = d->act_dtype == MOE_BF16 ? 2 : 4;
+  const int64_t de = d->latent ? d->latent : d->d_model;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.idx = take(rows * 4);
+  L.g = take(rows * 4);
+  L.gap = take(T * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.chunk = take(static_cast<size_t>(n_chunks(rows)) * E * 4);
+  L.perm = take(rows * 4);
+  L.stok = take(rows * 4);
+  L.inv = take(rows * 4);
+  L.sw = take(rows * 4);
+  L.max_tiles = grouped_tile_bound(rows, E, 16);  // smallest tile height in use
+  L.tiles = take(static_cast<size_t>(L.max_tiles) * 12);
+  L.ntiles = take(4);
+  L.ntie = take(4);
+  L.z = d->latent ? take(T * d->latent * es) : 0;
+  L.h = take(rows * d->d_ff * es);
+  L.y = take(rows * de * es);
+  L.hsh = d->d_shared ? take(T * d->d_shared * es) : 0;
+  L.r = d->latent ? take(T * d->latent * es) : 0;
+  L.total = o;
+  return L;
+}
+
+int check_desc(const moe_desc *d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_MODE;
+  if (d->route_mode < MOE_ROUTE_TOPK_SOFTMAX || d->route_mode > MOE_ROUTE_SIGMOID_BIAS)
+    return MOE_ERR_MODE;
+  if (d->has_rmsnorm && !d->latent) return MOE_ERR_MODE;
+  if (d->T < 0 || d->d_model <= 0 || d->d_ff <= 0 || d->n_experts < 1 || d->n_experts > 1024)
+    return MOE_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return MOE_ERR_SHAPE;
+  if (d->d_shared < 0 || d->latent < 0 || d->latent > kMaxLatent) return MOE_ERR_SHAPE;
+  if (d->d_model % 8 || d->d_ff % 8 || d->d_shared % 8 || d->latent % 8) return MOE_ERR_SHAPE;
+  if (d->T * static_cast<int64_t>(d->top_k) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int pick_grouped(int64_t rows, int64_t E) {
+  return rows <= 32 * E ? TILE_SMALL_M : TILE_LARGE;  // about 32 rows per expert or fewer
+}
+int pick_dense(int64_t M) { return M <= 64 ? TILE_SMALL_M : TILE_LARGE; }
+
+struct Probe {
+  const moe_probe *p;
+  hipStream_t s;
+  void begin(int stage) const {
+    if (p && p->stage == stage) hipEventRecord(static_cast<hipEvent_t>(p->ev_begin), s);
+  }
+  void end(int stage) const {
+    if (p && p->stage == stage) hipEventRecord(static_cast<hipEvent_t>(p->ev_end), s);
+  }
+};
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// Grouped SwiGLU over the sorted rows: GEMM 1 (gate/up + SiLU*up) into h,
+// GEMM 2 (down, times row_scale) into y.
+int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
+                 const int32_t *row_index, const int32_t *tiles, const int32_t *n_tiles, int cfg,
+                 const float *row_scale, void *h, void *y, const Probe &pr, hipStream_t s) {
+  const int64_t rows_n = d->T * d->top_k;
+  const int de = d->latent ? d->latent : d->d_model;
+  const int bf = d->act_dtype == MOE_BF16;
+  GemmArgs a{};
+  a.a = rows;
+  a.lda = de;
+  a.a_rows = row_index;
+  a.b0 = w->w_gate;
+  a.b1 = w->w_up;
+  a.ldb = de;
+  a.b_stride = static_cast<int64_t>(d->d_ff) * de;
+  a.K = de;
+  a.N = d->d_ff;
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, tile_bm(cfg));
+  a.out = h;
+  a.ldo = d->d_ff;
+  pr.begin(MOE_STAGE_EXPERT_GATE_UP);
+  MOE_TRY(launch_gemm(a, EPI_SWIGLU, cfg, bf, s));
+  pr.end(MOE_STAGE_EXPERT_GATE_UP);
+
+  GemmArgs b{};
+  b.a = h;
+  b.lda = d->d_ff;
+  b.b0 = w->w_down;
+  b.ldb = d->d_ff;
+  b.b_stride = static_cast<int64_t>(de) * d->d_ff;
+  b.K = d->d_ff;
+  b.N = de;
+  b.tiles = tiles;
+  b.n_tiles = n_tiles;
+  b.max_mtiles = a.max_mtiles;
+  b.out = y;
+  b.ldo = de;
+  b.row_scale = row_scale;
+  pr.begin(MOE_STAGE_EXPERT_DOWN);
+  MOE_TRY(launch_gemm(b, EPI_SCALE, cfg, bf, s));
+  pr.end(MOE_STAGE_EXPERT_DOWN);
+  return MOE_OK;
+}
+
+// Shared experts + combine (+ latent RMSNorm and up-projection) into out.
+int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const void *y,
+                   const int32_t *inv, void *out, char *ws, const Layout &L, const Probe &pr,
+                   hipStream_t s) {
+  const int64_t T = d->T;
+  const int bf = d->act_dtype == MOE_BF16;
+  const int dm = d->d_model;
+  const int cfg = pick_dense(T);
+  void *hsh = ws + L.hsh;
+  if (d->d_shared) {
+    GemmArgs a{};
+    a.a = x;
+    a.lda = dm;
+    a.b0 = w->ws_gate;
+    a.b1 = w->ws_up;
+    a.ldb = dm;
+    a.K = dm;
+    a.N = d->d_shared;
+    a.M = T;
+    a.out = hsh;
+    a.ldo = d->d_shared;
+    pr.begin(MOE_STAGE_SHARED_GATE_UP);
+    MOE_TRY(launch_gemm(a, EPI_SWIGLU, cfg, bf, s));
+    pr.end(MOE_STAGE_SHARED_GATE_UP);
+  }
+  pr.begin(MOE_STAGE_COMBINE);
+  if (!d->latent) {
+    if (d->d_shared) {
+      GemmArgs c{};
+      c.a = hsh;
+      c.lda = d->d_shared;
+      c.b0 = w->ws_down;
+      c.ldb = d->d_shared;
+      c.K = d->d_shared;
+      c.N = dm;
+      c.M = T;
+      c.out = out;
+      c.ldo = dm;
+      c.y = y;
+      c.ldy = dm;
+      c.inv = inv;
+      c.topk = d->top_k;
+      MOE_TRY(launch_gemm(c, EPI_COMBINE, cfg, bf, s));
+    } else {
+      MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, bf, s));
+    }
+  } else {
+    void *r = ws + L.r;
+    MOE_TRY(launch_combine_latent(y, inv, T, d->top_k, d->latent, d->has_rmsnorm, d->rms_eps,
+                                  w->rms_gamma, r, bf, s));
+    GemmArgs c{};
+    if (d->d_shared) {
+      c.a = hsh;
+      c.lda = d->d_shared;
+      c.b0 = w->ws_down;
+      c.ldb = d->d_shared;
+      c.K = d->d_shared;
+      c.a2 = r;
+      c.lda2 = d->latent;
+      c.b2 = w->w_lat_up;
+      c.ldb2 = d->latent;
+      c.K2 = d->latent;
+    } else {
+      c.a = r;
+      c.lda = d->latent;
+      c.b0 = w->w_lat_up;
+      c.ldb = d->latent;
+      c.K = d->latent;
+    }
+    c.N = dm;
+    c.M = T;
+    c.out = out;
+    c.ldo = dm;
+    MOE_TRY(launch_gemm(c, EPI_STORE, cfg, bf, s));
+  }
+  pr.end(MOE_STAGE_COMBINE);
+  return MOE_OK;
+}
+
+int check_expert_weights(const moe_desc *d, const moe_weights *w) {
+  if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+int check_combine_weights(const moe_desc *d, const moe_weights *w) {
+  if (!w) return MOE_ERR_NULL;
+  if (d->d_shared && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_NULL;
+  if (d->latent && !w->w_lat_up) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid shape";
+    case MOE_ERR_MODE: return "invalid dtype or mode combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char *moe_stage_name(int stage) {
+  static const char *names[MOE_STAGE_COUNT] = {"route", "dispatch", "latent_down",
+                                               "expert_gate_up", "expert_down",
+                                               "shared_gate_up", "combine"};
+  return (stage >= 0 && stage < MOE_STAGE_COUNT) ? names[stage] : "?";
+}
+
+int moe_workspace_size(const moe_desc *desc, size_t *bytes) {
+  const int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = layout_of(desc).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc *d, const moe_weights *w, const void *x, int32_t *idx, float *g,
+              float *gap, float *top_scores, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!w || !w->w_router || !idx || !g || (!x && d->T > 0)) return MOE_ERR_NULL;
+  RouterArgs a{};
+  a.x = x;
+  a.w = w->w_router;
+  a.bias = w->bias;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.E = d->n_experts;
+  a.K = d->top_k;
+  a.mode = d->route_mode;
+  a.renormalize = d->renormalize;
+  a.routed_scale = d->routed_scale;
+  a.idx = idx;
+  a.g = g;
+  a.gap = gap;
+  a.top = top_scores;
+  if (launch_router(a, d->act_dtype == MOE_BF16, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const void *rows,
+                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *sorted_token,
+                 int32_t *inv, float *sorted_w, void *rows_sorted, void *ws, size_t ws_bytes,
+                 void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!counts || !offsets || !perm || !sorted_token || !inv || !ws) return MOE_ERR_NULL;
+  if ((!idx && d->T > 0) || (sorted_w && !g) || (rows_sorted && !rows)) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *wsb = static_cast<char *>(ws);
+  const int64_t slots = d->T * d->top_k;
+  int32_t *chunk = reinterpret_cast<int32_t *>(wsb + L.chunk);
+  MOE_TRY(launch_hist(idx, slots, d->n_experts, chunk, s));
+  ScanArgs sa{};
+  sa.chunk_hist = chunk;
+  sa.chunk_base = chunk;
+  sa.slots = slots;
+  sa.E = d->n_experts;
+  sa.counts = counts;
+  sa.offsets = offsets;
+  MOE_TRY(launch_scan(sa, s));
+  ScatterArgs sc{};
+  sc.idx = idx;
+  sc.g = g;
+  sc.chunk_base = chunk;
+  sc.slots = slots;
+  sc.K = d->top_k;
+  sc.E = d->n_experts;
+  sc.perm = perm;
+  sc.sorted_token = sorted_token;
+  sc.inv = inv;
+  sc.sorted_w = sorted_w;
+  MOE_TRY(launch_scatter(sc, s));
+  if (rows_sorted) {
+    const int64_t de = d->latent ? d->latent : d->d_model;
+    const int64_t es = d->act_dtype == MOE_BF16 ? 2 : 4;
+    MOE_TRY(launch_gather(rows, sorted_token, slots, de * es, rows_sorted, s));
+  }
+  return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
+                   const int32_t *row_index, const int32_t *offsets, const float *row_scale,
+                   void *y_sorted, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_expert_weights(d, w))) return rc;
+  if (!offsets || !y_sorted || !ws || (!rows && d->T > 0)) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *wsb = static_cast<char *>(ws);
+  const int64_t rows_n = d->T * d->top_k;
+  const int cfg = pick_grouped(rows_n, d->n_experts);
+  int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
+  int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
+  MOE_TRY(launch_tiles(offsets, d->n_experts, tile_bm(cfg), tiles, nt, s));
+  const Probe pr{nullptr, s};
+  return expert_gemms(d, w, rows, row_index, tiles, nt, cfg, row_scale, wsb + L.h, y_sorted, pr,
+                      s);
+}
+
+int moe_combine(const moe_desc *d, const moe_weights *w, const void *x, const void *y_sorted,
+                const int32_t *inv, void *out, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if ((rc = check_combine_weights(d, w))) return rc;
+  if (d->T > 0 && (!y_sorted || !inv || !out || (d->d_shared && !x))) return MOE_ERR_NULL;
+  if (!ws) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Probe pr{nullptr, s};
+  return shared_combine(d, w, x, y_sorted, inv, out, static_cast<char *>(ws), L, pr, s);
+}
+
+int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *out,
+                int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
+                const moe_probe *probe, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!w || !w->w_router) return MOE_ERR_NULL;
+  if ((rc = check_expert_weights(d, w)) || (rc = check_combine_weights(d, w))) return rc;
+  if (d->latent && !w->w_lat_down) return MOE_ERR_NULL;
+  if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Probe pr{probe, s};
+  char *wsb = static_cast<char *>(ws);
+  const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
+  const int bf = d->act_dtype == MOE_BF16;
+  int32_t *idx = reinterpret_cast<int32_t *>(wsb + L.idx);
+  float *g = reinterpret_cast<float *>(wsb + L.g);
+  float *gap = reinterpret_cast<float *>(wsb + L.gap);
+  int32_t *cnt = counts ? counts : reinterpret_cast<int32_t *>(wsb + L.counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(wsb + L.offsets);
+  int32_t *chunk = reinterpret_cast<int32_t *>(wsb + L.chunk);
+  int32_t *perm = reinterpret_cast<int32_t *>(wsb + L.perm);
+  int32_t *stok = reinterpret_cast<int32_t *>(wsb + L.stok);
+  int32_t *inv = reinterpret_cast<int32_t *>(wsb + L.inv);
+  float *sw = reinterpret_cast<float *>(wsb + L.sw);
+  int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
+  int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
+  const int cfg = pick_grouped(rows, E);
+
+  // 1. router
+  RouterArgs ra{};
+  ra.x = x;
+  ra.w = w->w_router;
+  ra.bias = w->bias;
+  ra.T = T;
+  ra.d = d->d_model;
+  ra.E = static_cast<int>(E);
+  ra.K = static_cast<int>(K);
+  ra.mode = d->route_mode;
+  ra.renormalize = d->renormalize;
+  ra.routed_scale = d->routed_scale;
+  ra.idx = idx;
+  ra.g = g;
+  ra.gap = gap;
+  pr.begin(MOE_STAGE_ROUTE);
+  MOE_TRY(launch_router(ra, bf, s));
+  pr.end(MOE_STAGE_ROUTE);
+
+  // 2. dispatch (counts, offsets, tile table, stable positions)
+  pr.begin(MOE_STAGE_DISPATCH);
+  MOE_TRY(launch_hist(idx, rows, static_cast<int>(E), chunk, s));
+  ScanArgs sa{};
+  sa.chunk_hist = chunk;
+  sa.chunk_base = chunk;
+  sa.slots = rows;
+  sa.E = static_cast<int>(E);
+  sa.counts = cnt;
+  sa.offsets = offsets;
+  sa.bm = tile_bm(cfg);
+  sa.tiles = tiles;
+  sa.n_tiles = nt;
+  sa.gap = n_near_ties ? gap : nullptr;
+  sa.T = T;
+  sa.tie_eps = kTieEps;
+  sa.n_near_ties = n_near_ties;
+  MOE_TRY(launch_scan(sa, s));
+  ScatterArgs sc{};
+  sc.idx = idx;
+  sc.g = g;
+  sc.chunk_base = chunk;
+  sc.slots = rows;
+  sc.K = static_cast<int>(K);
+  sc.E = static_cast<int>(E);
+  sc.perm = perm;
+  sc.sorted_token = stok;
+  sc.inv = inv;
+  sc.sorted_w = sw;
+  MOE_TRY(launch_scatter(sc, s));
+  pr.end(MOE_STAGE_DISPATCH);
+  if (T == 0) return MOE_OK;
+
+  // 3. latent down-projection (routed rows are z = x W_lat_down^T)
+  const void *rsrc = x;
+  if (d->latent) {
+    GemmArgs a{};
+    a.a = x;
+    a.lda = d->d_model;
+    a.b0 = w->w_lat_down;
+    a.ldb = d->d_model;
+    a.K = d->d_model;
+    a.N = d->latent;
+    a.M = T;
+    a.out = wsb + L.z;
+    a.ldo = d->latent;
+    pr.begin(MOE_STAGE_LATENT_DOWN);
+    MOE_TRY(launch_gemm(a, EPI_STORE, pick_dense(T), bf, s));
+    pr.end(MOE_STAGE_LATENT_DOWN);
+    rsrc = wsb + L.z;
+  }
+
+  // 4. grouped expert SwiGLU (gather fused into GEMM 1's A load)
+  if ((rc = expert_gemms(d, w, rsrc, stok, tiles, nt, cfg, sw, wsb + L.h, wsb + L.y, pr, s)))
+    return rc;
+
+  // 5. shared experts + combine
+  return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
+}
+
+}  // extern "C"

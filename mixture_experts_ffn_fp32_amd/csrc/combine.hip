@@ -1,0 +1,125 @@
+// Atomic-free combine of the routed rows through the inverse permutation.
+//
+// APEX-1 Mathematical Reference - Part 3, 13.2: the routed part of token t is
+// sum_k g_k Expert_{e_k}(x_t). The grouped GEMM has already multiplied each
+// sorted row by its g, so token t's routed part is the sum of its K rows at
+// sorted positions inv[t*K + k] ("StableLatentMoE and QuantileBalancer": the
+// permutation is undone when contributions return to their token rows). Each
+// output row is produced by one workgroup, summing in fixed k order in fp32:
+// no atomics, and the result does not depend on scheduling.
+//
+// The latent variant ("StableLatentMoE", "Return to model width") then
+// applies RMSNorm in the latent width: R / sqrt(mean(R^2) + eps) * gamma.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_sum_kernel(const uint4 *__restrict__ y,
+                                                          const int32_t *__restrict__ inv, int K,
+                                                          int chunks, uint4 *__restrict__ out) {
+  constexpr int N = Chunk<T>::N;
+  const int64_t t = blockIdx.x;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int q = inv[t * K + k];
+      if (q < 0) continue;
+      float v[N];
+      Chunk<T>::unpack(y[static_cast<int64_t>(q) * chunks + c], v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    out[t * chunks + c] = Chunk<T>::pack(acc);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_latent_kernel(const uint4 *__restrict__ y,
+                                                             const int32_t *__restrict__ inv,
+                                                             int K, int chunks, int L,
+                                                             int has_rmsnorm, float eps,
+                                                             const float *__restrict__ gamma,
+                                                             uint4 *__restrict__ r) {
+  constexpr int N = Chunk<T>::N;
+  extern __shared__ float row[];  // [L]
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int q = inv[t * K + k];
+      if (q < 0) continue;
+      float v[N];
+      Chunk<T>::unpack(y[static_cast<int64_t>(q) * chunks + c], v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      row[c * N + i] = acc[i];
+      ss += acc[i] * acc[i];
+    }
+  }
+  float scale = 1.0f;
+  if (has_rmsnorm) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    scale = 1.0f / sqrtf(tot / static_cast<float>(L) + eps);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int l = c * N + i;
+      v[i] = has_rmsnorm ? row[l] * scale * (gamma ? gamma[l] : 1.0f) : row[l];
+    }
+    r[t * chunks + c] = Chunk<T>::pack(v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int K, int width,
+                              void *out, int act_bf16, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int chunks = width / (act_bf16 ? 8 : 4);
+  if (act_bf16)
+    combine_sum_kernel<bf16_t><<<static_cast<unsigned>(T), 256, 0, s>>>(
+        static_cast<const uint4 *>(y), inv, K, chunks, static_cast<uint4 *>(out));
+  else
+    combine_sum_kernel<float><<<static_cast<unsigned>(T), 256, 0, s>>>(
+        static_cast<const uint4 *>(y), inv, K, chunks, static_cast<uint4 *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, int K, int L,
+                                 int has_rmsnorm, float eps, const float *gamma, void *r,
+                                 int act_bf16, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int chunks = L / (act_bf16 ? 8 : 4);
+  const size_t shm = static_cast<size_t>(L) * sizeof(float);
+  if (act_bf16)
+    combine_latent_kernel<bf16_t><<<static_cast<unsigned>(T), 256, shm, s>>>(
+        static_cast<const uint4 *>(y), inv, K, chunks, L, has_rmsnorm, eps, gamma,
+        static_cast<uint4 *>(r));
+  else
+    combine_latent_kernel<float><<<static_cast<unsigned>(T), 256, shm, s>>>(
+        static_cast<const uint4 *>(y), inv, K, chunks, L, has_rmsnorm, eps, gamma,
+        static_cast<uint4 *>(r));
+  return hipGetLastError();
+}
+
+}  // namespace moe

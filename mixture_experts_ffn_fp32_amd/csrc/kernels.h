@@ -1,0 +1,119 @@
+// Internal launchers of libmoe.so. Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ router
+struct RouterArgs {
+  const void *x;         // [T, d] act
+  const float *w;        // [E, d]
+  const float *bias;     // [E] or null
+  int64_t T;
+  int d, E, K;
+  int mode;              // moe_route_mode
+  int renormalize;
+  float routed_scale;
+  int32_t *idx;          // [T, K]
+  float *g;              // [T, K]
+  float *gap;            // [T] or null
+  float *top;            // [T, K+1] or null
+};
+hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ dispatch
+// Slots per histogram / scatter chunk.
+constexpr int kChunkSlots = 4096;
+
+__host__ __device__ inline int64_t n_chunks(int64_t slots) { return (slots + kChunkSlots - 1) / kChunkSlots; }
+
+hipError_t launch_hist(const int32_t *idx, int64_t slots, int E, int32_t *chunk_hist,
+                       hipStream_t s);
+
+struct ScanArgs {
+  const int32_t *chunk_hist;  // [n_chunks, E] in; becomes absolute bases
+  int32_t *chunk_base;        // [n_chunks, E] out (may alias chunk_hist)
+  int64_t slots;
+  int E;
+  int32_t *counts;            // [E]
+  int32_t *offsets;           // [E+1]
+  // grouped GEMM m-tile table for tile height bm (tiles null -> skipped)
+  int bm;
+  int32_t *tiles;             // [max_tiles, 3] {expert, row_begin, row_end}
+  int32_t *n_tiles;           // [1]
+  // near-tie count of the router gap (gap null -> skipped)
+  const float *gap;
+  int64_t T;
+  float tie_eps;
+  int32_t *n_near_ties;
+};
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+
+// Tile table from existing offsets (for moe_expert_ffn).
+hipError_t launch_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles,
+                        int32_t *n_tiles, hipStream_t s);
+
+struct ScatterArgs {
+  const int32_t *idx;
+  const float *g;             // or null
+  const int32_t *chunk_base;  // [n_chunks, E] absolute
+  int64_t slots;
+  int K, E;
+  int32_t *perm, *sorted_token, *inv;
+  float *sorted_w;            // or null
+};
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+
+hipError_t launch_gather(const void *rows, const int32_t *sorted_token, int64_t n_rows,
+                         int64_t row_bytes, void *out, hipStream_t s);
+
+// ------------------------------------------------------------------ GEMM
+enum Epilogue { EPI_SWIGLU = 0, EPI_SCALE = 1, EPI_STORE = 2, EPI_COMBINE = 3 };
+
+// C = A B^T over one or two K segments, A [M, K] row-major (optionally row
+// gathered), B [N, K] row-major ("out x in" weights), grouped by expert via a
+// device tile table or dense.
+struct GemmArgs {
+  const void *a;
+  int64_t lda;
+  const int32_t *a_rows;     // gather: A row of tile row m is a_rows[m]
+  const void *b0;            // B (gate for SWIGLU)
+  const void *b1;            // up (SWIGLU only)
+  int64_t ldb;
+  int64_t b_stride;          // elements between experts' B matrices
+  int K;
+  const void *a2;            // second K segment (null: none)
+  int64_t lda2;
+  const void *b2;
+  int64_t ldb2;
+  int K2;
+  int64_t M;                 // rows (dense)
+  int N;                     // output columns
+  const int32_t *tiles;      // grouped tile table, or null (dense)
+  const int32_t *n_tiles;    // grouped: device count
+  int64_t max_mtiles;        // bound on m tiles (grid size)
+  void *out;
+  int64_t ldo;
+  const float *row_scale;    // SCALE (null -> 1)
+  const void *y;             // COMBINE: routed rows [T*K, ldy]
+  int64_t ldy;
+  const int32_t *inv;
+  int topk;
+};
+
+enum TileCfg { TILE_SMALL_M = 0, TILE_LARGE = 1 };
+int tile_bm(int cfg);
+hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ combine
+// out[t] = sum_k y[inv[t*K+k]] (no shared expert, model width).
+hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int K, int width,
+                              void *out, int act_bf16, hipStream_t s);
+// r[t] = RMSNorm(sum_k y[inv[t*K+k]]) * gamma (latent), or the plain sum.
+hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, int K, int L,
+                                 int has_rmsnorm, float eps, const float *gamma, void *r,
+                                 int act_bf16, hipStream_t s);
+
+}  // namespace moe

@@ -294,3 +294,11 @@ def as_f64(a: np.ndarray, act: str) -> np.ndarray:
     if a.dtype == np.uint16:
         return bf16_bits_to_f32(a).astype(np.float64)
     return a.astype(np.float64)
+
+
+def draw_rows(seed: int, shape, act: str, std: float = 1.0) -> np.ndarray:
+    """Extra seeded N(0, std) tensor (e.g. stand-in expert outputs for checking
+    a later stage alone), fp32 or bf16 bits."""
+    v = _rng(np.random.SeedSequence(seed)).standard_normal(int(np.prod(shape)), dtype=np.float32)
+    v = (v * np.float32(std)).reshape(shape)
+    return v if act == "f32" else f32_to_bf16_bits(v)

@@ -1,0 +1,36 @@
+"""GPU parity at the full sizes of the benchmark workloads, in the launch
+configuration the benchmark times: routing and dispatch on every token,
+layer outputs on a seeded token sample the oracle evaluates one by one."""
+import numpy as np
+import pytest
+
+import mixture_experts_ffn_fp32_amd as moe
+import moe_synth
+import oracle
+from _gpu import check_forward, check_route, layer_of, need_gpu, sample_tokens, say, torch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+SAMPLE = {"medium": 1024, "latent": 512, "large_decode": None, "large_prefill": 256}
+
+
+@pytest.mark.parametrize("name", ["medium", "latent", "large_decode", "large_prefill"])
+def test_full_size_workload(name):
+    need_gpu()
+    w = moe_synth.get(name)
+    say(f"case full {name}: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    orc = oracle.Oracle(w, a)
+    say(f"  {name}: route (all {w.T} tokens)")
+    r = check_route(w, a, layer, orc)
+    o_idx = r[0]
+    n = SAMPLE[name]
+    toks = None if n is None else sample_tokens(o_idx, w.E, n, seed=w.config_no)
+    say(f"  {name}: forward")
+    check_forward(w, a, layer, tokens=toks, orc=orc, o_route=r)
+    if name == "medium":
+        counts = np.bincount(o_idx.ravel(), minlength=w.E)
+        assert (counts == 0).sum() == moe_synth.ZIPF_EMPTY
+    del layer, a
+    torch.cuda.empty_cache()
