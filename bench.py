@@ -1,0 +1,184 @@
+"""Benchmark of the MoE SwiGLU feed-forward forward pass on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one moe_forward over one batch of synthetic tokens (router,
+dispatch, grouped expert SwiGLU, shared experts, combine), inputs resident
+in HBM. Prints ONE JSON line on stdout; details go to stderr.
+
+The dominant kernel (the grouped gate/up GEMM) is timed with HIP events
+recorded by the library around that launch on the launch stream, every
+timed step; its algorithmic flops (or bytes, for weight-streaming batches)
+per launch divided by the mean duration gives roofline.achieved.
+
+cpu_baseline: the CPU oracle timed on a bounded sample of the same tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec and achieved fraction of MFMA/HBM roofline, 1 GPU"
+PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X)
+HBM_GBS = 8000.0                        # HBM3E GB/s (MI355X)
+DEFAULT_WORKLOAD = "small"              # the second configuration of the layer
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, counts):
+    """Per-step algorithmic work of the layer and of the gate/up launch."""
+    es = 2 if w.act == "bf16" else 4
+    de, f, rows = w.d_e, w.d_ff, w.T * w.K
+    touched = int((counts > 0).sum())
+    fl_router = 2.0 * w.T * w.d * w.E
+    fl_routed = 6.0 * rows * de * f
+    fl_shared = 6.0 * w.T * w.d * w.d_shared
+    fl_latent = 4.0 * w.T * w.d * w.latent
+    bytes_w = (w.E * w.d * 4 + touched * 3 * de * f * es + 3 * w.d * w.d_shared * es
+               + 2 * w.d * w.latent * es)
+    bytes_act = 2 * w.T * w.d * es
+    gu_flops = 4.0 * rows * de * f
+    # gate/up launch: touched experts' gate+up weights, gathered rows in, h out
+    gu_bytes = touched * 2 * f * de * es + rows * de * es + rows * f * es
+    return dict(flops=fl_router + fl_routed + fl_shared + fl_latent, bytes=bytes_w + bytes_act,
+                gu_flops=gu_flops, gu_bytes=gu_bytes, touched=touched)
+
+
+def cpu_baseline(w, a, budget_s=12.0):
+    """Time the CPU oracle (as it stands) on a seeded token sample."""
+    import oracle
+    orc = oracle.Oracle(w, a)
+    rng = np.random.default_rng(7)
+    probe = rng.choice(w.T, size=min(w.T, 8), replace=False)
+    t0 = time.perf_counter()
+    orc.forward(tokens=probe)
+    per_tok = (time.perf_counter() - t0) / len(probe)
+    n = int(max(8, min(w.T, budget_s / max(per_tok, 1e-9))))
+    toks = np.sort(rng.choice(w.T, size=n, replace=False))
+    t0 = time.perf_counter()
+    orc.forward(tokens=toks)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.T} tokens (seeded), full layer per token in fp64, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "multi-GPU sharding is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_fp32_amd as moe
+    import moe_synth
+
+    w = moe_synth.get(args.workload)
+    log(f"workload {w.name}: T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K} "
+        f"shared={w.d_shared} latent={w.latent} act={w.act}")
+    t0 = time.perf_counter()
+    a = moe_synth.generate(w)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = moe.Layer(w, moe.to_device(a, dev), device=dev)
+    x = layer.dev["x"]
+    out = torch.empty((w.T, w.d), dtype=layer.act, device=dev)
+    counts = torch.zeros(w.E, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.forward(x, out, counts=counts)
+    torch.cuda.synchronize()
+
+    stage = moe.STAGES["expert_gate_up"]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for b, e in evs:  # materialise the events on the launch stream
+        b.record(stream)
+        e.record(stream)
+    probes = [moe.MoeProbe(stage=stage, ev_begin=b.cuda_event, ev_end=e.cuda_event)
+              for b, e in evs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layer.forward(x, out, counts=counts, probe=probes[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / args.steps * 1e3
+    gu_ms = float(np.mean([b.elapsed_time(e) for b, e in evs]))
+
+    cnt = counts.cpu().numpy()
+    alg = algorithmic(w, cnt)
+    tok_s = w.T / (ms / 1e3)
+    peak_tf = PEAK[w.act]
+    intensity = alg["gu_flops"] / alg["gu_bytes"]
+    ridge = peak_tf * 1e12 / (HBM_GBS * 1e9)
+    if intensity >= ridge:
+        ach = alg["gu_flops"] / (gu_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(ach / peak_tf, 4), "traffic": None}
+    else:
+        ach = alg["gu_bytes"] / (gu_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = "gemm_kernel (grouped gate/up + SiLU*up)"
+    roof["kernel_ms"] = round(gu_ms, 4)
+    log(f"step {ms:.4f} ms, {tok_s:.4g} tokens/s; gate/up kernel {gu_ms:.4f} ms; "
+        f"experts touched {alg['touched']}/{w.E}; loads max {cnt.max()} min {cnt.min()}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, a)
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.act,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "d_model": w.d, "d_ff": w.d_ff,
+                   "experts": w.E, "top_k": w.K, "shared_width": w.d_shared,
+                   "latent": w.latent, "route": w.route, "parallelism": "single-gpu"},
+        "layer": {"algorithmic_tflop": round(alg["flops"] / 1e12, 5),
+                  "tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
+                  "frac_of_mfma_peak": round(alg["flops"] / (ms / 1e3) / 1e12 / peak_tf, 4),
+                  "algorithmic_gb": round(alg["bytes"] / 1e9, 4),
+                  "gbs": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+                  "experts_touched": alg["touched"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -167,10 +167,14 @@ MOE_API int moe_workspace_size(const moe_desc *desc, size_t *bytes);
  *                 (K+1)-th is -inf if K == E); NULL to skip. For the sigmoid
  *                 rule these are the bias-corrected scores whose last entry
  *                 is each token's balancing threshold ("QuantileBalancer").
- * The router GEMM is fp32 whatever act_dtype is ("StableLatentMoE", FP32
- * router with autocast disabled). x is [T, d_model] act. */
+ * The router product x W_router^T is fp32 whatever act_dtype is
+ * ("StableLatentMoE", FP32 router with autocast disabled): for bf16 x the
+ * fp32 weight is split exactly into three bf16 planes whose products with x
+ * are exact, accumulated in fp32 on the matrix cores. x is [T, d_model] act.
+ * ws must hold moe_workspace_size() bytes (split planes, partial logits). */
 MOE_API int moe_route(const moe_desc *desc, const moe_weights *w, const void *x, int32_t *idx,
-              float *g, float *gap, float *top_scores, void *stream);
+                      float *g, float *gap, float *top_scores, void *ws, size_t ws_bytes,
+                      void *stream);
 
 /* Sorted dispatch ("StableLatentMoE and QuantileBalancer", section "Dispatch
  * is a stable permutation, not token duplication in model state"): the T*K

@@ -64,7 +64,7 @@ def lib():
         L.moe_stage_name.argtypes = [C.c_int]
         L.moe_stage_name.restype = C.c_char_p
         L.moe_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
-        L.moe_route.argtypes = [P, P, P, P, P, P, P, P]
+        L.moe_route.argtypes = [P, P, P, P, P, P, P, P, S, P]
         L.moe_dispatch.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, S, P]
         L.moe_expert_ffn.argtypes = [P, P, P, P, P, P, P, P, S, P]
         L.moe_combine.argtypes = [P, P, P, P, P, P, P, S, P]
@@ -122,9 +122,13 @@ def moe_workspace_size(desc: MoeDesc) -> int:
     return n.value
 
 
-def moe_route(desc, weights, x, idx, g, gap=None, top_scores=None, stream=None):
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_route(desc, weights, x, idx, g, gap=None, top_scores=None, ws=None, stream=None):
     _ok(lib().moe_route(C.byref(desc), C.byref(weights), _ptr(x), _ptr(idx), _ptr(g), _ptr(gap),
-                        _ptr(top_scores), _stream(stream)), "moe_route")
+                        _ptr(top_scores), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_route")
 
 
 def moe_dispatch(desc, idx, g, rows, counts, offsets, perm, sorted_token, inv, sorted_w,

@@ -17,6 +17,7 @@ constexpr int kMaxLatent = 16384;
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
+  size_t wsplit, logits;
   size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, ntie;
   size_t z, h, y, hsh, r;
   size_t total;
@@ -38,6 +39,9 @@ Layout layout_of(const moe_desc *d) {
     o += align256(bytes);
     return at;
   };
+  const int bf = d->act_dtype == MOE_BF16;
+  L.wsplit = take(router_split_bytes(E, d->d_model, bf));
+  L.logits = take(router_logit_bytes(T, E, bf));
   L.idx = take(rows * 4);
   L.g = take(rows * 4);
   L.gap = take(T * 4);
@@ -267,11 +271,15 @@ int moe_workspace_size(const moe_desc *desc, size_t *bytes) {
 }
 
 int moe_route(const moe_desc *d, const moe_weights *w, const void *x, int32_t *idx, float *g,
-              float *gap, float *top_scores, void *stream) {
+              float *gap, float *top_scores, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (!w || !w->w_router || !idx || !g || (!x && d->T > 0)) return MOE_ERR_NULL;
+  if (!w || !w->w_router || !idx || !g || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   RouterArgs a{};
+  a.w_split = static_cast<char *>(ws) + L.wsplit;
+  a.logits = reinterpret_cast<float *>(static_cast<char *>(ws) + L.logits);
   a.x = x;
   a.w = w->w_router;
   a.bias = w->bias;
@@ -405,6 +413,8 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   RouterArgs ra{};
   ra.x = x;
   ra.w = w->w_router;
+  ra.w_split = wsb + L.wsplit;
+  ra.logits = reinterpret_cast<float *>(wsb + L.logits);
   ra.bias = w->bias;
   ra.T = T;
   ra.d = d->d_model;

@@ -15,6 +15,7 @@
 //   SCALE   - out = row_scale[m] * acc (the routing weight of the row);
 //   STORE   - out = acc (optionally over two K segments: out = A1 B1^T +
 //             A2 B2^T, used for shared-down + latent-up in one pass);
+//   STORE_F32 - out = acc kept in fp32 (router logits);
 //   COMBINE - out[t] = acc + sum_k y[inv[t*K + k]] in fixed k order: the
 //             shared expert's down projection and the atomic-free combine
 //             of the routed rows (Math. Reference 13.2) in one pass.
@@ -258,7 +259,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         } else {
           v = acc[fm][fo][r];
         }
-        Elem<T>::store(p.out, m * p.ldo + col, v);
+        if (EPI == EPI_STORE_F32)
+          static_cast<float *>(p.out)[m * p.ldo + col] = v;
+        else
+          Elem<T>::store(p.out, m * p.ldo + col, v);
       }
     }
   }
@@ -293,6 +297,7 @@ hipError_t dispatch_epi(const GemmArgs &a, int epi, hipStream_t s) {
     case EPI_SCALE: return run<T, C, EPI_SCALE>(a, s);
     case EPI_STORE: return run<T, C, EPI_STORE>(a, s);
     case EPI_COMBINE: return run<T, C, EPI_COMBINE>(a, s);
+    case EPI_STORE_F32: return run<T, C, EPI_STORE_F32>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -10,6 +10,8 @@ namespace moe {
 struct RouterArgs {
   const void *x;         // [T, d] act
   const float *w;        // [E, d]
+  void *w_split;         // bf16 act: [3, E, d] bf16 planes of w (workspace)
+  float *logits;         // [T, parts * E] partial logits (workspace)
   const float *bias;     // [E] or null
   int64_t T;
   int d, E, K;
@@ -22,6 +24,13 @@ struct RouterArgs {
   float *top;            // [T, K+1] or null
 };
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
+// Workspace of the router: split weight planes and partial logits.
+inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
+  return act_bf16 ? static_cast<size_t>(3 * E * d * 2) : 0;
+}
+inline size_t router_logit_bytes(int64_t T, int64_t E, int act_bf16) {
+  return static_cast<size_t>(T * E * (act_bf16 ? 3 : 1) * 4);
+}
 
 // ------------------------------------------------------------------ dispatch
 // Slots per histogram / scatter chunk.
@@ -70,7 +79,7 @@ hipError_t launch_gather(const void *rows, const int32_t *sorted_token, int64_t 
                          int64_t row_bytes, void *out, hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM
-enum Epilogue { EPI_SWIGLU = 0, EPI_SCALE = 1, EPI_STORE = 2, EPI_COMBINE = 3 };
+enum Epilogue { EPI_SWIGLU = 0, EPI_SCALE = 1, EPI_STORE = 2, EPI_COMBINE = 3, EPI_STORE_F32 = 4 };
 
 // C = A B^T over one or two K segments, A [M, K] row-major (optionally row
 // gathered), B [N, K] row-major ("out x in" weights), grouped by expert via a

@@ -7,12 +7,20 @@
 // router, sigmoid scores, bias-corrected top-(K+1), last candidate dropped,
 // weights are the uncorrected sigmoid scores.
 //
-// One workgroup takes 16 tokens. Its 256 threads each own one expert of the
-// current 256-expert block and accumulate that expert's 16 fp32 logits from
-// LDS-staged tiles of x and W_router (fp32 FMA, k ascending). The logits of
-// the 16 tokens then sit in LDS, and each wavefront selects for one token at
-// a time: every lane holds E/64 scores, and K+1 rounds of a butterfly
-// (value, lower id) max-reduction over the 64 lanes pick the experts.
+// Logits (fp32 router on matrix cores). For bf16 activations, each fp32
+// router weight w is split exactly into three bf16 values, w = h + m + l
+// (h = bf16(w), m = bf16(w - h), l = w - h - m, which fits in bf16 because
+// 24 significand bits = 3 x 8). A bf16 x times a bf16 plane is exact in
+// fp32, so x W^T = x H^T + x M^T + x L^T is the fp32 router product computed
+// on v_mfma_f32_16x16x32_bf16 with fp32 accumulation: one GEMM against the
+// stacked planes [H; M; L] gives three partial logits per expert, summed
+// (h + m) + l in the selection kernel. For fp32 activations the GEMM runs on
+// v_mfma_f32_16x16x4_f32 directly. Either way the accumulation rounds once
+// per 32 (bf16) or 4 (fp32) products instead of once per product.
+//
+// Selection: one wavefront per token. Each lane holds E/64 scores; K+1
+// rounds of a butterfly (value, lower id) max-reduction over the 64 lanes
+// pick the experts in descending order, ties to the lower id.
 #include <math.h>
 
 #include "common.h"
@@ -22,173 +30,152 @@ namespace moe {
 
 namespace {
 
-constexpr int kTok = 16;    // tokens per workgroup
-constexpr int kDk = 16;     // k per LDS stage
-constexpr int kEb = 256;    // experts per pass (one per thread)
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 1024;
 constexpr int kPerLane = kMaxE / 64;
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-template <typename T>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  __shared__ float xs[kTok][kDk];
-  __shared__ float wsm[kEb][kDk + 1];
-  __shared__ float logit[kTok][kMaxE];
-
-  const int tid = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  const int ntok = static_cast<int>(min<int64_t>(kTok, a.T - t0));
-
-  for (int eb = 0; eb < a.E; eb += kEb) {
-    float acc[kTok];
-#pragma unroll
-    for (int m = 0; m < kTok; ++m) acc[m] = 0.f;
-    for (int k0 = 0; k0 < a.d; k0 += kDk) {
-      for (int i = tid; i < kTok * kDk; i += 256) {
-        const int m = i / kDk, k = i % kDk;
-        float v = 0.f;
-        if (m < ntok && k0 + k < a.d) v = Elem<T>::load(a.x, (t0 + m) * a.d + k0 + k);
-        xs[m][k] = v;
-      }
-      for (int i = tid; i < kEb * kDk; i += 256) {
-        const int r = i / kDk, k = i % kDk;
-        float v = 0.f;
-        if (eb + r < a.E && k0 + k < a.d) v = a.w[static_cast<int64_t>(eb + r) * a.d + k0 + k];
-        wsm[r][k] = v;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kDk; ++k) {
-        const float wv = wsm[tid][k];
-#pragma unroll
-        for (int m = 0; m < kTok; ++m) acc[m] = fmaf(xs[m][k], wv, acc[m]);
-      }
-      __syncthreads();
-    }
-    if (eb + tid < a.E) {
-#pragma unroll
-      for (int m = 0; m < kTok; ++m) logit[m][eb + tid] = acc[m];
-    }
+// planes[0..2][i] = exact bf16 split of w[i]
+__global__ __launch_bounds__(256) void split_kernel(const float *__restrict__ w, int64_t n,
+                                                    uint16_t *__restrict__ planes) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float v = w[i];
+    const uint16_t h = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h);
+    const uint16_t m = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(m);
+    planes[i] = h;
+    planes[n + i] = m;
+    planes[2 * n + i] = f32_to_bf16(r2);
   }
-  __syncthreads();
+}
 
-  const int wave = tid >> 6, lane = tid & 63;
+// One wavefront per token over the partial logits [T, parts * E].
+__global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K;
   const int nsel = K + 1 <= E ? K + 1 : E;
   const bool sig = a.mode == 2;
-  for (int m = wave; m < ntok; m += 4) {
-    const int64_t t = t0 + m;
-    float v[kPerLane];
-    float vmax = -INFINITY;
+  const float *lg = a.logits + t * static_cast<int64_t>(parts) * E;
+
+  float raw[kPerLane];  // logit x W^T per owned expert
+  float v[kPerLane];    // ranking score
+  float vmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-      const int e = lane + 64 * j;
-      float sc = -INFINITY;
-      if (e < E) {
-        const float l = logit[m][e];
-        const float b = a.bias ? a.bias[e] : 0.f;
-        sc = sig ? sigmoidf_(l) + b : l + b;
-        vmax = fmaxf(vmax, sc);
-      }
-      v[j] = sc;
+  for (int j = 0; j < kPerLane; ++j) {
+    const int e = lane + 64 * j;
+    float sc = -INFINITY, l = 0.f;
+    if (e < E) {
+      l = lg[e];
+      if (parts == 3) l = (l + lg[E + e]) + lg[2 * E + e];
+      const float b = a.bias ? a.bias[e] : 0.f;
+      sc = sig ? sigmoidf_(l) + b : l + b;
+      vmax = fmaxf(vmax, sc);
     }
-    // softmax-first rule reports probabilities: need the all-expert sum
-    float zall = 0.f;
-    if (a.mode == 1) {
+    raw[j] = l;
+    v[j] = sc;
+  }
+  // the softmax-first rule reports probabilities: all-expert normaliser
+  float zall = 1.f;
+  if (a.mode == 1) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    zall = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+      if (lane + 64 * j < E) zall += expf(v[j] - vmax);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) zall += __shfl_xor(zall, off);
+  }
+
+  float sv[kMaxK + 1], sraw[kMaxK + 1];
+  int si[kMaxK + 1];
+#pragma unroll
+  for (int r = 0; r <= kMaxK; ++r) {
+    sv[r] = -INFINITY;
+    sraw[r] = 0.f;
+    si[r] = 0;
+    if (r < nsel) {
+      float bv = -INFINITY, br = 0.f;
+      int bi = 0x7FFFFFFF;
 #pragma unroll
       for (int j = 0; j < kPerLane; ++j)
-        if (lane + 64 * j < E) zall += expf(v[j] - vmax);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) zall += __shfl_xor(zall, off);
-    }
-
-    float sv[kMaxK + 1];
-    int si[kMaxK + 1];
-#pragma unroll
-    for (int r = 0; r <= kMaxK; ++r) {
-      sv[r] = -INFINITY;
-      si[r] = 0;
-      if (r < nsel) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j)
-          if (v[j] > bv) {  // ascending id within the lane: ties keep the lower id
-            bv = v[j];
-            bi = lane + 64 * j;
-          }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const float ov = __shfl_xor(bv, off);
-          const int oi = __shfl_xor(bi, off);
-          if (ov > bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-          }
+        if (v[j] > bv) {  // ids ascend within a lane: ties keep the lower id
+          bv = v[j];
+          br = raw[j];
+          bi = lane + 64 * j;
         }
-        sv[r] = bv;
-        si[r] = bi;
 #pragma unroll
-        for (int j = 0; j < kPerLane; ++j)
-          if (lane + 64 * j == bi) v[j] = -INFINITY;
-      }
-    }
-
-    if (lane == 0) {
-      float gk[kMaxK];
-      float z = 0.f;
-      if (sig) {
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k)
-          if (k < K) {
-            gk[k] = sigmoidf_(logit[m][si[k]]);
-            z += gk[k];
-          }
-        if (a.renormalize) {
-#pragma unroll
-          for (int k = 0; k < kMaxK; ++k)
-            if (k < K) gk[k] = gk[k] / z;
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const float orw = __shfl_xor(br, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          br = orw;
+          bi = oi;
         }
-      } else {
-        const float top = sv[0];
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k)
-          if (k < K) {
-            gk[k] = expf(sv[k] - top);
-            z += gk[k];
-          }
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k)
-          if (k < K) gk[k] = gk[k] / z;
       }
+      sv[r] = bv;
+      sraw[r] = br;
+      si[r] = bi;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j)
+        if (lane + 64 * j == bi) v[j] = -INFINITY;
+    }
+  }
+  if (lane != 0) return;
+
+  float gk[kMaxK];
+  float z = 0.f;
+  if (sig) {
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (k < K) {
+        gk[k] = sigmoidf_(sraw[k]);
+        z += gk[k];
+      }
+    if (a.renormalize) {
 #pragma unroll
       for (int k = 0; k < kMaxK; ++k)
-        if (k < K) {
-          a.idx[t * K + k] = si[k];
-          a.g[t * K + k] = gk[k] * a.routed_scale;
-        }
-      // scores in the ranked space (probabilities for the softmax-first rule)
-      float rs[kMaxK + 1];
-#pragma unroll
-      for (int r = 0; r <= kMaxK; ++r)
-        rs[r] = (a.mode == 1 && r < nsel) ? expf(sv[r] - vmax) / zall : sv[r];
-      if (a.gap) {
-        float gp = INFINITY;
-#pragma unroll
-        for (int r = 1; r <= kMaxK; ++r)
-          if (r == K && K < E) gp = rs[r - 1] - rs[r];
-        a.gap[t] = gp;
-      }
-      if (a.top) {
-#pragma unroll
-        for (int r = 0; r <= kMaxK; ++r)
-          if (r <= K) a.top[t * (K + 1) + r] = r < nsel ? rs[r] : -INFINITY;
-      }
+        if (k < K) gk[k] = gk[k] / z;
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (k < K) {
+        gk[k] = expf(sv[k] - sv[0]);
+        z += gk[k];
+      }
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (k < K) gk[k] = gk[k] / z;
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k)
+    if (k < K) {
+      a.idx[t * K + k] = si[k];
+      a.g[t * K + k] = gk[k] * a.routed_scale;
+    }
+  float rs[kMaxK + 1];  // scores in the ranked space
+#pragma unroll
+  for (int r = 0; r <= kMaxK; ++r)
+    rs[r] = (a.mode == 1 && r < nsel) ? expf(sv[r] - vmax) / zall : sv[r];
+  if (a.gap) {
+    float gp = INFINITY;
+#pragma unroll
+    for (int r = 1; r <= kMaxK; ++r)
+      if (r == K && K < E) gp = rs[r - 1] - rs[r];
+    a.gap[t] = gp;
+  }
+  if (a.top) {
+#pragma unroll
+    for (int r = 0; r <= kMaxK; ++r)
+      if (r <= K) a.top[t * (K + 1) + r] = r < nsel ? rs[r] : -INFINITY;
   }
 }
 
@@ -196,11 +183,32 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((a.T + kTok - 1) / kTok));
-  if (act_bf16)
-    router_kernel<bf16_t><<<grid, 256, 0, s>>>(a);
-  else
-    router_kernel<float><<<grid, 256, 0, s>>>(a);
+  const int64_t nw = static_cast<int64_t>(a.E) * a.d;
+  GemmArgs g{};
+  g.a = a.x;
+  g.lda = a.d;
+  g.ldb = a.d;
+  g.K = a.d;
+  g.M = a.T;
+  g.out = a.logits;
+  const int parts = act_bf16 ? 3 : 1;
+  g.N = parts * a.E;
+  g.ldo = g.N;
+  if (act_bf16) {
+    int64_t blocks = (nw + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    split_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+        a.w, nw, static_cast<uint16_t *>(a.w_split));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g.b0 = a.w_split;
+  } else {
+    g.b0 = a.w;
+  }
+  hipError_t e = launch_gemm(g, EPI_STORE_F32, a.T <= 64 ? TILE_SMALL_M : TILE_LARGE,
+                             act_bf16, s);
+  if (e != hipSuccess) return e;
+  select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts);
   return hipGetLastError();
 }
 

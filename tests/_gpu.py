@@ -46,7 +46,7 @@ def gpu_route(layer):
     g = torch.full((w.T, w.K), -7.0, dtype=torch.float32, device=dv)
     gap = torch.full((w.T,), -7.0, dtype=torch.float32, device=dv)
     top = torch.full((w.T, w.K + 1), -7.0, dtype=torch.float32, device=dv)
-    moe.moe_route(layer.desc, layer.weights, layer.dev["x"], idx, g, gap, top)
+    moe.moe_route(layer.desc, layer.weights, layer.dev["x"], idx, g, gap, top, layer.ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), g.cpu().numpy(), gap.cpu().numpy(), top.cpu().numpy()
 

@@ -91,7 +91,7 @@ def test_exact_ties_take_lower_id():
     say("case exact ties")
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
     g = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
-    moe.moe_route(layer.desc, layer.weights, layer.dev["x"], idx, g)
+    moe.moe_route(layer.desc, layer.weights, layer.dev["x"], idx, g, ws=layer.ws)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     o_idx, _, _, _ = oracle.Oracle(w, a).route()
