@@ -80,10 +80,35 @@ int check_desc(const moe_desc *d) {
   return MOE_OK;
 }
 
-int pick_grouped(int64_t rows, int64_t E) {
-  return rows <= 32 * E ? TILE_SMALL_M : TILE_LARGE;  // about 32 rows per expert or fewer
+#ifndef MOE_GROUPED_BIG
+#define MOE_GROUPED_BIG TILE_LARGE
+#endif
+#ifndef MOE_GROUPED_V2
+#define MOE_GROUPED_V2 TILE2_256x256
+#endif
+
+// Kernel and tile shape of the grouped expert GEMMs (both share one m-tile
+// table, so one plan covers the pair).
+struct Plan {
+  int v2, cfg;
+  int bm() const { return v2 ? gemm2_bm(cfg) : tile_bm(cfg); }
+};
+
+Plan plan_grouped(const moe_desc *d) {
+  const int64_t rows = d->T * d->top_k, E = d->n_experts;
+  if (rows <= 32 * E) return {0, TILE_SMALL_M};  // about 32 rows per expert or fewer
+  const int64_t de = d->latent ? d->latent : d->d_model;
+  if (d->act_dtype == MOE_BF16 && de % 64 == 0 && d->d_ff % 64 == 0) {
+    const int bm = gemm2_bm(MOE_GROUPED_V2);
+    const int64_t mt = rows / bm + (rows < E ? rows : E);
+    if (mt * ((d->d_ff + 127) / 128) >= gemm2_min_tiles()) return {1, MOE_GROUPED_V2};
+  }
+  return {0, MOE_GROUPED_BIG};
 }
-int pick_dense(int64_t M) { return M <= 64 ? TILE_SMALL_M : TILE_LARGE; }
+
+hipError_t run_grouped(const GemmArgs &a, int epi, const Plan &pl, int bf, hipStream_t s) {
+  return pl.v2 ? launch_gemm2(a, epi, pl.cfg, s) : launch_gemm(a, epi, pl.cfg, bf, s);
+}
 
 struct Probe {
   const moe_probe *p;
@@ -104,8 +129,9 @@ struct Probe {
 // Grouped SwiGLU over the sorted rows: GEMM 1 (gate/up + SiLU*up) into h,
 // GEMM 2 (down, times row_scale) into y.
 int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
-                 const int32_t *row_index, const int32_t *tiles, const int32_t *n_tiles, int cfg,
-                 const float *row_scale, void *h, void *y, const Probe &pr, hipStream_t s) {
+                 const int32_t *row_index, const int32_t *tiles, const int32_t *n_tiles,
+                 const Plan &pl, const float *row_scale, void *h, void *y, const Probe &pr,
+                 hipStream_t s) {
   const int64_t rows_n = d->T * d->top_k;
   const int de = d->latent ? d->latent : d->d_model;
   const int bf = d->act_dtype == MOE_BF16;
@@ -121,11 +147,11 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   a.N = d->d_ff;
   a.tiles = tiles;
   a.n_tiles = n_tiles;
-  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, tile_bm(cfg));
+  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.bm());
   a.out = h;
   a.ldo = d->d_ff;
   pr.begin(MOE_STAGE_EXPERT_GATE_UP);
-  MOE_TRY(launch_gemm(a, EPI_SWIGLU, cfg, bf, s));
+  MOE_TRY(run_grouped(a, EPI_SWIGLU, pl, bf, s));
   pr.end(MOE_STAGE_EXPERT_GATE_UP);
 
   GemmArgs b{};
@@ -143,7 +169,7 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   b.ldo = de;
   b.row_scale = row_scale;
   pr.begin(MOE_STAGE_EXPERT_DOWN);
-  MOE_TRY(launch_gemm(b, EPI_SCALE, cfg, bf, s));
+  MOE_TRY(run_grouped(b, EPI_SCALE, pl, bf, s));
   pr.end(MOE_STAGE_EXPERT_DOWN);
   return MOE_OK;
 }
@@ -155,7 +181,6 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
   const int64_t T = d->T;
   const int bf = d->act_dtype == MOE_BF16;
   const int dm = d->d_model;
-  const int cfg = pick_dense(T);
   void *hsh = ws + L.hsh;
   if (d->d_shared) {
     GemmArgs a{};
@@ -170,7 +195,7 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
     a.out = hsh;
     a.ldo = d->d_shared;
     pr.begin(MOE_STAGE_SHARED_GATE_UP);
-    MOE_TRY(launch_gemm(a, EPI_SWIGLU, cfg, bf, s));
+    MOE_TRY(launch_dense(a, EPI_SWIGLU, bf, s));
     pr.end(MOE_STAGE_SHARED_GATE_UP);
   }
   pr.begin(MOE_STAGE_COMBINE);
@@ -190,7 +215,7 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
       c.ldy = dm;
       c.inv = inv;
       c.topk = d->top_k;
-      MOE_TRY(launch_gemm(c, EPI_COMBINE, cfg, bf, s));
+      MOE_TRY(launch_dense(c, EPI_COMBINE, bf, s));
     } else {
       MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, bf, s));
     }
@@ -221,7 +246,7 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
     c.M = T;
     c.out = out;
     c.ldo = dm;
-    MOE_TRY(launch_gemm(c, EPI_STORE, cfg, bf, s));
+    MOE_TRY(launch_dense(c, EPI_STORE, bf, s));
   }
   pr.end(MOE_STAGE_COMBINE);
   return MOE_OK;
@@ -355,12 +380,12 @@ int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *wsb = static_cast<char *>(ws);
   const int64_t rows_n = d->T * d->top_k;
-  const int cfg = pick_grouped(rows_n, d->n_experts);
+  const Plan pl = plan_grouped(d);
   int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
   int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
-  MOE_TRY(launch_tiles(offsets, d->n_experts, tile_bm(cfg), tiles, nt, s));
+  MOE_TRY(launch_tiles(offsets, d->n_experts, pl.bm(), tiles, nt, s));
   const Probe pr{nullptr, s};
-  return expert_gemms(d, w, rows, row_index, tiles, nt, cfg, row_scale, wsb + L.h, y_sorted, pr,
+  return expert_gemms(d, w, rows, row_index, tiles, nt, pl, row_scale, wsb + L.h, y_sorted, pr,
                       s);
 }
 
@@ -407,7 +432,7 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   float *sw = reinterpret_cast<float *>(wsb + L.sw);
   int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
   int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
-  const int cfg = pick_grouped(rows, E);
+  const Plan pl = plan_grouped(d);
 
   // 1. router
   RouterArgs ra{};
@@ -440,7 +465,7 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   sa.E = static_cast<int>(E);
   sa.counts = cnt;
   sa.offsets = offsets;
-  sa.bm = tile_bm(cfg);
+  sa.bm = pl.bm();
   sa.tiles = tiles;
   sa.n_tiles = nt;
   sa.gap = n_near_ties ? gap : nullptr;
@@ -477,13 +502,13 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
     a.out = wsb + L.z;
     a.ldo = d->latent;
     pr.begin(MOE_STAGE_LATENT_DOWN);
-    MOE_TRY(launch_gemm(a, EPI_STORE, pick_dense(T), bf, s));
+    MOE_TRY(launch_dense(a, EPI_STORE, bf, s));
     pr.end(MOE_STAGE_LATENT_DOWN);
     rsrc = wsb + L.z;
   }
 
   // 4. grouped expert SwiGLU (gather fused into GEMM 1's A load)
-  if ((rc = expert_gemms(d, w, rsrc, stok, tiles, nt, cfg, sw, wsb + L.h, wsb + L.y, pr, s)))
+  if ((rc = expert_gemms(d, w, rsrc, stok, tiles, nt, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
     return rc;
 
   // 5. shared experts + combine

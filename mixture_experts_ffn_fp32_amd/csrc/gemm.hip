@@ -274,6 +274,15 @@ struct CfgSmallM {  // few rows per expert (decode): stream B
 struct CfgLarge {
   static constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
 };
+struct CfgWide {
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 2;
+};
+struct CfgTall {
+  static constexpr int BM = 256, BN = 128, WM = 2, WN = 2;
+};
+struct CfgHuge {
+  static constexpr int BM = 256, BN = 256, WM = 2, WN = 2;
+};
 
 template <typename T, typename C, int EPI>
 hipError_t run(const GemmArgs &a, hipStream_t s) {
@@ -304,14 +313,28 @@ hipError_t dispatch_epi(const GemmArgs &a, int epi, hipStream_t s) {
 
 }  // namespace
 
-int tile_bm(int cfg) { return cfg == TILE_SMALL_M ? CfgSmallM::BM : CfgLarge::BM; }
+int tile_bm(int cfg) {
+  switch (cfg) {
+    case TILE_SMALL_M: return CfgSmallM::BM;
+    case TILE_LARGE: return CfgLarge::BM;
+    case TILE_WIDE: return CfgWide::BM;
+    case TILE_TALL: return CfgTall::BM;
+    case TILE_HUGE: return CfgHuge::BM;
+  }
+  return CfgLarge::BM;
+}
 
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s) {
-  if (act_bf16)
-    return cfg == TILE_SMALL_M ? dispatch_epi<bf16_t, CfgSmallM>(a, epi, s)
-                               : dispatch_epi<bf16_t, CfgLarge>(a, epi, s);
-  return cfg == TILE_SMALL_M ? dispatch_epi<float, CfgSmallM>(a, epi, s)
-                             : dispatch_epi<float, CfgLarge>(a, epi, s);
+  if (!act_bf16)  // fp32 runs the two base shapes only
+    return cfg == TILE_SMALL_M ? dispatch_epi<float, CfgSmallM>(a, epi, s)
+                               : dispatch_epi<float, CfgLarge>(a, epi, s);
+  switch (cfg) {
+    case TILE_SMALL_M: return dispatch_epi<bf16_t, CfgSmallM>(a, epi, s);
+    case TILE_WIDE: return dispatch_epi<bf16_t, CfgWide>(a, epi, s);
+    case TILE_TALL: return dispatch_epi<bf16_t, CfgTall>(a, epi, s);
+    case TILE_HUGE: return dispatch_epi<bf16_t, CfgHuge>(a, epi, s);
+    default: return dispatch_epi<bf16_t, CfgLarge>(a, epi, s);
+  }
 }
 
 }  // namespace moe

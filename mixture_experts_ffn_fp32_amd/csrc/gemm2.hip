@@ -1,0 +1,365 @@
+// Pipelined bf16 GEMM for large tiles (gfx950): C = A B^T, same contract and
+// epilogues as gemm.hip (grouped expert tiles from a device table or dense;
+// row-gathered A; SwiGLU, row-scale, store, fp32 store, combine epilogues;
+// optional second K segment).
+//
+// Main loop. A workgroup of 4 wavefronts owns a BM x BN tile (each
+// wavefront a (BM/2) x (BN/2) quarter of 16x16 accumulators on
+// v_mfma_f32_16x16x32_bf16). K advances 64 elements (128 bytes per row) per
+// stage, two MFMA k-steps. At the start of a stage each thread issues its
+// 16-byte global loads of the next stage (8 lanes per 128-byte row
+// segment); the stage's MFMAs (2 x 64 per wavefront) then cover their
+// latency, and the registers are written to the other LDS buffer before the
+// single barrier of the stage. All waits are local to one stage, which the
+// compiler's wait-count tracking handles exactly. Within a row the eight
+// 16-byte chunks are XOR-swizzled by row & 7 so the 16-byte fragment reads of
+// 8 consecutive rows fall in distinct bank groups. (Direct global->LDS
+// 16-byte loads were measured to issue per-dword cache accesses on this part
+// and are not used.)
+//
+// K must be a multiple of 64 (every workload's widths are); the host uses
+// gemm.hip otherwise. Rows of A past the tile end and columns of B past N
+// are read from a valid row (their results are never stored), so loads need
+// no predicates.
+//
+// Epilogue. Each wavefront stages its accumulators through LDS 16 rows at a
+// time and writes the output with 16-byte stores along rows; the combine
+// epilogue adds the token's K routed rows with 16-byte loads.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxStageBytes = (256 + 256) * 128;  // largest tile, one stage
+
+__shared__ __attribute__((aligned(1024))) u32x4 g2_s0[kMaxStageBytes / 16];
+__shared__ __attribute__((aligned(1024))) u32x4 g2_s1[kMaxStageBytes / 16];
+
+// s_waitcnt with vmcnt = n (<= 63), lgkmcnt = 0, expcnt untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// physical 16-byte chunk of logical chunk c in row r (rows of 8 chunks)
+__device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr bool GLU = EPI == EPI_SWIGLU;
+  constexpr int NOUT = GLU ? BN / 2 : BN;
+  constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte loads per thread per stage
+  constexpr int STAGE16 = (BM + BN) * 8;        // 16-byte units per stage
+  static_assert(STAGE16 * 16 <= kMaxStageBytes, "stage fits");
+  static_assert(!GLU || FN % 2 == 0, "paired gate/up fragments");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ------------------------------------------------------------ tile
+  const int n_tn = (p.N + NOUT - 1) / NOUT;
+  const int64_t n_m = p.tiles ? static_cast<int64_t>(*p.n_tiles) : p.max_mtiles;
+  const int64_t total = n_m * n_tn;
+  const int64_t per = (total + 7) / 8;
+  const int64_t local = blockIdx.x >> 3;
+  if (local >= per) return;
+  const int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
+  if (pid >= total) return;
+  constexpr int GM = 4;
+  const int64_t grp = pid / (GM * n_tn);
+  const int64_t first_m = grp * GM;
+  const int gsz = static_cast<int>(min<int64_t>(n_m - first_m, GM));
+  const int64_t in_g = pid - grp * GM * n_tn;
+  const int64_t mt = first_m + in_g % gsz;
+  const int nt = static_cast<int>(in_g / gsz);
+  int64_t expert = 0, m_begin, m_end;
+  if (p.tiles) {
+    expert = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt]);
+    m_begin = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt + 1]);
+    m_end = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt + 2]);
+  } else {
+    m_begin = mt * BM;
+    m_end = min<int64_t>(m_begin + BM, p.M);
+  }
+  const int n_begin = nt * NOUT;
+
+  // ------------------------------------------------------------ loaders
+  // load j of a thread covers tile row (tid / 8 + 32 j), logical chunk tid % 8
+  const int lrow = tid >> 3;
+  const int lchunk = tid & 7;
+  const char *arow[A_LD];
+  const char *brow[B_LD];
+  auto setup = [&](int seg) {
+    const char *abase = static_cast<const char *>(seg ? p.a2 : p.a);
+    const int64_t lda = seg ? p.lda2 : p.lda;
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+      const int r = lrow + 32 * j;
+      int64_t m = m_begin + r;
+      if (m >= m_end) m = m_begin;  // results of these rows are never stored
+      const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
+      arow[j] = abase + (src * lda + lchunk * 8) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) {
+      const int r = lrow + 32 * j;
+      const char *bbase;
+      int n;
+      int64_t ldb, off = 0;
+      if (seg) {
+        bbase = static_cast<const char *>(p.b2);
+        n = n_begin + r;
+        ldb = p.ldb2;
+      } else {
+        const bool up = GLU && r >= BN / 2;
+        bbase = static_cast<const char *>(up ? p.b1 : p.b0);
+        n = n_begin + (up ? r - BN / 2 : r);
+        ldb = p.ldb;
+        off = expert * p.b_stride;
+      }
+      if (n >= p.N) n = p.N - 1;
+      brow[j] = bbase + (off + static_cast<int64_t>(n) * ldb + lchunk * 8) * 2;
+    }
+  };
+
+  const int steps1 = p.K / 64;
+  const int steps = steps1 + (p.a2 ? p.K2 / 64 : 0);
+
+  // registers of the next stage
+  u32x4 ra[A_LD], rb[B_LD];
+  auto load = [&](int st) {
+    const int64_t kb = static_cast<int64_t>(st >= steps1 ? st - steps1 : st) * 128;
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) ra[j] = *reinterpret_cast<const u32x4 *>(arow[j] + kb);
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(brow[j] + kb);
+  };
+  auto put = [&](u32x4 *buf) {
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) buf[sw8(lrow + 32 * j, lchunk)] = ra[j];
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) buf[BM * 8 + sw8(lrow + 32 * j, lchunk)] = rb[j];
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment rows: A row of fm, B row of fn (within the stage)
+  const int fr = lane & 15, fc = lane >> 4;
+  auto brow_of = [&](int fn) {
+    if (GLU) {
+      constexpr int half = FN / 2;
+      return fn < half ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - half) * 16;
+    }
+    return wn * WTN + fn * 16;
+  };
+  // number of this wave's 16-row fragments that hold rows of the tile
+  const int64_t rows_left = m_end - (m_begin + wm * WTM);
+  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
+
+  // all fragments are read first (rows past the tile read stale LDS, and
+  // their MFMAs are skipped), so the MFMAs issue back to back
+  const int live = __builtin_amdgcn_readfirstlane(fm_live);
+  auto compute = [&](const u32x4 *buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kc = 4 * ks + fc;
+      bf16x8 bf[FN], af[FM];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bf[fn] = __builtin_bit_cast(bf16x8, buf[BM * 8 + sw8(brow_of(fn) + fr, kc)]);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = __builtin_bit_cast(bf16x8, buf[sw8(wm * WTM + fm * 16 + fr, kc)]);
+      // keep the reads ahead of the branches below (then MFMAs back to back)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) asm volatile("" : "+v"(af[fm]));
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (fm < live) {
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  setup(0);
+  load(0);
+  put(g2_s0);
+  barrier();
+  // Step st: issue the loads of stage st + 1, run the MFMAs of stage st from
+  // LDS buffer st % 2, write stage st + 1 into the other buffer, barrier.
+  // Unrolled by two so the buffers are named statically.
+#define G2_STAGE(ST, CUR, NXT)                  \
+  {                                             \
+    const int st_ = (ST);                       \
+    if (st_ >= steps) break;                    \
+    const bool more_ = st_ + 1 < steps;         \
+    if (more_) {                                \
+      if (st_ + 1 == steps1) setup(1);          \
+      load(st_ + 1);                            \
+    }                                           \
+    compute(CUR);                               \
+    if (more_) put(NXT);                        \
+    barrier();                                  \
+  }
+  for (int st = 0; st < steps; st += 2) {
+    G2_STAGE(st + 0, g2_s0, g2_s1)
+    G2_STAGE(st + 1, g2_s1, g2_s0)
+  }
+#undef G2_STAGE
+
+  // ------------------------------------------------------------ epilogue
+  // each wave: 16 rows x (OUT cols) of fp32 at a time in its 8 KB+ slice
+  constexpr int OUTW = GLU ? WTN / 2 : WTN;   // output columns per wave
+  constexpr int FO = GLU ? FN / 2 : FN;
+  constexpr int PITCH = OUTW + 4;             // floats per staged row
+  float *stg = reinterpret_cast<float *>(wave < 2 ? g2_s0 : g2_s1) + (wave & 1) * 16 * PITCH;
+  static_assert(2 * 16 * PITCH * 4 <= kMaxStageBytes, "epilogue staging fits");
+  const int col0 = n_begin + (GLU ? wn * (WTN / 2) : wn * WTN);
+  constexpr int ITEMS = 16 * OUTW / 8;        // (row, 8-column) items per 16 rows
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    if (fm >= live) break;  // unrolled: acc is indexed statically and stays in registers
+#pragma unroll
+    for (int fo = 0; fo < FO; ++fo)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[fm][fo][i];
+        if (GLU) v = silu_f(v) * acc[fm][fo + FO][i];
+        stg[(4 * fc + i) * PITCH + fo * 16 + fr] = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < (ITEMS + 63) / 64; ++it) {
+      const int item = it * 64 + lane;
+      if (item >= ITEMS) break;
+      const int r = item / (OUTW / 8), c8 = (item % (OUTW / 8)) * 8;
+      const int64_t m = m_begin + wm * WTM + fm * 16 + r;
+      const int col = col0 + c8;
+      if (m >= m_end || col >= p.N) continue;
+      float v[8];
+      const float4 lo = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8);
+      const float4 hi = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8 + 4);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      if (EPI == EPI_SCALE && p.row_scale) {
+        const float s = p.row_scale[m];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] *= s;
+      }
+      if (EPI == EPI_COMBINE) {
+        float rs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < p.topk; ++k) {
+          const int q = p.inv[m * p.topk + k];
+          if (q < 0) continue;
+          float y[8];
+          Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4 *>(
+                                    static_cast<const uint16_t *>(p.y) + static_cast<int64_t>(q) * p.ldy + col),
+                                y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rs[e] += y[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += rs[e];
+      }
+      if (EPI == EPI_STORE_F32) {
+        float *o = static_cast<float *>(p.out) + m * p.ldo + col;
+        *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + m * p.ldo + col) =
+            Chunk<bf16_t>::pack(v);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0): reads done before rewrite
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <int BM, int BN, int EPI>
+hipError_t run2(const GemmArgs &a, hipStream_t s) {
+  constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  const int64_t n_tn = (a.N + NOUT - 1) / NOUT;
+  const int64_t max_m = a.tiles ? a.max_mtiles : (a.M + BM - 1) / BM;
+  const int64_t total = max_m * n_tn;
+  if (total == 0) return hipSuccess;
+  GemmArgs b = a;
+  b.max_mtiles = max_m;
+  const int64_t blocks = 8 * ((total + 7) / 8);
+  gemm2_kernel<BM, BN, EPI><<<static_cast<unsigned>(blocks), 256, 0, s>>>(b);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU: return run2<BM, BN, EPI_SWIGLU>(a, s);
+    case EPI_SCALE: return run2<BM, BN, EPI_SCALE>(a, s);
+    case EPI_STORE: return run2<BM, BN, EPI_STORE>(a, s);
+    case EPI_COMBINE: return run2<BM, BN, EPI_COMBINE>(a, s);
+    case EPI_STORE_F32: return run2<BM, BN, EPI_STORE_F32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool gemm2_applicable(const GemmArgs &a, int epi) {
+  if (a.K % 64 || (a.a2 && a.K2 % 64)) return false;
+  if (a.N % 8) return false;
+  if (epi == EPI_COMBINE && a.ldy % 8) return false;
+  return a.ldo % 8 == 0;
+}
+
+int gemm2_bm(int cfg) { return cfg == TILE2_128x256 ? 128 : 256; }
+
+#ifndef MOE_V2_MIN_TILES
+#define MOE_V2_MIN_TILES 200
+#endif
+
+int64_t gemm2_min_tiles() { return MOE_V2_MIN_TILES; }
+
+// Dense GEMM: the pipelined kernel when it applies and the tile count fills
+// the chip, else the generic kernel.
+hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s) {
+  if (a.M <= 64) return launch_gemm(a, epi, TILE_SMALL_M, act_bf16, s);
+  if (act_bf16 && gemm2_applicable(a, epi)) {
+    const int64_t nout = epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout);
+    if (tiles >= MOE_V2_MIN_TILES) return launch_gemm2(a, epi, TILE2_256x256, s);
+  }
+  return launch_gemm(a, epi, TILE_LARGE, act_bf16, s);
+}
+
+hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case TILE2_256x256: return dispatch2<256, 256>(a, epi, s);
+    case TILE2_256x128: return dispatch2<256, 128>(a, epi, s);
+    case TILE2_128x256: return dispatch2<128, 256>(a, epi, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -112,9 +112,20 @@ struct GemmArgs {
   int topk;
 };
 
-enum TileCfg { TILE_SMALL_M = 0, TILE_LARGE = 1 };
+// Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,
+// WIDE 128x256, TALL 256x128, HUGE 256x256 (fp32 uses SMALL_M / LARGE).
+enum TileCfg { TILE_SMALL_M = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_TALL = 3, TILE_HUGE = 4 };
 int tile_bm(int cfg);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
+
+// Pipelined bf16 GEMM (gemm2.hip): large tiles, direct-to-LDS loads.
+enum Tile2Cfg { TILE2_256x256 = 0, TILE2_256x128 = 1, TILE2_128x256 = 2 };
+bool gemm2_applicable(const GemmArgs &a, int epi);
+int gemm2_bm(int cfg);
+hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s);
+int64_t gemm2_min_tiles();
+// Dense GEMM with the kernel and tile shape chosen from the problem size.
+hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ combine
 // out[t] = sum_k y[inv[t*K+k]] (no shared expert, model width).

@@ -205,8 +205,7 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   } else {
     g.b0 = a.w;
   }
-  hipError_t e = launch_gemm(g, EPI_STORE_F32, a.T <= 64 ? TILE_SMALL_M : TILE_LARGE,
-                             act_bf16, s);
+  hipError_t e = launch_dense(g, EPI_STORE_F32, act_bf16, s);
   if (e != hipSuccess) return e;
   select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts);
   return hipGetLastError();
