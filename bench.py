@@ -55,6 +55,45 @@ def algorithmic(w, counts):
                 gu_flops=gu_flops, gu_bytes=gu_bytes, touched=touched)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: traffic figures are only valid for the kernels they came from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_ffn_fp32_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (copy-calibrated), or None when absent or
+    taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibrate_copy(mib: int, reps: int = 5):
+    """Plain device-to-device copy of a known size, for counter calibration."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
 def cpu_baseline(w, a, budget_s=12.0):
     """Time the CPU oracle (as it stands) on a seeded token sample."""
     import oracle
@@ -82,7 +121,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is not part of this build", file=sys.stderr)
@@ -142,7 +186,8 @@ def main():
         ach = alg["gu_bytes"] / (gu_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = "gemm_kernel (grouped gate/up + SiLU*up)"
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "grouped gate/up GEMM + SiLU*up"
     roof["kernel_ms"] = round(gu_ms, 4)
     log(f"step {ms:.4f} ms, {tok_s:.4g} tokens/s; gate/up kernel {gu_ms:.4f} ms; "
         f"experts touched {alg['touched']}/{w.E}; loads max {cnt.max()} min {cnt.min()}")

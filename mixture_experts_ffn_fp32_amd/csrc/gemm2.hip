@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   const char *arow[A_LD];
   const char *brow[B_LD];
   auto setup = [&](int seg) {
+    if (seg && !p.a2) return;  // no second K segment: keep the first segment's rows
     const char *abase = static_cast<const char *>(seg ? p.a2 : p.a);
     const int64_t lda = seg ? p.lda2 : p.lda;
 #pragma unroll
