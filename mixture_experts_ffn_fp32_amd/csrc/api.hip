@@ -18,7 +18,8 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
   size_t wsplit, logits;
-  size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, ntie;
+  size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, tiles2,
+      ntiles2, ntie;
   size_t z, h, y, hsh, r;
   size_t total;
   int64_t max_tiles;
@@ -41,7 +42,7 @@ Layout layout_of(const moe_desc *d) {
   };
   const int bf = d->act_dtype == MOE_BF16;
   L.wsplit = take(router_split_bytes(E, d->d_model, bf));
-  L.logits = take(router_logit_bytes(T, E, bf));
+  L.logits = take(router_logit_bytes(T, E, d->d_model, bf));
   L.idx = take(rows * 4);
   L.g = take(rows * 4);
   L.gap = take(T * 4);
@@ -55,6 +56,8 @@ Layout layout_of(const moe_desc *d) {
   L.max_tiles = grouped_tile_bound(rows, E, 16);  // smallest tile height in use
   L.tiles = take(static_cast<size_t>(L.max_tiles) * 12);
   L.ntiles = take(4);
+  L.tiles2 = take(static_cast<size_t>(L.max_tiles) * 12);
+  L.ntiles2 = take(4);
   L.ntie = take(4);
   L.z = d->latent ? take(T * d->latent * es) : 0;
   L.h = take(rows * d->d_ff * es);
@@ -87,28 +90,48 @@ int check_desc(const moe_desc *d) {
 #define MOE_GROUPED_V2 TILE2_256x256
 #endif
 
-// Kernel and tile shape of the grouped expert GEMMs (both share one m-tile
-// table, so one plan covers the pair).
-struct Plan {
+// Kernel and tile shape of each grouped expert GEMM. Each has its own m-tile
+// table unless the two tile heights agree.
+struct GemmPlan {
   int v2, cfg;
   int bm() const { return v2 ? gemm2_bm(cfg) : tile_bm(cfg); }
 };
+struct Plan {
+  GemmPlan gu, dn;  // gate/up, down
+  bool shared_table() const { return gu.bm() == dn.bm(); }
+};
+
+// Largest tile that still gives the chip ~200+ (pipelined) or 256+ (generic)
+// workgroups; m-tiles counted as rows/bm plus one partial tile per expert.
+GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, int bf) {
+  auto mtiles = [&](int bm) { return rows / bm + (rows < E ? rows : E); };
+  if (rows <= 32 * E) return {0, TILE_SMALL_M};  // ~32 rows per expert or fewer
+  if (bf && K % 64 == 0 && n_out % 8 == 0) {
+    const int64_t nout = glu ? 128 : 256;
+    if (mtiles(gemm2_bm(MOE_GROUPED_V2)) * ((n_out + nout - 1) / nout) >= gemm2_min_tiles())
+      return {1, MOE_GROUPED_V2};
+  }
+  const int64_t mt = mtiles(tile_bm(MOE_GROUPED_BIG));
+  if (!bf || glu || mt * tile_count(MOE_GROUPED_BIG, 1, n_out, glu) >= 256)
+    return {0, MOE_GROUPED_BIG};
+  return {0, TILE_TALL_N64};  // few down tiles (narrow model, few experts)
+}
 
 Plan plan_grouped(const moe_desc *d) {
   const int64_t rows = d->T * d->top_k, E = d->n_experts;
-  if (rows <= 32 * E) return {0, TILE_SMALL_M};  // about 32 rows per expert or fewer
   const int64_t de = d->latent ? d->latent : d->d_model;
-  if (d->act_dtype == MOE_BF16 && de % 64 == 0 && d->d_ff % 64 == 0) {
-    const int bm = gemm2_bm(MOE_GROUPED_V2);
-    const int64_t mt = rows / bm + (rows < E ? rows : E);
-    if (mt * ((d->d_ff + 127) / 128) >= gemm2_min_tiles()) return {1, MOE_GROUPED_V2};
-  }
-  return {0, MOE_GROUPED_BIG};
+  const int bf = d->act_dtype == MOE_BF16;
+  return {plan_one(rows, E, de, d->d_ff, 1, bf), plan_one(rows, E, d->d_ff, de, 0, bf)};
 }
 
-hipError_t run_grouped(const GemmArgs &a, int epi, const Plan &pl, int bf, hipStream_t s) {
+hipError_t run_grouped(const GemmArgs &a, int epi, const GemmPlan &pl, int bf, hipStream_t s) {
   return pl.v2 ? launch_gemm2(a, epi, pl.cfg, s) : launch_gemm(a, epi, pl.cfg, bf, s);
 }
+
+// m-tile tables of the two grouped GEMMs (gate/up, down)
+struct Tables {
+  const int32_t *gu, *gu_n, *dn, *dn_n;
+};
 
 struct Probe {
   const moe_probe *p;
@@ -129,9 +152,8 @@ struct Probe {
 // Grouped SwiGLU over the sorted rows: GEMM 1 (gate/up + SiLU*up) into h,
 // GEMM 2 (down, times row_scale) into y.
 int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
-                 const int32_t *row_index, const int32_t *tiles, const int32_t *n_tiles,
-                 const Plan &pl, const float *row_scale, void *h, void *y, const Probe &pr,
-                 hipStream_t s) {
+                 const int32_t *row_index, const Tables &tb, const Plan &pl,
+                 const float *row_scale, void *h, void *y, const Probe &pr, hipStream_t s) {
   const int64_t rows_n = d->T * d->top_k;
   const int de = d->latent ? d->latent : d->d_model;
   const int bf = d->act_dtype == MOE_BF16;
@@ -145,13 +167,13 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   a.b_stride = static_cast<int64_t>(d->d_ff) * de;
   a.K = de;
   a.N = d->d_ff;
-  a.tiles = tiles;
-  a.n_tiles = n_tiles;
-  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.bm());
+  a.tiles = tb.gu;
+  a.n_tiles = tb.gu_n;
+  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.gu.bm());
   a.out = h;
   a.ldo = d->d_ff;
   pr.begin(MOE_STAGE_EXPERT_GATE_UP);
-  MOE_TRY(run_grouped(a, EPI_SWIGLU, pl, bf, s));
+  MOE_TRY(run_grouped(a, EPI_SWIGLU, pl.gu, bf, s));
   pr.end(MOE_STAGE_EXPERT_GATE_UP);
 
   GemmArgs b{};
@@ -162,14 +184,14 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   b.b_stride = static_cast<int64_t>(de) * d->d_ff;
   b.K = d->d_ff;
   b.N = de;
-  b.tiles = tiles;
-  b.n_tiles = n_tiles;
-  b.max_mtiles = a.max_mtiles;
+  b.tiles = tb.dn;
+  b.n_tiles = tb.dn_n;
+  b.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.dn.bm());
   b.out = y;
   b.ldo = de;
   b.row_scale = row_scale;
   pr.begin(MOE_STAGE_EXPERT_DOWN);
-  MOE_TRY(run_grouped(b, EPI_SCALE, pl, bf, s));
+  MOE_TRY(run_grouped(b, EPI_SCALE, pl.dn, bf, s));
   pr.end(MOE_STAGE_EXPERT_DOWN);
   return MOE_OK;
 }
@@ -367,6 +389,14 @@ int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const vo
   return MOE_OK;
 }
 
+Tables tables_of(char *wsb, const Layout &L, const Plan &pl) {
+  const int32_t *t1 = reinterpret_cast<int32_t *>(wsb + L.tiles);
+  const int32_t *n1 = reinterpret_cast<int32_t *>(wsb + L.ntiles);
+  if (pl.shared_table()) return {t1, n1, t1, n1};
+  return {t1, n1, reinterpret_cast<int32_t *>(wsb + L.tiles2),
+          reinterpret_cast<int32_t *>(wsb + L.ntiles2)};
+}
+
 int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
                    const int32_t *row_index, const int32_t *offsets, const float *row_scale,
                    void *y_sorted, void *ws, size_t ws_bytes, void *stream) {
@@ -381,12 +411,14 @@ int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
   char *wsb = static_cast<char *>(ws);
   const int64_t rows_n = d->T * d->top_k;
   const Plan pl = plan_grouped(d);
-  int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
-  int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
-  MOE_TRY(launch_tiles(offsets, d->n_experts, pl.bm(), tiles, nt, s));
+  const Tables tb = tables_of(wsb, L, pl);
+  MOE_TRY(launch_tiles(offsets, d->n_experts, pl.gu.bm(), const_cast<int32_t *>(tb.gu),
+                       const_cast<int32_t *>(tb.gu_n), s));
+  if (!pl.shared_table())
+    MOE_TRY(launch_tiles(offsets, d->n_experts, pl.dn.bm(), const_cast<int32_t *>(tb.dn),
+                         const_cast<int32_t *>(tb.dn_n), s));
   const Probe pr{nullptr, s};
-  return expert_gemms(d, w, rows, row_index, tiles, nt, pl, row_scale, wsb + L.h, y_sorted, pr,
-                      s);
+  return expert_gemms(d, w, rows, row_index, tb, pl, row_scale, wsb + L.h, y_sorted, pr, s);
 }
 
 int moe_combine(const moe_desc *d, const moe_weights *w, const void *x, const void *y_sorted,
@@ -430,9 +462,8 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   int32_t *stok = reinterpret_cast<int32_t *>(wsb + L.stok);
   int32_t *inv = reinterpret_cast<int32_t *>(wsb + L.inv);
   float *sw = reinterpret_cast<float *>(wsb + L.sw);
-  int32_t *tiles = reinterpret_cast<int32_t *>(wsb + L.tiles);
-  int32_t *nt = reinterpret_cast<int32_t *>(wsb + L.ntiles);
   const Plan pl = plan_grouped(d);
+  const Tables tb = tables_of(wsb, L, pl);
 
   // 1. router
   RouterArgs ra{};
@@ -465,9 +496,14 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   sa.E = static_cast<int>(E);
   sa.counts = cnt;
   sa.offsets = offsets;
-  sa.bm = pl.bm();
-  sa.tiles = tiles;
-  sa.n_tiles = nt;
+  sa.bm = pl.gu.bm();
+  sa.tiles = const_cast<int32_t *>(tb.gu);
+  sa.n_tiles = const_cast<int32_t *>(tb.gu_n);
+  if (!pl.shared_table()) {
+    sa.bm2 = pl.dn.bm();
+    sa.tiles2 = const_cast<int32_t *>(tb.dn);
+    sa.n_tiles2 = const_cast<int32_t *>(tb.dn_n);
+  }
   sa.gap = n_near_ties ? gap : nullptr;
   sa.T = T;
   sa.tie_eps = kTieEps;
@@ -508,7 +544,7 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   }
 
   // 4. grouped expert SwiGLU (gather fused into GEMM 1's A load)
-  if ((rc = expert_gemms(d, w, rsrc, stok, tiles, nt, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
+  if ((rc = expert_gemms(d, w, rsrc, stok, tb, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
     return rc;
 
   // 5. shared experts + combine

@@ -94,6 +94,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
   }
   __syncthreads();
   if (a.tiles) build_tiles(off, a.E, a.bm, start, tmp, a.tiles, a.n_tiles);
+  __syncthreads();
+  if (a.tiles2) build_tiles(off, a.E, a.bm2, start, tmp, a.tiles2, a.n_tiles2);
+  __syncthreads();
   if (a.gap && a.n_near_ties) {
     int n = 0;
     for (int64_t i = t; i < a.T; i += 1024) n += (a.gap[i] < a.tie_eps) ? 1 : 0;

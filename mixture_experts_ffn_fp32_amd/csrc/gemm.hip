@@ -87,17 +87,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // ---------------------------------------------------------------- tile
   const int n_tn = (p.N + NOUT - 1) / NOUT;
   const int64_t n_m = p.tiles ? static_cast<int64_t>(*p.n_tiles) : p.max_mtiles;
-  const int64_t total = n_m * n_tn;
+  const int ksplit = p.k_split > 1 ? p.k_split : 1;
+  const int64_t total = n_m * n_tn * ksplit;
   const int64_t per = (total + 7) / 8;
   const int64_t local = blockIdx.x >> 3;
   if (local >= per) return;
   const int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
   if (pid >= total) return;
+  const int64_t tiles2d = n_m * n_tn;
+  const int split = static_cast<int>(pid / tiles2d);
+  const int64_t tpid = pid - split * tiles2d;
   constexpr int GM = 4;
-  const int64_t grp = pid / (GM * n_tn);
+  const int64_t grp = tpid / (GM * n_tn);
   const int64_t first_m = grp * GM;
   const int gsz = static_cast<int>(min<int64_t>(n_m - first_m, GM));
-  const int64_t in_g = pid - grp * GM * n_tn;
+  const int64_t in_g = tpid - grp * GM * n_tn;
   const int64_t mt = first_m + in_g % gsz;
   const int nt = static_cast<int>(in_g / gsz);
   int64_t expert = 0, m_begin, m_end;
@@ -154,6 +158,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 
   const int steps1 = (p.K + BK - 1) / BK;
   const int steps = steps1 + (p.a2 ? (p.K2 + BK - 1) / BK : 0);
+  // this split's stages (single-segment GEMMs only are split)
+  const int per_split = (steps + ksplit - 1) / ksplit;
+  const int st_begin = min(steps, split * per_split);
+  const int st_end = min(steps, st_begin + per_split);
   uint4 ra[A_LD], rb[B_LD];
   auto load = [&](int st) {
     const bool s2 = st >= steps1;
@@ -200,12 +208,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   setup(0);
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < steps;
+  if (st_begin < st_end) {
+    load(st_begin);
+    store(0);
+    __syncthreads();
+  }
+  for (int st = st_begin; st < st_end; ++st) {
+    const int cur = (st - st_begin) & 1;
+    const bool more = st + 1 < st_end;
     if (more) {
       if (st + 1 == steps1) setup(1);
       load(st + 1);
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
           v = acc[fm][fo][r];
         }
         if (EPI == EPI_STORE_F32)
-          static_cast<float *>(p.out)[m * p.ldo + col] = v;
+          static_cast<float *>(p.out)[split * p.split_stride + m * p.ldo + col] = v;
         else
           Elem<T>::store(p.out, m * p.ldo + col, v);
       }
@@ -274,6 +284,15 @@ struct CfgSmallM {  // few rows per expert (decode): stream B
 struct CfgLarge {
   static constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
 };
+struct CfgTallN64 {  // few output columns: half-width tiles
+  static constexpr int BM = 128, BN = 64, WM = 2, WN = 2;
+};
+struct CfgMid {  // small problems: more, smaller tiles
+  static constexpr int BM = 64, BN = 64, WM = 2, WN = 2;
+};
+struct CfgSmallN64 {  // few rows (decode-sized dense GEMMs): narrow tiles, many workgroups
+  static constexpr int BM = 16, BN = 64, WM = 1, WN = 2;
+};
 struct CfgWide {
   static constexpr int BM = 128, BN = 256, WM = 2, WN = 2;
 };
@@ -286,10 +305,11 @@ struct CfgHuge {
 
 template <typename T, typename C, int EPI>
 hipError_t run(const GemmArgs &a, hipStream_t s) {
+  if (a.k_split > 1 && (EPI != EPI_STORE_F32 || a.a2)) return hipErrorInvalidValue;
   constexpr int NOUT = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;
   const int64_t n_tn = (a.N + NOUT - 1) / NOUT;
   const int64_t max_m = a.tiles ? a.max_mtiles : (a.M + C::BM - 1) / C::BM;
-  const int64_t total = max_m * n_tn;
+  const int64_t total = max_m * n_tn * (a.k_split > 1 ? a.k_split : 1);
   if (total == 0) return hipSuccess;
   GemmArgs b = a;
   b.max_mtiles = max_m;
@@ -313,8 +333,27 @@ hipError_t dispatch_epi(const GemmArgs &a, int epi, hipStream_t s) {
 
 }  // namespace
 
+template <typename C>
+int64_t tiles_of(int64_t rows, int64_t n_out, int glu) {
+  const int64_t nout = glu ? C::BN / 2 : C::BN;
+  return ((rows + C::BM - 1) / C::BM) * ((n_out + nout - 1) / nout);
+}
+
+int64_t tile_count(int cfg, int64_t rows, int64_t n_out, int glu) {
+  switch (cfg) {
+    case TILE_SMALL_M: return tiles_of<CfgSmallM>(rows, n_out, glu);
+    case TILE_MID: return tiles_of<CfgMid>(rows, n_out, glu);
+    case TILE_TALL_N64: return tiles_of<CfgTallN64>(rows, n_out, glu);
+    case TILE_SMALL_N64: return tiles_of<CfgSmallN64>(rows, n_out, glu);
+    default: return tiles_of<CfgLarge>(rows, n_out, glu);
+  }
+}
+
 int tile_bm(int cfg) {
   switch (cfg) {
+    case TILE_MID: return CfgMid::BM;
+    case TILE_TALL_N64: return CfgTallN64::BM;
+    case TILE_SMALL_N64: return CfgSmallN64::BM;
     case TILE_SMALL_M: return CfgSmallM::BM;
     case TILE_LARGE: return CfgLarge::BM;
     case TILE_WIDE: return CfgWide::BM;
@@ -330,6 +369,9 @@ hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStr
                                : dispatch_epi<float, CfgLarge>(a, epi, s);
   switch (cfg) {
     case TILE_SMALL_M: return dispatch_epi<bf16_t, CfgSmallM>(a, epi, s);
+    case TILE_MID: return dispatch_epi<bf16_t, CfgMid>(a, epi, s);
+    case TILE_TALL_N64: return dispatch_epi<bf16_t, CfgTallN64>(a, epi, s);
+    case TILE_SMALL_N64: return dispatch_epi<bf16_t, CfgSmallN64>(a, epi, s);
     case TILE_WIDE: return dispatch_epi<bf16_t, CfgWide>(a, epi, s);
     case TILE_TALL: return dispatch_epi<bf16_t, CfgTall>(a, epi, s);
     case TILE_HUGE: return dispatch_epi<bf16_t, CfgHuge>(a, epi, s);

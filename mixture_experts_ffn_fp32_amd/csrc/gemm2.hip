@@ -328,6 +328,7 @@ hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
 }  // namespace
 
 bool gemm2_applicable(const GemmArgs &a, int epi) {
+  if (a.k_split > 1) return false;
   if (a.K % 64 || (a.a2 && a.K2 % 64)) return false;
   if (a.N % 8) return false;
   if (epi == EPI_COMBINE && a.ldy % 8) return false;
@@ -342,16 +343,26 @@ int gemm2_bm(int cfg) { return cfg == TILE2_128x256 ? 128 : 256; }
 
 int64_t gemm2_min_tiles() { return MOE_V2_MIN_TILES; }
 
-// Dense GEMM: the pipelined kernel when it applies and the tile count fills
-// the chip, else the generic kernel.
+// Dense GEMM: the pipelined kernel when it applies and its tile count fills
+// the chip; else the largest generic tile that still gives every CU a
+// workgroup (few rows: 16-row tiles, as wide as that allows).
 hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s) {
-  if (a.M <= 64) return launch_gemm(a, epi, TILE_SMALL_M, act_bf16, s);
+  const int glu = epi == EPI_SWIGLU;
+  const int64_t ks = a.k_split > 1 ? a.k_split : 1;
+  constexpr int64_t kFill = 256;
+  if (a.M <= 64) {
+    const bool wide = ks * tile_count(TILE_SMALL_M, a.M, a.N, glu) >= kFill;
+    return launch_gemm(a, epi, wide || !act_bf16 ? TILE_SMALL_M : TILE_SMALL_N64, act_bf16, s);
+  }
   if (act_bf16 && gemm2_applicable(a, epi)) {
-    const int64_t nout = epi == EPI_SWIGLU ? 128 : 256;
+    const int64_t nout = glu ? 128 : 256;
     const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout);
     if (tiles >= MOE_V2_MIN_TILES) return launch_gemm2(a, epi, TILE2_256x256, s);
   }
-  return launch_gemm(a, epi, TILE_LARGE, act_bf16, s);
+  if (!act_bf16) return launch_gemm(a, epi, TILE_LARGE, act_bf16, s);
+  for (int cfg : {TILE_LARGE, TILE_TALL_N64, TILE_MID})
+    if (ks * tile_count(cfg, a.M, a.N, glu) >= kFill) return launch_gemm(a, epi, cfg, act_bf16, s);
+  return launch_gemm(a, epi, TILE_SMALL_N64, act_bf16, s);
 }
 
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s) {

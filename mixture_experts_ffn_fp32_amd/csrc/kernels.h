@@ -28,13 +28,21 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
 inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
   return act_bf16 ? static_cast<size_t>(3 * E * d * 2) : 0;
 }
-inline size_t router_logit_bytes(int64_t T, int64_t E, int act_bf16) {
-  return static_cast<size_t>(T * E * (act_bf16 ? 3 : 1) * 4);
+// K splits of the router GEMM: few tokens (decode) cannot fill the chip
+// with output tiles alone, so the reduction over d is split and the
+// partial logits are summed in fixed order by the selection kernel.
+inline int router_splits(int64_t T, int64_t d) {
+  if (T > 256) return 1;
+  const int64_t s = d / 512;
+  return s < 1 ? 1 : (s > 8 ? 8 : static_cast<int>(s));
+}
+inline size_t router_logit_bytes(int64_t T, int64_t E, int64_t d, int act_bf16) {
+  return static_cast<size_t>(T * E * (act_bf16 ? 3 : 1) * 4 * router_splits(T, d));
 }
 
 // ------------------------------------------------------------------ dispatch
 // Slots per histogram / scatter chunk.
-constexpr int kChunkSlots = 4096;
+constexpr int kChunkSlots = 1024;
 
 __host__ __device__ inline int64_t n_chunks(int64_t slots) { return (slots + kChunkSlots - 1) / kChunkSlots; }
 
@@ -48,10 +56,13 @@ struct ScanArgs {
   int E;
   int32_t *counts;            // [E]
   int32_t *offsets;           // [E+1]
-  // grouped GEMM m-tile table for tile height bm (tiles null -> skipped)
+  // grouped GEMM m-tile tables for tile heights bm / bm2 (tiles null -> skipped)
   int bm;
   int32_t *tiles;             // [max_tiles, 3] {expert, row_begin, row_end}
   int32_t *n_tiles;           // [1]
+  int bm2;
+  int32_t *tiles2;
+  int32_t *n_tiles2;
   // near-tie count of the router gap (gap null -> skipped)
   const float *gap;
   int64_t T;
@@ -110,11 +121,20 @@ struct GemmArgs {
   int64_t ldy;
   const int32_t *inv;
   int topk;
+  int k_split;               // fp32-store only: K split count (0 or 1 = none);
+  int64_t split_stride;      // elements between the splits' partial outputs
 };
 
 // Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,
-// WIDE 128x256, TALL 256x128, HUGE 256x256 (fp32 uses SMALL_M / LARGE).
-enum TileCfg { TILE_SMALL_M = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_TALL = 3, TILE_HUGE = 4 };
+// WIDE 128x256, TALL 256x128, HUGE 256x256, MID 64x64, SMALL_N64 16x64,
+// TALL_N64 128x64 (fp32 uses SMALL_M / LARGE only).
+enum TileCfg {
+  TILE_SMALL_M = 0, TILE_LARGE = 1, TILE_WIDE = 2, TILE_TALL = 3, TILE_HUGE = 4, TILE_MID = 5,
+  TILE_SMALL_N64 = 6, TILE_TALL_N64 = 7
+};
+// Output tiles of a GEMM of `rows` x `n_out` under a tile shape (SwiGLU
+// halves the B rows of a tile into output columns).
+int64_t tile_count(int cfg, int64_t rows, int64_t n_out, int glu);
 int tile_bm(int cfg);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
 

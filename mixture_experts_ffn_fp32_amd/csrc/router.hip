@@ -52,8 +52,11 @@ __global__ __launch_bounds__(256) void split_kernel(const float *__restrict__ w,
   }
 }
 
-// One wavefront per token over the partial logits [T, parts * E].
-__global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts) {
+// One wavefront per token over the partial logits [splits][T, parts * E]:
+// the K-split partials of each plane are summed in split order, then the
+// planes high + mid + low.
+__global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, int splits,
+                                                     int64_t split_stride) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int lane = threadIdx.x & 63;
@@ -70,8 +73,16 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts) {
     const int e = lane + 64 * j;
     float sc = -INFINITY, l = 0.f;
     if (e < E) {
-      l = lg[e];
-      if (parts == 3) l = (l + lg[E + e]) + lg[2 * E + e];
+      float pl[3] = {0.f, 0.f, 0.f};
+      for (int q = 0; q < splits; ++q) {
+        const float *ls = lg + q * split_stride;
+        pl[0] += ls[e];
+        if (parts == 3) {
+          pl[1] += ls[E + e];
+          pl[2] += ls[2 * E + e];
+        }
+      }
+      l = parts == 3 ? (pl[0] + pl[1]) + pl[2] : pl[0];
       const float b = a.bias ? a.bias[e] : 0.f;
       sc = sig ? sigmoidf_(l) + b : l + b;
       vmax = fmaxf(vmax, sc);
@@ -194,6 +205,9 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   const int parts = act_bf16 ? 3 : 1;
   g.N = parts * a.E;
   g.ldo = g.N;
+  const int splits = router_splits(a.T, a.d);
+  g.k_split = splits;
+  g.split_stride = a.T * g.N;
   if (act_bf16) {
     int64_t blocks = (nw + 255) / 256;
     if (blocks > 4096) blocks = 4096;
@@ -207,7 +221,8 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   }
   hipError_t e = launch_dense(g, EPI_STORE_F32, act_bf16, s);
   if (e != hipSuccess) return e;
-  select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts);
+  select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts, splits,
+                                                                      g.split_stride);
   return hipGetLastError();
 }
 
