@@ -103,10 +103,15 @@ struct Plan {
 
 // Largest tile that still gives the chip ~200+ (pipelined) or 256+ (generic)
 // workgroups; m-tiles counted as rows/bm plus one partial tile per expert.
-GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, int bf) {
+// (a_rows: rows the GEMM's A operand spans; the pipelined kernel addresses
+// A and each expert's B with 32-bit offsets.)
+GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, int bf,
+                  int64_t a_rows) {
   auto mtiles = [&](int bm) { return rows / bm + (rows < E ? rows : E); };
   if (rows <= 32 * E) return {0, TILE_SMALL_M};  // ~32 rows per expert or fewer
-  if (bf && K % 64 == 0 && n_out % 8 == 0) {
+  constexpr int64_t kLim = int64_t(1) << 32;
+  const bool small_extent = a_rows * K * 2 < kLim && n_out * K * 2 < kLim;
+  if (bf && K % 64 == 0 && n_out % 8 == 0 && small_extent) {
     const int64_t nout = glu ? 128 : 256;
     if (mtiles(gemm2_bm(MOE_GROUPED_V2)) * ((n_out + nout - 1) / nout) >= gemm2_min_tiles())
       return {1, MOE_GROUPED_V2};
@@ -121,11 +126,14 @@ Plan plan_grouped(const moe_desc *d) {
   const int64_t rows = d->T * d->top_k, E = d->n_experts;
   const int64_t de = d->latent ? d->latent : d->d_model;
   const int bf = d->act_dtype == MOE_BF16;
-  return {plan_one(rows, E, de, d->d_ff, 1, bf), plan_one(rows, E, d->d_ff, de, 0, bf)};
+  return {plan_one(rows, E, de, d->d_ff, 1, bf, rows),  // A: T tokens or T*K gathered rows
+          plan_one(rows, E, d->d_ff, de, 0, bf, rows)};
 }
 
 hipError_t run_grouped(const GemmArgs &a, int epi, const GemmPlan &pl, int bf, hipStream_t s) {
-  return pl.v2 ? launch_gemm2(a, epi, pl.cfg, s) : launch_gemm(a, epi, pl.cfg, bf, s);
+  if (!pl.v2) return launch_gemm(a, epi, pl.cfg, bf, s);
+  if (!gemm2_applicable(a, epi)) return hipErrorInvalidValue;  // the plan checked this
+  return launch_gemm2(a, epi, pl.cfg, s);
 }
 
 // m-tile tables of the two grouped GEMMs (gate/up, down)
@@ -167,6 +175,7 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   a.b_stride = static_cast<int64_t>(d->d_ff) * de;
   a.K = de;
   a.N = d->d_ff;
+  a.a_extent = row_index ? d->T : rows_n;  // tokens, or rows already gathered
   a.tiles = tb.gu;
   a.n_tiles = tb.gu_n;
   a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.gu.bm());
@@ -184,6 +193,7 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   b.b_stride = static_cast<int64_t>(de) * d->d_ff;
   b.K = d->d_ff;
   b.N = de;
+  b.a_extent = rows_n;
   b.tiles = tb.dn;
   b.n_tiles = tb.dn_n;
   b.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.dn.bm());

@@ -56,6 +56,10 @@ __device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+#ifndef MOE_G2_PIPE
+#define MOE_G2_PIPE 1
+#endif
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -101,39 +105,47 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   // load j of a thread covers tile row (tid / 8 + 32 j), logical chunk tid % 8
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
-  const char *arow[A_LD];
-  const char *brow[B_LD];
+  // Loads go through buffer resources: a uniform base and byte extent per
+  // operand (per gate / up half, per expert) and a 32-bit offset per load
+  // (extents below 4 GiB are a launch precondition); the stage's k offset is
+  // the scalar offset. Accesses past an extent would read zeros.
+  auto rsrc = [](const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(static_cast<uint32_t>(bytes)),
+                                             0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t ar, br0, br1;
+  uint32_t aoff[A_LD], boff[B_LD];
   auto setup = [&](int seg) {
     if (seg && !p.a2) return;  // no second K segment: keep the first segment's rows
-    const char *abase = static_cast<const char *>(seg ? p.a2 : p.a);
     const int64_t lda = seg ? p.lda2 : p.lda;
+    const int64_t a_rows = seg ? p.M : (p.a_extent ? p.a_extent : p.M);
+    ar = rsrc(seg ? p.a2 : p.a, a_rows * lda * 2);
 #pragma unroll
     for (int j = 0; j < A_LD; ++j) {
       const int r = lrow + 32 * j;
       int64_t m = m_begin + r;
       if (m >= m_end) m = m_begin;  // results of these rows are never stored
       const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
-      arow[j] = abase + (src * lda + lchunk * 8) * 2;
+      aoff[j] = static_cast<uint32_t>((src * lda + lchunk * 8) * 2);
+    }
+    int64_t ldb;
+    if (seg) {
+      ldb = p.ldb2;
+      br0 = br1 = rsrc(p.b2, static_cast<int64_t>(p.N) * ldb * 2);
+    } else {
+      ldb = p.ldb;
+      const int64_t eoff = expert * p.b_stride * 2, bytes = static_cast<int64_t>(p.N) * ldb * 2;
+      br0 = rsrc(static_cast<const char *>(p.b0) + eoff, bytes);
+      br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, bytes) : br0;
     }
 #pragma unroll
     for (int j = 0; j < B_LD; ++j) {
       const int r = lrow + 32 * j;
-      const char *bbase;
-      int n;
-      int64_t ldb, off = 0;
-      if (seg) {
-        bbase = static_cast<const char *>(p.b2);
-        n = n_begin + r;
-        ldb = p.ldb2;
-      } else {
-        const bool up = GLU && r >= BN / 2;
-        bbase = static_cast<const char *>(up ? p.b1 : p.b0);
-        n = n_begin + (up ? r - BN / 2 : r);
-        ldb = p.ldb;
-        off = expert * p.b_stride;
-      }
+      const bool up = !seg && GLU && r >= BN / 2;
+      int n = n_begin + (up ? r - BN / 2 : r);
       if (n >= p.N) n = p.N - 1;
-      brow[j] = bbase + (off + static_cast<int64_t>(n) * ldb + lchunk * 8) * 2;
+      boff[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * ldb + lchunk * 8) * 2);
     }
   };
 
@@ -142,12 +154,19 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
 
   // registers of the next stage
   u32x4 ra[A_LD], rb[B_LD];
+  auto load_one = [&](int st, int j) {
+    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
+    if (j < A_LD) {
+      ra[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[j], kb, 0);
+    } else {
+      const int jb = j - A_LD;  // gate rows first, then up rows (SwiGLU)
+      rb[jb] = __builtin_amdgcn_raw_buffer_load_b128((GLU && jb >= B_LD / 2) ? br1 : br0,
+                                                     boff[jb], kb, 0);
+    }
+  };
   auto load = [&](int st) {
-    const int64_t kb = static_cast<int64_t>(st >= steps1 ? st - steps1 : st) * 128;
 #pragma unroll
-    for (int j = 0; j < A_LD; ++j) ra[j] = *reinterpret_cast<const u32x4 *>(arow[j] + kb);
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(brow[j] + kb);
+    for (int j = 0; j < A_LD + B_LD; ++j) load_one(st, j);
   };
   auto put = [&](u32x4 *buf) {
 #pragma unroll
@@ -175,9 +194,96 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   const int64_t rows_left = m_end - (m_begin + wm * WTM);
   const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
 
+  const int live = __builtin_amdgcn_readfirstlane(fm_live);
+#if MOE_G2_PIPE
+  // Software pipeline over half-stages (one MFMA k-step each). Fragment
+  // registers come in two sets: set 0 holds k-step 0 of the current stage,
+  // set 1 k-step 1. Per stage, with `cur` the stage's LDS buffer:
+  //   M0: MFMAs of set 0, interleaved row by row with the reads of set 1
+  //       (from cur), the LDS writes of the next stage into the other buffer
+  //       (from the staging registers) and the global loads of the stage
+  //       after next into the freed staging registers;
+  //   barrier (after lgkmcnt 0): the next stage is visible, and every read
+  //       of the other buffer issued before it has completed;
+  //   M1: MFMAs of set 1, interleaved with the reads of the next stage's
+  //       k-step 0 into set 0.
+  // Each MFMA group's operands were requested one half-stage earlier, and the
+  // global loads have a full stage to land. sched_barrier keeps this order.
+  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
+  auto rd = [&](const u32x4 *buf, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
+    const int kc = 4 * ks + fc;
+    if (i < FN)
+      xb[i] = __builtin_bit_cast(bf16x8, buf[BM * 8 + sw8(brow_of(i) + fr, kc)]);
+    else
+      xa[i - FN] = __builtin_bit_cast(bf16x8, buf[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
+  };
+  auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
+  };
+  constexpr int NRD = FM + FN;              // fragment reads per set
+  constexpr int RD_PER = (NRD + FM - 1) / FM;
+  constexpr int WR_PER = (A_LD + B_LD + FM - 1) / FM;
+  auto put_one = [&](u32x4 *buf, int j) {
+    if (j < A_LD) buf[sw8(lrow + 32 * j, lchunk)] = ra[j];
+    else buf[BM * 8 + sw8(lrow + 32 * (j - A_LD), lchunk)] = rb[j - A_LD];
+  };
+
+  setup(0);
+  load(0);
+  put(g2_s0);
+  if (steps1 == 1 && steps > 1) setup(1);
+  load(steps > 1 ? 1 : 0);
+  barrier();
+#pragma unroll
+  for (int i = 0; i < NRD; ++i) rd(g2_s0, 0, i, xa0, xb0);
+  // One stage from CUR; NXT receives the next stage. Near the end the loads
+  // repeat the last stage and the next-stage writes and reads are unused,
+  // so the body has no conditions beyond the rows check of partial tiles.
+#define G2_STAGE(ST, CUR, NXT)                                                   \
+  {                                                                              \
+    const int st_ = (ST);                                                        \
+    if (st_ >= steps) break;                                                     \
+    if (st_ + 2 == steps1 && st_ + 2 < steps) setup(1);                          \
+    const int ld_ = st_ + 2 < steps ? st_ + 2 : steps - 1;                       \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): set 0 has landed */       \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) {                          \
+      if (fm < live) mrow(fm, xa0, xb0);                                         \
+      _Pragma("unroll") for (int q = 0; q < RD_PER; ++q) {                       \
+        const int i = fm * RD_PER + q;                                           \
+        if (i < NRD) rd(CUR, 1, i, xa1, xb1);                                    \
+      }                                                                          \
+      _Pragma("unroll") for (int q = 0; q < WR_PER; ++q) {                       \
+        const int j = fm * WR_PER + q;                                           \
+        if (j < A_LD + B_LD) {                                                   \
+          put_one(NXT, j);                                                       \
+          load_one(ld_, j);                                                      \
+        }                                                                        \
+      }                                                                          \
+      __builtin_amdgcn_sched_barrier(0);                                         \
+    }                                                                            \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                         \
+    barrier();                                                                   \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) {                          \
+      if (fm < live) mrow(fm, xa1, xb1);                                         \
+      _Pragma("unroll") for (int q = 0; q < RD_PER; ++q) {                       \
+        const int i = fm * RD_PER + q;                                           \
+        if (i < NRD) rd(NXT, 0, i, xa0, xb0);                                    \
+      }                                                                          \
+      __builtin_amdgcn_sched_barrier(0);                                         \
+    }                                                                            \
+  }
+  for (int st = 0; st < steps; st += 2) {
+    G2_STAGE(st + 0, g2_s0, g2_s1)
+    G2_STAGE(st + 1, g2_s1, g2_s0)
+  }
+#undef G2_STAGE
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier();  // the epilogue reuses the stage buffers
+#else
   // all fragments are read first (rows past the tile read stale LDS, and
   // their MFMAs are skipped), so the MFMAs issue back to back
-  const int live = __builtin_amdgcn_readfirstlane(fm_live);
   auto compute = [&](const u32x4 *buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -229,6 +335,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
     G2_STAGE(st + 1, g2_s1, g2_s0)
   }
 #undef G2_STAGE
+#endif
 
   // ------------------------------------------------------------ epilogue
   // each wave: 16 rows x (OUT cols) of fp32 at a time in its 8 KB+ slice
@@ -329,6 +436,11 @@ hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
 
 bool gemm2_applicable(const GemmArgs &a, int epi) {
   if (a.k_split > 1) return false;
+  // 32-bit load offsets: A (rows it may address), each B slice, below 4 GiB
+  constexpr int64_t kLim = int64_t(1) << 32;
+  const int64_t a_rows = a.a_extent ? a.a_extent : (a.tiles ? 0 : a.M);
+  if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim || int64_t(a.N) * a.ldb * 2 >= kLim) return false;
+  if (a.a2 && (a.M * a.lda2 * 2 >= kLim || int64_t(a.N) * a.ldb2 * 2 >= kLim)) return false;
   if (a.K % 64 || (a.a2 && a.K2 % 64)) return false;
   if (a.N % 8) return false;
   if (epi == EPI_COMBINE && a.ldy % 8) return false;

@@ -121,6 +121,7 @@ struct GemmArgs {
   int64_t ldy;
   const int32_t *inv;
   int topk;
+  int64_t a_extent;          // rows A may address (0: M; required for tile tables)
   int k_split;               // fp32-store only: K split count (0 or 1 = none);
   int64_t split_stride;      // elements between the splits' partial outputs
 };
