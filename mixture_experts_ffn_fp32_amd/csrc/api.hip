@@ -110,7 +110,7 @@ GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, in
   auto mtiles = [&](int bm) { return rows / bm + (rows < E ? rows : E); };
   if (rows <= 32 * E) return {0, TILE_SMALL_M};  // ~32 rows per expert or fewer
   constexpr int64_t kLim = int64_t(1) << 32;
-  const bool small_extent = a_rows * K * 2 < kLim && n_out * K * 2 < kLim;
+  const bool small_extent = a_rows * K * 2 < kLim && (n_out + 256) * K * 2 < kLim;
   if (bf && K % 64 == 0 && n_out % 8 == 0 && small_extent) {
     const int64_t nout = glu ? 128 : 256;
     if (mtiles(gemm2_bm(MOE_GROUPED_V2)) * ((n_out + nout - 1) / nout) >= gemm2_min_tiles())

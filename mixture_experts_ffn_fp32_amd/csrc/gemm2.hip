@@ -34,16 +34,40 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxStageBytes = (256 + 256) * 128;  // largest tile, one stage
+#ifndef MOE_G2_PIPE
+#define MOE_G2_PIPE 1
+#endif
+#ifndef MOE_G2_ROLL
+#define MOE_G2_ROLL 1
+#endif
+#ifndef MOE_G2_DMA
+#define MOE_G2_DMA 1
+#endif
 
-__shared__ __attribute__((aligned(1024))) u32x4 g2_s0[kMaxStageBytes / 16];
-__shared__ __attribute__((aligned(1024))) u32x4 g2_s1[kMaxStageBytes / 16];
+constexpr int kMaxStageBytes = (256 + 256) * 128;  // largest tile, one stage
+// direct-to-LDS loads: two A buffers and three B buffers of one stage each
+constexpr int kLdsBytes = MOE_G2_DMA ? (2 * 256 + 3 * 256) * 128 : 2 * kMaxStageBytes;
+
+// stage buffers, back to back
+__shared__ __attribute__((aligned(1024))) u32x4 g2_lds[kLdsBytes / 16];
+#define g2_s0 (g2_lds)
+#define g2_s1 (g2_lds + kMaxStageBytes / 16)
 
 // s_waitcnt with vmcnt = n (<= 63), lgkmcnt = 0, expcnt untouched.
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// 16-byte direct-to-LDS load: lane i's data lands at lds + 16 i (lds is
+// wave-uniform). (Device-pass only: the host pass does not know the builtin.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, u32x4 *lds, uint32_t voff,
+                                           int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           voff, soff, 0, 0);
+#endif
 }
 
 __device__ __forceinline__ void barrier() {
@@ -56,9 +80,6 @@ __device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
-#ifndef MOE_G2_PIPE
-#define MOE_G2_PIPE 1
-#endif
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
@@ -105,6 +126,10 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   // load j of a thread covers tile row (tid / 8 + 32 j), logical chunk tid % 8
   const int lrow = tid >> 3;
   const int lchunk = tid & 7;
+  // chunk this thread fetches: its own (registers, swizzled on the LDS
+  // write), or the one its LDS slot holds (direct-to-LDS loads land at
+  // lane-consecutive addresses)
+  const int lchunk_g = MOE_G2_DMA ? (lchunk ^ (lrow & 7)) : lchunk;
   // Loads go through buffer resources: a uniform base and byte extent per
   // operand (per gate / up half, per expert) and a 32-bit offset per load
   // (extents below 4 GiB are a launch precondition); the stage's k offset is
@@ -115,8 +140,11 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
                                              0x00020000);
   };
   __amdgpu_buffer_rsrc_t ar, br0, br1;
-  uint32_t aoff[A_LD], boff[B_LD];
-  auto setup = [&](int seg) {
+  uint32_t aoff[A_LD];
+  uint32_t boff0 = 0, bstep = 0;  // B: row lrow's offset; 32 rows further (uniform)
+  // operand set-up for K segment seg (A and B separately: the direct-to-LDS
+  // pipeline requests B a stage further ahead than A)
+  auto setup_a = [&](int seg) {
     if (seg && !p.a2) return;  // no second K segment: keep the first segment's rows
     const int64_t lda = seg ? p.lda2 : p.lda;
     const int64_t a_rows = seg ? p.M : (p.a_extent ? p.a_extent : p.M);
@@ -127,26 +155,26 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
       int64_t m = m_begin + r;
       if (m >= m_end) m = m_begin;  // results of these rows are never stored
       const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
-      aoff[j] = static_cast<uint32_t>((src * lda + lchunk * 8) * 2);
+      aoff[j] = static_cast<uint32_t>((src * lda + lchunk_g * 8) * 2);
     }
-    int64_t ldb;
+  };
+  auto setup_b = [&](int seg) {
+    if (seg && !p.a2) return;
+    // B rows past N lie past the resource's extent and read as zeros
+    const int64_t ldb = seg ? p.ldb2 : p.ldb, bytes = static_cast<int64_t>(p.N) * ldb * 2;
     if (seg) {
-      ldb = p.ldb2;
-      br0 = br1 = rsrc(p.b2, static_cast<int64_t>(p.N) * ldb * 2);
+      br0 = br1 = rsrc(p.b2, bytes);
     } else {
-      ldb = p.ldb;
-      const int64_t eoff = expert * p.b_stride * 2, bytes = static_cast<int64_t>(p.N) * ldb * 2;
+      const int64_t eoff = expert * p.b_stride * 2;
       br0 = rsrc(static_cast<const char *>(p.b0) + eoff, bytes);
       br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, bytes) : br0;
     }
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j) {
-      const int r = lrow + 32 * j;
-      const bool up = !seg && GLU && r >= BN / 2;
-      int n = n_begin + (up ? r - BN / 2 : r);
-      if (n >= p.N) n = p.N - 1;
-      boff[j] = static_cast<uint32_t>((static_cast<int64_t>(n) * ldb + lchunk * 8) * 2);
-    }
+    boff0 = static_cast<uint32_t>((static_cast<int64_t>(n_begin + lrow) * ldb + lchunk_g * 8) * 2);
+    bstep = static_cast<uint32_t>(32 * ldb * 2);
+  };
+  auto setup = [&](int seg) {
+    setup_a(seg);
+    setup_b(seg);
   };
 
   const int steps1 = p.K / 64;
@@ -160,8 +188,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
       ra[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[j], kb, 0);
     } else {
       const int jb = j - A_LD;  // gate rows first, then up rows (SwiGLU)
-      rb[jb] = __builtin_amdgcn_raw_buffer_load_b128((GLU && jb >= B_LD / 2) ? br1 : br0,
-                                                     boff[jb], kb, 0);
+      const bool up = GLU && jb >= B_LD / 2;
+      rb[jb] = __builtin_amdgcn_raw_buffer_load_b128(
+          up ? br1 : br0, boff0 + (up ? jb - B_LD / 2 : jb) * bstep, kb, 0);
     }
   };
   auto load = [&](int st) {
@@ -195,7 +224,125 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
 
   const int live = __builtin_amdgcn_readfirstlane(fm_live);
-#if MOE_G2_PIPE
+#if MOE_G2_DMA
+  // Direct-to-LDS pipeline. Each 16-byte load of a thread lands in LDS at
+  // its lane's slot of a 1 KB block (8 rows of 128 bytes), so the thread
+  // fetches the logical chunk that slot holds under the row swizzle. A has
+  // two stage buffers and B three, so B (the streamed weights) is requested
+  // two stages ahead and A one. Per stage s (A buffer s % 2, B buffer s % 3):
+  //   M0: MFMAs of k-step 0 (fragment set 0), interleaved with the reads of
+  //       k-step 1 (set 1) from the stage's buffers;
+  //   wait until A and B of stage s + 1 have landed (B of s + 2 may still
+  //       be in flight), lgkmcnt 0, barrier: stage s + 1 is visible and
+  //       stage s's buffers are free;
+  //   M1: MFMAs of set 1, interleaved with the loads of A(s + 2) and
+  //       B(s + 3) into the freed buffers and the reads of k-step 0 of
+  //       stage s + 1 (set 0).
+  // Loads past the last stage repeat it (their buffers are never read).
+  constexpr int A16 = BM * 8, B16 = BN * 8;  // 16-byte units per stage buffer
+  u32x4 *const abuf = g2_lds;                // A: 2 x A16
+  u32x4 *const bbuf = g2_lds + 2 * A16;      // B: 3 x B16
+  static_assert((2 * A16 + 3 * B16) * 16 <= kLdsBytes, "stage buffers fit");
+  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
+  auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
+    const int kc = 4 * ks + fc;
+    if (i < FN)
+      xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(i) + fr, kc)]);
+    else
+      xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
+  };
+  auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
+  };
+  // load j of a stage: rows 32 j + lrow; the wave's 1 KB block starts at
+  // row 32 j + 8 wave
+  auto dma_a = [&](u32x4 *ab, int st, int j) {
+    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
+    load_lds16(ar, ab + (32 * j + 8 * wave) * 8, aoff[j], kb);
+  };
+  auto dma_b = [&](u32x4 *bb, int st, int j) {
+    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
+    const bool up = GLU && j >= B_LD / 2;
+    load_lds16(up ? br1 : br0, bb + (32 * j + 8 * wave) * 8, boff0 + (up ? j - B_LD / 2 : j) * bstep,
+               kb);
+  };
+  constexpr int NRD = FM + FN;
+  constexpr int RD_PER = (NRD + FM - 1) / FM;
+  constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;
+
+  // (stages are requested in order per operand; an operand switches to the
+  // second K segment's rows before its first load from that segment)
+  setup(0);
+  const int last = steps - 1;
+  auto seg_a = [&](int st) {
+    if (st == steps1) setup_a(1);
+  };
+  auto seg_b = [&](int st) {
+    if (st == steps1) setup_b(1);
+  };
+#pragma unroll
+  for (int j = 0; j < A_LD; ++j) dma_a(abuf, 0, j);
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) dma_b(bbuf, 0, j);
+  seg_a(min(1, last));
+  seg_b(min(1, last));
+#pragma unroll
+  for (int j = 0; j < A_LD; ++j) dma_a(abuf + A16, min(1, last), j);
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) dma_b(bbuf + B16, min(1, last), j);
+  seg_b(min(2, last));
+#pragma unroll
+  for (int j = 0; j < B_LD; ++j) dma_b(bbuf + 2 * B16, min(2, last), j);
+  wait_vm_lgkm0<2 * B_LD + A_LD>();  // stage 0 has landed
+  barrier();
+#pragma unroll
+  for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
+
+  int b_cur = 0;  // s % 3
+  for (int st = 0; st < steps; ++st) {
+    const int a_cur = st & 1;
+    const int b_nxt = b_cur == 2 ? 0 : b_cur + 1;
+    u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + (a_cur ^ 1) * A16;
+    u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): set 0 has landed
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm < live) mrow(fm, xa0, xb0);
+#pragma unroll
+      for (int q = 0; q < RD_PER; ++q) {
+        const int i = fm * RD_PER + q;
+        if (i < NRD) rd(ac, bc, 1, i, xa1, xb1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm_lgkm0<B_LD>();  // A and B of st + 1 have landed
+    barrier();
+    const int sa = min(st + 2, last), sb = min(st + 3, last);
+    if (st + 2 <= last) seg_a(sa);
+    if (st + 3 <= last) seg_b(sb);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm < live) mrow(fm, xa1, xb1);
+#pragma unroll
+      for (int q = 0; q < LD_PER; ++q) {
+        const int j = fm * LD_PER + q;
+        if (j < A_LD) dma_a(ac, sa, j);
+        else if (j < A_LD + B_LD) dma_b(bc, sb, j - A_LD);
+      }
+#pragma unroll
+      for (int q = 0; q < RD_PER; ++q) {
+        const int i = fm * RD_PER + q;
+        if (i < NRD) rd(an, bn, 0, i, xa0, xb0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    b_cur = b_nxt;
+  }
+  wait_vm_lgkm0<0>();
+  barrier();  // the epilogue reuses the stage buffers
+#elif MOE_G2_PIPE
   // Software pipeline over half-stages (one MFMA k-step each). Fragment
   // registers come in two sets: set 0 holds k-step 0 of the current stage,
   // set 1 k-step 1. Per stage, with `cur` the stage's LDS buffer:
@@ -274,10 +421,20 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);                                         \
     }                                                                            \
   }
+#if MOE_G2_ROLL
+  // one stage per iteration, buffers picked by parity (one register
+  // assignment for the loop-carried fragments and staging registers)
+  for (int st = 0; st < steps; ++st) {
+    u32x4 *cur = g2_lds + (st & 1) * (kMaxStageBytes / 16);
+    u32x4 *nxt = g2_lds + ((st & 1) ^ 1) * (kMaxStageBytes / 16);
+    G2_STAGE(st, cur, nxt)
+  }
+#else
   for (int st = 0; st < steps; st += 2) {
     G2_STAGE(st + 0, g2_s0, g2_s1)
     G2_STAGE(st + 1, g2_s1, g2_s0)
   }
+#endif
 #undef G2_STAGE
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier();  // the epilogue reuses the stage buffers
@@ -437,10 +594,12 @@ hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
 bool gemm2_applicable(const GemmArgs &a, int epi) {
   if (a.k_split > 1) return false;
   // 32-bit load offsets: A (rows it may address), each B slice, below 4 GiB
+  // (B offsets run up to one tile past N)
   constexpr int64_t kLim = int64_t(1) << 32;
   const int64_t a_rows = a.a_extent ? a.a_extent : (a.tiles ? 0 : a.M);
-  if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim || int64_t(a.N) * a.ldb * 2 >= kLim) return false;
-  if (a.a2 && (a.M * a.lda2 * 2 >= kLim || int64_t(a.N) * a.ldb2 * 2 >= kLim)) return false;
+  if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim || (a.N + 256LL) * a.ldb * 2 >= kLim)
+    return false;
+  if (a.a2 && (a.M * a.lda2 * 2 >= kLim || (a.N + 256LL) * a.ldb2 * 2 >= kLim)) return false;
   if (a.K % 64 || (a.a2 && a.K2 % 64)) return false;
   if (a.N % 8) return false;
   if (epi == EPI_COMBINE && a.ldy % 8) return false;
