@@ -87,7 +87,7 @@ int check_desc(const moe_desc *d) {
 #define MOE_GROUPED_BIG TILE_LARGE
 #endif
 #ifndef MOE_GROUPED_V2
-#define MOE_GROUPED_V2 TILE2_256x256
+#define MOE_GROUPED_V2 TILE2_256x256_TALLW
 #endif
 
 // Kernel and tile shape of each grouped expert GEMM. Each has its own m-tile

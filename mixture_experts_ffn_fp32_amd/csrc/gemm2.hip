@@ -3,28 +3,42 @@
 // row-gathered A; SwiGLU, row-scale, store, fp32 store, combine epilogues;
 // optional second K segment).
 //
-// Main loop. A workgroup of 4 wavefronts owns a BM x BN tile (each
-// wavefront a (BM/2) x (BN/2) quarter of 16x16 accumulators on
-// v_mfma_f32_16x16x32_bf16). K advances 64 elements (128 bytes per row) per
-// stage, two MFMA k-steps. At the start of a stage each thread issues its
-// 16-byte global loads of the next stage (8 lanes per 128-byte row
-// segment); the stage's MFMAs (2 x 64 per wavefront) then cover their
-// latency, and the registers are written to the other LDS buffer before the
-// single barrier of the stage. All waits are local to one stage, which the
-// compiler's wait-count tracking handles exactly. Within a row the eight
-// 16-byte chunks are XOR-swizzled by row & 7 so the 16-byte fragment reads of
-// 8 consecutive rows fall in distinct bank groups. (Direct global->LDS
-// 16-byte loads were measured to issue per-dword cache accesses on this part
-// and are not used.)
+// Work split. A workgroup of WGM x WGN wavefronts owns a BM x BN tile; each
+// wavefront holds a (BM/WGM) x (BN/WGN) block of 16x16 fp32 accumulators fed
+// by v_mfma_f32_16x16x32_bf16. The 256x256 tile runs 8 wavefronts (two per
+// SIMD): one wavefront alone cannot issue MFMAs back to back at the full rate
+// nor keep the LDS busy, and the second hides the first's waits.
 //
-// K must be a multiple of 64 (every workload's widths are); the host uses
-// gemm.hip otherwise. Rows of A past the tile end and columns of B past N
-// are read from a valid row (their results are never stored), so loads need
-// no predicates.
+// Loads. K advances 64 elements (128 bytes per row) per stage. Operand rows
+// go straight from global memory to LDS with 16-byte buffer loads: lane i of
+// a load lands at byte 16 i of a 1 KB block of 8 rows, and the eight 16-byte
+// chunks of a row are XOR-swizzled by row & 7 (so the fragment reads of 8
+// consecutive rows hit distinct banks); each lane therefore fetches the
+// logical chunk its slot holds. A has two stage buffers and B three, so the
+// streamed weights are requested two stages ahead and the activations one.
+// Offsets are 32-bit against per-operand buffer resources (extents below
+// 4 GiB are a launch precondition); B rows past N lie past the resource's
+// extent and read as zeros; A rows past the tile's end repeat its first row
+// (their results are never stored).
+//
+// Main loop, per stage s (A buffer s % 2, B buffer s % 3), fragments in two
+// register sets (set 0: k-step 0, set 1: k-step 1):
+//   M0: MFMAs of set 0, interleaved row by row with the LDS reads of set 1;
+//   wait until stage s + 1 has landed (B of s + 2 may still be in flight),
+//       lgkmcnt 0, barrier: stage s + 1 is visible and stage s's buffers
+//       are free;
+//   M1: MFMAs of set 1, interleaved with the loads of A(s + 2) and B(s + 3)
+//       into the freed buffers and the reads of stage s + 1's k-step 0.
+// Each MFMA group's operands were requested half a stage earlier. Loads past
+// the last stage repeat it (their buffers are never read), so every stage
+// issues the same number of loads and the wait counts are constants.
+// sched_barrier keeps the interleaving in program order.
 //
 // Epilogue. Each wavefront stages its accumulators through LDS 16 rows at a
 // time and writes the output with 16-byte stores along rows; the combine
 // epilogue adds the token's K routed rows with 16-byte loads.
+//
+// K (and K2) must be multiples of 64; the host uses gemm.hip otherwise.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,31 +48,18 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef MOE_G2_PIPE
-#define MOE_G2_PIPE 1
-#endif
-#ifndef MOE_G2_ROLL
-#define MOE_G2_ROLL 1
-#endif
-#ifndef MOE_G2_DMA
-#define MOE_G2_DMA 1
-#endif
-
-constexpr int kMaxStageBytes = (256 + 256) * 128;  // largest tile, one stage
-// direct-to-LDS loads: two A buffers and three B buffers of one stage each
-constexpr int kLdsBytes = MOE_G2_DMA ? (2 * 256 + 3 * 256) * 128 : 2 * kMaxStageBytes;
-
-// stage buffers, back to back
+// two A and three B stage buffers of the largest tile (256 rows x 128 bytes)
+constexpr int kRowBytes = 128;
+constexpr int kLdsBytes = (2 * 256 + 3 * 256) * kRowBytes;
 __shared__ __attribute__((aligned(1024))) u32x4 g2_lds[kLdsBytes / 16];
-#define g2_s0 (g2_lds)
-#define g2_s1 (g2_lds + kMaxStageBytes / 16)
 
-// s_waitcnt with vmcnt = n (<= 63), lgkmcnt = 0, expcnt untouched.
+// s_waitcnt with vmcnt = N (< 64), lgkmcnt = 0, expcnt untouched.
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // 16-byte direct-to-LDS load: lane i's data lands at lds + 16 i (lds is
 // wave-uniform). (Device-pass only: the host pass does not know the builtin.)
@@ -80,22 +81,34 @@ __device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7));
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                           static_cast<int>(static_cast<uint32_t>(bytes)),
+                                           0x00020000);
+}
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
+  constexpr int NW = WGM * WGN, THREADS = 64 * NW;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr bool GLU = EPI == EPI_SWIGLU;
   constexpr int NOUT = GLU ? BN / 2 : BN;
-  constexpr int A_LD = BM / 32, B_LD = BN / 32;  // 16-byte loads per thread per stage
-  constexpr int STAGE16 = (BM + BN) * 8;        // 16-byte units per stage
-  static_assert(STAGE16 * 16 <= kMaxStageBytes, "stage fits");
+  constexpr int ROWS = THREADS / 8;                 // rows covered by one load of every thread
+  constexpr int A_LD = BM / ROWS, B_LD = BN / ROWS;  // loads per thread per stage
+  constexpr int A16 = BM * 8, B16 = BN * 8;          // 16-byte units per stage buffer
+  static_assert(BM % ROWS == 0 && BN % ROWS == 0, "whole loads per stage");
+  static_assert(!GLU || (BN / 2) % ROWS == 0, "gate and up rows in separate loads");
   static_assert(!GLU || FN % 2 == 0, "paired gate/up fragments");
+  static_assert((2 * A16 + 3 * B16) * 16 <= kLdsBytes, "stage buffers fit");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // ------------------------------------------------------------ tile
+  // consecutive workgroups go to different XCDs: give each XCD a contiguous
+  // range of tiles, grouped 4 m-tiles at a time so tiles sharing B or A run
+  // together
   const int n_tn = (p.N + NOUT - 1) / NOUT;
   const int64_t n_m = p.tiles ? static_cast<int64_t>(*p.n_tiles) : p.max_mtiles;
   const int64_t total = n_m * n_tn;
@@ -122,45 +135,32 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   }
   const int n_begin = nt * NOUT;
 
-  // ------------------------------------------------------------ loaders
-  // load j of a thread covers tile row (tid / 8 + 32 j), logical chunk tid % 8
+  // ------------------------------------------------------------ loads
+  // load j of a thread: tile row ROWS j + lrow, in the 1 KB block starting at
+  // row ROWS j + 8 wave; the slot of lane (lrow, lchunk) holds logical chunk
+  // lchunk ^ (lrow & 7)
   const int lrow = tid >> 3;
-  const int lchunk = tid & 7;
-  // chunk this thread fetches: its own (registers, swizzled on the LDS
-  // write), or the one its LDS slot holds (direct-to-LDS loads land at
-  // lane-consecutive addresses)
-  const int lchunk_g = MOE_G2_DMA ? (lchunk ^ (lrow & 7)) : lchunk;
-  // Loads go through buffer resources: a uniform base and byte extent per
-  // operand (per gate / up half, per expert) and a 32-bit offset per load
-  // (extents below 4 GiB are a launch precondition); the stage's k offset is
-  // the scalar offset. Accesses past an extent would read zeros.
-  auto rsrc = [](const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
-                                             static_cast<int>(static_cast<uint32_t>(bytes)),
-                                             0x00020000);
-  };
+  const int lchunk = (tid & 7) ^ (lrow & 7);
   __amdgpu_buffer_rsrc_t ar, br0, br1;
   uint32_t aoff[A_LD];
-  uint32_t boff0 = 0, bstep = 0;  // B: row lrow's offset; 32 rows further (uniform)
-  // operand set-up for K segment seg (A and B separately: the direct-to-LDS
-  // pipeline requests B a stage further ahead than A)
+  uint32_t boff0 = 0, bstep = 0;  // B: row lrow's offset; ROWS rows further (uniform)
+  // operand set-up for K segment seg (A and B separately: B is requested a
+  // stage further ahead)
   auto setup_a = [&](int seg) {
-    if (seg && !p.a2) return;  // no second K segment: keep the first segment's rows
+    if (seg && !p.a2) return;
     const int64_t lda = seg ? p.lda2 : p.lda;
     const int64_t a_rows = seg ? p.M : (p.a_extent ? p.a_extent : p.M);
     ar = rsrc(seg ? p.a2 : p.a, a_rows * lda * 2);
 #pragma unroll
     for (int j = 0; j < A_LD; ++j) {
-      const int r = lrow + 32 * j;
-      int64_t m = m_begin + r;
-      if (m >= m_end) m = m_begin;  // results of these rows are never stored
+      int64_t m = m_begin + ROWS * j + lrow;
+      if (m >= m_end) m = m_begin;
       const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
-      aoff[j] = static_cast<uint32_t>((src * lda + lchunk_g * 8) * 2);
+      aoff[j] = static_cast<uint32_t>((src * lda + lchunk * 8) * 2);
     }
   };
   auto setup_b = [&](int seg) {
     if (seg && !p.a2) return;
-    // B rows past N lie past the resource's extent and read as zeros
     const int64_t ldb = seg ? p.ldb2 : p.ldb, bytes = static_cast<int64_t>(p.N) * ldb * 2;
     if (seg) {
       br0 = br1 = rsrc(p.b2, bytes);
@@ -169,40 +169,38 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
       br0 = rsrc(static_cast<const char *>(p.b0) + eoff, bytes);
       br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, bytes) : br0;
     }
-    boff0 = static_cast<uint32_t>((static_cast<int64_t>(n_begin + lrow) * ldb + lchunk_g * 8) * 2);
-    bstep = static_cast<uint32_t>(32 * ldb * 2);
-  };
-  auto setup = [&](int seg) {
-    setup_a(seg);
-    setup_b(seg);
+    boff0 = static_cast<uint32_t>((static_cast<int64_t>(n_begin + lrow) * ldb + lchunk * 8) * 2);
+    bstep = static_cast<uint32_t>(ROWS * ldb * 2);
   };
 
   const int steps1 = p.K / 64;
   const int steps = steps1 + (p.a2 ? p.K2 / 64 : 0);
+  const int last = steps - 1;
+  auto kbytes = [&](int st) {
+    return __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * kRowBytes);
+  };
+  auto load_a = [&](u32x4 *ab, int st, int j) {
+    load_lds16(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j], kbytes(st));
+  };
+  auto load_b = [&](u32x4 *bb, int st, int j) {
+    const bool up = GLU && j >= B_LD / 2;  // gate rows first, then up rows
+    load_lds16(up ? br1 : br0, bb + (ROWS * j + 8 * wave) * 8,
+               boff0 + (up ? j - B_LD / 2 : j) * bstep, kbytes(st));
+  };
 
-  // registers of the next stage
-  u32x4 ra[A_LD], rb[B_LD];
-  auto load_one = [&](int st, int j) {
-    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
-    if (j < A_LD) {
-      ra[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[j], kb, 0);
-    } else {
-      const int jb = j - A_LD;  // gate rows first, then up rows (SwiGLU)
-      const bool up = GLU && jb >= B_LD / 2;
-      rb[jb] = __builtin_amdgcn_raw_buffer_load_b128(
-          up ? br1 : br0, boff0 + (up ? jb - B_LD / 2 : jb) * bstep, kb, 0);
+  // ------------------------------------------------------------ fragments
+  const int fr = lane & 15, fc = lane >> 4;
+  auto brow_of = [&](int fn) {  // B row (within the tile) of fragment fn
+    if (GLU) {
+      constexpr int half = FN / 2;
+      return fn < half ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - half) * 16;
     }
+    return wn * WTN + fn * 16;
   };
-  auto load = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < A_LD + B_LD; ++j) load_one(st, j);
-  };
-  auto put = [&](u32x4 *buf) {
-#pragma unroll
-    for (int j = 0; j < A_LD; ++j) buf[sw8(lrow + 32 * j, lchunk)] = ra[j];
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j) buf[BM * 8 + sw8(lrow + 32 * j, lchunk)] = rb[j];
-  };
+  // this wave's 16-row fragments that hold rows of the tile
+  const int64_t rows_left = m_end - (m_begin + wm * WTM);
+  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
+  const int live = __builtin_amdgcn_readfirstlane(fm_live);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -210,39 +208,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows: A row of fm, B row of fn (within the stage)
-  const int fr = lane & 15, fc = lane >> 4;
-  auto brow_of = [&](int fn) {
-    if (GLU) {
-      constexpr int half = FN / 2;
-      return fn < half ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - half) * 16;
-    }
-    return wn * WTN + fn * 16;
-  };
-  // number of this wave's 16-row fragments that hold rows of the tile
-  const int64_t rows_left = m_end - (m_begin + wm * WTM);
-  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
-
-  const int live = __builtin_amdgcn_readfirstlane(fm_live);
-#if MOE_G2_DMA
-  // Direct-to-LDS pipeline. Each 16-byte load of a thread lands in LDS at
-  // its lane's slot of a 1 KB block (8 rows of 128 bytes), so the thread
-  // fetches the logical chunk that slot holds under the row swizzle. A has
-  // two stage buffers and B three, so B (the streamed weights) is requested
-  // two stages ahead and A one. Per stage s (A buffer s % 2, B buffer s % 3):
-  //   M0: MFMAs of k-step 0 (fragment set 0), interleaved with the reads of
-  //       k-step 1 (set 1) from the stage's buffers;
-  //   wait until A and B of stage s + 1 have landed (B of s + 2 may still
-  //       be in flight), lgkmcnt 0, barrier: stage s + 1 is visible and
-  //       stage s's buffers are free;
-  //   M1: MFMAs of set 1, interleaved with the loads of A(s + 2) and
-  //       B(s + 3) into the freed buffers and the reads of k-step 0 of
-  //       stage s + 1 (set 0).
-  // Loads past the last stage repeat it (their buffers are never read).
-  constexpr int A16 = BM * 8, B16 = BN * 8;  // 16-byte units per stage buffer
-  u32x4 *const abuf = g2_lds;                // A: 2 x A16
-  u32x4 *const bbuf = g2_lds + 2 * A16;      // B: 3 x B16
-  static_assert((2 * A16 + 3 * B16) * 16 <= kLdsBytes, "stage buffers fit");
+  u32x4 *const abuf = g2_lds;            // A: 2 x A16
+  u32x4 *const bbuf = g2_lds + 2 * A16;  // B: 3 x B16
   bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
   auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
     const int kc = 4 * ks + fc;
@@ -256,26 +223,15 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
     for (int fn = 0; fn < FN; ++fn)
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
   };
-  // load j of a stage: rows 32 j + lrow; the wave's 1 KB block starts at
-  // row 32 j + 8 wave
-  auto dma_a = [&](u32x4 *ab, int st, int j) {
-    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
-    load_lds16(ar, ab + (32 * j + 8 * wave) * 8, aoff[j], kb);
-  };
-  auto dma_b = [&](u32x4 *bb, int st, int j) {
-    const int kb = __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * 128);
-    const bool up = GLU && j >= B_LD / 2;
-    load_lds16(up ? br1 : br0, bb + (32 * j + 8 * wave) * 8, boff0 + (up ? j - B_LD / 2 : j) * bstep,
-               kb);
-  };
-  constexpr int NRD = FM + FN;
-  constexpr int RD_PER = (NRD + FM - 1) / FM;
-  constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;
+  constexpr int NRD = FM + FN;                         // fragment reads per set
+  constexpr int RD_PER = (NRD + FM - 1) / FM;          // ... per MFMA row
+  constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;  // loads per MFMA row
 
-  // (stages are requested in order per operand; an operand switches to the
-  // second K segment's rows before its first load from that segment)
-  setup(0);
-  const int last = steps - 1;
+  // ------------------------------------------------------------ main loop
+  // (each operand switches to the second K segment's rows before its first
+  // load from that segment; loads are issued in stage order per operand)
+  setup_a(0);
+  setup_b(0);
   auto seg_a = [&](int st) {
     if (st == steps1) setup_a(1);
   };
@@ -283,30 +239,30 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
     if (st == steps1) setup_b(1);
   };
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j) dma_a(abuf, 0, j);
+  for (int j = 0; j < A_LD; ++j) load_a(abuf, 0, j);
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) dma_b(bbuf, 0, j);
+  for (int j = 0; j < B_LD; ++j) load_b(bbuf, 0, j);
   seg_a(min(1, last));
   seg_b(min(1, last));
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j) dma_a(abuf + A16, min(1, last), j);
+  for (int j = 0; j < A_LD; ++j) load_a(abuf + A16, min(1, last), j);
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) dma_b(bbuf + B16, min(1, last), j);
+  for (int j = 0; j < B_LD; ++j) load_b(bbuf + B16, min(1, last), j);
   seg_b(min(2, last));
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) dma_b(bbuf + 2 * B16, min(2, last), j);
-  wait_vm_lgkm0<2 * B_LD + A_LD>();  // stage 0 has landed
+  for (int j = 0; j < B_LD; ++j) load_b(bbuf + 2 * B16, min(2, last), j);
+  wait_vm_lgkm0<A_LD + 2 * B_LD>();  // stage 0 has landed
   barrier();
 #pragma unroll
   for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
 
-  int b_cur = 0;  // s % 3
+  int b_cur = 0;  // st % 3
   for (int st = 0; st < steps; ++st) {
     const int a_cur = st & 1;
     const int b_nxt = b_cur == 2 ? 0 : b_cur + 1;
     u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + (a_cur ^ 1) * A16;
     u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): set 0 has landed
+    wait_lgkm0();  // set 0 has landed
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (fm < live) mrow(fm, xa0, xb0);
@@ -328,8 +284,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < LD_PER; ++q) {
         const int j = fm * LD_PER + q;
-        if (j < A_LD) dma_a(ac, sa, j);
-        else if (j < A_LD + B_LD) dma_b(bc, sb, j - A_LD);
+        if (j < A_LD) load_a(ac, sa, j);
+        else if (j < A_LD + B_LD) load_b(bc, sb, j - A_LD);
       }
 #pragma unroll
       for (int q = 0; q < RD_PER; ++q) {
@@ -342,165 +298,14 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   }
   wait_vm_lgkm0<0>();
   barrier();  // the epilogue reuses the stage buffers
-#elif MOE_G2_PIPE
-  // Software pipeline over half-stages (one MFMA k-step each). Fragment
-  // registers come in two sets: set 0 holds k-step 0 of the current stage,
-  // set 1 k-step 1. Per stage, with `cur` the stage's LDS buffer:
-  //   M0: MFMAs of set 0, interleaved row by row with the reads of set 1
-  //       (from cur), the LDS writes of the next stage into the other buffer
-  //       (from the staging registers) and the global loads of the stage
-  //       after next into the freed staging registers;
-  //   barrier (after lgkmcnt 0): the next stage is visible, and every read
-  //       of the other buffer issued before it has completed;
-  //   M1: MFMAs of set 1, interleaved with the reads of the next stage's
-  //       k-step 0 into set 0.
-  // Each MFMA group's operands were requested one half-stage earlier, and the
-  // global loads have a full stage to land. sched_barrier keeps this order.
-  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
-  auto rd = [&](const u32x4 *buf, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
-    const int kc = 4 * ks + fc;
-    if (i < FN)
-      xb[i] = __builtin_bit_cast(bf16x8, buf[BM * 8 + sw8(brow_of(i) + fr, kc)]);
-    else
-      xa[i - FN] = __builtin_bit_cast(bf16x8, buf[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
-  };
-  auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
-  };
-  constexpr int NRD = FM + FN;              // fragment reads per set
-  constexpr int RD_PER = (NRD + FM - 1) / FM;
-  constexpr int WR_PER = (A_LD + B_LD + FM - 1) / FM;
-  auto put_one = [&](u32x4 *buf, int j) {
-    if (j < A_LD) buf[sw8(lrow + 32 * j, lchunk)] = ra[j];
-    else buf[BM * 8 + sw8(lrow + 32 * (j - A_LD), lchunk)] = rb[j - A_LD];
-  };
-
-  setup(0);
-  load(0);
-  put(g2_s0);
-  if (steps1 == 1 && steps > 1) setup(1);
-  load(steps > 1 ? 1 : 0);
-  barrier();
-#pragma unroll
-  for (int i = 0; i < NRD; ++i) rd(g2_s0, 0, i, xa0, xb0);
-  // One stage from CUR; NXT receives the next stage. Near the end the loads
-  // repeat the last stage and the next-stage writes and reads are unused,
-  // so the body has no conditions beyond the rows check of partial tiles.
-#define G2_STAGE(ST, CUR, NXT)                                                   \
-  {                                                                              \
-    const int st_ = (ST);                                                        \
-    if (st_ >= steps) break;                                                     \
-    if (st_ + 2 == steps1 && st_ + 2 < steps) setup(1);                          \
-    const int ld_ = st_ + 2 < steps ? st_ + 2 : steps - 1;                       \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): set 0 has landed */       \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) {                          \
-      if (fm < live) mrow(fm, xa0, xb0);                                         \
-      _Pragma("unroll") for (int q = 0; q < RD_PER; ++q) {                       \
-        const int i = fm * RD_PER + q;                                           \
-        if (i < NRD) rd(CUR, 1, i, xa1, xb1);                                    \
-      }                                                                          \
-      _Pragma("unroll") for (int q = 0; q < WR_PER; ++q) {                       \
-        const int j = fm * WR_PER + q;                                           \
-        if (j < A_LD + B_LD) {                                                   \
-          put_one(NXT, j);                                                       \
-          load_one(ld_, j);                                                      \
-        }                                                                        \
-      }                                                                          \
-      __builtin_amdgcn_sched_barrier(0);                                         \
-    }                                                                            \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                         \
-    barrier();                                                                   \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm) {                          \
-      if (fm < live) mrow(fm, xa1, xb1);                                         \
-      _Pragma("unroll") for (int q = 0; q < RD_PER; ++q) {                       \
-        const int i = fm * RD_PER + q;                                           \
-        if (i < NRD) rd(NXT, 0, i, xa0, xb0);                                    \
-      }                                                                          \
-      __builtin_amdgcn_sched_barrier(0);                                         \
-    }                                                                            \
-  }
-#if MOE_G2_ROLL
-  // one stage per iteration, buffers picked by parity (one register
-  // assignment for the loop-carried fragments and staging registers)
-  for (int st = 0; st < steps; ++st) {
-    u32x4 *cur = g2_lds + (st & 1) * (kMaxStageBytes / 16);
-    u32x4 *nxt = g2_lds + ((st & 1) ^ 1) * (kMaxStageBytes / 16);
-    G2_STAGE(st, cur, nxt)
-  }
-#else
-  for (int st = 0; st < steps; st += 2) {
-    G2_STAGE(st + 0, g2_s0, g2_s1)
-    G2_STAGE(st + 1, g2_s1, g2_s0)
-  }
-#endif
-#undef G2_STAGE
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  barrier();  // the epilogue reuses the stage buffers
-#else
-  // all fragments are read first (rows past the tile read stale LDS, and
-  // their MFMAs are skipped), so the MFMAs issue back to back
-  auto compute = [&](const u32x4 *buf) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kc = 4 * ks + fc;
-      bf16x8 bf[FN], af[FM];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        bf[fn] = __builtin_bit_cast(bf16x8, buf[BM * 8 + sw8(brow_of(fn) + fr, kc)]);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = __builtin_bit_cast(bf16x8, buf[sw8(wm * WTM + fm * 16 + fr, kc)]);
-      // keep the reads ahead of the branches below (then MFMAs back to back)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) asm volatile("" : "+v"(af[fm]));
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        if (fm < live) {
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  setup(0);
-  load(0);
-  put(g2_s0);
-  barrier();
-  // Step st: issue the loads of stage st + 1, run the MFMAs of stage st from
-  // LDS buffer st % 2, write stage st + 1 into the other buffer, barrier.
-  // Unrolled by two so the buffers are named statically.
-#define G2_STAGE(ST, CUR, NXT)                  \
-  {                                             \
-    const int st_ = (ST);                       \
-    if (st_ >= steps) break;                    \
-    const bool more_ = st_ + 1 < steps;         \
-    if (more_) {                                \
-      if (st_ + 1 == steps1) setup(1);          \
-      load(st_ + 1);                            \
-    }                                           \
-    compute(CUR);                               \
-    if (more_) put(NXT);                        \
-    barrier();                                  \
-  }
-  for (int st = 0; st < steps; st += 2) {
-    G2_STAGE(st + 0, g2_s0, g2_s1)
-    G2_STAGE(st + 1, g2_s1, g2_s0)
-  }
-#undef G2_STAGE
-#endif
 
   // ------------------------------------------------------------ epilogue
-  // each wave: 16 rows x (OUT cols) of fp32 at a time in its 8 KB+ slice
+  // each wave: 16 rows x OUTW columns of fp32 at a time in its own slice
   constexpr int OUTW = GLU ? WTN / 2 : WTN;   // output columns per wave
   constexpr int FO = GLU ? FN / 2 : FN;
   constexpr int PITCH = OUTW + 4;             // floats per staged row
-  float *stg = reinterpret_cast<float *>(wave < 2 ? g2_s0 : g2_s1) + (wave & 1) * 16 * PITCH;
-  static_assert(2 * 16 * PITCH * 4 <= kMaxStageBytes, "epilogue staging fits");
+  static_assert(NW * 16 * PITCH * 4 <= kLdsBytes, "epilogue staging fits");
+  float *stg = reinterpret_cast<float *>(g2_lds) + wave * 16 * PITCH;
   const int col0 = n_begin + (GLU ? wn * (WTN / 2) : wn * WTN);
   constexpr int ITEMS = 16 * OUTW / 8;        // (row, 8-column) items per 16 rows
 #pragma unroll
@@ -563,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t run2(const GemmArgs &a, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   const int64_t n_tn = (a.N + NOUT - 1) / NOUT;
@@ -573,18 +378,18 @@ hipError_t run2(const GemmArgs &a, hipStream_t s) {
   GemmArgs b = a;
   b.max_mtiles = max_m;
   const int64_t blocks = 8 * ((total + 7) / 8);
-  gemm2_kernel<BM, BN, EPI><<<static_cast<unsigned>(blocks), 256, 0, s>>>(b);
+  gemm2_kernel<BM, BN, WGM, WGN, EPI><<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b);
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return run2<BM, BN, EPI_SWIGLU>(a, s);
-    case EPI_SCALE: return run2<BM, BN, EPI_SCALE>(a, s);
-    case EPI_STORE: return run2<BM, BN, EPI_STORE>(a, s);
-    case EPI_COMBINE: return run2<BM, BN, EPI_COMBINE>(a, s);
-    case EPI_STORE_F32: return run2<BM, BN, EPI_STORE_F32>(a, s);
+    case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, EPI_SWIGLU>(a, s);
+    case EPI_SCALE: return run2<BM, BN, WGM, WGN, EPI_SCALE>(a, s);
+    case EPI_STORE: return run2<BM, BN, WGM, WGN, EPI_STORE>(a, s);
+    case EPI_COMBINE: return run2<BM, BN, WGM, WGN, EPI_COMBINE>(a, s);
+    case EPI_STORE_F32: return run2<BM, BN, WGM, WGN, EPI_STORE_F32>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -608,6 +413,9 @@ bool gemm2_applicable(const GemmArgs &a, int epi) {
 
 int gemm2_bm(int cfg) { return cfg == TILE2_128x256 ? 128 : 256; }
 
+#ifndef MOE_DENSE_V2
+#define MOE_DENSE_V2 TILE2_256x256_TALLW
+#endif
 #ifndef MOE_V2_MIN_TILES
 #define MOE_V2_MIN_TILES 200
 #endif
@@ -628,7 +436,7 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
   if (act_bf16 && gemm2_applicable(a, epi)) {
     const int64_t nout = glu ? 128 : 256;
     const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout);
-    if (tiles >= MOE_V2_MIN_TILES) return launch_gemm2(a, epi, TILE2_256x256, s);
+    if (tiles >= MOE_V2_MIN_TILES) return launch_gemm2(a, epi, MOE_DENSE_V2, s);
   }
   if (!act_bf16) return launch_gemm(a, epi, TILE_LARGE, act_bf16, s);
   for (int cfg : {TILE_LARGE, TILE_TALL_N64, TILE_MID})
@@ -638,9 +446,11 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
 
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s) {
   switch (cfg) {
-    case TILE2_256x256: return dispatch2<256, 256>(a, epi, s);
-    case TILE2_256x128: return dispatch2<256, 128>(a, epi, s);
-    case TILE2_128x256: return dispatch2<128, 256>(a, epi, s);
+    case TILE2_256x256: return dispatch2<256, 256, 2, 4>(a, epi, s);
+    case TILE2_256x256_TALLW: return dispatch2<256, 256, 4, 2>(a, epi, s);
+    case TILE2_256x256_W4: return dispatch2<256, 256, 2, 2>(a, epi, s);
+    case TILE2_256x128: return dispatch2<256, 128, 2, 2>(a, epi, s);
+    case TILE2_128x256: return dispatch2<128, 256, 2, 2>(a, epi, s);
   }
   return hipErrorInvalidValue;
 }

@@ -140,7 +140,12 @@ int tile_bm(int cfg);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
 
 // Pipelined bf16 GEMM (gemm2.hip): large tiles, direct-to-LDS loads.
-enum Tile2Cfg { TILE2_256x256 = 0, TILE2_256x128 = 1, TILE2_128x256 = 2 };
+// (256x256: 8 wavefronts as 2 x 4 of 128x64 blocks; _TALLW: 4 x 2 of 64x128;
+// _W4 and the others: 4 wavefronts, 2 x 2)
+enum Tile2Cfg {
+  TILE2_256x256 = 0, TILE2_256x128 = 1, TILE2_128x256 = 2, TILE2_256x256_W4 = 3,
+  TILE2_256x256_TALLW = 4
+};
 bool gemm2_applicable(const GemmArgs &a, int epi);
 int gemm2_bm(int cfg);
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s);
