@@ -55,7 +55,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if not os.path.exists(_LIB) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB):
             build(force=True)
         L = C.CDLL(_LIB)
         P = C.c_void_p
@@ -64,6 +64,7 @@ def lib():
         L.or_expert_rows.argtypes = [P, P, P, P, P, C.c_int64, P]
         L.or_combine.argtypes = [P, P, P, C.c_int32, P, P, C.c_int64, P]
         L.or_dispatch.argtypes = [C.c_int64, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P]
+        L.or_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P]
         for f in ("or_route", "or_forward", "or_expert_rows", "or_combine", "or_dispatch"):
             getattr(L, f).restype = C.c_int
         L.or_silu.argtypes = [C.c_double]
@@ -200,3 +201,13 @@ def dispatch(idx, g, E: int) -> dict:
                              _p(st), _p(inv), _p(sw) if gf is not None else None), "dispatch")
     return dict(counts=counts, offsets=offsets, perm=perm, sorted_token=st, inv=inv,
                 sorted_w=sw if gf is not None else None)
+
+
+def balance_bias(counts, bias, alpha: float, n_tokens: int, K: int) -> np.ndarray:
+    """Bias-based balancer step (Part 3, section 14.3): returns the new fp32
+    bias for per-expert counts of a step with n_tokens tokens and top-K."""
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    assert c.shape == b.shape and c.ndim == 1
+    _check(lib().or_balance_bias(len(c), K, n_tokens, _p(c), alpha, _p(b)), "or_balance_bias")
+    return b

@@ -388,3 +388,27 @@ int or_dispatch(int64_t T, int32_t K, int32_t E, const int32_t *idx, const float
   free(next);
   return 0;
 }
+
+/* Bias-based load balancing ("APEX-1 Mathematical Reference - Part 3",
+ * section 14.3): after a step with n_tokens tokens, expert e's observed load
+ * is f_e = counts[e] / (n_tokens * K) against the target 1/E; its bias moves
+ * by alpha * sign(1/E - f_e) and is clamped to [-1, 1] (section 14.4: a
+ * balanced expert, f_e = 1/E, does not move). The sign is taken exactly, on
+ * the integers n_tokens * K - E * counts[e] (same sign as 1/E - f_e). The new
+ * bias is the fp64 value b + alpha * s, clamped, and stored as fp32: b and
+ * alpha are fp32 values, so this is the correctly rounded fp32 sum.
+ * n_tokens = 0 leaves the bias unchanged (no load was observed). */
+int or_balance_bias(int32_t E, int32_t K, int64_t n_tokens, const int32_t *counts, float alpha,
+                    float *bias) {
+  if (E <= 0 || K <= 0 || n_tokens < 0 || !counts || !bias) return -1;
+  if (n_tokens == 0) return 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t diff = n_tokens * (int64_t)K - (int64_t)E * counts[e];
+    const double s = diff > 0 ? 1.0 : (diff < 0 ? -1.0 : 0.0);
+    double b = (double)bias[e] + (double)alpha * s;
+    if (b > 1.0) b = 1.0;
+    if (b < -1.0) b = -1.0;
+    bias[e] = (float)b;
+  }
+  return 0;
+}

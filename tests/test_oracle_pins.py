@@ -485,3 +485,60 @@ def test_softmax_first_scores_are_probabilities():
     assert np.allclose(top.sum(1), 1.0, atol=1e-14)
     assert np.all(top > 0) and np.all(np.diff(top, axis=1) <= 0)
     assert np.allclose(gap, top[:, 3] - top[:, 4], atol=0)
+
+
+# ---------------------------------------------------------------- balancer
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def test_balancer_worked_example():
+    """Part 3, section 14.5: counts [5, 4, 3, 4] of 8 tokens x top-2 over 4
+    experts move the zero bias to [-0.1, 0, +0.1, 0]."""
+    g = _gold("balancer_example.json")
+    counts = np.array(g["counts"], dtype=np.int32)
+    rates = counts / (g["n_tokens"] * g["K"])
+    assert np.allclose(rates, g["observed_rates"], atol=0.5 * 10 ** -g["decimals"])
+    out = oracle.balance_bias(counts, g["bias_before"], g["alpha"], g["n_tokens"], g["K"])
+    assert np.array_equal(np.sign(out - np.float32(g["bias_before"])), g["signs"])
+    assert np.array_equal(out, np.float32(g["bias_after"]))
+
+
+def test_balancer_balanced_expert_does_not_move():
+    """Section 14.4: f_e equal to 1/E gives sign 0. With E = 3 and N*K = 9,
+    counts [3, 3, 3] are exactly balanced although 1/3 and 3/9 are not exact
+    binary fractions."""
+    out = oracle.balance_bias([3, 3, 3], [0.25, -0.5, 0.0], 0.1, 9, 1)
+    assert np.array_equal(out, np.float32([0.25, -0.5, 0.0]))
+
+
+def test_balancer_clamps_to_unit_interval():
+    """Section 14.3 step 5: the bias stays in [-1, 1]."""
+    out = oracle.balance_bias([0, 16, 8, 8], [0.95, -0.95, 1.0, -1.0], 0.1, 8, 4)
+    # expert 0 under-loaded (+), 1 over-loaded (-), 2 and 3 balanced (8 = 32/4)
+    assert np.array_equal(out, np.float32([1.0, -1.0, 1.0, -1.0]))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_balancer_matches_rule_on_random_counts(seed):
+    """The update written out with exact rationals: sign(1/E - c/(N K))
+    compared as fractions, then a clamped fp32 step."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    E, K, N = int(rng.integers(2, 64)), int(rng.integers(1, 9)), int(rng.integers(1, 500))
+    K = min(K, E)
+    counts = rng.multinomial(N * K, np.ones(E) / E).astype(np.int32)
+    bias = rng.uniform(-1.2, 1.2, E).astype(np.float32)
+    alpha = np.float32(rng.uniform(0.001, 0.3))
+    out = oracle.balance_bias(counts, bias, float(alpha), N, K)
+    for e in range(E):
+        d = Fraction(1, E) - Fraction(int(counts[e]), N * K)
+        s = (d > 0) - (d < 0)
+        want = min(1.0, max(-1.0, float(Fraction(float(bias[e])) + Fraction(float(alpha)) * s)))
+        assert out[e] == np.float32(want), (e, out[e], want)
+
+
+def test_balancer_no_tokens_is_a_no_op():
+    out = oracle.balance_bias([0, 0], [0.3, -0.2], 0.1, 0, 1)
+    assert np.array_equal(out, np.float32([0.3, -0.2]))
