@@ -174,6 +174,19 @@ def main():
 
     cnt = counts.cpu().numpy()
     alg = algorithmic(w, cnt)
+
+    # bias-based balancer step on this step's loads (a scratch bias, so the
+    # layer's routing is untouched)
+    bias_scratch = torch.zeros(w.E, dtype=torch.float32, device=dev)
+    b_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 200
+    moe.moe_balance_bias(w.E, w.K, w.T, counts, 1e-3, bias_scratch, stream)
+    b_ev.record(stream)
+    for _ in range(reps):
+        moe.moe_balance_bias(w.E, w.K, w.T, counts, 1e-3, bias_scratch, stream)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    balance_us = b_ev.elapsed_time(e_ev) / reps * 1e3
     tok_s = w.T / (ms / 1e3)
     peak_tf = PEAK[w.act]
     intensity = alg["gu_flops"] / alg["gu_bytes"]
@@ -220,6 +233,8 @@ def main():
                   "gbs": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
                   "experts_touched": alg["touched"]},
         "roofline": roof,
+        "balance_bias": {"us_per_call": round(balance_us, 2), "experts": w.E,
+                         "note": "one bias-based balancer step, back-to-back launches"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -232,6 +232,22 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream);
 
+/* Bias-based load balancing, one step ("APEX-1 Mathematical Reference -
+ * Part 3", section 14.3; the sign rule of section 14.4). For a step of
+ * n_tokens tokens routed top-k over n_experts experts with per-expert loads
+ * counts[e] (as moe_forward / moe_dispatch return them), every bias[e] moves
+ * by alpha * sign(1/E - counts[e] / (n_tokens * top_k)) and is clamped to
+ * [-1, 1]. The sign is decided exactly on integers (n_tokens * top_k versus
+ * E * counts[e]); the update is one fp32 add. bias: fp32 [E] device array,
+ * updated in place (the same array moe_weights.bias points at); counts: int32
+ * [E] device array. Enqueued on stream, no host synchronisation.
+ * n_tokens == 0 is a no-op. Errors: MOE_ERR_NULL (counts or bias NULL),
+ * MOE_ERR_SHAPE (n_experts outside 1..1024, top_k outside 1..n_experts,
+ * n_tokens < 0, or n_tokens * top_k beyond int32), MOE_ERR_MODE (alpha not
+ * finite), MOE_ERR_HIP (launch failure). */
+MOE_API int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens,
+                             const int32_t *counts, float alpha, float *bias, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

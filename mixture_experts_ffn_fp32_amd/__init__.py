@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_expert_ffn", "moe_combine", "moe_forward")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_balance_bias")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -69,8 +69,9 @@ def lib():
         L.moe_expert_ffn.argtypes = [P, P, P, P, P, P, P, P, S, P]
         L.moe_combine.argtypes = [P, P, P, P, P, P, P, S, P]
         L.moe_forward.argtypes = [P, P, P, P, P, P, P, S, P, P]
+        L.moe_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
-                  "moe_combine", "moe_forward"):
+                  "moe_combine", "moe_forward", "moe_balance_bias"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -129,6 +130,13 @@ def _nbytes(t):
 def moe_route(desc, weights, x, idx, g, gap=None, top_scores=None, ws=None, stream=None):
     _ok(lib().moe_route(C.byref(desc), C.byref(weights), _ptr(x), _ptr(idx), _ptr(g), _ptr(gap),
                         _ptr(top_scores), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_route")
+
+
+def moe_balance_bias(n_experts, top_k, n_tokens, counts, alpha, bias, stream=None):
+    """One bias-based balancer step on device arrays (counts int32 [E], bias
+    fp32 [E], updated in place)."""
+    _ok(lib().moe_balance_bias(int(n_experts), int(top_k), int(n_tokens), _ptr(counts),
+                               float(alpha), _ptr(bias), _stream(stream)), "moe_balance_bias")
 
 
 def moe_dispatch(desc, idx, g, rows, counts, offsets, perm, sorted_token, inv, sorted_w,

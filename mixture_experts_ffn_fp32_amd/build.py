@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "gemm2.hip", "combine.hip", "api.hip"]
+SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "gemm2.hip", "combine.hip", "balance.hip",
+           "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

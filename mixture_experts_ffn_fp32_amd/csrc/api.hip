@@ -561,4 +561,17 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
 }
 
+int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens, const int32_t *counts,
+                     float alpha, float *bias, void *stream) {
+  if (n_experts < 1 || n_experts > 1024 || top_k < 1 || top_k > n_experts || n_tokens < 0 ||
+      n_tokens * static_cast<int64_t>(top_k) > 0x7FFFFFFF)
+    return MOE_ERR_SHAPE;
+  if (!counts || !bias) return MOE_ERR_NULL;
+  if (!(alpha == alpha) || alpha > 3.4e38f || alpha < -3.4e38f) return MOE_ERR_MODE;
+  if (n_tokens == 0) return MOE_OK;
+  MOE_TRY(launch_balance(n_experts, n_tokens * top_k, counts, alpha, bias,
+                         static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

@@ -48,6 +48,10 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef MOE_G2_GM
+#define MOE_G2_GM 4
+#endif
+
 // two A and three B stage buffers of the largest tile (256 rows x 128 bytes)
 constexpr int kRowBytes = 128;
 constexpr int kLdsBytes = (2 * 256 + 3 * 256) * kRowBytes;
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
   if (local >= per) return;
   const int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
   if (pid >= total) return;
-  constexpr int GM = 4;
+  constexpr int GM = MOE_G2_GM;
   const int64_t grp = pid / (GM * n_tn);
   const int64_t first_m = grp * GM;
   const int gsz = static_cast<int>(min<int64_t>(n_m - first_m, GM));

@@ -162,4 +162,8 @@ hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, i
                                  int has_rmsnorm, float eps, const float *gamma, void *r,
                                  int act_bf16, hipStream_t s);
 
+// Bias-based balancer step (balance.hip); nk = tokens x top-k.
+hipError_t launch_balance(int E, int64_t nk, const int32_t *counts, float alpha, float *bias,
+                          hipStream_t s);
+
 }  // namespace moe

@@ -99,3 +99,23 @@ def test_workspace_too_small_rejected():
     rc = moe.lib().moe_dispatch(C.byref(d), fake, fake, None, fake, fake, fake, fake, fake, None,
                                 None, fake, 16, None)
     assert rc == -4
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 8), -2), ((1025, 1, 8), -2), ((4, 0, 8), -2), ((4, 5, 8), -2), ((4, 2, -1), -2),
+    ((4, 2, 2 ** 31), -2),
+])
+def test_balance_bias_bad_shapes_rejected(args, status):
+    """Checked on the host before any launch (no device pointers needed)."""
+    dummy = C.c_void_p(16)
+    assert moe.lib().moe_balance_bias(*args, dummy, 0.1, dummy, None) == status
+
+
+def test_balance_bias_null_and_alpha_rejected():
+    dummy = C.c_void_p(16)
+    assert moe.lib().moe_balance_bias(4, 2, 8, None, 0.1, dummy, None) == -1
+    assert moe.lib().moe_balance_bias(4, 2, 8, dummy, 0.1, None, None) == -1
+    assert moe.lib().moe_balance_bias(4, 2, 8, dummy, float("nan"), dummy, None) == -3
+    assert moe.lib().moe_balance_bias(4, 2, 8, dummy, float("inf"), dummy, None) == -3
+    # zero tokens: a no-op that touches nothing
+    assert moe.lib().moe_balance_bias(4, 2, 0, dummy, 0.1, dummy, None) == 0

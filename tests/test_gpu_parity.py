@@ -258,3 +258,71 @@ def test_probe_records_stage_events():
     layer.forward(layer.dev["x"], probe=probe)
     torch.cuda.synchronize()
     assert b.elapsed_time(e) > 0
+
+
+# ---------------------------------------------------------------- balancer
+def _balance_gpu(E, K, N, counts, bias, alpha):
+    c = torch.from_numpy(np.ascontiguousarray(counts, dtype=np.int32)).cuda()
+    b = torch.from_numpy(np.array(bias, dtype=np.float32)).cuda()
+    moe.moe_balance_bias(E, K, N, c, alpha, b)
+    torch.cuda.synchronize()
+    return b.cpu().numpy()
+
+
+def test_balance_bias_worked_example():
+    """Part 3, section 14.5 on the device: [0]*4 -> [-0.1, 0, 0.1, 0]."""
+    say("case balance worked example")
+    out = _balance_gpu(4, 2, 8, [5, 4, 3, 4], [0, 0, 0, 0], 0.1)
+    assert np.array_equal(out, oracle.balance_bias([5, 4, 3, 4], [0, 0, 0, 0], 0.1, 8, 2))
+    assert np.array_equal(out, np.float32([-0.1, 0.0, 0.1, 0.0]))
+
+
+@pytest.mark.parametrize("E,K,N,seed", [(4, 2, 2048, 0), (64, 8, 8192, 1), (256, 8, 16384, 2),
+                                        (1024, 2, 40, 3), (300, 7, 977, 4), (1, 1, 5, 5)])
+def test_balance_bias_matches_oracle(E, K, N, seed):
+    """Bit-exact against the oracle on random loads, biases beyond the clamp
+    range included; a third of the experts are set exactly balanced."""
+    say(f"case balance E={E} K={K} N={N} seed={seed}")
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(N * K, np.ones(E) / E).astype(np.int32)
+    if (N * K) % E == 0:
+        counts[: E // 3] = (N * K) // E
+    bias = rng.uniform(-1.3, 1.3, E).astype(np.float32)
+    alpha = float(np.float32(rng.uniform(0.001, 0.3)))
+    got = _balance_gpu(E, K, N, counts, bias, alpha)
+    want = oracle.balance_bias(counts, bias, alpha, N, K)
+    assert np.array_equal(got, want)
+
+
+def test_balance_bias_exact_at_large_token_counts():
+    """N K = 2^30 with E = 256: an expert off by one assignment must still
+    move (1/E - c/(N K) = 2^-30, below fp32 resolution of 1/E), a balanced
+    one must not."""
+    say("case balance large N")
+    E, K, N = 256, 8, 2 ** 27
+    counts = np.full(E, N * K // E, dtype=np.int32)
+    counts[0] += 1
+    counts[1] -= 1
+    got = _balance_gpu(E, K, N, counts, np.zeros(E, np.float32), 0.01)
+    assert got[0] == np.float32(-0.01) and got[1] == np.float32(0.01)
+    assert np.all(got[2:] == 0)
+    assert np.array_equal(got, oracle.balance_bias(counts, np.zeros(E), 0.01, N, K))
+
+
+def test_balance_bias_after_forward():
+    """The balancer consumes the loads moe_forward returns; the bias it
+    writes is the one the next forward's router adds."""
+    w = moe_synth.get("small")
+    say("case balance after forward small")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    counts = torch.zeros(w.E, dtype=torch.int32, device="cuda")
+    layer.forward(layer.dev["x"], counts=counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    assert int(c.sum()) == w.T * w.K
+    b0 = layer.dev["bias"].cpu().numpy().copy()
+    moe.moe_balance_bias(w.E, w.K, w.T, counts, 0.05, layer.dev["bias"])
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.dev["bias"].cpu().numpy(),
+                          oracle.balance_bias(c, b0, 0.05, w.T, w.K))
