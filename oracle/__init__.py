@@ -65,6 +65,7 @@ def lib():
         L.or_combine.argtypes = [P, P, P, C.c_int32, P, P, C.c_int64, P]
         L.or_dispatch.argtypes = [C.c_int64, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P]
         L.or_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P]
+        L.or_quantile_balance.argtypes = [P, P, P]
         for f in ("or_route", "or_forward", "or_expert_rows", "or_combine", "or_dispatch"):
             getattr(L, f).restype = C.c_int
         L.or_silu.argtypes = [C.c_double]
@@ -159,6 +160,14 @@ class Oracle:
         _check(lib().or_forward(C.byref(self.layer), C.byref(self.tensors), _p(t), n,
                                 _p(ov), _p(out), _p(idx), _p(g), _p(gap)), "forward")
         return out, idx, g, gap
+
+    def quantile_balance(self):
+        """QuantileBalancer update over all T tokens (sigmoid routing): the new
+        centred bias [E] in fp64."""
+        out = np.zeros(self.spec.E, dtype=np.float64)
+        _check(lib().or_quantile_balance(C.byref(self.layer), C.byref(self.tensors), _p(out)),
+               "or_quantile_balance")
+        return out
 
     def expert_rows(self, rows, expert, scale=None):
         """fp64 scale[p] * FFN_{expert[p]}(rows[p]) at the routed width."""

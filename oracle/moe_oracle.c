@@ -412,3 +412,60 @@ int or_balance_bias(int32_t E, int32_t K, int64_t n_tokens, const int32_t *count
   }
   return 0;
 }
+
+static int cmp_double(const void *a, const void *b) {
+  const double x = *(const double *)a, y = *(const double *)b;
+  return (x > y) - (x < y);
+}
+
+/* QuantileBalancer update ("StableLatentMoE and QuantileBalancer",
+ * "QuantileBalancer: persistent biases, no gradient update"; sigmoid routing
+ * only). For every token t: s[t,e] = sigmoid(x_t . W_router[e]) (raw scores),
+ * corrected scores s + b with the current bias b, and the threshold thresh_t =
+ * the (K+1)-th largest corrected score. For every expert e the new bias is
+ * the p = K/E quantile over tokens of thresh_t - s[t,e] with the "higher"
+ * rule (the sorted value at position ceil(p (T-1)), taken exactly as
+ * ceil(K (T-1) / E)); the E quantiles are then centred by their mean.
+ * Needs K < E and T >= 1; writes new_bias[E] (fp64). */
+int or_quantile_balance(const or_layer *L, const or_tensors *W, double *new_bias) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->route != OR_ROUTE_SIGMOID_BIAS) return -3;
+  const int E = L->E, K = L->K, d = L->d;
+  const int64_t T = L->T;
+  if (K >= E || T < 1 || !new_bias) return -2;
+  double *diff = (double *)malloc(sizeof(double) * (size_t)(T * E)); /* [E][T] */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *raw = (double *)malloc(sizeof(double) * (size_t)E * 2);
+    double *corr = raw + E;
+    int *taken = (int *)malloc(sizeof(int) * (size_t)E);
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+    load_row(W->x, L->act, t, d, xv);
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int i = 0; i < d; ++i) s += (double)W->w_router[(int64_t)e * d + i] * xv[i];
+      raw[e] = or_sigmoid(s);
+      corr[e] = raw[e] + (W->bias ? (double)W->bias[e] : 0.0);
+    }
+    rank_top(corr, E, K + 1, taken, sel);
+    const double thresh = corr[sel[K]];
+    for (int e = 0; e < E; ++e) diff[(int64_t)e * T + t] = thresh - raw[e];
+    free(sel);
+    free(taken);
+    free(raw);
+    free(xv);
+  }
+  const int64_t pos = ((int64_t)K * (T - 1) + E - 1) / E; /* ceil(K (T-1) / E) */
+  double mean = 0.0;
+  for (int e = 0; e < E; ++e) {
+    qsort(diff + (int64_t)e * T, (size_t)T, sizeof(double), cmp_double);
+    new_bias[e] = diff[(int64_t)e * T + pos];
+    mean += new_bias[e];
+  }
+  mean /= E;
+  for (int e = 0; e < E; ++e) new_bias[e] -= mean;
+  free(diff);
+  return 0;
+}

@@ -542,3 +542,91 @@ def test_balancer_matches_rule_on_random_counts(seed):
 def test_balancer_no_tokens_is_a_no_op():
     out = oracle.balance_bias([0, 0], [0.3, -0.2], 0.1, 0, 1)
     assert np.array_equal(out, np.float32([0.3, -0.2]))
+
+
+# ---------------------------------------------------------------- QuantileBalancer
+def _qb_layer(T, E, K, seed, bias_std=0.3, d=None):
+    w = custom("qb", T=T, d=d or E, E=E, K=K, route="sigmoid_bias", n_shared=0, d_ff_shared=0,
+               bias_std=bias_std, router_std=0.8)
+    a = moe_synth.generate(w, experts=False)
+    return w, a
+
+
+def _qb_by_numpy(w, a):
+    """The update written with numpy's quantile: thresholds from the oracle's
+    own router (its (K+1)-th ranked score), raw scores sigmoid(x W^T)."""
+    orc = oracle.Oracle(w, a)
+    _, _, _, top = orc.route()
+    thresh = top[:, w.K]
+    s = 1.0 / (1.0 + np.exp(-(f64(a["x"]) @ f64(a["w_router"]).T)))
+    q = np.quantile(thresh[:, None] - s, w.K / w.E, axis=0, method="higher")
+    return q - q.mean(), thresh, s
+
+
+@pytest.mark.parametrize("T,E,K,seed", [(37, 6, 2, 0), (64, 8, 3, 1), (101, 12, 4, 2), (5, 3, 1, 3)])
+def test_quantile_balancer_matches_numpy_quantile(T, E, K, seed):
+    """StableLatentMoE page, QuantileBalancer: quantile over tokens of
+    thresh - s at p = K/E, interpolation "higher", then centred. p (T-1) is
+    exact in fp64 for these sizes, so numpy's rank equals ceil(K (T-1) / E)."""
+    w, a = _qb_layer(T, E, K, seed)
+    want, _, _ = _qb_by_numpy(w, a)
+    got = oracle.Oracle(w, a).quantile_balance()
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_quantile_balancer_higher_rule_takes_upper_neighbour():
+    """T = 4, E = 2, K = 1: p (T - 1) = 1.5, so the 'higher' rule picks the
+    third smallest difference (linear interpolation would average 2nd and 3rd)."""
+    w, a = _qb_layer(4, 2, 1, 7)
+    got = oracle.Oracle(w, a).quantile_balance()
+    _, thresh, s = _qb_by_numpy(w, a)
+    dsort = np.sort(thresh[:, None] - s, axis=0)
+    q = dsort[2]
+    assert np.allclose(got, q - q.mean(), atol=1e-12)
+    lin = 0.5 * (dsort[1] + dsort[2])
+    assert not np.allclose(got, lin - lin.mean(), atol=1e-9)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_quantile_balancer_invariants(seed):
+    """Centred (sums to 0); unchanged by a common shift of the current bias;
+    each expert's uncentred value is an order statistic of its differences
+    with at least ceil(K (T-1)/E) + 1 differences at or below it."""
+    T, E, K = 50, 10, 3
+    w, a = _qb_layer(T, E, K, seed)
+    got = oracle.Oracle(w, a).quantile_balance()
+    assert abs(got.sum()) < 1e-12
+    a2 = dict(a)
+    a2["bias"] = (a["bias"] + np.float32(0.25)).astype(np.float32)
+    got2 = oracle.Oracle(w, a2).quantile_balance()
+    # (the shifted bias is stored in fp32: equal up to its rounding)
+    assert np.max(np.abs(got2 - got)) < 1e-6
+    _, thresh, s = _qb_by_numpy(w, a)
+    dd = thresh[:, None] - s
+    pos = -(-K * (T - 1) // E)
+    for e in range(E):
+        col = dd[:, e]
+        qe = got[e] + np.mean(np.sort(dd, axis=0)[pos])  # un-centre
+        assert np.min(np.abs(col - qe)) < 1e-12
+        assert np.sum(col <= qe + 1e-12) >= pos + 1 and np.sum(col < qe - 1e-12) <= pos
+
+
+def test_quantile_balancer_identical_tokens_closed_form():
+    """Every token equal: the differences are constant over tokens, so the new
+    bias is (thresh - s_e) - mean_e(thresh - s_e) = mean(s) - s_e."""
+    w, a = _qb_layer(9, 5, 2, 11)
+    a = dict(a)
+    a["x"] = np.repeat(a["x"][:1], 9, axis=0)
+    got = oracle.Oracle(w, a).quantile_balance()
+    s = 1.0 / (1.0 + np.exp(-(f64(a["x"][0]) @ f64(a["w_router"]).T)))
+    assert np.allclose(got, s.mean() - s, atol=1e-12)
+
+
+def test_quantile_balancer_rejects_non_sigmoid_and_k_equal_e():
+    w, a = _qb_layer(10, 4, 2, 0)
+    w2 = custom("qb2", T=10, d=4, E=4, K=2, route="topk_softmax", n_shared=0, d_ff_shared=0)
+    with pytest.raises(RuntimeError):
+        oracle.Oracle(w2, moe_synth.generate(w2, experts=False)).quantile_balance()
+    w3 = custom("qb3", T=10, d=4, E=4, K=4, route="sigmoid_bias", n_shared=0, d_ff_shared=0)
+    with pytest.raises(RuntimeError):
+        oracle.Oracle(w3, moe_synth.generate(w3, experts=False)).quantile_balance()
