@@ -187,6 +187,19 @@ def main():
     e_ev.record(stream)
     torch.cuda.synchronize()
     balance_us = b_ev.elapsed_time(e_ev) / reps * 1e3
+
+    # QuantileBalancer update (sigmoid-routed layers): router + per-expert
+    # quantile of thresh - s over all tokens, into a scratch bias
+    qb = None
+    if w.route == "sigmoid_bias" and w.K < w.E:
+        nb = torch.empty(w.E, dtype=torch.float32, device=dev)
+        moe.moe_quantile_balance(layer.desc, layer.weights, x, nb, layer.ws, stream)
+        b_ev.record(stream)
+        for _ in range(10):
+            moe.moe_quantile_balance(layer.desc, layer.weights, x, nb, layer.ws, stream)
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        qb = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E}
     tok_s = w.T / (ms / 1e3)
     peak_tf = PEAK[w.act]
     intensity = alg["gu_flops"] / alg["gu_bytes"]
@@ -235,6 +248,7 @@ def main():
         "roofline": roof,
         "balance_bias": {"us_per_call": round(balance_us, 2), "experts": w.E,
                          "note": "one bias-based balancer step, back-to-back launches"},
+        "quantile_balance": qb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -232,6 +232,26 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream);
 
+/* QuantileBalancer update ("StableLatentMoE and QuantileBalancer", sections
+ * "QuantileBalancer: persistent biases, no gradient update" and "FP32 router
+ * and training-only QB update"); sigmoid routing (MOE_ROUTE_SIGMOID_BIAS)
+ * with top_k < n_experts only. From the router of this layer on x (fp32
+ * logits as moe_route computes them, raw scores s = sigmoid(logits),
+ * corrected scores s + bias with the current w->bias): per token the
+ * threshold is the (K+1)-th largest corrected score; per expert e, new_bias[e]
+ * is the value at position ceil(K (T-1) / E) of the ascending token-sorted
+ * thresh - s[., e] (the p = K/E quantile, "higher" rule); the E values are
+ * then centred by their mean (summed in fp64). new_bias: fp32 [E] device
+ * array; it may be w->bias itself (the pages replace the buffer in place:
+ * every read of the old bias precedes the write on the stream). The caller
+ * applies it to later forwards (training-mode forwards only, per the page).
+ * T == 0 is a no-op. Errors: MOE_ERR_MODE (other routing rules), MOE_ERR_SHAPE
+ * (top_k >= n_experts, or a bad descriptor), MOE_ERR_NULL, MOE_ERR_WORKSPACE
+ * (ws_bytes below moe_workspace_size, which includes this call's buffers
+ * for sigmoid-routed layers), MOE_ERR_HIP. */
+MOE_API int moe_quantile_balance(const moe_desc *desc, const moe_weights *w, const void *x,
+                                 float *new_bias, void *ws, size_t ws_bytes, void *stream);
+
 /* Bias-based load balancing, one step ("APEX-1 Mathematical Reference -
  * Part 3", section 14.3; the sign rule of section 14.4). For a step of
  * n_tokens tokens routed top-k over n_experts experts with per-expert loads

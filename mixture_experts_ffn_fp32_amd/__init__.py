@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_balance_bias")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
+           "moe_balance_bias")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -70,8 +71,9 @@ def lib():
         L.moe_combine.argtypes = [P, P, P, P, P, P, P, S, P]
         L.moe_forward.argtypes = [P, P, P, P, P, P, P, S, P, P]
         L.moe_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P, P]
+        L.moe_quantile_balance.argtypes = [P, P, P, P, P, S, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
-                  "moe_combine", "moe_forward", "moe_balance_bias"):
+                  "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -130,6 +132,12 @@ def _nbytes(t):
 def moe_route(desc, weights, x, idx, g, gap=None, top_scores=None, ws=None, stream=None):
     _ok(lib().moe_route(C.byref(desc), C.byref(weights), _ptr(x), _ptr(idx), _ptr(g), _ptr(gap),
                         _ptr(top_scores), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_route")
+
+
+def moe_quantile_balance(desc, weights, x, new_bias, ws, stream=None):
+    """QuantileBalancer update of a sigmoid-routed layer: new_bias fp32 [E]."""
+    _ok(lib().moe_quantile_balance(C.byref(desc), C.byref(weights), _ptr(x), _ptr(new_bias),
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), "moe_quantile_balance")
 
 
 def moe_balance_bias(n_experts, top_k, n_tokens, counts, alpha, bias, stream=None):

@@ -21,6 +21,7 @@ struct Layout {
   size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, tiles2,
       ntiles2, ntie;
   size_t z, h, y, hsh, r;
+  size_t qb_top, qb_diff, qb_q;  // QuantileBalancer (sigmoid routing only)
   size_t total;
   int64_t max_tiles;
 };
@@ -64,6 +65,11 @@ Layout layout_of(const moe_desc *d) {
   L.y = take(rows * de * es);
   L.hsh = d->d_shared ? take(T * d->d_shared * es) : 0;
   L.r = d->latent ? take(T * d->latent * es) : 0;
+  if (d->route_mode == MOE_ROUTE_SIGMOID_BIAS) {
+    L.qb_top = take(T * (K + 1) * 4);
+    L.qb_diff = take(T * E * 4);
+    L.qb_q = take(E * 4);
+  }
   L.total = o;
   return L;
 }
@@ -352,6 +358,41 @@ int moe_route(const moe_desc *d, const moe_weights *w, const void *x, int32_t *i
   a.gap = gap;
   a.top = top_scores;
   if (launch_router(a, d->act_dtype == MOE_BF16, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_quantile_balance(const moe_desc *d, const moe_weights *w, const void *x,
+                         float *new_bias, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->route_mode != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_MODE;
+  if (d->top_k >= d->n_experts) return MOE_ERR_SHAPE;
+  if (!w || !w->w_router || !new_bias || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  char *wsb = static_cast<char *>(ws);
+  RouterArgs a{};
+  a.w_split = wsb + L.wsplit;
+  a.logits = reinterpret_cast<float *>(wsb + L.logits);
+  a.x = x;
+  a.w = w->w_router;
+  a.bias = w->bias;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.E = d->n_experts;
+  a.K = d->top_k;
+  a.mode = d->route_mode;
+  a.renormalize = d->renormalize;
+  a.routed_scale = d->routed_scale;
+  a.idx = reinterpret_cast<int32_t *>(wsb + L.idx);
+  a.g = reinterpret_cast<float *>(wsb + L.g);
+  a.gap = nullptr;
+  a.top = reinterpret_cast<float *>(wsb + L.qb_top);
+  if (launch_quantile_balance(a, d->act_dtype == MOE_BF16, reinterpret_cast<float *>(wsb + L.qb_diff),
+                              reinterpret_cast<float *>(wsb + L.qb_q), new_bias,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -24,6 +24,11 @@ struct RouterArgs {
   float *top;            // [T, K+1] or null
 };
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
+// QuantileBalancer update (sigmoid routing): runs the router (a.top must be
+// set: its column K is the threshold), then the differences diff [E, T],
+// per-expert order statistics q [E] and the centred new_bias [E].
+hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *diff, float *q,
+                                   float *new_bias, hipStream_t s);
 // Workspace of the router: split weight planes and partial logits.
 inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
   return act_bf16 ? static_cast<size_t>(3 * E * d * 2) : 0;

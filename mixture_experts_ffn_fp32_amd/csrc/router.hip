@@ -36,6 +36,24 @@ constexpr int kPerLane = kMaxE / 64;
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Logit of expert e from the partials of token row lg ([splits][T, parts*E]
+// with split stride ss): each plane's K-split partials summed in split
+// order, then the planes high + mid + low. Every consumer of the logits
+// calls this, so they all see the same fp32 value.
+__device__ __forceinline__ float logit_of(const float *lg, int e, int E, int parts, int splits,
+                                          int64_t ss) {
+  float pl[3] = {0.f, 0.f, 0.f};
+  for (int q = 0; q < splits; ++q) {
+    const float *ls = lg + q * ss;
+    pl[0] += ls[e];
+    if (parts == 3) {
+      pl[1] += ls[E + e];
+      pl[2] += ls[2 * E + e];
+    }
+  }
+  return parts == 3 ? (pl[0] + pl[1]) + pl[2] : pl[0];
+}
+
 // planes[0..2][i] = exact bf16 split of w[i]
 __global__ __launch_bounds__(256) void split_kernel(const float *__restrict__ w, int64_t n,
                                                     uint16_t *__restrict__ planes) {
@@ -73,16 +91,7 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
     const int e = lane + 64 * j;
     float sc = -INFINITY, l = 0.f;
     if (e < E) {
-      float pl[3] = {0.f, 0.f, 0.f};
-      for (int q = 0; q < splits; ++q) {
-        const float *ls = lg + q * split_stride;
-        pl[0] += ls[e];
-        if (parts == 3) {
-          pl[1] += ls[E + e];
-          pl[2] += ls[2 * E + e];
-        }
-      }
-      l = parts == 3 ? (pl[0] + pl[1]) + pl[2] : pl[0];
+      l = logit_of(lg, e, E, parts, splits, split_stride);
       const float b = a.bias ? a.bias[e] : 0.f;
       sc = sig ? sigmoidf_(l) + b : l + b;
       vmax = fmaxf(vmax, sc);
@@ -190,6 +199,95 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
   }
 }
 
+// ------------------------------------------------------------ QuantileBalancer
+// d[e][t] = thresh_t - sigmoid(logit[t, e]), thresh_t = the token's (K+1)-th
+// corrected score (top[t, K]). 64 tokens x 64 experts per workgroup,
+// transposed through LDS so both the logit reads and the writes coalesce.
+__global__ __launch_bounds__(256) void qb_diff_kernel(const float *logits, int parts, int splits,
+                                                      int64_t ss, const float *top, int64_t T,
+                                                      int E, int K, float *d) {
+  __shared__ float tile[64][65];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int e0 = blockIdx.y * 64;
+  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;  // 4 rows per pass
+  const int64_t rowlen = static_cast<int64_t>(parts) * E;
+  for (int r = ly; r < 64; r += 4) {
+    const int64_t t = t0 + r;
+    const int e = e0 + lx;
+    if (t < T && e < E) {
+      const float l = logit_of(logits + t * rowlen, e, E, parts, splits, ss);
+      tile[r][lx] = top[t * (K + 1) + K] - sigmoidf_(l);
+    }
+  }
+  __syncthreads();
+  for (int r = ly; r < 64; r += 4) {
+    const int e = e0 + r;
+    const int64_t t = t0 + lx;
+    if (t < T && e < E) d[static_cast<int64_t>(e) * T + t] = tile[lx][r];
+  }
+}
+
+// order-preserving map of a finite float to uint32 and back
+__device__ __forceinline__ uint32_t ord_of(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// q[e] = the rank-th smallest of d[e][0..T) (one workgroup per expert):
+// four 8-bit radix passes, most significant digit first, each counting the
+// candidates that match the digits fixed so far.
+__global__ __launch_bounds__(256) void qb_select_kernel(const float *d, int64_t T, int64_t rank,
+                                                        float *q) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix, s_rank;
+  const int e = blockIdx.x;
+  const float *col = d + static_cast<int64_t>(e) * T;
+  if (threadIdx.x == 0) {
+    s_prefix = 0;
+    s_rank = static_cast<uint32_t>(rank);
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    for (int64_t t = threadIdx.x; t < T; t += 256) {
+      const uint32_t k = ord_of(col[t]);
+      if ((k & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {  // first digit whose running count passes the rank
+      uint32_t acc = 0, r = s_rank;
+      int dg = 0;
+      for (; dg < 255; ++dg) {
+        if (acc + hist[dg] > r) break;
+        acc += hist[dg];
+      }
+      s_rank = r - acc;
+      s_prefix = prefix | (static_cast<uint32_t>(dg) << shift);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) q[e] = float_of(s_prefix);
+}
+
+// new_bias[e] = q[e] - mean(q), the mean summed in fp64 in expert order
+__global__ __launch_bounds__(256) void qb_center_kernel(const float *q, int E, float *new_bias) {
+  __shared__ double s_mean;
+  if (threadIdx.x == 0) {
+    double m = 0.0;
+    for (int e = 0; e < E; ++e) m += static_cast<double>(q[e]);
+    s_mean = m / E;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    new_bias[e] = static_cast<float>(static_cast<double>(q[e]) - s_mean);
+}
+
 }  // namespace
 
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
@@ -223,6 +321,25 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (e != hipSuccess) return e;
   select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts, splits,
                                                                       g.split_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *diff, float *q,
+                                   float *new_bias, hipStream_t s) {
+  if (a.T == 0 || !a.top) return hipErrorInvalidValue;
+  hipError_t e = launch_router(a, act_bf16, s);
+  if (e != hipSuccess) return e;
+  const int parts = act_bf16 ? 3 : 1;
+  const int splits = router_splits(a.T, a.d);
+  const int64_t ss = a.T * parts * a.E;
+  dim3 grid(static_cast<unsigned>((a.T + 63) / 64), static_cast<unsigned>((a.E + 63) / 64));
+  qb_diff_kernel<<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.top, a.T, a.E, a.K, diff);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // position ceil(p (T - 1)) of the sorted differences, p = K / E, exactly
+  const int64_t rank = (static_cast<int64_t>(a.K) * (a.T - 1) + a.E - 1) / a.E;
+  qb_select_kernel<<<a.E, 256, 0, s>>>(diff, a.T, rank, q);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  qb_center_kernel<<<1, 256, 0, s>>>(q, a.E, new_bias);
   return hipGetLastError();
 }
 

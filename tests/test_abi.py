@@ -119,3 +119,23 @@ def test_balance_bias_null_and_alpha_rejected():
     assert moe.lib().moe_balance_bias(4, 2, 8, dummy, float("inf"), dummy, None) == -3
     # zero tokens: a no-op that touches nothing
     assert moe.lib().moe_balance_bias(4, 2, 0, dummy, 0.1, dummy, None) == 0
+
+
+def test_quantile_balance_checked_before_launch():
+    """Sigmoid routing with K < E only; NULLs and a short workspace are
+    reported before anything is enqueued; the workspace of a sigmoid-routed
+    layer holds the balancer's buffers."""
+    fake = C.c_void_p(1 << 20)
+    w = moe.MoeWeights()
+    w.w_router = fake
+    sig = _desc(T=16, route_mode=2)
+    n_sig = moe.moe_workspace_size(sig)
+    assert n_sig > moe.moe_workspace_size(_desc(T=16))
+    L = moe.lib()
+    assert L.moe_quantile_balance(C.byref(_desc(T=16)), C.byref(w), fake, fake, fake, n_sig,
+                                  None) == -3
+    assert L.moe_quantile_balance(C.byref(_desc(T=16, route_mode=2, top_k=4)), C.byref(w), fake,
+                                  fake, fake, 1 << 30, None) == -2
+    assert L.moe_quantile_balance(C.byref(sig), C.byref(w), fake, None, fake, n_sig, None) == -1
+    assert L.moe_quantile_balance(C.byref(sig), C.byref(w), fake, fake, fake, n_sig - 1,
+                                  None) == -4

@@ -32,5 +32,13 @@ def test_full_size_workload(name):
     if name == "medium":
         counts = np.bincount(o_idx.ravel(), minlength=w.E)
         assert (counts == 0).sum() == moe_synth.ZIPF_EMPTY
+    if name == "latent":  # QuantileBalancer update over all tokens
+        say("  latent: quantile balance")
+        nb = torch.empty(w.E, dtype=torch.float32, device="cuda")
+        moe.moe_quantile_balance(layer.desc, layer.weights, layer.dev["x"], nb, layer.ws)
+        torch.cuda.synchronize()
+        err = float(np.max(np.abs(nb.cpu().numpy() - orc.quantile_balance())))
+        say(f"  latent: quantile balance max abs err {err:.2e}")
+        assert err <= 2e-5
     del layer, a
     torch.cuda.empty_cache()

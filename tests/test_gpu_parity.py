@@ -326,3 +326,45 @@ def test_balance_bias_after_forward():
     torch.cuda.synchronize()
     assert np.array_equal(layer.dev["bias"].cpu().numpy(),
                           oracle.balance_bias(c, b0, 0.05, w.T, w.K))
+
+
+# ---------------------------------------------------------------- QuantileBalancer
+QB_TOL = 2e-5  # absolute, on biases of order 0.1: fp32 router and scores vs fp64
+
+
+@pytest.mark.parametrize("name", ["sigmoid", "sigmoid_renorm_scaled", "latent_f32",
+                                  "latent_bf16_noshared", "qb_e1024", "qb_one_token"])
+def test_quantile_balance_matches_oracle(name):
+    extra = {"qb_e1024": dict(T=300, d=32, d_ff=8, E=1024, K=8, route="sigmoid_bias",
+                              bias_std=0.05, act="bf16"),
+             "qb_one_token": dict(T=1, E=9, K=3, route="sigmoid_bias", bias_std=0.1)}
+    w = custom(name, **(EDGE.get(name) or extra[name]))
+    say(f"case quantile_balance {name} T={w.T} E={w.E} K={w.K} act={w.act}")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    nb = torch.full((w.E,), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_quantile_balance(layer.desc, layer.weights, layer.dev["x"], nb, layer.ws)
+    torch.cuda.synchronize()
+    got = nb.cpu().numpy().astype(np.float64)
+    want = oracle.Oracle(w, a).quantile_balance()
+    err = float(np.max(np.abs(got - want)))
+    say(f"  max abs err {err:.2e}, sum {got.sum():.2e}")
+    assert err <= QB_TOL
+    assert abs(got.sum()) <= 1e-5 * w.E
+
+
+def test_quantile_balance_in_place_replaces_the_buffer():
+    """new_bias may be the layer's own bias (the page copies into the
+    buffer): same result as writing elsewhere, and the next route uses it."""
+    w = custom("qb_inplace", **EDGE["sigmoid"])
+    say("case quantile_balance in place")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    other = torch.empty(w.E, dtype=torch.float32, device="cuda")
+    moe.moe_quantile_balance(layer.desc, layer.weights, layer.dev["x"], other, layer.ws)
+    moe.moe_quantile_balance(layer.desc, layer.weights, layer.dev["x"], layer.dev["bias"], layer.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(other, layer.dev["bias"])
+    a2 = dict(a)
+    a2["bias"] = layer.dev["bias"].cpu().numpy()
+    check_route(w, a2, layer)
