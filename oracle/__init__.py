@@ -66,6 +66,7 @@ def lib():
         L.or_dispatch.argtypes = [C.c_int64, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P]
         L.or_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P]
         L.or_quantile_balance.argtypes = [P, P, P]
+        L.or_router_losses.argtypes = [P, P, P, C.c_double, C.c_double, P]
         for f in ("or_route", "or_forward", "or_expert_rows", "or_combine", "or_dispatch"):
             getattr(L, f).restype = C.c_int
         L.or_silu.argtypes = [C.c_double]
@@ -168,6 +169,14 @@ class Oracle:
         _check(lib().or_quantile_balance(C.byref(self.layer), C.byref(self.tensors), _p(out)),
                "or_quantile_balance")
         return out
+
+    def router_losses(self, counts, alpha: float, z_weight: float):
+        """(load-balancing loss, router z-loss) over all T tokens, fp64."""
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        out = np.zeros(2, dtype=np.float64)
+        _check(lib().or_router_losses(C.byref(self.layer), C.byref(self.tensors), _p(c),
+                                      float(alpha), float(z_weight), _p(out)), "or_router_losses")
+        return float(out[0]), float(out[1])
 
     def expert_rows(self, rows, expert, scale=None):
         """fp64 scale[p] * FFN_{expert[p]}(rows[p]) at the routed width."""

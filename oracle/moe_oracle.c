@@ -469,3 +469,50 @@ int or_quantile_balance(const or_layer *L, const or_tensors *W, double *new_bias
   free(diff);
   return 0;
 }
+
+/* Router auxiliary losses over the T tokens of a step, on the router's own
+ * logits r_t = x_t . W_router (the balance bias is a non-gradient nudge and
+ * is left out):
+ *  - load-balancing loss ("A working MoE layer in PyTorch", the Switch
+ *    load-balancing loss of MoELayer.forward): alpha * E * sum_e f_e * P_e,
+ *    f_e = counts[e] / (T K), P_e = mean over tokens of softmax(r_t)_e;
+ *  - router z-loss ("Mixture of Experts (MoE)", transformer book chapter 16,
+ *    MoEAuxiliaryLoss.router_z_loss, weight 0.001 there): z_weight * mean
+ *    over tokens of logsumexp(r_t)^2.
+ * Writes out[0] = load-balancing loss, out[1] = z-loss (fp64). Needs T >= 1. */
+int or_router_losses(const or_layer *L, const or_tensors *W, const int32_t *counts, double alpha,
+                     double z_weight, double *out) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  const int E = L->E, d = L->d;
+  const int64_t T = L->T;
+  if (T < 1 || !counts || !out) return -2;
+  double *psum = (double *)calloc((size_t)E, sizeof(double));
+  double zsum = 0.0;
+  double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+  double *r = (double *)malloc(sizeof(double) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    load_row(W->x, L->act, t, d, xv);
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int i = 0; i < d; ++i) s += (double)W->w_router[(int64_t)e * d + i] * xv[i];
+      r[e] = s;
+      m = s > m ? s : m;
+    }
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) z += exp(r[e] - m);
+    for (int e = 0; e < E; ++e) psum[e] += exp(r[e] - m) / z;
+    const double lse = m + log(z);
+    zsum += lse * lse;
+  }
+  double aux = 0.0;
+  for (int e = 0; e < E; ++e)
+    aux += ((double)counts[e] / ((double)T * L->K)) * (psum[e] / (double)T);
+  out[0] = alpha * E * aux;
+  out[1] = z_weight * zsum / (double)T;
+  free(r);
+  free(xv);
+  free(psum);
+  return 0;
+}

@@ -630,3 +630,42 @@ def test_quantile_balancer_rejects_non_sigmoid_and_k_equal_e():
     w3 = custom("qb3", T=10, d=4, E=4, K=4, route="sigmoid_bias", n_shared=0, d_ff_shared=0)
     with pytest.raises(RuntimeError):
         oracle.Oracle(w3, moe_synth.generate(w3, experts=False)).quantile_balance()
+
+
+# ---------------------------------------------------------------- router losses
+def _loss_layer(T, E, K, seed, act="f32"):
+    w = custom("losses", T=T, d=16, E=E, K=K, route="topk_softmax", n_shared=0, d_ff_shared=0,
+               router_std=0.5, act=act)
+    return w, moe_synth.generate(w, experts=False)
+
+
+@pytest.mark.parametrize("T,E,K,seed,act", [(37, 6, 2, 0, "f32"), (64, 16, 4, 1, "bf16"),
+                                            (3, 2, 1, 2, "f32")])
+def test_router_losses_match_scipy(T, E, K, seed, act):
+    """Switch loss (FromScratch page, MoELayer.forward: alpha * E * sum f P,
+    f = counts / (T K), P = mean softmax) and z-loss (transformer book page,
+    router_z_loss: mean logsumexp^2, weighted) with scipy's softmax and
+    logsumexp on the same fp64 logits."""
+    from scipy.special import logsumexp, softmax
+    w, a = _loss_layer(T, E, K, seed, act)
+    r = f64(a["x"]) @ f64(a["w_router"]).T
+    counts = np.bincount(np.argsort(-r, axis=1)[:, :K].ravel(), minlength=E)
+    got = oracle.Oracle(w, a).router_losses(counts, 0.01, 0.001)
+    f = counts / (T * K)
+    P = softmax(r, axis=1).mean(0)
+    assert abs(got[0] - 0.01 * E * np.sum(f * P)) < 1e-14
+    assert abs(got[1] - 0.001 * np.mean(logsumexp(r, axis=1) ** 2)) < 1e-14
+
+
+def test_router_losses_uniform_closed_form():
+    """Zero router weights: every softmax is uniform (P = 1/E) and
+    logsumexp = log E; with uniform loads f = 1/E the Switch loss equals
+    alpha (its minimum, per the page) and the z-loss is w (log E)^2."""
+    T, E, K = 40, 8, 2
+    w, a = _loss_layer(T, E, K, 0)
+    a = dict(a)
+    a["w_router"] = np.zeros_like(a["w_router"])
+    counts = np.full(E, T * K // E, dtype=np.int32)
+    aux, z = oracle.Oracle(w, a).router_losses(counts, 0.01, 0.001)
+    assert abs(aux - 0.01) < 1e-15
+    assert abs(z - 0.001 * math.log(E) ** 2) < 1e-15
