@@ -200,6 +200,19 @@ def main():
         e_ev.record(stream)
         torch.cuda.synchronize()
         qb = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E}
+    # router auxiliary losses (load-balancing + z-loss) on this step's loads
+    losses = torch.empty(2, dtype=torch.float32, device=dev)
+    moe.moe_router_losses(layer.desc, layer.weights, x, counts, 0.01, 0.001, losses, layer.ws,
+                          stream)
+    b_ev.record(stream)
+    for _ in range(10):
+        moe.moe_router_losses(layer.desc, layer.weights, x, counts, 0.01, 0.001, losses, layer.ws,
+                              stream)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    rl = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E,
+          "load_balancing_loss": round(float(losses[0]), 7),
+          "z_loss": round(float(losses[1]), 7)}
     tok_s = w.T / (ms / 1e3)
     peak_tf = PEAK[w.act]
     intensity = alg["gu_flops"] / alg["gu_bytes"]
@@ -249,6 +262,7 @@ def main():
         "balance_bias": {"us_per_call": round(balance_us, 2), "experts": w.E,
                          "note": "one bias-based balancer step, back-to-back launches"},
         "quantile_balance": qb,
+        "router_losses": rl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -252,6 +252,28 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
 MOE_API int moe_quantile_balance(const moe_desc *desc, const moe_weights *w, const void *x,
                                  float *new_bias, void *ws, size_t ws_bytes, void *stream);
 
+/* Router auxiliary losses of one training step, on this layer's router
+ * logits r_t = x_t W_router^T (fp32, as moe_route computes them; the balance
+ * bias is a non-gradient nudge and is not part of them):
+ *  - losses[0], the load-balancing loss of "A working MoE layer in PyTorch"
+ *    (the Switch loss its MoELayer computes): alpha * E * sum_e f_e * P_e with
+ *    f_e = counts[e] / (T * top_k) and P_e the mean over the T tokens of
+ *    softmax(r_t)_e;
+ *  - losses[1], the router z-loss of the transformer book's mixture-of-experts
+ *    chapter (MoEAuxiliaryLoss.router_z_loss, weight 0.001 there):
+ *    z_weight * mean over tokens of logsumexp(r_t)^2.
+ * counts: int32 [E] device array, the expert loads of the same T tokens (as
+ * moe_forward / moe_dispatch return them). losses: fp32 [2] device array.
+ * Any routing rule (the losses are defined on the softmax of the logits).
+ * Sums are taken in a fixed order (per 64 tokens in fp32, then in fp64):
+ * results are deterministic. Enqueued on stream, no host synchronisation.
+ * T == 0 is a no-op (losses untouched). Errors: MOE_ERR_NULL, MOE_ERR_MODE
+ * (alpha or z_weight not finite, or a bad descriptor), MOE_ERR_SHAPE,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+MOE_API int moe_router_losses(const moe_desc *desc, const moe_weights *w, const void *x,
+                              const int32_t *counts, float alpha, float z_weight, float *losses,
+                              void *ws, size_t ws_bytes, void *stream);
+
 /* Bias-based load balancing, one step ("APEX-1 Mathematical Reference -
  * Part 3", section 14.3; the sign rule of section 14.4). For a step of
  * n_tokens tokens routed top-k over n_experts experts with per-expert loads

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
-           "moe_balance_bias")
+           "moe_balance_bias", "moe_router_losses")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -72,8 +72,10 @@ def lib():
         L.moe_forward.argtypes = [P, P, P, P, P, P, P, S, P, P]
         L.moe_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P, P]
         L.moe_quantile_balance.argtypes = [P, P, P, P, P, S, P]
+        L.moe_router_losses.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, S, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
-                  "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance"):
+                  "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance",
+                  "moe_router_losses"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -138,6 +140,14 @@ def moe_quantile_balance(desc, weights, x, new_bias, ws, stream=None):
     """QuantileBalancer update of a sigmoid-routed layer: new_bias fp32 [E]."""
     _ok(lib().moe_quantile_balance(C.byref(desc), C.byref(weights), _ptr(x), _ptr(new_bias),
                                    _ptr(ws), _nbytes(ws), _stream(stream)), "moe_quantile_balance")
+
+
+def moe_router_losses(desc, weights, x, counts, alpha, z_weight, losses, ws, stream=None):
+    """Load-balancing loss and router z-loss of one step into losses fp32 [2]
+    (counts: int32 [E] loads of the same tokens)."""
+    _ok(lib().moe_router_losses(C.byref(desc), C.byref(weights), _ptr(x), _ptr(counts),
+                                float(alpha), float(z_weight), _ptr(losses), _ptr(ws),
+                                _nbytes(ws), _stream(stream)), "moe_router_losses")
 
 
 def moe_balance_bias(n_experts, top_k, n_tokens, counts, alpha, bias, stream=None):

@@ -22,6 +22,7 @@ struct Layout {
       ntiles2, ntie;
   size_t z, h, y, hsh, r;
   size_t qb_top, qb_diff, qb_q;  // QuantileBalancer (sigmoid routing only)
+  size_t loss;                   // router-loss partial sums
   size_t total;
   int64_t max_tiles;
 };
@@ -70,6 +71,7 @@ Layout layout_of(const moe_desc *d) {
     L.qb_diff = take(T * E * 4);
     L.qb_q = take(E * 4);
   }
+  L.loss = take(static_cast<size_t>(router_loss_chunks(T)) * (E + 1) * 4);
   L.total = o;
   return L;
 }
@@ -393,6 +395,35 @@ int moe_quantile_balance(const moe_desc *d, const moe_weights *w, const void *x,
   if (launch_quantile_balance(a, d->act_dtype == MOE_BF16, reinterpret_cast<float *>(wsb + L.qb_diff),
                               reinterpret_cast<float *>(wsb + L.qb_q), new_bias,
                               static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_router_losses(const moe_desc *d, const moe_weights *w, const void *x,
+                      const int32_t *counts, float alpha, float z_weight, float *losses, void *ws,
+                      size_t ws_bytes, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!w || !w->w_router || !counts || !losses || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  if (!(alpha == alpha) || alpha > 3.4e38f || alpha < -3.4e38f || !(z_weight == z_weight) ||
+      z_weight > 3.4e38f || z_weight < -3.4e38f)
+    return MOE_ERR_MODE;
+  const Layout L = layout_of(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  char *wsb = static_cast<char *>(ws);
+  RouterArgs a{};
+  a.w_split = wsb + L.wsplit;
+  a.logits = reinterpret_cast<float *>(wsb + L.logits);
+  a.x = x;
+  a.w = w->w_router;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.E = d->n_experts;
+  a.K = d->top_k;
+  if (launch_router_losses(a, d->act_dtype == MOE_BF16, counts, alpha, z_weight,
+                           reinterpret_cast<float *>(wsb + L.loss), losses,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

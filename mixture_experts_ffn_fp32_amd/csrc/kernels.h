@@ -29,6 +29,13 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
 // per-expert order statistics q [E] and the centred new_bias [E].
 hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *diff, float *q,
                                    float *new_bias, hipStream_t s);
+// Router auxiliary losses (load-balancing loss and z-loss) of one step:
+// runs the router GEMM, then per-64-token partial sums into part
+// [router_loss_chunks(T), E + 1] and the two losses into losses [2].
+hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t *counts,
+                                float alpha, float z_weight, float *part, float *losses,
+                                hipStream_t s);
+int64_t router_loss_chunks(int64_t T);
 // Workspace of the router: split weight planes and partial logits.
 inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
   return act_bf16 ? static_cast<size_t>(3 * E * d * 2) : 0;

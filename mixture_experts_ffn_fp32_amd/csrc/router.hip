@@ -288,9 +288,105 @@ __global__ __launch_bounds__(256) void qb_center_kernel(const float *q, int E, f
     new_bias[e] = static_cast<float>(static_cast<double>(q[e]) - s_mean);
 }
 
+// ------------------------------------------------------------ router losses
+// Load-balancing (Switch) loss of "A working MoE layer in PyTorch": alpha * E
+// * sum_e f_e P_e with f_e = counts[e] / (T K) and P_e the mean over tokens of
+// softmax(logits_t)_e; router z-loss of the transformer book's MoE chapter
+// (MoEAuxiliaryLoss.router_z_loss): z_weight * mean over tokens of
+// logsumexp(logits_t)^2. Both read the router's own logits x W^T (the balance
+// bias is a non-gradient nudge and stays out).
+//
+// Stage 1: one workgroup per 64 tokens (16 per wavefront, in token order);
+// each lane keeps the running softmax sums of the experts it owns; the four
+// wavefronts' sums are added in wavefront order. part[chunk] = {P sums [E],
+// sum of lse^2}. Stage 2 adds the chunks in chunk order in fp64.
+constexpr int kLossTokens = 64;
+
+__global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, int parts,
+                                                           int splits, int64_t ss, int64_t T,
+                                                           int E, float *part) {
+  __shared__ float sh[4][kMaxE + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t_begin = static_cast<int64_t>(blockIdx.x) * kLossTokens + wave * (kLossTokens / 4);
+  float acc[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) acc[j] = 0.f;
+  float zacc = 0.f;
+  for (int i = 0; i < kLossTokens / 4; ++i) {
+    const int64_t t = t_begin + i;
+    if (t >= T) break;
+    const float *lg = logits + t * static_cast<int64_t>(parts) * E;
+    float l[kPerLane];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int e = lane + 64 * j;
+      l[j] = e < E ? logit_of(lg, e, E, parts, splits, ss) : -INFINITY;
+      m = fmaxf(m, l[j]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      l[j] = lane + 64 * j < E ? expf(l[j] - m) : 0.f;
+      z += l[j];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) acc[j] += l[j] * rz;
+    const float lse = m + logf(z);
+    zacc += lse * lse;
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j)
+    if (lane + 64 * j < E) sh[wave][lane + 64 * j] = acc[j];
+  if (lane == 0) sh[wave][E] = zacc;
+  __syncthreads();
+  float *out = part + static_cast<int64_t>(blockIdx.x) * (E + 1);
+  for (int e = threadIdx.x; e <= E; e += 256)
+    out[e] = ((sh[0][e] + sh[1][e]) + sh[2][e]) + sh[3][e];
+}
+
+// losses[0] = alpha E sum_e (counts[e] / (T K)) (P_e / T), losses[1] =
+// z_weight (sum lse^2) / T; chunk sums in chunk order, expert terms reduced
+// in a fixed tree, all in fp64.
+__global__ __launch_bounds__(256) void loss_final_kernel(const float *part, int64_t n_chunks,
+                                                         int64_t T, int E, int K,
+                                                         const int32_t *counts, float alpha,
+                                                         float z_weight, float *losses) {
+  __shared__ double sa[256], sz[256];
+  double a = 0.0, zs = 0.0;
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    double s = 0.0;
+    for (int64_t c = 0; c < n_chunks; ++c) s += static_cast<double>(part[c * (E + 1) + e]);
+    if (e < E)
+      a += (static_cast<double>(counts[e]) / (static_cast<double>(T) * K)) * (s / static_cast<double>(T));
+    else
+      zs = s;
+  }
+  sa[threadIdx.x] = a;
+  sz[threadIdx.x] = zs;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      sa[threadIdx.x] += sa[threadIdx.x + w];
+      sz[threadIdx.x] += sz[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    losses[0] = static_cast<float>(static_cast<double>(alpha) * E * sa[0]);
+    losses[1] = static_cast<float>(static_cast<double>(z_weight) * sz[0] / static_cast<double>(T));
+  }
+}
+
 }  // namespace
 
-hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
+// Router GEMM only: partial logits [splits][T, parts * E] into a.logits.
+hipError_t launch_router_logits(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int64_t nw = static_cast<int64_t>(a.E) * a.d;
   GemmArgs g{};
@@ -317,10 +413,36 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   } else {
     g.b0 = a.w;
   }
-  hipError_t e = launch_dense(g, EPI_STORE_F32, act_bf16, s);
+  return launch_dense(g, EPI_STORE_F32, act_bf16, s);
+}
+
+hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipError_t e = launch_router_logits(a, act_bf16, s);
   if (e != hipSuccess) return e;
+  const int parts = act_bf16 ? 3 : 1;
+  const int splits = router_splits(a.T, a.d);
   select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts, splits,
-                                                                      g.split_stride);
+                                                                      a.T * parts * a.E);
+  return hipGetLastError();
+}
+
+int64_t router_loss_chunks(int64_t T) { return (T + kLossTokens - 1) / kLossTokens; }
+
+hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t *counts,
+                                float alpha, float z_weight, float *part, float *losses,
+                                hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipError_t e = launch_router_logits(a, act_bf16, s);
+  if (e != hipSuccess) return e;
+  const int parts = act_bf16 ? 3 : 1;
+  const int splits = router_splits(a.T, a.d);
+  const int64_t chunks = router_loss_chunks(a.T);
+  loss_partial_kernel<<<static_cast<unsigned>(chunks), 256, 0, s>>>(
+      a.logits, parts, splits, a.T * parts * a.E, a.T, a.E, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  loss_final_kernel<<<1, 256, 0, s>>>(part, chunks, a.T, a.E, a.K, counts, alpha, z_weight,
+                                      losses);
   return hipGetLastError();
 }
 

@@ -139,3 +139,29 @@ def test_quantile_balance_checked_before_launch():
     assert L.moe_quantile_balance(C.byref(sig), C.byref(w), fake, None, fake, n_sig, None) == -1
     assert L.moe_quantile_balance(C.byref(sig), C.byref(w), fake, fake, fake, n_sig - 1,
                                   None) == -4
+
+
+def test_router_losses_checked_before_launch():
+    """NULLs, non-finite weights and a short workspace are reported before
+    anything is enqueued; T = 0 is a no-op."""
+    fake = C.c_void_p(1 << 20)
+    w = moe.MoeWeights()
+    w.w_router = fake
+    d = _desc(T=16)
+    n = moe.moe_workspace_size(d)
+    L = moe.lib()
+    assert L.moe_router_losses(C.byref(d), C.byref(w), fake, None, 0.01, 0.001, fake, fake, n,
+                               None) == -1
+    assert L.moe_router_losses(C.byref(d), C.byref(w), fake, fake, 0.01, 0.001, None, fake, n,
+                               None) == -1
+    assert L.moe_router_losses(C.byref(d), C.byref(moe.MoeWeights()), fake, fake, 0.01, 0.001,
+                               fake, fake, n, None) == -1
+    assert L.moe_router_losses(C.byref(d), C.byref(w), fake, fake, float("nan"), 0.001, fake,
+                               fake, n, None) == -3
+    assert L.moe_router_losses(C.byref(d), C.byref(w), fake, fake, 0.01, float("inf"), fake,
+                               fake, n, None) == -3
+    assert L.moe_router_losses(C.byref(d), C.byref(w), fake, fake, 0.01, 0.001, fake, fake,
+                               n - 1, None) == -4
+    d0 = _desc(T=0)
+    assert L.moe_router_losses(C.byref(d0), C.byref(w), None, fake, 0.01, 0.001, fake, fake,
+                               moe.moe_workspace_size(d0), None) == 0

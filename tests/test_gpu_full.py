@@ -32,6 +32,16 @@ def test_full_size_workload(name):
     if name == "medium":
         counts = np.bincount(o_idx.ravel(), minlength=w.E)
         assert (counts == 0).sum() == moe_synth.ZIPF_EMPTY
+        say("  medium: router losses (skewed loads)")
+        c = torch.tensor(counts, dtype=torch.int32, device="cuda")
+        losses = torch.empty(2, dtype=torch.float32, device="cuda")
+        moe.moe_router_losses(layer.desc, layer.weights, layer.dev["x"], c, 0.01, 0.001, losses,
+                              layer.ws)
+        torch.cuda.synchronize()
+        got = losses.cpu().numpy().astype(np.float64)
+        want = np.array(orc.router_losses(counts, 0.01, 0.001))
+        say(f"  medium: losses {got} oracle {want}")
+        assert np.all(np.abs(got - want) <= 1e-5 * np.abs(want))
     if name == "latent":  # QuantileBalancer update over all tokens
         say("  latent: quantile balance")
         nb = torch.empty(w.E, dtype=torch.float32, device="cuda")

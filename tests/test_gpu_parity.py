@@ -368,3 +368,59 @@ def test_quantile_balance_in_place_replaces_the_buffer():
     a2 = dict(a)
     a2["bias"] = layer.dev["bias"].cpu().numpy()
     check_route(w, a2, layer)
+
+
+# ---------------------------------------------------------------- router losses
+LOSS_RTOL = 1e-5  # fp32 logits and per-token softmax vs fp64
+
+
+def _router_losses_gpu(layer, counts, alpha, z_weight):
+    losses = torch.full((2,), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_router_losses(layer.desc, layer.weights, layer.dev["x"], counts, alpha, z_weight,
+                          losses, layer.ws)
+    torch.cuda.synchronize()
+    return losses.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "sigmoid", "e1024", "k16", "many_chunks",
+                                  "split_router"])
+def test_router_losses_match_oracle(name):
+    """Switch load-balancing loss (moe-from-scratch page) and router z-loss
+    (transformer book page) on the loads the forward returned, against the
+    oracle on the same loads; split_router has few tokens and a wide model,
+    so the router GEMM splits its reduction."""
+    extra = {"split_router": dict(T=100, d=2048, d_ff=16, E=64, K=8, act="bf16",
+                                  router_std=0.02, w_std=0.02)}
+    if name in ("tiny", "small"):
+        w = moe_synth.get(name)
+    else:
+        w = custom(name, config_no=700 + len(name), **(EDGE.get(name) or extra[name]))
+    say(f"case router_losses {name} T={w.T} d={w.d} E={w.E} K={w.K} act={w.act}")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    layer.forward(layer.dev["x"], counts=counts)
+    got = _router_losses_gpu(layer, counts, 0.01, 0.001)
+    want = np.array(oracle.Oracle(w, a).router_losses(counts.cpu().numpy(), 0.01, 0.001))
+    rel = np.abs(got - want) / np.abs(want)
+    say(f"  losses gpu {got} oracle {want} rel {rel}")
+    assert np.all(rel <= LOSS_RTOL)
+
+
+def test_router_losses_uniform_router_and_determinism():
+    """Zero router weights: every softmax is uniform, so with equal loads
+    the Switch loss is alpha exactly and the z-loss z_weight (log E)^2; two
+    calls give the same bits; T = 0 leaves the output untouched."""
+    w = custom("loss_uniform", T=256, E=8, K=2, act="bf16", router_std=0.0, bias_std=0.0)
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    counts = torch.full((w.E,), w.T * w.K // w.E, dtype=torch.int32, device="cuda")
+    got = _router_losses_gpu(layer, counts, 0.01, 0.001)
+    assert abs(got[0] - 0.01) <= 1e-7
+    assert abs(got[1] - 0.001 * np.log(w.E) ** 2) <= 1e-8
+    assert np.array_equal(got, _router_losses_gpu(layer, counts, 0.01, 0.001))
+    d0 = moe.make_desc(w.with_T(0))
+    keep = torch.full((2,), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_router_losses(d0, layer.weights, layer.dev["x"], counts, 0.01, 0.001, keep, layer.ws)
+    torch.cuda.synchronize()
+    assert keep.tolist() == [7.0, 7.0]
