@@ -91,13 +91,6 @@ int check_desc(const moe_desc *d) {
   return MOE_OK;
 }
 
-#ifndef MOE_GROUPED_BIG
-#define MOE_GROUPED_BIG TILE_LARGE
-#endif
-#ifndef MOE_GROUPED_V2
-#define MOE_GROUPED_V2 TILE2_256x256_TALLW
-#endif
-
 // Kernel and tile shape of each grouped expert GEMM. Each has its own m-tile
 // table unless the two tile heights agree.
 struct GemmPlan {
@@ -109,24 +102,21 @@ struct Plan {
   bool shared_table() const { return gu.bm() == dn.bm(); }
 };
 
-// Largest tile that still gives the chip ~200+ (pipelined) or 256+ (generic)
-// workgroups; m-tiles counted as rows/bm plus one partial tile per expert.
+// The pipelined kernel when it applies (bf16, K a multiple of 32, 32-bit
+// operand extents, more than ~32 rows per expert); else the generic kernel:
+// 16-row tiles for few rows per expert, 128x128 otherwise (128x64 for bf16
+// down projections that would give fewer than 256 workgroups).
 // (a_rows: rows the GEMM's A operand spans; the pipelined kernel addresses
 // A and each expert's B with 32-bit offsets.)
 GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, int bf,
                   int64_t a_rows) {
-  auto mtiles = [&](int bm) { return rows / bm + (rows < E ? rows : E); };
   if (rows <= 32 * E) return {0, TILE_SMALL_M};  // ~32 rows per expert or fewer
   constexpr int64_t kLim = int64_t(1) << 32;
   const bool small_extent = a_rows * K * 2 < kLim && (n_out + 256) * K * 2 < kLim;
-  if (bf && K % 64 == 0 && n_out % 8 == 0 && small_extent) {
-    const int64_t nout = glu ? 128 : 256;
-    if (mtiles(gemm2_bm(MOE_GROUPED_V2)) * ((n_out + nout - 1) / nout) >= gemm2_min_tiles())
-      return {1, MOE_GROUPED_V2};
-  }
-  const int64_t mt = mtiles(tile_bm(MOE_GROUPED_BIG));
-  if (!bf || glu || mt * tile_count(MOE_GROUPED_BIG, 1, n_out, glu) >= 256)
-    return {0, MOE_GROUPED_BIG};
+  if (bf && K % 32 == 0 && n_out % 8 == 0 && small_extent)
+    return {1, gemm2_pick(rows, E, K, n_out, glu)};
+  const int64_t mt = rows / tile_bm(TILE_LARGE) + (rows < E ? rows : E);
+  if (!bf || glu || mt * tile_count(TILE_LARGE, 1, n_out, glu) >= 256) return {0, TILE_LARGE};
   return {0, TILE_TALL_N64};  // few down tiles (narrow model, few experts)
 }
 

@@ -14,20 +14,22 @@
 // a load lands at byte 16 i of a 1 KB block of 8 rows, and the eight 16-byte
 // chunks of a row are XOR-swizzled by row & 7 (so the fragment reads of 8
 // consecutive rows hit distinct banks); each lane therefore fetches the
-// logical chunk its slot holds. A has two stage buffers and B three, so the
-// streamed weights are requested two stages ahead and the activations one.
+// logical chunk its slot holds. A has NA stage buffers and B NA + 1, so the
+// streamed weights are requested NA stages ahead and the activations NA - 1
+// (NA = 2 for the 256x256 tiles, which fill the LDS; up to 4 for smaller
+// tiles, whose short K loops are bound by load latency rather than MFMAs).
 // Offsets are 32-bit against per-operand buffer resources (extents below
 // 4 GiB are a launch precondition); B rows past N lie past the resource's
 // extent and read as zeros; A rows past the tile's end repeat its first row
 // (their results are never stored).
 //
-// Main loop, per stage s (A buffer s % 2, B buffer s % 3), fragments in two
+// Main loop, per stage s (A buffer s % NA, B buffer s % (NA + 1)), fragments in two
 // register sets (set 0: k-step 0, set 1: k-step 1):
 //   M0: MFMAs of set 0, interleaved row by row with the LDS reads of set 1;
-//   wait until stage s + 1 has landed (B of s + 2 may still be in flight),
+//   wait until stage s + 1 has landed (later stages may still be in flight),
 //       lgkmcnt 0, barrier: stage s + 1 is visible and stage s's buffers
 //       are free;
-//   M1: MFMAs of set 1, interleaved with the loads of A(s + 2) and B(s + 3)
+//   M1: MFMAs of set 1, interleaved with the loads of A(s + NA) and B(s + NA + 1)
 //       into the freed buffers and the reads of stage s + 1's k-step 0.
 // Each MFMA group's operands were requested half a stage earlier. Loads past
 // the last stage repeat it (their buffers are never read), so every stage
@@ -38,7 +40,8 @@
 // time and writes the output with 16-byte stores along rows; the combine
 // epilogue adds the token's K routed rows with 16-byte loads.
 //
-// K (and K2) must be multiples of 64; the host uses gemm.hip otherwise.
+// K must be a multiple of 32 (the first of two K segments, of 64); the host
+// uses gemm.hip otherwise.
 #include "common.h"
 #include "kernels.h"
 
@@ -52,10 +55,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define MOE_G2_GM 4
 #endif
 
-// two A and three B stage buffers of the largest tile (256 rows x 128 bytes)
+// bytes of one operand row per stage (64 bf16)
 constexpr int kRowBytes = 128;
-constexpr int kLdsBytes = (2 * 256 + 3 * 256) * kRowBytes;
-__shared__ __attribute__((aligned(1024))) u32x4 g2_lds[kLdsBytes / 16];
 
 // s_waitcnt with vmcnt = N (< 64), lgkmcnt = 0, expcnt untouched.
 template <int N>
@@ -91,8 +92,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t
                                            0x00020000);
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
+// LDS of one workgroup: NA A and NA + 1 B stage buffers, reused by the
+// epilogue's staging rows; 4-wavefront tiles of at most 80 KB let two
+// workgroups share a CU.
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
+struct G2Shape {
+  static constexpr int NW = WGM * WGN;
+  static constexpr int WTN = BN / WGN;
+  static constexpr bool GLU = EPI == EPI_SWIGLU;
+  static constexpr int OUTW = GLU ? WTN / 2 : WTN;  // output columns per wave
+  static constexpr int PITCH = OUTW + 4;            // floats per staged row
+  static constexpr int STAGE16 = (NA * BM + (NA + 1) * BN) * 8;
+  static constexpr int STG16 = NW * 16 * PITCH / 4;
+  static constexpr int LDS16 = STAGE16 > STG16 ? STAGE16 : STG16;
+  static constexpr int MIN_WAVES = (NW == 4 && LDS16 * 16 <= 80 * 1024) ? 2 : 1;
+};
+
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, (G2Shape<BM, BN, WGM, WGN, NA, EPI>::MIN_WAVES))
+void gemm2_kernel(GemmArgs p) {
+  using Sh = G2Shape<BM, BN, WGM, WGN, NA, EPI>;
+  constexpr int NB = NA + 1;  // B stage buffers
+  static_assert(NA >= 2, "at least double-buffered");
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -104,7 +125,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
   static_assert(BM % ROWS == 0 && BN % ROWS == 0, "whole loads per stage");
   static_assert(!GLU || (BN / 2) % ROWS == 0, "gate and up rows in separate loads");
   static_assert(!GLU || FN % 2 == 0, "paired gate/up fragments");
-  static_assert((2 * A16 + 3 * B16) * 16 <= kLdsBytes, "stage buffers fit");
+  static_assert(FM >= 1 && FN >= 1, "at least one fragment per wave");
+  __shared__ __attribute__((aligned(1024))) u32x4 g2_lds[Sh::LDS16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -177,9 +199,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
     bstep = static_cast<uint32_t>(ROWS * ldb * 2);
   };
 
-  const int steps1 = p.K / 64;
-  const int steps = steps1 + (p.a2 ? p.K2 / 64 : 0);
+  // a last K segment that ends 32 columns into a stage runs only that
+  // stage's first k-step (the other half of its buffers holds columns past
+  // the row: the next row's, or zeros past the operand's extent)
+  const int steps1 = (p.K + 63) / 64;
+  const int steps = steps1 + (p.a2 ? (p.K2 + 63) / 64 : 0);
   const int last = steps - 1;
+  const bool half_last = ((p.a2 ? p.K2 : p.K) & 63) != 0;
   auto kbytes = [&](int st) {
     return __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * kRowBytes);
   };
@@ -212,8 +238,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 *const abuf = g2_lds;            // A: 2 x A16
-  u32x4 *const bbuf = g2_lds + 2 * A16;  // B: 3 x B16
+  u32x4 *const abuf = g2_lds;             // A: NA x A16
+  u32x4 *const bbuf = g2_lds + NA * A16;  // B: NB x B16
   bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
   auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
     const int kc = 4 * ks + fc;
@@ -242,29 +268,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
   auto seg_b = [&](int st) {
     if (st == steps1) setup_b(1);
   };
+  // prologue: A(0..NA-1) and B(0..NB-1), interleaved in stage order
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j) load_a(abuf, 0, j);
+  for (int s0 = 0; s0 < NB; ++s0) {
+    const int sl = min(s0, last);
+    if (s0 < NA) {
+      seg_a(sl);
 #pragma unroll
-  for (int j = 0; j < B_LD; ++j) load_b(bbuf, 0, j);
-  seg_a(min(1, last));
-  seg_b(min(1, last));
+      for (int j = 0; j < A_LD; ++j) load_a(abuf + s0 * A16, sl, j);
+    }
+    seg_b(sl);
 #pragma unroll
-  for (int j = 0; j < A_LD; ++j) load_a(abuf + A16, min(1, last), j);
-#pragma unroll
-  for (int j = 0; j < B_LD; ++j) load_b(bbuf + B16, min(1, last), j);
-  seg_b(min(2, last));
-#pragma unroll
-  for (int j = 0; j < B_LD; ++j) load_b(bbuf + 2 * B16, min(2, last), j);
-  wait_vm_lgkm0<A_LD + 2 * B_LD>();  // stage 0 has landed
+    for (int j = 0; j < B_LD; ++j) load_b(bbuf + s0 * B16, sl, j);
+  }
+  wait_vm_lgkm0<(NA - 1) * A_LD + (NB - 1) * B_LD>();  // stage 0 has landed
   barrier();
 #pragma unroll
   for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
 
-  int b_cur = 0;  // st % 3
+  int a_cur = 0, b_cur = 0;  // st % NA, st % NB
   for (int st = 0; st < steps; ++st) {
-    const int a_cur = st & 1;
-    const int b_nxt = b_cur == 2 ? 0 : b_cur + 1;
-    u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + (a_cur ^ 1) * A16;
+    const int a_nxt = a_cur == NA - 1 ? 0 : a_cur + 1;
+    const int b_nxt = b_cur == NB - 1 ? 0 : b_cur + 1;
+    u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + a_nxt * A16;
     u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
     wait_lgkm0();  // set 0 has landed
 #pragma unroll
@@ -277,14 +303,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm_lgkm0<B_LD>();  // A and B of st + 1 have landed
+    // A and B of st + 1 have landed (the loads issued after them: the B
+    // half of A(st + 1)'s batch and NA - 2 full batches)
+    wait_vm_lgkm0<(NA - 2) * A_LD + (NB - 2) * B_LD>();
     barrier();
-    const int sa = min(st + 2, last), sb = min(st + 3, last);
-    if (st + 2 <= last) seg_a(sa);
-    if (st + 3 <= last) seg_b(sb);
+    const int sa = min(st + NA, last), sb = min(st + NB, last);
+    if (st + NA <= last) seg_a(sa);
+    if (st + NB <= last) seg_b(sb);
+    const int live1 = (half_last && st == last) ? 0 : live;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      if (fm < live) mrow(fm, xa1, xb1);
+      if (fm < live1) mrow(fm, xa1, xb1);
 #pragma unroll
       for (int q = 0; q < LD_PER; ++q) {
         const int j = fm * LD_PER + q;
@@ -298,6 +327,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    a_cur = a_nxt;
     b_cur = b_nxt;
   }
   wait_vm_lgkm0<0>();
@@ -305,10 +335,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
 
   // ------------------------------------------------------------ epilogue
   // each wave: 16 rows x OUTW columns of fp32 at a time in its own slice
-  constexpr int OUTW = GLU ? WTN / 2 : WTN;   // output columns per wave
+  constexpr int OUTW = Sh::OUTW;
   constexpr int FO = GLU ? FN / 2 : FN;
-  constexpr int PITCH = OUTW + 4;             // floats per staged row
-  static_assert(NW * 16 * PITCH * 4 <= kLdsBytes, "epilogue staging fits");
+  constexpr int PITCH = Sh::PITCH;
   float *stg = reinterpret_cast<float *>(g2_lds) + wave * 16 * PITCH;
   const int col0 = n_begin + (GLU ? wn * (WTN / 2) : wn * WTN);
   constexpr int ITEMS = 16 * OUTW / 8;        // (row, 8-column) items per 16 rows
@@ -372,7 +401,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm2_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
 hipError_t run2(const GemmArgs &a, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   const int64_t n_tn = (a.N + NOUT - 1) / NOUT;
@@ -382,18 +411,18 @@ hipError_t run2(const GemmArgs &a, hipStream_t s) {
   GemmArgs b = a;
   b.max_mtiles = max_m;
   const int64_t blocks = 8 * ((total + 7) / 8);
-  gemm2_kernel<BM, BN, WGM, WGN, EPI><<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b);
+  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI><<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int NA = 2>
 hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, EPI_SWIGLU>(a, s);
-    case EPI_SCALE: return run2<BM, BN, WGM, WGN, EPI_SCALE>(a, s);
-    case EPI_STORE: return run2<BM, BN, WGM, WGN, EPI_STORE>(a, s);
-    case EPI_COMBINE: return run2<BM, BN, WGM, WGN, EPI_COMBINE>(a, s);
-    case EPI_STORE_F32: return run2<BM, BN, WGM, WGN, EPI_STORE_F32>(a, s);
+    case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, NA, EPI_SWIGLU>(a, s);
+    case EPI_SCALE: return run2<BM, BN, WGM, WGN, NA, EPI_SCALE>(a, s);
+    case EPI_STORE: return run2<BM, BN, WGM, WGN, NA, EPI_STORE>(a, s);
+    case EPI_COMBINE: return run2<BM, BN, WGM, WGN, NA, EPI_COMBINE>(a, s);
+    case EPI_STORE_F32: return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -409,26 +438,56 @@ bool gemm2_applicable(const GemmArgs &a, int epi) {
   if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim || (a.N + 256LL) * a.ldb * 2 >= kLim)
     return false;
   if (a.a2 && (a.M * a.lda2 * 2 >= kLim || (a.N + 256LL) * a.ldb2 * 2 >= kLim)) return false;
-  if (a.K % 64 || (a.a2 && a.K2 % 64)) return false;
+  // K a multiple of 32 (64 for the first of two segments)
+  if (a.K % 32 || (a.a2 && (a.K % 64 || a.K2 % 32))) return false;
   if (a.N % 8) return false;
   if (epi == EPI_COMBINE && a.ldy % 8) return false;
   return a.ldo % 8 == 0;
 }
 
-int gemm2_bm(int cfg) { return cfg == TILE2_128x256 ? 128 : 256; }
+int gemm2_bm(int cfg) {
+  switch (cfg) {
+    case TILE2_128x256: case TILE2_128x128: case TILE2_128x64: case TILE2_128x128_D4:
+    case TILE2_128x128_W8D4: case TILE2_128x256_W8: return 128;
+    case TILE2_64x128: case TILE2_64x128_D4: return 64;
+  }
+  return 256;
+}
 
-#ifndef MOE_DENSE_V2
-#define MOE_DENSE_V2 TILE2_256x256_TALLW
-#endif
-#ifndef MOE_V2_MIN_TILES
-#define MOE_V2_MIN_TILES 200
-#endif
+int gemm2_bn(int cfg) {
+  switch (cfg) {
+    case TILE2_256x128: case TILE2_128x128: case TILE2_64x128: case TILE2_128x128_D4:
+    case TILE2_128x128_W8D4: case TILE2_256x128_W8D3: case TILE2_64x128_D4: return 128;
+    case TILE2_128x64: return 64;
+  }
+  return 256;
+}
 
-int64_t gemm2_min_tiles() { return MOE_V2_MIN_TILES; }
+// Tile of the pipelined kernel for an output of rows x n_out over a reduction
+// of K (grouped: `groups` experts, each of which may end in a partial m-tile;
+// dense: groups = 0). From sweeps of every tile on MI355X over the
+// benchmark layers: 256x256 wins whenever it gives each of the 256 CUs a
+// workgroup; below that, 128x128 with two workgroups per CU (their
+// prologues and epilogues overlap the other's K loop), or 256x128 for long
+// reductions; with fewer than 256 such tiles, the 8-wavefront 128x128 with a
+// deeper look-ahead, and 64x128 for the fewest.
+int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu) {
+  auto tiles = [&](int cfg) {
+    const int64_t bm = gemm2_bm(cfg), nout = glu ? gemm2_bn(cfg) / 2 : gemm2_bn(cfg);
+    const int64_t mt = groups ? rows / bm + (rows < groups ? rows : groups) : (rows + bm - 1) / bm;
+    return mt * ((n_out + nout - 1) / nout);
+  };
+  constexpr int64_t kCUs = 256;
+  if (tiles(TILE2_256x256_TALLW) >= kCUs) return TILE2_256x256_TALLW;
+  if (K >= 2048 && tiles(TILE2_256x128_W8D3) >= kCUs) return TILE2_256x128_W8D3;
+  if (tiles(TILE2_128x128) >= kCUs) return TILE2_128x128;
+  if (tiles(TILE2_128x128_W8D4) >= kCUs / 2) return TILE2_128x128_W8D4;
+  return TILE2_64x128;
+}
 
-// Dense GEMM: the pipelined kernel when it applies and its tile count fills
-// the chip; else the largest generic tile that still gives every CU a
-// workgroup (few rows: 16-row tiles, as wide as that allows).
+// Dense GEMM: the pipelined kernel when it applies (bf16, K a multiple of
+// 32, more than 64 rows); else the largest generic tile that still gives
+// every CU a workgroup (few rows: 16-row tiles, as wide as that allows).
 hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s) {
   const int glu = epi == EPI_SWIGLU;
   const int64_t ks = a.k_split > 1 ? a.k_split : 1;
@@ -437,11 +496,8 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
     const bool wide = ks * tile_count(TILE_SMALL_M, a.M, a.N, glu) >= kFill;
     return launch_gemm(a, epi, wide || !act_bf16 ? TILE_SMALL_M : TILE_SMALL_N64, act_bf16, s);
   }
-  if (act_bf16 && gemm2_applicable(a, epi)) {
-    const int64_t nout = glu ? 128 : 256;
-    const int64_t tiles = ((a.M + 255) / 256) * ((a.N + nout - 1) / nout);
-    if (tiles >= MOE_V2_MIN_TILES) return launch_gemm2(a, epi, MOE_DENSE_V2, s);
-  }
+  if (act_bf16 && gemm2_applicable(a, epi))
+    return launch_gemm2(a, epi, gemm2_pick(a.M, 0, a.K + (a.a2 ? a.K2 : 0), a.N, glu), s);
   if (!act_bf16) return launch_gemm(a, epi, TILE_LARGE, act_bf16, s);
   for (int cfg : {TILE_LARGE, TILE_TALL_N64, TILE_MID})
     if (ks * tile_count(cfg, a.M, a.N, glu) >= kFill) return launch_gemm(a, epi, cfg, act_bf16, s);
@@ -455,6 +511,14 @@ hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s) {
     case TILE2_256x256_W4: return dispatch2<256, 256, 2, 2>(a, epi, s);
     case TILE2_256x128: return dispatch2<256, 128, 2, 2>(a, epi, s);
     case TILE2_128x256: return dispatch2<128, 256, 2, 2>(a, epi, s);
+    case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, epi, s);
+    case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, epi, s);
+    case TILE2_128x64: return dispatch2<128, 64, 2, 2>(a, epi, s);
+    case TILE2_128x128_D4: return dispatch2<128, 128, 2, 2, 4>(a, epi, s);
+    case TILE2_128x128_W8D4: return dispatch2<128, 128, 4, 2, 4>(a, epi, s);
+    case TILE2_256x128_W8D3: return dispatch2<256, 128, 4, 2, 3>(a, epi, s);
+    case TILE2_128x256_W8: return dispatch2<128, 256, 2, 4>(a, epi, s);
+    case TILE2_64x128_D4: return dispatch2<64, 128, 2, 2, 4>(a, epi, s);
   }
   return hipErrorInvalidValue;
 }

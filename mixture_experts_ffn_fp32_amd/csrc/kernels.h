@@ -151,17 +151,25 @@ int64_t tile_count(int cfg, int64_t rows, int64_t n_out, int glu);
 int tile_bm(int cfg);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
 
-// Pipelined bf16 GEMM (gemm2.hip): large tiles, direct-to-LDS loads.
+// Pipelined bf16 GEMM (gemm2.hip): direct-to-LDS loads.
 // (256x256: 8 wavefronts as 2 x 4 of 128x64 blocks; _TALLW: 4 x 2 of 64x128;
-// _W4 and the others: 4 wavefronts, 2 x 2)
+// _W4 and the others: 4 wavefronts, 2 x 2;
+// 128x128, 64x128 and 128x64 run 4 wavefronts (2 x 2) in at most 80 KB of LDS,
+// so two workgroups can share a CU.)
 enum Tile2Cfg {
   TILE2_256x256 = 0, TILE2_256x128 = 1, TILE2_128x256 = 2, TILE2_256x256_W4 = 3,
-  TILE2_256x256_TALLW = 4
+  TILE2_256x256_TALLW = 4, TILE2_128x128 = 5, TILE2_64x128 = 6, TILE2_128x64 = 7,
+  // deeper look-ahead (A NA stages ahead, B NA + 1) for tiles that leave LDS room:
+  TILE2_128x128_D4 = 8, TILE2_128x128_W8D4 = 9, TILE2_256x128_W8D3 = 10, TILE2_128x256_W8 = 11,
+  TILE2_64x128_D4 = 12
 };
 bool gemm2_applicable(const GemmArgs &a, int epi);
 int gemm2_bm(int cfg);
+int gemm2_bn(int cfg);  // B rows per tile (output columns, or gate + up halves)
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s);
-int64_t gemm2_min_tiles();
+// Pipelined tile for rows x n_out over K (grouped over `groups` experts, or
+// dense with groups = 0).
+int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu);
 // Dense GEMM with the kernel and tile shape chosen from the problem size.
 hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s);
 

@@ -6,8 +6,8 @@ import pytest
 import mixture_experts_ffn_fp32_amd as moe
 import moe_synth
 import oracle
-from _gpu import (TOL, check_forward, check_route, dev_of, f64, layer_of, need_gpu, say,
-                  torch)
+from _gpu import (TOL, check_forward, check_route, dev_of, f64, layer_of, need_gpu,
+                  sample_tokens, say, torch)
 from _layers import custom, max_abs_rel
 
 pytestmark = pytest.mark.gpu
@@ -54,6 +54,32 @@ def test_workload_route_and_forward(name):
     if name == "tiny":
         # moe-from-scratch's allclose check of sorted dispatch vs the naive loop
         assert np.max(np.abs(got - ref)) <= 1e-5
+
+
+# Pipelined-GEMM shapes: reductions ending 32 columns into a 64-column stage
+# (d or d_ff = 32 mod 64), at sizes that pick each tile shape: few tiles
+# (64x128 / 8-wavefront 128x128), 128x128 two per CU, 256x256.
+TAIL = {
+    "tail_few": (dict(T=300, d=96, d_ff=160, E=4, K=2, act="bf16", n_shared=1, d_ff_shared=160,
+                      w_std=0.05, router_std=0.05), None),
+    "tail_mid": (dict(T=4096, d=480, d_ff=800, E=4, K=2, act="bf16", n_shared=1,
+                      d_ff_shared=800, w_std=0.03, router_std=0.03), 512),
+    "tail_big": (dict(T=8192, d=480, d_ff=1056, E=4, K=2, act="bf16", n_shared=1,
+                      d_ff_shared=1056, w_std=0.03, router_std=0.03), 384),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TAIL))
+def test_pipelined_gemm_k_tail(name):
+    kw, n = TAIL[name]
+    w = custom(name=name, config_no=600 + sorted(TAIL).index(name), **kw)
+    say(f"case k-tail {name} T={w.T} d={w.d} d_ff={w.d_ff}")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    orc = oracle.Oracle(w, a)
+    r = check_route(w, a, layer, orc)
+    toks = None if n is None else sample_tokens(r[0], w.E, n, seed=w.config_no)
+    check_forward(w, a, layer, tokens=toks, orc=orc, o_route=r)
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
