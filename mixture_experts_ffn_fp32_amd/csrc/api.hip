@@ -282,6 +282,16 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
   return MOE_OK;
 }
 
+// Counting-sort dispatch: one workgroup for few slots and experts, else
+// histogram, scan and scatter launches.
+hipError_t run_dispatch(const ScanArgs &sa, const ScatterArgs &sc, hipStream_t s) {
+  if (dispatch_fused_ok(sa.slots, sa.E)) return launch_dispatch_fused(sa, sc, s);
+  hipError_t e = launch_hist(sc.idx, sa.slots, sa.E, const_cast<int32_t *>(sa.chunk_hist), s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_scan(sa, s)) != hipSuccess) return e;
+  return launch_scatter(sc, s);
+}
+
 int check_expert_weights(const moe_desc *d, const moe_weights *w) {
   if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
   return MOE_OK;
@@ -432,7 +442,6 @@ int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const vo
   char *wsb = static_cast<char *>(ws);
   const int64_t slots = d->T * d->top_k;
   int32_t *chunk = reinterpret_cast<int32_t *>(wsb + L.chunk);
-  MOE_TRY(launch_hist(idx, slots, d->n_experts, chunk, s));
   ScanArgs sa{};
   sa.chunk_hist = chunk;
   sa.chunk_base = chunk;
@@ -440,7 +449,6 @@ int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const vo
   sa.E = d->n_experts;
   sa.counts = counts;
   sa.offsets = offsets;
-  MOE_TRY(launch_scan(sa, s));
   ScatterArgs sc{};
   sc.idx = idx;
   sc.g = g;
@@ -452,7 +460,7 @@ int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const vo
   sc.sorted_token = sorted_token;
   sc.inv = inv;
   sc.sorted_w = sorted_w;
-  MOE_TRY(launch_scatter(sc, s));
+  MOE_TRY(run_dispatch(sa, sc, s));
   if (rows_sorted) {
     const int64_t de = d->latent ? d->latent : d->d_model;
     const int64_t es = d->act_dtype == MOE_BF16 ? 2 : 4;
@@ -560,7 +568,6 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
 
   // 2. dispatch (counts, offsets, tile table, stable positions)
   pr.begin(MOE_STAGE_DISPATCH);
-  MOE_TRY(launch_hist(idx, rows, static_cast<int>(E), chunk, s));
   ScanArgs sa{};
   sa.chunk_hist = chunk;
   sa.chunk_base = chunk;
@@ -580,7 +587,6 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   sa.T = T;
   sa.tie_eps = kTieEps;
   sa.n_near_ties = n_near_ties;
-  MOE_TRY(launch_scan(sa, s));
   ScatterArgs sc{};
   sc.idx = idx;
   sc.g = g;
@@ -592,7 +598,7 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   sc.sorted_token = stok;
   sc.inv = inv;
   sc.sorted_w = sw;
-  MOE_TRY(launch_scatter(sc, s));
+  MOE_TRY(run_dispatch(sa, sc, s));
   pr.end(MOE_STAGE_DISPATCH);
   if (T == 0) return MOE_OK;
 

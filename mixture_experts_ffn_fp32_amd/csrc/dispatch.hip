@@ -4,7 +4,8 @@
 // permutation, not token duplication in model state": the flattened expert
 // ids are sorted stably, sorted_token = order / K, counts by bincount and
 // cumulative ends mark each expert's slice. Here the sort is a counting
-// sort in three launches, with no host round trip:
+// sort, with no host round trip: for up to 16384 slots and 256 experts one
+// workgroup does it all (dispatch_fused_kernel); otherwise three launches:
 //   hist    - per chunk of 4096 slots, an LDS histogram of expert ids;
 //   scan    - one workgroup: counts, exclusive offsets, the absolute base of
 //             every (chunk, expert) pair, the grouped-GEMM m-tile table and
@@ -21,6 +22,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxE = 1024;
+constexpr int kFusedMaxE = 256;  // experts of the one-workgroup dispatch
 
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ idx, int64_t slots,
                                                    int E, int32_t *__restrict__ chunk_hist) {
@@ -164,6 +166,94 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   }
 }
 
+// The whole dispatch in one workgroup of 1024 threads, for few slots and
+// experts (a launch per step costs more than the work there): LDS histogram,
+// scan (counts, offsets, m-tile tables, near-tie count as scan_kernel), then
+// rounds of 1024 slots in slot order: a slot's position is its expert's
+// running base + the slots of that expert in earlier wavefronts of the round
+// (per-wavefront peer counts in LDS) + its rank among its wavefront's peers.
+__global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, ScatterArgs sc) {
+  __shared__ int tmp[1024];
+  __shared__ int run[kMaxE + 1];
+  __shared__ int off[kMaxE + 1];
+  __shared__ int start[kMaxE + 1];
+  __shared__ int wcnt[16][kFusedMaxE];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int E = a.E;
+  for (int e = t; e < E; e += 1024) run[e] = 0;
+  __syncthreads();
+  for (int64_t s = t; s < a.slots; s += 1024) {
+    const int e = sc.idx[s];
+    if (e >= 0 && e < E) atomicAdd(&run[e], 1);
+  }
+  __syncthreads();
+  const int cnt_t = t < E ? run[t] : 0;
+  int total;
+  const int ex = block_exscan_1024(cnt_t, tmp, &total);
+  if (t < E) {
+    off[t] = ex;
+    run[t] = ex;
+    a.counts[t] = cnt_t;
+    a.offsets[t] = ex;
+  }
+  if (t == 0) {
+    off[E] = total;
+    a.offsets[E] = total;
+  }
+  __syncthreads();
+  if (a.tiles) build_tiles(off, E, a.bm, start, tmp, a.tiles, a.n_tiles);
+  __syncthreads();
+  if (a.tiles2) build_tiles(off, E, a.bm2, start, tmp, a.tiles2, a.n_tiles2);
+  __syncthreads();
+  if (a.gap && a.n_near_ties) {
+    int n = 0;
+    for (int64_t i = t; i < a.T; i += 1024) n += (a.gap[i] < a.tie_eps) ? 1 : 0;
+    int tot;
+    block_exscan_1024(n, tmp, &tot);
+    if (t == 0) *a.n_near_ties = tot;
+  }
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t r0 = 0; r0 < a.slots; r0 += 1024) {
+    const int64_t s = r0 + t;
+    const int e = s < a.slots ? sc.idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t peers = ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    const int cnt = __popcll(peers);
+    for (int i = lane; i < E; i += 64) wcnt[wave][i] = 0;  // this wave's row (in order)
+    if (valid && rank == cnt - 1) wcnt[wave][e] = cnt;
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+      pos = run[e] + pre + rank;
+    }
+    __syncthreads();  // every read of run[] and wcnt[] of this round is done
+    if (t < E) {
+      int add = 0;
+      for (int w = 0; w < 16; ++w) add += wcnt[w][t];
+      run[t] += add;
+    }
+    if (valid) {
+      sc.perm[pos] = static_cast<int32_t>(s);
+      sc.sorted_token[pos] = static_cast<int32_t>(s / sc.K);
+      sc.inv[s] = pos;
+      if (sc.sorted_w) sc.sorted_w[pos] = sc.g[s];
+    } else if (s < a.slots) {
+      sc.inv[s] = -1;
+    }
+    __syncthreads();  // run[] updated before the next round reads it
+  }
+}
+
 // One wavefront per sorted row: out[p, :] = rows[sorted_token[p], :].
 __global__ __launch_bounds__(256) void gather_kernel(const uint4 *__restrict__ rows,
                                                      const int32_t *__restrict__ sorted_token,
@@ -194,6 +284,16 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
 hipError_t launch_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles,
                         hipStream_t s) {
   tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, bm, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+bool dispatch_fused_ok(int64_t slots, int E) {
+  return slots <= kFusedMaxSlots && E <= kFusedMaxE;
+}
+
+hipError_t launch_dispatch_fused(const ScanArgs &a, const ScatterArgs &sc, hipStream_t s) {
+  if (!dispatch_fused_ok(a.slots, a.E)) return hipErrorInvalidValue;
+  dispatch_fused_kernel<<<1, 1024, 0, s>>>(a, sc);
   return hipGetLastError();
 }
 

@@ -98,6 +98,12 @@ struct ScatterArgs {
 };
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
 
+// Histogram, scan and scatter in one workgroup (same outputs as the three
+// launches; chunk_hist / chunk_base unused) when dispatch_fused_ok().
+constexpr int64_t kFusedMaxSlots = 16384;
+bool dispatch_fused_ok(int64_t slots, int E);
+hipError_t launch_dispatch_fused(const ScanArgs &a, const ScatterArgs &sc, hipStream_t s);
+
 hipError_t launch_gather(const void *rows, const int32_t *sorted_token, int64_t n_rows,
                          int64_t row_bytes, void *out, hipStream_t s);
 

@@ -33,6 +33,9 @@ namespace {
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 1024;
 constexpr int kPerLane = kMaxE / 64;
+// one-wavefront-per-token router: at most 64 experts and this model width
+constexpr int kValuMaxE = 64;
+constexpr int kValuMaxD = 2048;
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
@@ -70,33 +73,26 @@ __global__ __launch_bounds__(256) void split_kernel(const float *__restrict__ w,
   }
 }
 
-// One wavefront per token over the partial logits [splits][T, parts * E]:
-// the K-split partials of each plane are summed in split order, then the
-// planes high + mid + low.
-__global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, int splits,
-                                                     int64_t split_stride) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int lane = threadIdx.x & 63;
+// Selection of token t by one wavefront from its logits: lane l holds the
+// logits of experts l + 64 j (j < PL, PL * 64 >= E) in raw[j]. Writes idx, g
+// and the optional gap / top scores.
+template <int PL>
+__device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int lane,
+                                            const float (&raw)[PL]) {
   const int E = a.E, K = a.K;
   const int nsel = K + 1 <= E ? K + 1 : E;
   const bool sig = a.mode == 2;
-  const float *lg = a.logits + t * static_cast<int64_t>(parts) * E;
-
-  float raw[kPerLane];  // logit x W^T per owned expert
-  float v[kPerLane];    // ranking score
+  float v[PL];  // ranking score
   float vmax = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
+  for (int j = 0; j < PL; ++j) {
     const int e = lane + 64 * j;
-    float sc = -INFINITY, l = 0.f;
+    float sc = -INFINITY;
     if (e < E) {
-      l = logit_of(lg, e, E, parts, splits, split_stride);
       const float b = a.bias ? a.bias[e] : 0.f;
-      sc = sig ? sigmoidf_(l) + b : l + b;
+      sc = sig ? sigmoidf_(raw[j]) + b : raw[j] + b;
       vmax = fmaxf(vmax, sc);
     }
-    raw[j] = l;
     v[j] = sc;
   }
   // the softmax-first rule reports probabilities: all-expert normaliser
@@ -106,7 +102,7 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
     for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
     zall = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
+    for (int j = 0; j < PL; ++j)
       if (lane + 64 * j < E) zall += expf(v[j] - vmax);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) zall += __shfl_xor(zall, off);
@@ -123,7 +119,7 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
       float bv = -INFINITY, br = 0.f;
       int bi = 0x7FFFFFFF;
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j)
+      for (int j = 0; j < PL; ++j)
         if (v[j] > bv) {  // ids ascend within a lane: ties keep the lower id
           bv = v[j];
           br = raw[j];
@@ -144,7 +140,7 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
       sraw[r] = br;
       si[r] = bi;
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j)
+      for (int j = 0; j < PL; ++j)
         if (lane + 64 * j == bi) v[j] = -INFINITY;
     }
   }
@@ -196,6 +192,83 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
 #pragma unroll
     for (int r = 0; r <= kMaxK; ++r)
       if (r <= K) a.top[t * (K + 1) + r] = r < nsel ? rs[r] : -INFINITY;
+  }
+}
+
+// One wavefront per token over the partial logits [splits][T, parts * E]:
+// the K-split partials of each plane are summed in split order, then the
+// planes high + mid + low.
+template <int PL>
+__global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, int splits,
+                                                     int64_t split_stride) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  const float *lg = a.logits + t * static_cast<int64_t>(parts) * a.E;
+  float raw[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int e = lane + 64 * j;
+    raw[j] = e < a.E ? logit_of(lg, e, a.E, parts, splits, split_stride) : 0.f;
+  }
+  select_from<PL>(a, t, lane, raw);
+}
+
+// Router for few experts and a narrow model, one wavefront per token: lane l
+// holds elements [512 c + 8 l, 512 c + 8 l + 8) of x for every 512-column
+// chunk c; per expert its fp32 partial dot product (fused multiply-adds in
+// column order) is summed over the 64 lanes by a fixed xor butterfly, so
+// every lane holds the logit; the logits go to a.logits [T, E] (one plane,
+// one split) and, if `select`, straight into the selection.
+template <typename T>
+__global__ __launch_bounds__(256) void router_valu_kernel(RouterArgs a, int select) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int kMaxChunks = kValuMaxD / 512;
+  float xv[kMaxChunks][8];
+  const int chunks = (a.d + 511) / 512;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int i0 = 512 * c + 8 * lane;  // d is a multiple of 8: a lane's 8 are all in or out
+    const bool in = c < chunks && i0 < a.d;
+#pragma unroll
+    for (int h = 0; h < 8 / Chunk<T>::N; ++h) {
+      uint4 raw4 = make_uint4(0u, 0u, 0u, 0u);
+      if (in)
+        raw4 = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.x) +
+                                                (t * a.d + i0) * sizeof(T) + 16 * h);
+      Chunk<T>::unpack(raw4, &xv[c][h * Chunk<T>::N]);
+    }
+  }
+  float raw = 0.f;  // logit of expert `lane`
+  for (int e = 0; e < a.E; ++e) {
+    const float *w = a.w + static_cast<int64_t>(e) * a.d;
+    float p = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const int i0 = 512 * c + 8 * lane;
+      if (c < chunks && i0 < a.d) {
+        const float4 w0 = *reinterpret_cast<const float4 *>(w + i0);
+        const float4 w1 = *reinterpret_cast<const float4 *>(w + i0 + 4);
+        p = fmaf(xv[c][0], w0.x, p);
+        p = fmaf(xv[c][1], w0.y, p);
+        p = fmaf(xv[c][2], w0.z, p);
+        p = fmaf(xv[c][3], w0.w, p);
+        p = fmaf(xv[c][4], w1.x, p);
+        p = fmaf(xv[c][5], w1.y, p);
+        p = fmaf(xv[c][6], w1.z, p);
+        p = fmaf(xv[c][7], w1.w, p);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+    if (lane == e) raw = p;
+  }
+  if (lane < a.E) a.logits[t * a.E + lane] = raw;
+  if (select) {
+    const float r1[1] = {raw};
+    select_from<1>(a, t, lane, r1);
   }
 }
 
@@ -385,9 +458,37 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const float *part, int6
 
 }  // namespace
 
-// Router GEMM only: partial logits [splits][T, parts * E] into a.logits.
+// Few experts, a narrow model and little work: the one-wavefront-per-token
+// router (no weight split, no GEMM launch); else the matrix-core GEMM.
+bool router_valu(const RouterArgs &a) {
+  return a.E <= kValuMaxE && a.d <= kValuMaxD &&
+         a.T * static_cast<int64_t>(a.E) * a.d <= (int64_t(1) << 26);
+}
+
+// Layout of the logits the router pass leaves in a.logits: planes x splits.
+void logit_layout(const RouterArgs &a, int act_bf16, int *parts, int *splits) {
+  if (router_valu(a)) {
+    *parts = 1;
+    *splits = 1;
+  } else {
+    *parts = act_bf16 ? 3 : 1;
+    *splits = router_splits(a.T, a.d);
+  }
+}
+
+hipError_t launch_router_valu(const RouterArgs &a, int act_bf16, int select, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((a.T + 3) / 4);
+  if (act_bf16)
+    router_valu_kernel<bf16_t><<<blocks, 256, 0, s>>>(a, select);
+  else
+    router_valu_kernel<float><<<blocks, 256, 0, s>>>(a, select);
+  return hipGetLastError();
+}
+
+// Router logits only, in the layout logit_layout() reports.
 hipError_t launch_router_logits(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (router_valu(a)) return launch_router_valu(a, act_bf16, 0, s);
   const int64_t nw = static_cast<int64_t>(a.E) * a.d;
   GemmArgs g{};
   g.a = a.x;
@@ -418,12 +519,19 @@ hipError_t launch_router_logits(const RouterArgs &a, int act_bf16, hipStream_t s
 
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (router_valu(a)) return launch_router_valu(a, act_bf16, 1, s);
   hipError_t e = launch_router_logits(a, act_bf16, s);
   if (e != hipSuccess) return e;
-  const int parts = act_bf16 ? 3 : 1;
-  const int splits = router_splits(a.T, a.d);
-  select_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(a, parts, splits,
-                                                                      a.T * parts * a.E);
+  int parts, splits;
+  logit_layout(a, act_bf16, &parts, &splits);
+  const unsigned blocks = static_cast<unsigned>((a.T + 3) / 4);
+  const int64_t ss = a.T * parts * a.E;
+  if (a.E <= 64)
+    select_kernel<1><<<blocks, 256, 0, s>>>(a, parts, splits, ss);
+  else if (a.E <= 256)
+    select_kernel<4><<<blocks, 256, 0, s>>>(a, parts, splits, ss);
+  else
+    select_kernel<kPerLane><<<blocks, 256, 0, s>>>(a, parts, splits, ss);
   return hipGetLastError();
 }
 
@@ -435,8 +543,8 @@ hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t
   if (a.T == 0) return hipSuccess;
   hipError_t e = launch_router_logits(a, act_bf16, s);
   if (e != hipSuccess) return e;
-  const int parts = act_bf16 ? 3 : 1;
-  const int splits = router_splits(a.T, a.d);
+  int parts, splits;
+  logit_layout(a, act_bf16, &parts, &splits);
   const int64_t chunks = router_loss_chunks(a.T);
   loss_partial_kernel<<<static_cast<unsigned>(chunks), 256, 0, s>>>(
       a.logits, parts, splits, a.T * parts * a.E, a.T, a.E, part);
@@ -451,8 +559,8 @@ hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *dif
   if (a.T == 0 || !a.top) return hipErrorInvalidValue;
   hipError_t e = launch_router(a, act_bf16, s);
   if (e != hipSuccess) return e;
-  const int parts = act_bf16 ? 3 : 1;
-  const int splits = router_splits(a.T, a.d);
+  int parts, splits;
+  logit_layout(a, act_bf16, &parts, &splits);
   const int64_t ss = a.T * parts * a.E;
   dim3 grid(static_cast<unsigned>((a.T + 63) / 64), static_cast<unsigned>((a.E + 63) / 64));
   qb_diff_kernel<<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.top, a.T, a.E, a.K, diff);

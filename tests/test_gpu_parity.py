@@ -34,6 +34,9 @@ EDGE = {
     "many_chunks": dict(T=1537, d=32, d_ff=24, E=16, K=8, act="bf16"),
     "wide_bf16": dict(T=200, d=256, d_ff=520, E=8, K=2, act="bf16", w_std=0.05,
                       router_std=0.05),
+    # few experts but a model too wide for the wavefront-per-token router
+    "mfma_router": dict(T=1100, d=2560, d_ff=64, E=16, K=2, act="bf16", w_std=0.02,
+                        router_std=0.02),
 }
 
 
@@ -151,7 +154,7 @@ def test_tiny_token_counts(T):
 DISPATCH_CASES = [
     # (T, K, E) ; the page's example first
     (3, 2, 3), (1, 1, 1), (5000, 2, 4), (4096 * 3 // 8 + 37, 8, 64), (700, 3, 1000),
-    (2049, 8, 256),
+    (2049, 8, 256), (2048, 8, 256), (9000, 2, 16),
 ]
 
 
@@ -409,13 +412,16 @@ def _router_losses_gpu(layer, counts, alpha, z_weight):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "sigmoid", "e1024", "k16", "many_chunks",
-                                  "split_router"])
+                                  "valu_wide", "split_router"])
 def test_router_losses_match_oracle(name):
     """Switch load-balancing loss (moe-from-scratch page) and router z-loss
     (transformer book page) on the loads the forward returned, against the
-    oracle on the same loads; split_router has few tokens and a wide model,
-    so the router GEMM splits its reduction."""
-    extra = {"split_router": dict(T=100, d=2048, d_ff=16, E=64, K=8, act="bf16",
+    oracle on the same loads; valu_wide is the widest model of the
+    wavefront-per-token router, split_router has few tokens and a wider
+    model, so the matrix-core router GEMM splits its reduction."""
+    extra = {"valu_wide": dict(T=100, d=2048, d_ff=16, E=64, K=8, act="bf16",
+                               router_std=0.02, w_std=0.02),
+             "split_router": dict(T=100, d=2560, d_ff=16, E=64, K=8, act="bf16",
                                   router_std=0.02, w_std=0.02)}
     if name in ("tiny", "small"):
         w = moe_synth.get(name)
