@@ -7,9 +7,11 @@ dispatch, grouped expert SwiGLU, shared experts, combine), inputs resident
 in HBM. Prints ONE JSON line on stdout; details go to stderr.
 
 The dominant kernel (the grouped gate/up GEMM) is timed with HIP events
-recorded by the library around that launch on the launch stream, every
-timed step; its algorithmic flops (or bytes, for weight-streaming batches)
-per launch divided by the mean duration gives roofline.achieved.
+recorded by the library on the launch stream: around that launch in every
+timed step, and around 20 back-to-back passes of it right after the timed
+steps (which removes the events' own overhead from short launches); its
+algorithmic flops (or bytes, for weight-streaming batches) per launch divided
+by the mean duration of one pass gives roofline.achieved.
 
 cpu_baseline: the CPU oracle timed on a bounded sample of the same tokens.
 """
@@ -36,8 +38,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, counts):
-    """Per-step algorithmic work of the layer and of the gate/up launch."""
+def algorithmic(w, counts, merged=False):
+    """Per-step algorithmic work of the layer and of the gate/up launch
+    (merged: the shared experts' gate/up GEMM runs in the same launch)."""
     es = 2 if w.act == "bf16" else 4
     de, f, rows = w.d_e, w.d_ff, w.T * w.K
     touched = int((counts > 0).sum())
@@ -51,6 +54,9 @@ def algorithmic(w, counts):
     gu_flops = 4.0 * rows * de * f
     # gate/up launch: touched experts' gate+up weights, gathered rows in, h out
     gu_bytes = touched * 2 * f * de * es + rows * de * es + rows * f * es
+    if merged:  # + shared gate/up: its weights, x in, its h out
+        gu_flops += 4.0 * w.T * w.d * w.d_shared
+        gu_bytes += 2 * w.d_shared * w.d * es + w.T * w.d * es + w.T * w.d_shared * es
     return dict(flops=fl_router + fl_routed + fl_shared + fl_latent, bytes=bytes_w + bytes_act,
                 gu_flops=gu_flops, gu_bytes=gu_bytes, touched=touched)
 
@@ -161,7 +167,7 @@ def main():
     for b, e in evs:  # materialise the events on the launch stream
         b.record(stream)
         e.record(stream)
-    probes = [moe.MoeProbe(stage=stage, ev_begin=b.cuda_event, ev_end=e.cuda_event)
+    probes = [moe.MoeProbe(stage=stage, repeat=1, ev_begin=b.cuda_event, ev_end=e.cuda_event)
               for b, e in evs]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -170,10 +176,29 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt / args.steps * 1e3
-    gu_ms = float(np.mean([b.elapsed_time(e) for b, e in evs]))
+    gu_ms_event = float(np.mean([b.elapsed_time(e) for b, e in evs]))
+
+    # The same launch timed without the events' own overhead (a few us, which
+    # matters for short launches): forwards whose gate/up stage enqueues the
+    # launch REPS times back to back between the two events (each pass
+    # recomputes the same rows); one launch = elapsed / REPS.
+    REPS, PASSES = 20, 5
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(PASSES)]
+    for b, e in rev:
+        b.record(stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    for b, e in rev:
+        layer.forward(x, out, counts=counts,
+                      probe=moe.MoeProbe(stage=stage, repeat=REPS, ev_begin=b.cuda_event,
+                                         ev_end=e.cuda_event))
+    torch.cuda.synchronize()
+    gu_ms = float(np.mean([b.elapsed_time(e) for b, e in rev])) / REPS
 
     cnt = counts.cpu().numpy()
-    alg = algorithmic(w, cnt)
+    plan = moe.moe_plan(layer.desc)
+    alg = algorithmic(w, cnt, merged=bool(plan["merged_shared"]))
 
     # bias-based balancer step on this step's loads (a scratch bias, so the
     # layer's routing is untouched)
@@ -226,8 +251,13 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_GBS, 4), "traffic": None}
     roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "grouped gate/up GEMM + SiLU*up"
+    roof["kernel"] = "grouped gate/up GEMM + SiLU*up" + (
+        " (+ the shared experts' gate/up GEMM in the same launch)" if plan["merged_shared"] else "")
+    roof["tile"] = f"{plan['gate_up_tile_m']}x{plan['gate_up_tile_n']}"
     roof["kernel_ms"] = round(gu_ms, 4)
+    roof["timing"] = (f"mean of {PASSES} x {REPS} back-to-back launches between HIP events on "
+                      f"the launch stream; single launch bracketed by events in each timed step: "
+                      f"{gu_ms_event:.4f} ms (includes the events' own overhead)")
     log(f"step {ms:.4f} ms, {tok_s:.4g} tokens/s; gate/up kernel {gu_ms:.4f} ms; "
         f"experts touched {alg['touched']}/{w.E}; loads max {cnt.max()} min {cnt.min()}")
 

@@ -127,7 +127,13 @@ typedef struct moe_weights {
 
 /* Optional timing probe for moe_forward: if stage >= 0, ev_begin and ev_end
  * (hipEvent_t, created by the caller) are recorded on the stream right
- * before the first and right after the last kernel of that stage. */
+ * before the first and right after the last kernel of that stage. With
+ * repeat > 1 the kernels of a GEMM stage (latent_down, expert_gate_up,
+ * expert_down, shared_gate_up) are enqueued that many times back to back
+ * between the two events, each pass recomputing the same outputs from the
+ * same inputs: (ev_end - ev_begin) / repeat then times one pass without the
+ * events' own overhead (a benchmarking aid; the layer's result is the same).
+ * Other stages ignore repeat. */
 typedef enum moe_stage {
   MOE_STAGE_ROUTE = 0,         /* router GEMM + selection + weights          */
   MOE_STAGE_DISPATCH = 1,      /* histogram, scan, stable scatter            */
@@ -142,9 +148,29 @@ typedef enum moe_stage {
 
 typedef struct moe_probe {
   int32_t stage;   /* moe_stage, or -1 for none */
+  int32_t repeat;  /* passes of a GEMM stage between the events (0 or 1: one) */
   void *ev_begin;  /* hipEvent_t */
   void *ev_end;    /* hipEvent_t */
 } moe_probe;
+
+/* How moe_forward runs a layer (filled by moe_plan; host memory). */
+typedef struct moe_plan_info {
+  int32_t merged_shared;          /* 1: the shared experts' gate/up and down GEMMs
+                                     run inside the grouped gate/up and down
+                                     launches (stages expert_gate_up /
+                                     expert_down), stage shared_gate_up is empty
+                                     and stage combine is the gather-sum alone */
+  int32_t gate_up_pipelined;      /* 1: grouped gate/up on the pipelined kernel */
+  int32_t gate_up_tile_m;         /* its output tile: rows ...               */
+  int32_t gate_up_tile_n;         /* ... x weight rows (gate + up halves)     */
+  int32_t down_pipelined;
+  int32_t down_tile_m;
+  int32_t down_tile_n;
+  int32_t router_per_token;       /* 1: one wavefront per token computes the
+                                     fp32 logits (few experts, narrow model);
+                                     0: matrix-core router GEMM             */
+  int32_t dispatch_one_workgroup; /* 1: the whole dispatch in one workgroup  */
+} moe_plan_info;
 
 /* Text of a status code (static storage). */
 MOE_API const char *moe_strerror(int status);
@@ -232,6 +258,10 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream);
 
+/* The kernel plan moe_forward uses for this layer (it depends on the
+ * descriptor only). Errors: a bad descriptor, MOE_ERR_NULL. */
+MOE_API int moe_plan(const moe_desc *desc, moe_plan_info *info);
+
 /* QuantileBalancer update ("StableLatentMoE and QuantileBalancer", sections
  * "QuantileBalancer: persistent biases, no gradient update" and "FP32 router
  * and training-only QB update"); sigmoid routing (MOE_ROUTE_SIGMOID_BIAS)
@@ -265,7 +295,7 @@ MOE_API int moe_quantile_balance(const moe_desc *desc, const moe_weights *w, con
  * counts: int32 [E] device array, the expert loads of the same T tokens (as
  * moe_forward / moe_dispatch return them). losses: fp32 [2] device array.
  * Any routing rule (the losses are defined on the softmax of the logits).
- * Sums are taken in a fixed order (per 64 tokens in fp32, then in fp64):
+ * Sums are taken in a fixed order (per 16 tokens in fp32, then in fp64):
  * results are deterministic. Enqueued on stream, no host synchronisation.
  * T == 0 is a no-op (losses untouched). Errors: MOE_ERR_NULL, MOE_ERR_MODE
  * (alpha or z_weight not finite, or a bad descriptor), MOE_ERR_SHAPE,

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
-           "moe_balance_bias", "moe_router_losses")
+           "moe_balance_bias", "moe_router_losses", "moe_plan")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -44,8 +44,16 @@ class MoeWeights(C.Structure):
         "w_lat_down", "w_lat_up", "rms_gamma")]
 
 
+class MoePlanInfo(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "merged_shared", "gate_up_pipelined", "gate_up_tile_m", "gate_up_tile_n",
+        "down_pipelined", "down_tile_m", "down_tile_n", "router_per_token",
+        "dispatch_one_workgroup")]
+
+
 class MoeProbe(C.Structure):
-    _fields_ = [("stage", C.c_int32), ("ev_begin", C.c_void_p), ("ev_end", C.c_void_p)]
+    _fields_ = [("stage", C.c_int32), ("repeat", C.c_int32), ("ev_begin", C.c_void_p),
+                ("ev_end", C.c_void_p)]
 
 
 _lib = None
@@ -73,9 +81,10 @@ def lib():
         L.moe_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P, P]
         L.moe_quantile_balance.argtypes = [P, P, P, P, P, S, P]
         L.moe_router_losses.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, S, P]
+        L.moe_plan.argtypes = [P, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                   "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance",
-                  "moe_router_losses"):
+                  "moe_router_losses", "moe_plan"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -119,6 +128,13 @@ def make_weights(t: dict) -> MoeWeights:
     """moe_weights from a dict of device tensors (keys as in moe_weights).
     The caller keeps the tensors alive while the struct is in use."""
     return MoeWeights(**{k: _ptr(t.get(k)) for k, _ in MoeWeights._fields_})
+
+
+def moe_plan(desc: MoeDesc) -> dict:
+    """How moe_forward runs this layer (kernel paths and tile shapes)."""
+    info = MoePlanInfo()
+    _ok(lib().moe_plan(C.byref(desc), C.byref(info)), "moe_plan")
+    return {n: int(getattr(info, n)) for n, _ in MoePlanInfo._fields_}
 
 
 def moe_workspace_size(desc: MoeDesc) -> int:

@@ -20,7 +20,7 @@ struct Layout {
   size_t wsplit, logits;
   size_t idx, g, gap, counts, offsets, chunk, perm, stok, inv, sw, tiles, ntiles, tiles2,
       ntiles2, ntie;
-  size_t z, h, y, hsh, r;
+  size_t z, h, y, hsh, sh, r;
   size_t qb_top, qb_diff, qb_q;  // QuantileBalancer (sigmoid routing only)
   size_t loss;                   // router-loss partial sums
   size_t total;
@@ -30,6 +30,8 @@ struct Layout {
 int64_t grouped_tile_bound(int64_t rows, int64_t E, int bm) {
   return rows / bm + (rows < E ? rows : E) + 1;
 }
+
+bool merged_plan(const moe_desc *d);
 
 Layout layout_of(const moe_desc *d) {
   Layout L{};
@@ -65,6 +67,7 @@ Layout layout_of(const moe_desc *d) {
   L.h = take(rows * d->d_ff * es);
   L.y = take(rows * de * es);
   L.hsh = d->d_shared ? take(T * d->d_shared * es) : 0;
+  L.sh = merged_plan(d) ? take(T * d->d_model * 4) : 0;  // fp32
   L.r = d->latent ? take(T * d->latent * es) : 0;
   if (d->route_mode == MOE_ROUTE_SIGMOID_BIAS) {
     L.qb_top = take(T * (K + 1) * 4);
@@ -99,6 +102,7 @@ struct GemmPlan {
 };
 struct Plan {
   GemmPlan gu, dn;  // gate/up, down
+  bool merged;      // the shared experts' GEMMs run inside the grouped launches
   bool shared_table() const { return gu.bm() == dn.bm(); }
 };
 
@@ -120,13 +124,29 @@ GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, in
   return {0, TILE_TALL_N64};  // few down tiles (narrow model, few experts)
 }
 
+// Layers too small for 256x256 grouped tiles leave CUs idle in every GEMM
+// launch; there the shared experts' gate/up and down GEMMs join the grouped
+// launches as second problems (same tile), and the combine becomes a
+// gather-sum that adds their output.
 Plan plan_grouped(const moe_desc *d) {
   const int64_t rows = d->T * d->top_k, E = d->n_experts;
   const int64_t de = d->latent ? d->latent : d->d_model;
   const int bf = d->act_dtype == MOE_BF16;
-  return {plan_one(rows, E, de, d->d_ff, 1, bf, rows),  // A: T tokens or T*K gathered rows
-          plan_one(rows, E, d->d_ff, de, 0, bf, rows)};
+  Plan pl{plan_one(rows, E, de, d->d_ff, 1, bf, rows),  // A: T tokens or T*K gathered rows
+          plan_one(rows, E, d->d_ff, de, 0, bf, rows), false};
+  const int64_t T = d->T, dm = d->d_model, ds = d->d_shared;
+  constexpr int64_t kLim = int64_t(1) << 32;
+  if (!d->latent && ds > 0 && bf && pl.gu.v2 && pl.dn.v2 && pl.gu.cfg != TILE2_256x256_TALLW &&
+      dm % 32 == 0 && ds % 32 == 0 && T * dm * 2 < kLim && T * ds * 2 < kLim &&
+      (ds + 256) * dm * 2 < kLim && (dm + 256) * ds * 2 < kLim) {
+    pl.merged = true;
+    pl.gu.cfg = gemm2_pick(rows, E, dm, d->d_ff, 1, T, ds);
+    pl.dn.cfg = gemm2_pick(rows, E, d->d_ff > ds ? d->d_ff : ds, dm, 0, T, dm);
+  }
+  return pl;
 }
+
+bool merged_plan(const moe_desc *d) { return plan_grouped(d).merged; }
 
 hipError_t run_grouped(const GemmArgs &a, int epi, const GemmPlan &pl, int bf, hipStream_t s) {
   if (!pl.v2) return launch_gemm(a, epi, pl.cfg, bf, s);
@@ -147,6 +167,10 @@ struct Probe {
   }
   void end(int stage) const {
     if (p && p->stage == stage) hipEventRecord(static_cast<hipEvent_t>(p->ev_end), s);
+  }
+  // passes of a GEMM stage to enqueue (repeat > 1 on the probed stage only)
+  int reps(int stage) const {
+    return (p && p->stage == stage && p->repeat > 1) ? p->repeat : 1;
   }
 };
 
@@ -180,7 +204,8 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   a.out = h;
   a.ldo = d->d_ff;
   pr.begin(MOE_STAGE_EXPERT_GATE_UP);
-  MOE_TRY(run_grouped(a, EPI_SWIGLU, pl.gu, bf, s));
+  for (int r = 0; r < pr.reps(MOE_STAGE_EXPERT_GATE_UP); ++r)
+    MOE_TRY(run_grouped(a, EPI_SWIGLU, pl.gu, bf, s));
   pr.end(MOE_STAGE_EXPERT_GATE_UP);
 
   GemmArgs b{};
@@ -199,7 +224,8 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   b.ldo = de;
   b.row_scale = row_scale;
   pr.begin(MOE_STAGE_EXPERT_DOWN);
-  MOE_TRY(run_grouped(b, EPI_SCALE, pl.dn, bf, s));
+  for (int r = 0; r < pr.reps(MOE_STAGE_EXPERT_DOWN); ++r)
+    MOE_TRY(run_grouped(b, EPI_SCALE, pl.dn, bf, s));
   pr.end(MOE_STAGE_EXPERT_DOWN);
   return MOE_OK;
 }
@@ -225,7 +251,8 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
     a.out = hsh;
     a.ldo = d->d_shared;
     pr.begin(MOE_STAGE_SHARED_GATE_UP);
-    MOE_TRY(launch_dense(a, EPI_SWIGLU, bf, s));
+    for (int r = 0; r < pr.reps(MOE_STAGE_SHARED_GATE_UP); ++r)
+      MOE_TRY(launch_dense(a, EPI_SWIGLU, bf, s));
     pr.end(MOE_STAGE_SHARED_GATE_UP);
   }
   pr.begin(MOE_STAGE_COMBINE);
@@ -290,6 +317,87 @@ hipError_t run_dispatch(const ScanArgs &sa, const ScatterArgs &sc, hipStream_t s
   if (e != hipSuccess) return e;
   if ((e = launch_scan(sa, s)) != hipSuccess) return e;
   return launch_scatter(sc, s);
+}
+
+// Merged plan: grouped gate/up + shared gate/up in one launch, grouped down
+// + shared down (into sh, fp32) in one launch, then out = sh + the routed
+// rows.
+int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const void *rows,
+                 const int32_t *row_index, const Tables &tb, const Plan &pl,
+                 const float *row_scale, const int32_t *inv, void *out, char *ws,
+                 const Layout &L, const Probe &pr, hipStream_t s) {
+  const int64_t T = d->T, rows_n = T * d->top_k;
+  const int dm = d->d_model, ds = d->d_shared;
+  void *h = ws + L.h, *y = ws + L.y, *hsh = ws + L.hsh, *sh = ws + L.sh;
+  GemmArgs a{};  // routed gate/up
+  a.a = rows;
+  a.lda = dm;
+  a.a_rows = row_index;
+  a.b0 = w->w_gate;
+  a.b1 = w->w_up;
+  a.ldb = dm;
+  a.b_stride = static_cast<int64_t>(d->d_ff) * dm;
+  a.K = dm;
+  a.N = d->d_ff;
+  a.a_extent = row_index ? T : rows_n;
+  a.tiles = tb.gu;
+  a.n_tiles = tb.gu_n;
+  a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.gu.bm());
+  a.out = h;
+  a.ldo = d->d_ff;
+  GemmArgs sa{};  // shared gate/up
+  sa.a = x;
+  sa.lda = dm;
+  sa.b0 = w->ws_gate;
+  sa.b1 = w->ws_up;
+  sa.ldb = dm;
+  sa.K = dm;
+  sa.N = ds;
+  sa.M = T;
+  sa.out = hsh;
+  sa.ldo = ds;
+  if (!gemm2_applicable(a, EPI_SWIGLU) || !gemm2_applicable(sa, EPI_SWIGLU)) return MOE_ERR_HIP;
+  pr.begin(MOE_STAGE_EXPERT_GATE_UP);
+  for (int r = 0; r < pr.reps(MOE_STAGE_EXPERT_GATE_UP); ++r)
+    MOE_TRY(launch_gemm2(a, EPI_SWIGLU, pl.gu.cfg, s, &sa));
+  pr.end(MOE_STAGE_EXPERT_GATE_UP);
+
+  GemmArgs b{};  // routed down, times the routing weight
+  b.a = h;
+  b.lda = d->d_ff;
+  b.b0 = w->w_down;
+  b.ldb = d->d_ff;
+  b.b_stride = static_cast<int64_t>(dm) * d->d_ff;
+  b.K = d->d_ff;
+  b.N = dm;
+  b.a_extent = rows_n;
+  b.tiles = tb.dn;
+  b.n_tiles = tb.dn_n;
+  b.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.dn.bm());
+  b.out = y;
+  b.ldo = dm;
+  b.row_scale = row_scale;
+  GemmArgs sb{};  // shared down (weight 1)
+  sb.a = hsh;
+  sb.lda = ds;
+  sb.b0 = w->ws_down;
+  sb.ldb = ds;
+  sb.K = ds;
+  sb.N = dm;
+  sb.M = T;
+  sb.out = sh;
+  sb.ldo = dm;
+  sb.out_f32 = 1;  // fp32, added to the routed rows in fp32 by the combine
+  if (!gemm2_applicable(b, EPI_SCALE) || !gemm2_applicable(sb, EPI_SCALE)) return MOE_ERR_HIP;
+  pr.begin(MOE_STAGE_EXPERT_DOWN);
+  for (int r = 0; r < pr.reps(MOE_STAGE_EXPERT_DOWN); ++r)
+    MOE_TRY(launch_gemm2(b, EPI_SCALE, pl.dn.cfg, s, &sb));
+  pr.end(MOE_STAGE_EXPERT_DOWN);
+
+  pr.begin(MOE_STAGE_COMBINE);
+  MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, 1, s, static_cast<const float *>(sh)));
+  pr.end(MOE_STAGE_COMBINE);
+  return MOE_OK;
 }
 
 int check_expert_weights(const moe_desc *d, const moe_weights *w) {
@@ -616,17 +724,40 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
     a.out = wsb + L.z;
     a.ldo = d->latent;
     pr.begin(MOE_STAGE_LATENT_DOWN);
-    MOE_TRY(launch_dense(a, EPI_STORE, bf, s));
+    for (int r = 0; r < pr.reps(MOE_STAGE_LATENT_DOWN); ++r)
+      MOE_TRY(launch_dense(a, EPI_STORE, bf, s));
     pr.end(MOE_STAGE_LATENT_DOWN);
     rsrc = wsb + L.z;
   }
 
-  // 4. grouped expert SwiGLU (gather fused into GEMM 1's A load)
+  // 4. grouped expert SwiGLU (gather fused into GEMM 1's A load), shared
+  // experts, combine
+  if (pl.merged) return merged_gemms(d, w, x, rsrc, stok, tb, pl, sw, inv, out, wsb, L, pr, s);
   if ((rc = expert_gemms(d, w, rsrc, stok, tb, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
     return rc;
-
-  // 5. shared experts + combine
   return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
+}
+
+int moe_plan(const moe_desc *d, moe_plan_info *info) {
+  const int rc = check_desc(d);
+  if (rc) return rc;
+  if (!info) return MOE_ERR_NULL;
+  const Plan pl = plan_grouped(d);
+  RouterArgs ra{};
+  ra.T = d->T;
+  ra.d = d->d_model;
+  ra.E = d->n_experts;
+  *info = moe_plan_info{};
+  info->merged_shared = pl.merged ? 1 : 0;
+  info->gate_up_pipelined = pl.gu.v2;
+  info->gate_up_tile_m = pl.gu.bm();
+  info->gate_up_tile_n = pl.gu.v2 ? gemm2_bn(pl.gu.cfg) : tile_bn(pl.gu.cfg);
+  info->down_pipelined = pl.dn.v2;
+  info->down_tile_m = pl.dn.bm();
+  info->down_tile_n = pl.dn.v2 ? gemm2_bn(pl.dn.cfg) : tile_bn(pl.dn.cfg);
+  info->router_per_token = router_valu(ra) ? 1 : 0;
+  info->dispatch_one_workgroup = dispatch_fused_ok(d->T * d->top_k, d->n_experts) ? 1 : 0;
+  return MOE_OK;
 }
 
 int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens, const int32_t *counts,

@@ -17,13 +17,18 @@ namespace moe {
 
 namespace {
 
+// out[t] = sum_k y[inv[t*K+k]] (+ add[t], fp32): one wavefront per token,
+// 16-byte chunks, the K rows summed in k order in fp32, then add.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_sum_kernel(const uint4 *__restrict__ y,
                                                           const int32_t *__restrict__ inv, int K,
-                                                          int chunks, uint4 *__restrict__ out) {
+                                                          int chunks, int64_t n_tok,
+                                                          const float *__restrict__ add,
+                                                          uint4 *__restrict__ out) {
   constexpr int N = Chunk<T>::N;
-  const int64_t t = blockIdx.x;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  for (int c = threadIdx.x & 63; c < chunks; c += 64) {
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
@@ -34,6 +39,17 @@ __global__ __launch_bounds__(256) void combine_sum_kernel(const uint4 *__restric
       Chunk<T>::unpack(y[static_cast<int64_t>(q) * chunks + c], v);
 #pragma unroll
       for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    if (add) {
+      const float4 *a4 = reinterpret_cast<const float4 *>(add + (t * chunks + c) * N);
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const float4 v = a4[i];
+        acc[4 * i] += v.x;
+        acc[4 * i + 1] += v.y;
+        acc[4 * i + 2] += v.z;
+        acc[4 * i + 3] += v.w;
+      }
     }
     out[t * chunks + c] = Chunk<T>::pack(acc);
   }
@@ -93,15 +109,16 @@ __global__ __launch_bounds__(256) void combine_latent_kernel(const uint4 *__rest
 }  // namespace
 
 hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int K, int width,
-                              void *out, int act_bf16, hipStream_t s) {
+                              void *out, int act_bf16, hipStream_t s, const float *add) {
   if (T == 0) return hipSuccess;
   const int chunks = width / (act_bf16 ? 8 : 4);
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
   if (act_bf16)
-    combine_sum_kernel<bf16_t><<<static_cast<unsigned>(T), 256, 0, s>>>(
-        static_cast<const uint4 *>(y), inv, K, chunks, static_cast<uint4 *>(out));
+    combine_sum_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const uint4 *>(y), inv, K, chunks,
+                                                    T, add, static_cast<uint4 *>(out));
   else
-    combine_sum_kernel<float><<<static_cast<unsigned>(T), 256, 0, s>>>(
-        static_cast<const uint4 *>(y), inv, K, chunks, static_cast<uint4 *>(out));
+    combine_sum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const uint4 *>(y), inv, K, chunks,
+                                                   T, add, static_cast<uint4 *>(out));
   return hipGetLastError();
 }
 

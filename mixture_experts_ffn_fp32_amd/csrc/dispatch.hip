@@ -167,11 +167,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
 }
 
 // The whole dispatch in one workgroup of 1024 threads, for few slots and
-// experts (a launch per step costs more than the work there): LDS histogram,
-// scan (counts, offsets, m-tile tables, near-tie count as scan_kernel), then
-// rounds of 1024 slots in slot order: a slot's position is its expert's
-// running base + the slots of that expert in earlier wavefronts of the round
-// (per-wavefront peer counts in LDS) + its rank among its wavefront's peers.
+// experts (a launch per step costs more than the work there). Each thread
+// owns slots t, t + 1024, ... (one per round of 1024): their ids, weights and
+// the router gaps are loaded once, up front. Per round and wavefront, slots
+// of equal id find each other with one ballot per id bit (peer masks), so
+// the LDS histogram takes one atomic per (wavefront, id), and a slot's
+// position is its expert's running base + the slots of that id in earlier
+// wavefronts of the round (per-wavefront peer counts in LDS) + its rank among
+// its wavefront's peers. Scan, m-tile tables and near-tie count as in
+// scan_kernel.
+constexpr int kFusedRounds = static_cast<int>(kFusedMaxSlots / 1024);
+
 __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, ScatterArgs sc) {
   __shared__ int tmp[1024];
   __shared__ int run[kMaxE + 1];
@@ -180,11 +186,41 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, Scatte
   __shared__ int wcnt[16][kFusedMaxE];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int E = a.E;
+  const int rounds = static_cast<int>((a.slots + 1023) / 1024);
+  int ids[kFusedRounds];
+  float gs[kFusedRounds];
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int64_t s = static_cast<int64_t>(r) * 1024 + t;
+    ids[r] = (r < rounds && s < a.slots) ? sc.idx[s] : -1;
+    gs[r] = (r < rounds && s < a.slots && sc.sorted_w) ? sc.g[s] : 0.f;
+  }
+  int ntie = 0;
+  if (a.gap && a.n_near_ties)
+    for (int64_t i = t; i < a.T; i += 1024) ntie += (a.gap[i] < a.tie_eps) ? 1 : 0;
   for (int e = t; e < E; e += 1024) run[e] = 0;
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rk[kFusedRounds], cn[kFusedRounds];
   __syncthreads();
-  for (int64_t s = t; s < a.slots; s += 1024) {
-    const int e = sc.idx[s];
-    if (e >= 0 && e < E) atomicAdd(&run[e], 1);
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    rk[r] = 0;
+    cn[r] = 0;
+    if (r < rounds) {
+      const int e = ids[r];
+      const bool valid = e >= 0 && e < E;
+      uint64_t peers = ballot(valid);
+      for (int b = 0; b < bits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bal = ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      rk[r] = __popcll(peers & lt_mask);
+      cn[r] = __popcll(peers);
+      if (valid && rk[r] == cn[r] - 1) atomicAdd(&run[e], cn[r]);
+    }
   }
   __syncthreads();
   const int cnt_t = t < E ? run[t] : 0;
@@ -206,39 +242,29 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, Scatte
   if (a.tiles2) build_tiles(off, E, a.bm2, start, tmp, a.tiles2, a.n_tiles2);
   __syncthreads();
   if (a.gap && a.n_near_ties) {
-    int n = 0;
-    for (int64_t i = t; i < a.T; i += 1024) n += (a.gap[i] < a.tie_eps) ? 1 : 0;
     int tot;
-    block_exscan_1024(n, tmp, &tot);
+    block_exscan_1024(ntie, tmp, &tot);
     if (t == 0) *a.n_near_ties = tot;
   }
-  int bits = 0;
-  while ((1 << bits) < E) ++bits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t r0 = 0; r0 < a.slots; r0 += 1024) {
-    const int64_t s = r0 + t;
-    const int e = s < a.slots ? sc.idx[s] : -1;
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    if (r >= rounds) break;
+    const int64_t s = static_cast<int64_t>(r) * 1024 + t;
+    const int e = ids[r];
     const bool valid = e >= 0 && e < E;
-    uint64_t peers = ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bal = ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(peers & lt_mask);
-    const int cnt = __popcll(peers);
     for (int i = lane; i < E; i += 64) wcnt[wave][i] = 0;  // this wave's row (in order)
-    if (valid && rank == cnt - 1) wcnt[wave][e] = cnt;
+    if (valid && rk[r] == cn[r] - 1) wcnt[wave][e] = cn[r];
     __syncthreads();
     int pos = 0;
     if (valid) {
       int pre = 0;
       for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-      pos = run[e] + pre + rank;
+      pos = run[e] + pre + rk[r];
     }
     __syncthreads();  // every read of run[] and wcnt[] of this round is done
     if (t < E) {
       int add = 0;
+#pragma unroll
       for (int w = 0; w < 16; ++w) add += wcnt[w][t];
       run[t] += add;
     }
@@ -246,7 +272,7 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, Scatte
       sc.perm[pos] = static_cast<int32_t>(s);
       sc.sorted_token[pos] = static_cast<int32_t>(s / sc.K);
       sc.inv[s] = pos;
-      if (sc.sorted_w) sc.sorted_w[pos] = sc.g[s];
+      if (sc.sorted_w) sc.sorted_w[pos] = gs[r];
     } else if (s < a.slots) {
       sc.inv[s] = -1;
     }

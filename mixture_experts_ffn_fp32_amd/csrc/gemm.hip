@@ -363,6 +363,20 @@ int tile_bm(int cfg) {
   return CfgLarge::BM;
 }
 
+int tile_bn(int cfg) {
+  switch (cfg) {
+    case TILE_MID: return CfgMid::BN;
+    case TILE_TALL_N64: return CfgTallN64::BN;
+    case TILE_SMALL_N64: return CfgSmallN64::BN;
+    case TILE_SMALL_M: return CfgSmallM::BN;
+    case TILE_LARGE: return CfgLarge::BN;
+    case TILE_WIDE: return CfgWide::BN;
+    case TILE_TALL: return CfgTall::BN;
+    case TILE_HUGE: return CfgHuge::BN;
+  }
+  return CfgLarge::BN;
+}
+
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s) {
   if (!act_bf16)  // fp32 runs the two base shapes only
     return cfg == TILE_SMALL_M ? dispatch_epi<float, CfgSmallM>(a, epi, s)

@@ -110,7 +110,7 @@ struct G2Shape {
 
 template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN, (G2Shape<BM, BN, WGM, WGN, NA, EPI>::MIN_WAVES))
-void gemm2_kernel(GemmArgs p) {
+void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   using Sh = G2Shape<BM, BN, WGM, WGN, NA, EPI>;
   constexpr int NB = NA + 1;  // B stage buffers
   static_assert(NA >= 2, "at least double-buffered");
@@ -132,17 +132,26 @@ void gemm2_kernel(GemmArgs p) {
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ------------------------------------------------------------ tile
-  // consecutive workgroups go to different XCDs: give each XCD a contiguous
-  // range of tiles, grouped 4 m-tiles at a time so tiles sharing B or A run
-  // together
-  const int n_tn = (p.N + NOUT - 1) / NOUT;
-  const int64_t n_m = p.tiles ? static_cast<int64_t>(*p.n_tiles) : p.max_mtiles;
-  const int64_t total = n_m * n_tn;
+  // Two problems may share the launch (p1.N == 0: none): the tiles of p0,
+  // then those of p1. Consecutive workgroups go to different XCDs: give each
+  // XCD a contiguous range of tiles, grouped 4 m-tiles at a time so tiles
+  // sharing B or A run together.
+  const int n_tn0 = (p0.N + NOUT - 1) / NOUT;
+  const int64_t n_m0 = p0.tiles ? static_cast<int64_t>(*p0.n_tiles) : p0.max_mtiles;
+  const int64_t total0 = n_m0 * n_tn0;
+  const int n_tn1 = (p1.N + NOUT - 1) / NOUT;
+  const int64_t n_m1 = p1.N <= 0 ? 0 : (p1.tiles ? static_cast<int64_t>(*p1.n_tiles) : p1.max_mtiles);
+  const int64_t total = total0 + n_m1 * n_tn1;
   const int64_t per = (total + 7) / 8;
   const int64_t local = blockIdx.x >> 3;
   if (local >= per) return;
-  const int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
+  int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
   if (pid >= total) return;
+  const bool second = pid >= total0;
+  const GemmArgs &p = second ? p1 : p0;
+  const int n_tn = second ? n_tn1 : n_tn0;
+  const int64_t n_m = second ? n_m1 : n_m0;
+  if (second) pid -= total0;
   constexpr int GM = MOE_G2_GM;
   const int64_t grp = pid / (GM * n_tn);
   const int64_t first_m = grp * GM;
@@ -387,7 +396,7 @@ void gemm2_kernel(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += rs[e];
       }
-      if (EPI == EPI_STORE_F32) {
+      if (EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32)) {
         float *o = static_cast<float *>(p.out) + m * p.ldo + col;
         *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -402,27 +411,33 @@ void gemm2_kernel(GemmArgs p) {
 }
 
 template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
-hipError_t run2(const GemmArgs &a, hipStream_t s) {
+hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  const int64_t n_tn = (a.N + NOUT - 1) / NOUT;
-  const int64_t max_m = a.tiles ? a.max_mtiles : (a.M + BM - 1) / BM;
-  const int64_t total = max_m * n_tn;
+  auto bound = [&](GemmArgs &g) {  // m-tile bound (grid size) of one problem
+    g.max_mtiles = g.tiles ? g.max_mtiles : (g.M + BM - 1) / BM;
+    return g.max_mtiles * ((g.N + NOUT - 1) / NOUT);
+  };
+  GemmArgs b0 = a, b1{};
+  int64_t total = bound(b0);
+  if (second && second->N > 0) {
+    b1 = *second;
+    total += bound(b1);
+  }
   if (total == 0) return hipSuccess;
-  GemmArgs b = a;
-  b.max_mtiles = max_m;
   const int64_t blocks = 8 * ((total + 7) / 8);
-  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI><<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b);
+  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI>
+      <<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b0, b1);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, int NA = 2>
-hipError_t dispatch2(const GemmArgs &a, int epi, hipStream_t s) {
+hipError_t dispatch2(const GemmArgs &a, const GemmArgs *b, int epi, hipStream_t s) {
   switch (epi) {
-    case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, NA, EPI_SWIGLU>(a, s);
-    case EPI_SCALE: return run2<BM, BN, WGM, WGN, NA, EPI_SCALE>(a, s);
-    case EPI_STORE: return run2<BM, BN, WGM, WGN, NA, EPI_STORE>(a, s);
-    case EPI_COMBINE: return run2<BM, BN, WGM, WGN, NA, EPI_COMBINE>(a, s);
-    case EPI_STORE_F32: return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32>(a, s);
+    case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, NA, EPI_SWIGLU>(a, b, s);
+    case EPI_SCALE: return run2<BM, BN, WGM, WGN, NA, EPI_SCALE>(a, b, s);
+    case EPI_STORE: return run2<BM, BN, WGM, WGN, NA, EPI_STORE>(a, b, s);
+    case EPI_COMBINE: return run2<BM, BN, WGM, WGN, NA, EPI_COMBINE>(a, b, s);
+    case EPI_STORE_F32: return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32>(a, b, s);
   }
   return hipErrorInvalidValue;
 }
@@ -465,20 +480,25 @@ int gemm2_bn(int cfg) {
 
 // Tile of the pipelined kernel for an output of rows x n_out over a reduction
 // of K (grouped: `groups` experts, each of which may end in a partial m-tile;
-// dense: groups = 0). From sweeps of every tile on MI355X over the
-// benchmark layers: 256x256 wins whenever it gives each of the 256 CUs a
-// workgroup; below that, 128x128 with two workgroups per CU (their
+// dense: groups = 0; plus an optional dense rows2 x n_out2 problem sharing the
+// launch). From sweeps of every tile on MI355X over the
+// benchmark layers: 256x256 wins when it gives each of the 256 CUs two
+// workgroups, or one over a long reduction; below that, 128x128 with two
+// workgroups per CU (their
 // prologues and epilogues overlap the other's K loop), or 256x128 for long
 // reductions; with fewer than 256 such tiles, the 8-wavefront 128x128 with a
 // deeper look-ahead, and 64x128 for the fewest.
-int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu) {
+int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu, int64_t rows2,
+               int64_t n_out2) {
   auto tiles = [&](int cfg) {
     const int64_t bm = gemm2_bm(cfg), nout = glu ? gemm2_bn(cfg) / 2 : gemm2_bn(cfg);
     const int64_t mt = groups ? rows / bm + (rows < groups ? rows : groups) : (rows + bm - 1) / bm;
-    return mt * ((n_out + nout - 1) / nout);
+    return mt * ((n_out + nout - 1) / nout) +
+           (rows2 > 0 ? ((rows2 + bm - 1) / bm) * ((n_out2 + nout - 1) / nout) : 0);
   };
   constexpr int64_t kCUs = 256;
-  if (tiles(TILE2_256x256_TALLW) >= kCUs) return TILE2_256x256_TALLW;
+  const int64_t t256 = tiles(TILE2_256x256_TALLW);
+  if (t256 >= 2 * kCUs || (t256 >= kCUs && K >= 1024)) return TILE2_256x256_TALLW;
   if (K >= 2048 && tiles(TILE2_256x128_W8D3) >= kCUs) return TILE2_256x128_W8D3;
   if (tiles(TILE2_128x128) >= kCUs) return TILE2_128x128;
   if (tiles(TILE2_128x128_W8D4) >= kCUs / 2) return TILE2_128x128_W8D4;
@@ -504,21 +524,21 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
   return launch_gemm(a, epi, TILE_SMALL_N64, act_bf16, s);
 }
 
-hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s) {
+hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, const GemmArgs *b) {
   switch (cfg) {
-    case TILE2_256x256: return dispatch2<256, 256, 2, 4>(a, epi, s);
-    case TILE2_256x256_TALLW: return dispatch2<256, 256, 4, 2>(a, epi, s);
-    case TILE2_256x256_W4: return dispatch2<256, 256, 2, 2>(a, epi, s);
-    case TILE2_256x128: return dispatch2<256, 128, 2, 2>(a, epi, s);
-    case TILE2_128x256: return dispatch2<128, 256, 2, 2>(a, epi, s);
-    case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, epi, s);
-    case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, epi, s);
-    case TILE2_128x64: return dispatch2<128, 64, 2, 2>(a, epi, s);
-    case TILE2_128x128_D4: return dispatch2<128, 128, 2, 2, 4>(a, epi, s);
-    case TILE2_128x128_W8D4: return dispatch2<128, 128, 4, 2, 4>(a, epi, s);
-    case TILE2_256x128_W8D3: return dispatch2<256, 128, 4, 2, 3>(a, epi, s);
-    case TILE2_128x256_W8: return dispatch2<128, 256, 2, 4>(a, epi, s);
-    case TILE2_64x128_D4: return dispatch2<64, 128, 2, 2, 4>(a, epi, s);
+    case TILE2_256x256: return dispatch2<256, 256, 2, 4>(a, b, epi, s);
+    case TILE2_256x256_TALLW: return dispatch2<256, 256, 4, 2>(a, b, epi, s);
+    case TILE2_256x256_W4: return dispatch2<256, 256, 2, 2>(a, b, epi, s);
+    case TILE2_256x128: return dispatch2<256, 128, 2, 2>(a, b, epi, s);
+    case TILE2_128x256: return dispatch2<128, 256, 2, 2>(a, b, epi, s);
+    case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, b, epi, s);
+    case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, b, epi, s);
+    case TILE2_128x64: return dispatch2<128, 64, 2, 2>(a, b, epi, s);
+    case TILE2_128x128_D4: return dispatch2<128, 128, 2, 2, 4>(a, b, epi, s);
+    case TILE2_128x128_W8D4: return dispatch2<128, 128, 4, 2, 4>(a, b, epi, s);
+    case TILE2_256x128_W8D3: return dispatch2<256, 128, 4, 2, 3>(a, b, epi, s);
+    case TILE2_128x256_W8: return dispatch2<128, 256, 2, 4>(a, b, epi, s);
+    case TILE2_64x128_D4: return dispatch2<64, 128, 2, 2, 4>(a, b, epi, s);
   }
   return hipErrorInvalidValue;
 }

@@ -24,13 +24,16 @@ struct RouterArgs {
   float *top;            // [T, K+1] or null
 };
 hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s);
+// True when the router runs one wavefront per token (few experts, a narrow
+// model, little work; reads a.T, a.E, a.d) instead of the matrix-core GEMM.
+bool router_valu(const RouterArgs &a);
 // QuantileBalancer update (sigmoid routing): runs the router (a.top must be
 // set: its column K is the threshold), then the differences diff [E, T],
 // per-expert order statistics q [E] and the centred new_bias [E].
 hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *diff, float *q,
                                    float *new_bias, hipStream_t s);
 // Router auxiliary losses (load-balancing loss and z-loss) of one step:
-// runs the router GEMM, then per-64-token partial sums into part
+// runs the router, then per-16-token partial sums into part
 // [router_loss_chunks(T), E + 1] and the two losses into losses [2].
 hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t *counts,
                                 float alpha, float z_weight, float *part, float *losses,
@@ -142,6 +145,7 @@ struct GemmArgs {
   int64_t a_extent;          // rows A may address (0: M; required for tile tables)
   int k_split;               // fp32-store only: K split count (0 or 1 = none);
   int64_t split_stride;      // elements between the splits' partial outputs
+  int out_f32;               // SCALE, pipelined kernel: fp32 output instead of act dtype
 };
 
 // Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,
@@ -155,6 +159,7 @@ enum TileCfg {
 // halves the B rows of a tile into output columns).
 int64_t tile_count(int cfg, int64_t rows, int64_t n_out, int glu);
 int tile_bm(int cfg);
+int tile_bn(int cfg);
 hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStream_t s);
 
 // Pipelined bf16 GEMM (gemm2.hip): direct-to-LDS loads.
@@ -172,17 +177,24 @@ enum Tile2Cfg {
 bool gemm2_applicable(const GemmArgs &a, int epi);
 int gemm2_bm(int cfg);
 int gemm2_bn(int cfg);  // B rows per tile (output columns, or gate + up halves)
-hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s);
+// b (optional, N > 0): a second problem of the same epilogue and tile
+// shape, run in the same launch after a's tiles.
+hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s,
+                        const GemmArgs *b = nullptr);
 // Pipelined tile for rows x n_out over K (grouped over `groups` experts, or
-// dense with groups = 0).
-int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu);
+// dense with groups = 0), with an optional dense rows2 x n_out2 problem in
+// the same launch.
+int gemm2_pick(int64_t rows, int64_t groups, int64_t K, int64_t n_out, int glu,
+               int64_t rows2 = 0, int64_t n_out2 = 0);
 // Dense GEMM with the kernel and tile shape chosen from the problem size.
 hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s);
 
 // ------------------------------------------------------------------ combine
-// out[t] = sum_k y[inv[t*K+k]] (no shared expert, model width).
+// out[t] = sum_k y[inv[t*K+k]] (+ add[t], the shared experts' fp32 output,
+// if given), at model width.
 hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int K, int width,
-                              void *out, int act_bf16, hipStream_t s);
+                              void *out, int act_bf16, hipStream_t s,
+                              const float *add = nullptr);
 // r[t] = RMSNorm(sum_k y[inv[t*K+k]]) * gamma (latent), or the plain sum.
 hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, int K, int L,
                                  int has_rmsnorm, float eps, const float *gamma, void *r,

@@ -369,30 +369,31 @@ __global__ __launch_bounds__(256) void qb_center_kernel(const float *q, int E, f
 // logsumexp(logits_t)^2. Both read the router's own logits x W^T (the balance
 // bias is a non-gradient nudge and stays out).
 //
-// Stage 1: one workgroup per 64 tokens (16 per wavefront, in token order);
+// Stage 1: one workgroup per 16 tokens (4 per wavefront, in token order);
 // each lane keeps the running softmax sums of the experts it owns; the four
 // wavefronts' sums are added in wavefront order. part[chunk] = {P sums [E],
 // sum of lse^2}. Stage 2 adds the chunks in chunk order in fp64.
-constexpr int kLossTokens = 64;
+constexpr int kLossTokens = 16;
 
+template <int PL>
 __global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, int parts,
                                                            int splits, int64_t ss, int64_t T,
                                                            int E, float *part) {
   __shared__ float sh[4][kMaxE + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t_begin = static_cast<int64_t>(blockIdx.x) * kLossTokens + wave * (kLossTokens / 4);
-  float acc[kPerLane];
+  float acc[PL];
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j) acc[j] = 0.f;
+  for (int j = 0; j < PL; ++j) acc[j] = 0.f;
   float zacc = 0.f;
   for (int i = 0; i < kLossTokens / 4; ++i) {
     const int64_t t = t_begin + i;
     if (t >= T) break;
     const float *lg = logits + t * static_cast<int64_t>(parts) * E;
-    float l[kPerLane];
+    float l[PL];
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
+    for (int j = 0; j < PL; ++j) {
       const int e = lane + 64 * j;
       l[j] = e < E ? logit_of(lg, e, E, parts, splits, ss) : -INFINITY;
       m = fmaxf(m, l[j]);
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, 
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     float z = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
+    for (int j = 0; j < PL; ++j) {
       l[j] = lane + 64 * j < E ? expf(l[j] - m) : 0.f;
       z += l[j];
     }
@@ -409,12 +410,12 @@ __global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, 
     for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
     const float rz = 1.0f / z;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) acc[j] += l[j] * rz;
+    for (int j = 0; j < PL; ++j) acc[j] += l[j] * rz;
     const float lse = m + logf(z);
     zacc += lse * lse;
   }
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j)
+  for (int j = 0; j < PL; ++j)
     if (lane + 64 * j < E) sh[wave][lane + 64 * j] = acc[j];
   if (lane == 0) sh[wave][E] = zacc;
   __syncthreads();
@@ -546,8 +547,15 @@ hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t
   int parts, splits;
   logit_layout(a, act_bf16, &parts, &splits);
   const int64_t chunks = router_loss_chunks(a.T);
-  loss_partial_kernel<<<static_cast<unsigned>(chunks), 256, 0, s>>>(
-      a.logits, parts, splits, a.T * parts * a.E, a.T, a.E, part);
+  const unsigned grid = static_cast<unsigned>(chunks);
+  const int64_t ss = a.T * parts * a.E;
+  if (a.E <= 64)
+    loss_partial_kernel<1><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, part);
+  else if (a.E <= 256)
+    loss_partial_kernel<4><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, part);
+  else
+    loss_partial_kernel<kPerLane><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E,
+                                                       part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   loss_final_kernel<<<1, 256, 0, s>>>(part, chunks, a.T, a.E, a.K, counts, alpha, z_weight,
                                       losses);

@@ -165,3 +165,21 @@ def test_router_losses_checked_before_launch():
     d0 = _desc(T=0)
     assert L.moe_router_losses(C.byref(d0), C.byref(w), None, fake, 0.01, 0.001, fake, fake,
                                moe.moe_workspace_size(d0), None) == 0
+
+
+def test_plan_paths_of_the_workloads():
+    """Host-side plan (no GPU): which kernel path and tile each benchmark
+    layer takes, so the parity cases can be tied to the paths they cover."""
+    P = {n: moe.moe_plan(moe.make_desc(moe_synth.get(n))) for n in
+         ("tiny", "small", "medium", "large_prefill", "large_decode", "latent")}
+    assert P["small"]["merged_shared"] == 1 and P["small"]["gate_up_pipelined"] == 1
+    assert P["small"]["router_per_token"] == 1 and P["small"]["dispatch_one_workgroup"] == 1
+    for n in ("medium", "large_prefill", "latent"):
+        assert P[n]["merged_shared"] == 0
+        assert (P[n]["gate_up_tile_m"], P[n]["gate_up_tile_n"]) == (256, 256)
+        assert P[n]["router_per_token"] == 0 and P[n]["dispatch_one_workgroup"] == 0
+    assert P["tiny"]["gate_up_pipelined"] == 0  # fp32: generic kernel
+    assert P["large_decode"]["gate_up_tile_m"] == 16 and P["large_decode"]["merged_shared"] == 0
+    assert P["large_decode"]["dispatch_one_workgroup"] == 1
+    with pytest.raises(moe.MoeError):
+        moe.moe_plan(_desc(T=-1))

@@ -65,7 +65,7 @@ def test_workload_route_and_forward(name):
 TAIL = {
     "tail_few": (dict(T=300, d=96, d_ff=160, E=4, K=2, act="bf16", n_shared=1, d_ff_shared=160,
                       w_std=0.05, router_std=0.05), None),
-    "tail_mid": (dict(T=4096, d=480, d_ff=800, E=4, K=2, act="bf16", n_shared=1,
+    "tail_mid": (dict(T=4096, d=1056, d_ff=800, E=4, K=2, act="bf16", n_shared=1,
                       d_ff_shared=800, w_std=0.03, router_std=0.03), 512),
     "tail_big": (dict(T=8192, d=480, d_ff=1056, E=4, K=2, act="bf16", n_shared=1,
                       d_ff_shared=1056, w_std=0.03, router_std=0.03), 384),
@@ -83,6 +83,12 @@ def test_pipelined_gemm_k_tail(name):
     r = check_route(w, a, layer, orc)
     toks = None if n is None else sample_tokens(r[0], w.E, n, seed=w.config_no)
     check_forward(w, a, layer, tokens=toks, orc=orc, o_route=r)
+    plan = moe.moe_plan(layer.desc)
+    say(f"  plan {plan}")
+    assert plan["gate_up_pipelined"] and plan["down_pipelined"]
+    # few tiles / merged 256x256 / separate 256x256
+    want = {"tail_few": (1, 64), "tail_mid": (1, 256), "tail_big": (0, 256)}[name]
+    assert (plan["merged_shared"], plan["gate_up_tile_m"]) == want
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
@@ -287,6 +293,32 @@ def test_probe_records_stage_events():
     layer.forward(layer.dev["x"], probe=probe)
     torch.cuda.synchronize()
     assert b.elapsed_time(e) > 0
+
+
+@pytest.mark.parametrize("stage,merged", [("expert_gate_up", 1), ("expert_down", 1),
+                                          ("expert_gate_up", 0), ("shared_gate_up", 0)])
+def test_probe_repeat_keeps_the_result(stage, merged):
+    """Repeated passes of a GEMM stage (timing aid) leave the output bitwise
+    unchanged, with the shared experts merged into the grouped launches
+    (small layer) or not (an expert width the pipelined kernel does not
+    take)."""
+    w = moe_synth.get("small").with_T(512) if merged else custom(
+        "probe_sep", T=300, d=64, d_ff=40, E=4, K=2, act="bf16", n_shared=1, d_ff_shared=64)
+    assert moe.moe_plan(moe.make_desc(w))["merged_shared"] == merged
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    ref = layer.forward(layer.dev["x"]).clone()
+    b = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    b.record()
+    e.record()
+    torch.cuda.synchronize()
+    probe = moe.MoeProbe(stage=moe.STAGES[stage], repeat=7, ev_begin=b.cuda_event,
+                         ev_end=e.cuda_event)
+    out = layer.forward(layer.dev["x"], probe=probe)
+    torch.cuda.synchronize()
+    assert b.elapsed_time(e) > 0
+    assert torch.equal(out, ref)
 
 
 # ---------------------------------------------------------------- balancer
