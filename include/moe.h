@@ -295,7 +295,8 @@ MOE_API int moe_quantile_balance(const moe_desc *desc, const moe_weights *w, con
  * counts: int32 [E] device array, the expert loads of the same T tokens (as
  * moe_forward / moe_dispatch return them). losses: fp32 [2] device array.
  * Any routing rule (the losses are defined on the softmax of the logits).
- * Sums are taken in a fixed order (per 16 tokens in fp32, then in fp64):
+ * Sums are taken in a fixed order (per chunk of 16 to 64 tokens in fp32, then
+ * over the chunks in fp64):
  * results are deterministic. Enqueued on stream, no host synchronisation.
  * T == 0 is a no-op (losses untouched). Errors: MOE_ERR_NULL, MOE_ERR_MODE
  * (alpha or z_weight not finite, or a bad descriptor), MOE_ERR_SHAPE,

@@ -58,9 +58,9 @@ Layout layout_of(const moe_desc *d) {
   L.inv = take(rows * 4);
   L.sw = take(rows * 4);
   L.max_tiles = grouped_tile_bound(rows, E, 16);  // smallest tile height in use
-  L.tiles = take(static_cast<size_t>(L.max_tiles) * 12);
+  L.tiles = take(static_cast<size_t>(L.max_tiles) * kTileInts * 4);
   L.ntiles = take(4);
-  L.tiles2 = take(static_cast<size_t>(L.max_tiles) * 12);
+  L.tiles2 = take(static_cast<size_t>(L.max_tiles) * kTileInts * 4);
   L.ntiles2 = take(4);
   L.ntie = take(4);
   L.z = d->latent ? take(T * d->latent * es) : 0;

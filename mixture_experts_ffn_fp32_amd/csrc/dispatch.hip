@@ -41,7 +41,10 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
 }
 
 // Fill the m-tile table of height bm from offsets held in LDS (1024 threads).
-// tile i = {expert, row_begin, row_end}; experts with no rows get no tile.
+// tile i = {expert, row_begin, row_end, group_first, group_size}; experts
+// with no rows get no tile. A group is a run of at most kTileGroup m-tiles
+// of one expert (the GEMMs schedule a group's tiles together so they share
+// the expert's weight slices in L2).
 __device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
                             int32_t *tiles, int32_t *n_tiles) {
   const int t = threadIdx.x;
@@ -60,9 +63,13 @@ __device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
     }
     const int e = lo;
     const int r0 = off[e] + (i - start[e]) * bm;
-    tiles[3 * i + 0] = e;
-    tiles[3 * i + 1] = r0;
-    tiles[3 * i + 2] = min(r0 + bm, off[e + 1]);
+    const int gfirst = start[e] + (i - start[e]) / kTileGroup * kTileGroup;
+    int32_t *ti = tiles + kTileInts * static_cast<int64_t>(i);
+    ti[0] = e;
+    ti[1] = r0;
+    ti[2] = min(r0 + bm, off[e + 1]);
+    ti[3] = gfirst;
+    ti[4] = min(kTileGroup, start[e + 1] - gfirst);
   }
   if (t == 0) *n_tiles = total;
 }
@@ -73,13 +80,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
   __shared__ int start[kMaxE + 1];
   const int t = threadIdx.x;
   const int64_t nch = n_chunks(a.slots);
-  // per expert: running prefix over chunks (relative), then total
+  // per expert: total over chunks, then each chunk's absolute base; the
+  // chunk counts are read kBatch at a time so their loads overlap (chunk_base
+  // may alias chunk_hist: each element is read before it is written)
+  constexpr int kBatch = 16;
   int cnt = 0;
   if (t < a.E) {
-    for (int64_t c = 0; c < nch; ++c) {
-      const int v = a.chunk_hist[c * a.E + t];
-      a.chunk_base[c * a.E + t] = cnt;
-      cnt += v;
+    for (int64_t c0 = 0; c0 < nch; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * a.E + t] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) cnt += v[j];
     }
   }
   int total;
@@ -88,7 +101,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
     off[t] = ex;
     a.counts[t] = cnt;
     a.offsets[t] = ex;
-    for (int64_t c = 0; c < nch; ++c) a.chunk_base[c * a.E + t] += ex;
+    int run = ex;
+    for (int64_t c0 = 0; c0 < nch; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * a.E + t] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (c0 + j < nch) {
+          a.chunk_base[(c0 + j) * a.E + t] = run;
+          run += v[j];
+        }
+    }
   }
   if (t == 0) {
     off[a.E] = total;
@@ -101,7 +126,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
   __syncthreads();
   if (a.gap && a.n_near_ties) {
     int n = 0;
-    for (int64_t i = t; i < a.T; i += 1024) n += (a.gap[i] < a.tie_eps) ? 1 : 0;
+    for (int64_t i0 = t; i0 < a.T; i0 += 1024 * kBatch) {
+      float gv[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t i = i0 + 1024 * j;
+        gv[j] = i < a.T ? a.gap[i] : INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) n += (gv[j] < a.tie_eps) ? 1 : 0;
+    }
     int tot;
     block_exscan_1024(n, tmp, &tot);
     if (t == 0) *a.n_near_ties = tot;

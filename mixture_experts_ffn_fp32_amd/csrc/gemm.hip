@@ -106,9 +106,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   const int nt = static_cast<int>(in_g / gsz);
   int64_t expert = 0, m_begin, m_end;
   if (p.tiles) {
-    expert = p.tiles[3 * mt];
-    m_begin = p.tiles[3 * mt + 1];
-    m_end = p.tiles[3 * mt + 2];
+    expert = p.tiles[kTileInts * mt];
+    m_begin = p.tiles[kTileInts * mt + 1];
+    m_end = p.tiles[kTileInts * mt + 2];
   } else {
     m_begin = mt * BM;
     m_end = min<int64_t>(m_begin + BM, p.M);

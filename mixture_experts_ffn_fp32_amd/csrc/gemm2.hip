@@ -134,8 +134,8 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // ------------------------------------------------------------ tile
   // Two problems may share the launch (p1.N == 0: none): the tiles of p0,
   // then those of p1. Consecutive workgroups go to different XCDs: give each
-  // XCD a contiguous range of tiles, grouped 4 m-tiles at a time so tiles
-  // sharing B or A run together.
+  // XCD a contiguous range of tiles, in groups of m-tiles that run together
+  // over all n-tiles so tiles sharing B or A meet in L2.
   const int n_tn0 = (p0.N + NOUT - 1) / NOUT;
   const int64_t n_m0 = p0.tiles ? static_cast<int64_t>(*p0.n_tiles) : p0.max_mtiles;
   const int64_t total0 = n_m0 * n_tn0;
@@ -152,18 +152,29 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   const int n_tn = second ? n_tn1 : n_tn0;
   const int64_t n_m = second ? n_m1 : n_m0;
   if (second) pid -= total0;
+  // groups of m-tiles: one expert's (from the table; a group of g m-tiles
+  // owns tiles [first n_tn, (first + g) n_tn), so pid / n_tn is one of its
+  // m-tiles) or GM consecutive ones (dense); inside a group the m-tile
+  // index runs fastest
   constexpr int GM = MOE_G2_GM;
-  const int64_t grp = pid / (GM * n_tn);
-  const int64_t first_m = grp * GM;
-  const int gsz = static_cast<int>(min<int64_t>(n_m - first_m, GM));
-  const int64_t in_g = pid - grp * GM * n_tn;
+  int64_t first_m;
+  int gsz;
+  if (p.tiles) {
+    const int64_t j = pid / n_tn;
+    first_m = __builtin_amdgcn_readfirstlane(p.tiles[kTileInts * j + 3]);
+    gsz = __builtin_amdgcn_readfirstlane(p.tiles[kTileInts * j + 4]);
+  } else {
+    first_m = pid / (GM * n_tn) * GM;
+    gsz = static_cast<int>(min<int64_t>(n_m - first_m, GM));
+  }
+  const int64_t in_g = pid - first_m * n_tn;
   const int64_t mt = first_m + in_g % gsz;
   const int nt = static_cast<int>(in_g / gsz);
   int64_t expert = 0, m_begin, m_end;
   if (p.tiles) {
-    expert = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt]);
-    m_begin = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt + 1]);
-    m_end = __builtin_amdgcn_readfirstlane(p.tiles[3 * mt + 2]);
+    expert = __builtin_amdgcn_readfirstlane(p.tiles[kTileInts * mt]);
+    m_begin = __builtin_amdgcn_readfirstlane(p.tiles[kTileInts * mt + 1]);
+    m_end = __builtin_amdgcn_readfirstlane(p.tiles[kTileInts * mt + 2]);
   } else {
     m_begin = mt * BM;
     m_end = min<int64_t>(m_begin + BM, p.M);

@@ -33,7 +33,7 @@ bool router_valu(const RouterArgs &a);
 hipError_t launch_quantile_balance(const RouterArgs &a, int act_bf16, float *diff, float *q,
                                    float *new_bias, hipStream_t s);
 // Router auxiliary losses (load-balancing loss and z-loss) of one step:
-// runs the router, then per-16-token partial sums into part
+// runs the router, then per-chunk (16 to 64 tokens) partial sums into part
 // [router_loss_chunks(T), E + 1] and the two losses into losses [2].
 hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t *counts,
                                 float alpha, float z_weight, float *part, float *losses,
@@ -56,6 +56,10 @@ inline size_t router_logit_bytes(int64_t T, int64_t E, int64_t d, int act_bf16) 
 }
 
 // ------------------------------------------------------------------ dispatch
+// Grouped-GEMM m-tile table entry: {expert, row_begin, row_end, group_first,
+// group_size}; a group is a run of at most kTileGroup m-tiles of one expert.
+constexpr int kTileInts = 5;
+constexpr int kTileGroup = 8;
 // Slots per histogram / scatter chunk.
 constexpr int kChunkSlots = 1024;
 
@@ -73,7 +77,7 @@ struct ScanArgs {
   int32_t *offsets;           // [E+1]
   // grouped GEMM m-tile tables for tile heights bm / bm2 (tiles null -> skipped)
   int bm;
-  int32_t *tiles;             // [max_tiles, 3] {expert, row_begin, row_end}
+  int32_t *tiles;             // [max_tiles, kTileInts] (see below)
   int32_t *n_tiles;           // [1]
   int bm2;
   int32_t *tiles2;

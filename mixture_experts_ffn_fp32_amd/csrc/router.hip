@@ -369,24 +369,26 @@ __global__ __launch_bounds__(256) void qb_center_kernel(const float *q, int E, f
 // logsumexp(logits_t)^2. Both read the router's own logits x W^T (the balance
 // bias is a non-gradient nudge and stays out).
 //
-// Stage 1: one workgroup per 16 tokens (4 per wavefront, in token order);
+// Stage 1: one workgroup per chunk of 16 to 64 tokens (a quarter per
+// wavefront, in token order; chunks sized so a call has about 256 of them);
 // each lane keeps the running softmax sums of the experts it owns; the four
 // wavefronts' sums are added in wavefront order. part[chunk] = {P sums [E],
 // sum of lse^2}. Stage 2 adds the chunks in chunk order in fp64.
-constexpr int kLossTokens = 16;
+constexpr int kLossMinTokens = 16, kLossMaxTokens = 64, kLossChunks = 256;
 
 template <int PL>
 __global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, int parts,
                                                            int splits, int64_t ss, int64_t T,
-                                                           int E, float *part) {
+                                                           int E, int chunk_tokens, float *part) {
   __shared__ float sh[4][kMaxE + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t_begin = static_cast<int64_t>(blockIdx.x) * kLossTokens + wave * (kLossTokens / 4);
+  const int per_wave = chunk_tokens / 4;
+  const int64_t t_begin = static_cast<int64_t>(blockIdx.x) * chunk_tokens + wave * per_wave;
   float acc[PL];
 #pragma unroll
   for (int j = 0; j < PL; ++j) acc[j] = 0.f;
   float zacc = 0.f;
-  for (int i = 0; i < kLossTokens / 4; ++i) {
+  for (int i = 0; i < per_wave; ++i) {
     const int64_t t = t_begin + i;
     if (t >= T) break;
     const float *lg = logits + t * static_cast<int64_t>(parts) * E;
@@ -433,9 +435,17 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const float *part, int6
                                                          float z_weight, float *losses) {
   __shared__ double sa[256], sz[256];
   double a = 0.0, zs = 0.0;
+  constexpr int kBatch = 16;  // chunk partials loaded together, added in order
   for (int e = threadIdx.x; e <= E; e += 256) {
     double s = 0.0;
-    for (int64_t c = 0; c < n_chunks; ++c) s += static_cast<double>(part[c * (E + 1) + e]);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < n_chunks ? part[(c0 + j) * (E + 1) + e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) s += static_cast<double>(v[j]);
+    }
     if (e < E)
       a += (static_cast<double>(counts[e]) / (static_cast<double>(T) * K)) * (s / static_cast<double>(T));
     else
@@ -536,7 +546,16 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t router_loss_chunks(int64_t T) { return (T + kLossTokens - 1) / kLossTokens; }
+// tokens per chunk: a multiple of 4 between 16 and 64, about T / 256
+int router_loss_chunk_tokens(int64_t T) {
+  int64_t c = (T / kLossChunks + 3) / 4 * 4;
+  return static_cast<int>(c < kLossMinTokens ? kLossMinTokens : (c > kLossMaxTokens ? kLossMaxTokens : c));
+}
+
+int64_t router_loss_chunks(int64_t T) {
+  const int ct = router_loss_chunk_tokens(T);
+  return (T + ct - 1) / ct;
+}
 
 hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t *counts,
                                 float alpha, float z_weight, float *part, float *losses,
@@ -548,14 +567,15 @@ hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t
   logit_layout(a, act_bf16, &parts, &splits);
   const int64_t chunks = router_loss_chunks(a.T);
   const unsigned grid = static_cast<unsigned>(chunks);
+  const int ct = router_loss_chunk_tokens(a.T);
   const int64_t ss = a.T * parts * a.E;
   if (a.E <= 64)
-    loss_partial_kernel<1><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, part);
+    loss_partial_kernel<1><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, ct, part);
   else if (a.E <= 256)
-    loss_partial_kernel<4><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, part);
+    loss_partial_kernel<4><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E, ct, part);
   else
     loss_partial_kernel<kPerLane><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E,
-                                                       part);
+                                                       ct, part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   loss_final_kernel<<<1, 256, 0, s>>>(part, chunks, a.T, a.E, a.K, counts, alpha, z_weight,
                                       losses);
