@@ -67,6 +67,8 @@ def lib():
         L.or_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P]
         L.or_quantile_balance.argtypes = [P, P, P]
         L.or_router_losses.argtypes = [P, P, P, C.c_double, C.c_double, P]
+        L.or_backward.argtypes = [P, P, P, P, C.c_int64, P, C.c_int32] + [P] * 8
+        L.or_backward.restype = C.c_int
         for f in ("or_route", "or_forward", "or_expert_rows", "or_combine", "or_dispatch"):
             getattr(L, f).restype = C.c_int
         L.or_silu.argtypes = [C.c_double]
@@ -177,6 +179,39 @@ class Oracle:
         _check(lib().or_router_losses(C.byref(self.layer), C.byref(self.tensors), _p(c),
                                       float(alpha), float(z_weight), _p(out)), "or_router_losses")
         return float(out[0]), float(out[1])
+
+    def backward(self, d_out, tokens=None, idx_override=None, experts="all",
+                 router=True, shared=True):
+        """Backward of the (non-latent) layer in fp64 for output gradients
+        d_out [n, d] of the listed tokens (all if None). Returns a dict: dx
+        [n, d]; w_router [E, d] (router=True); w_gate / w_up [E or 1, d_ff, d]
+        and w_down [E or 1, d, d_ff] for experts="all", one expert id, or None;
+        ws_gate / ws_up [d_shared, d], ws_down [d, d_shared] (shared=True).
+        Weight gradients are summed over the listed tokens only."""
+        sp = self.spec
+        t, n = self._tokens(tokens)
+        dy = np.ascontiguousarray(d_out, np.float64)
+        assert dy.shape == (n, sp.d)
+        ov = None if idx_override is None else np.ascontiguousarray(idx_override, np.int32)
+        want = -1 if experts == "all" else (-2 if experts is None else int(experts))
+        ne = sp.E if want == -1 else 1
+        out = {"dx": np.empty((n, sp.d))}
+        if router:
+            out["w_router"] = np.empty((sp.E, sp.d))
+        if want >= -1:
+            out["w_gate"] = np.empty((ne, sp.d_ff, sp.d))
+            out["w_up"] = np.empty((ne, sp.d_ff, sp.d))
+            out["w_down"] = np.empty((ne, sp.d, sp.d_ff))
+        if shared and sp.d_shared:
+            out["ws_gate"] = np.empty((sp.d_shared, sp.d))
+            out["ws_up"] = np.empty((sp.d_shared, sp.d))
+            out["ws_down"] = np.empty((sp.d, sp.d_shared))
+        g = out.get
+        _check(lib().or_backward(C.byref(self.layer), C.byref(self.tensors), _p(dy), _p(t), n,
+                                 _p(ov), want, _p(g("dx")), _p(g("w_router")), _p(g("w_gate")),
+                                 _p(g("w_up")), _p(g("w_down")), _p(g("ws_gate")),
+                                 _p(g("ws_up")), _p(g("ws_down"))), "or_backward")
+        return out
 
     def expert_rows(self, rows, expert, scale=None):
         """fp64 scale[p] * FFN_{expert[p]}(rows[p]) at the routed width."""

@@ -31,6 +31,13 @@
  * weights (it is part of the ranked logits) but not the sigmoid weights;
  * RMSNorm is R / sqrt(mean(R^2) + eps) * gamma.
  *
+ * The backward pass (or_backward) differentiates the same definition by
+ * hand: SiLU' = sigma (1 + x (1 - sigma)), the routing weights' Jacobians of
+ * the three rules, no gradient through the (piecewise constant) selection or
+ * into the balance bias; weight gradients reach only the experts that some
+ * token selected ("StableLatentMoE and QuantileBalancer": inactive experts
+ * get no gradient). Its pins are central finite differences of the forward.
+ *
  * Parity pins live in the test suite: the SiLU table of section 12.3, the
  * derivable part of the section 12.5 worked example, the router example of
  * section 13.5, the dispatch example of the StableLatentMoE page, closed-form
@@ -514,5 +521,180 @@ int or_router_losses(const or_layer *L, const or_tensors *W, const int32_t *coun
   free(r);
   free(xv);
   free(psum);
+  return 0;
+}
+
+/* ------------------------------------------------------------ backward */
+
+/* Gradient of the routing weights g[K] of one token with respect to its
+ * router logits r = x W_router^T (the balance bias is a fixed input and
+ * gets none; the selection is piecewise constant, so it passes no gradient).
+ * Weight rules as in route_one:
+ *  - softmax over the selected (Math. Reference Part 3, 13.2) and the
+ *    moe-from-scratch rule (softmax over all, top-K, renormalised: the same
+ *    function of the selected logits): g_k = c q_k, q = softmax over the
+ *    selected of r + b, c = routed_scale, so dr_k = q_k (c dg_k - sum_j q_j c dg_j);
+ *  - sigmoid rule (StableLatentMoE): g_k = c s_k, or c s_k / sum_j s_j when
+ *    renormalised, s = sigmoid(r), ds/dr = s (1 - s).
+ * dr[E] is zero outside the selection. */
+static void route_grad(const or_layer *L, const or_tensors *W, const double *xv,
+                       const int32_t *sel, const double *dg, double *dr) {
+  const int E = L->E, K = L->K, d = L->d;
+  const double c = L->routed_scale;
+  for (int e = 0; e < E; ++e) dr[e] = 0.0;
+  double *r = (double *)malloc(sizeof(double) * (size_t)K);
+  for (int k = 0; k < K; ++k) {
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) s += (double)W->w_router[(int64_t)sel[k] * d + i] * xv[i];
+    r[k] = s;
+  }
+  if (L->route == OR_ROUTE_SIGMOID_BIAS) {
+    double S = 0.0, sdg = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double s = or_sigmoid(r[k]);
+      S += s;
+      sdg += dg[k] * s;
+    }
+    for (int k = 0; k < K; ++k) {
+      const double s = or_sigmoid(r[k]);
+      const double ds = L->renormalize ? c * (dg[k] / S - sdg / (S * S)) : c * dg[k];
+      dr[sel[k]] += ds * s * (1.0 - s);
+    }
+  } else {
+    double m = -INFINITY, z = 0.0, qdg = 0.0;
+    double *q = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int k = 0; k < K; ++k) {
+      q[k] = r[k] + (W->bias ? (double)W->bias[sel[k]] : 0.0);
+      m = q[k] > m ? q[k] : m;
+    }
+    for (int k = 0; k < K; ++k) { q[k] = exp(q[k] - m); z += q[k]; }
+    for (int k = 0; k < K; ++k) { q[k] /= z; qdg += q[k] * c * dg[k]; }
+    for (int k = 0; k < K; ++k) dr[sel[k]] += q[k] * (c * dg[k] - qdg);
+    free(q);
+  }
+  free(r);
+}
+
+/* Backward of one SwiGLU FFN (Math. Reference Part 3, 12.2) on input v[n]
+ * with output gradient dy[n] scaled by w (the routing weight; 1 for shared
+ * experts): y = W_down h, h = SiLU(a) * u, a = W_gate v, u = W_up v,
+ * SiLU'(a) = sigmoid(a) (1 + a (1 - sigmoid(a))). Adds the input gradient to
+ * dv and the weight gradients to dwg / dwu [f, n] and dwd [n, f] (any may be
+ * NULL); returns <dy, y> (the gradient of the routing weight). */
+static double swiglu_backward(const void *wg, const void *wu, const void *wd, int act,
+                              int64_t base_gu, int64_t base_d, int n, int f, const double *v,
+                              const double *dy, double w, double *dv, double *dwg, double *dwu,
+                              double *dwd, double *buf) {
+  double *a = buf, *u = buf + f, *h = buf + 2 * f, *dh = buf + 3 * f;
+  for (int j = 0; j < f; ++j) {
+    a[j] = dot(wg, act, base_gu + (int64_t)j * n, v, n);
+    u[j] = dot(wu, act, base_gu + (int64_t)j * n, v, n);
+    h[j] = or_silu(a[j]) * u[j];
+  }
+  double dg = 0.0;
+  for (int i = 0; i < n; ++i) dg += dy[i] * dot(wd, act, base_d + (int64_t)i * f, h, f);
+  for (int j = 0; j < f; ++j) {
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += ld(wd, act, base_d + (int64_t)i * f + j) * w * dy[i];
+    dh[j] = s;
+  }
+  if (dwd)
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < f; ++j) dwd[(int64_t)i * f + j] += w * dy[i] * h[j];
+  for (int j = 0; j < f; ++j) {
+    const double sg = or_sigmoid(a[j]);
+    const double da = dh[j] * u[j] * sg * (1.0 + a[j] * (1.0 - sg));
+    const double du = dh[j] * or_silu(a[j]);
+    for (int i = 0; i < n; ++i) {
+      dv[i] += ld(wg, act, base_gu + (int64_t)j * n + i) * da +
+               ld(wu, act, base_gu + (int64_t)j * n + i) * du;
+      if (dwg) dwg[(int64_t)j * n + i] += da * v[i];
+      if (dwu) dwu[(int64_t)j * n + i] += du * v[i];
+    }
+  }
+  return dg;
+}
+
+/* Backward of the layer (non-latent) for the listed tokens (all if NULL)
+ * with output gradients d_out[n, d] (row j belongs to token tokens[j]):
+ *  - dx[n, d] (may be NULL): input gradients (routed experts, shared
+ *    experts, router);
+ *  - dw_router[E, d] (may be NULL);
+ *  - expert weight gradients summed over the listed tokens: for every
+ *    expert if want_expert == -1 (dw_gate / dw_up [E, d_ff, d], dw_down
+ *    [E, d, d_ff]), for expert want_expert only (one expert's shape), or
+ *    none if want_expert < -1 (the three may also be NULL);
+ *  - dws_gate / dws_up [d_shared, d], dws_down [d, d_shared] (may be NULL).
+ * Gradient outputs are zeroed first. Experts no listed token selects keep
+ * zero gradients. idx_override [n, K] replaces the selection (near ties).
+ * Tokens run in parallel when no weight gradient is requested. */
+int or_backward(const or_layer *L, const or_tensors *W, const double *d_out,
+                const int64_t *tokens, int64_t n, const int32_t *idx_override,
+                int32_t want_expert, double *dx, double *dw_router, double *dw_gate,
+                double *dw_up, double *dw_down, double *dws_gate, double *dws_up,
+                double *dws_down) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->latent) return -3;
+  const int d = L->d, f = L->d_ff, E = L->E, K = L->K, ds = L->d_shared;
+  const int64_t egu = (int64_t)f * d;
+  const int want_w = want_expert >= -1 && (dw_gate || dw_up || dw_down);
+  const int serial = want_w || dw_router || dws_gate || dws_up || dws_down;
+  if (dx) memset(dx, 0, sizeof(double) * (size_t)(n * d));
+  if (dw_router) memset(dw_router, 0, sizeof(double) * (size_t)E * d);
+  const int64_t n_exp = want_expert == -1 ? E : 1;
+  if (want_w) {
+    if (dw_gate) memset(dw_gate, 0, sizeof(double) * (size_t)(n_exp * egu));
+    if (dw_up) memset(dw_up, 0, sizeof(double) * (size_t)(n_exp * egu));
+    if (dw_down) memset(dw_down, 0, sizeof(double) * (size_t)(n_exp * egu));
+  }
+  if (ds > 0) {
+    if (dws_gate) memset(dws_gate, 0, sizeof(double) * (size_t)ds * d);
+    if (dws_up) memset(dws_up, 0, sizeof(double) * (size_t)ds * d);
+    if (dws_down) memset(dws_down, 0, sizeof(double) * (size_t)ds * d);
+  }
+#pragma omp parallel for schedule(dynamic, 1) if (!serial)
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t t = tokens ? tokens[j] : j;
+    const int fm = f > ds ? f : ds;
+    double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dv = (double *)calloc((size_t)d, sizeof(double));
+    double *buf = (double *)malloc(sizeof(double) * (size_t)(4 * (fm > 0 ? fm : 1)));
+    double *g = (double *)malloc(sizeof(double) * (size_t)K * 2);
+    double *dg = g + K;
+    double *dr = (double *)malloc(sizeof(double) * (size_t)E);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    double gap;
+    const double *dy = d_out + j * d;
+    load_row(W->x, L->act, t, d, xv);
+    route_one(L, W, xv, idx_override ? idx_override + j * K : NULL, idx, g, &gap, NULL);
+    for (int k = 0; k < K; ++k) {
+      const int64_t e = idx[k];
+      const int mine = want_w && (want_expert == -1 || want_expert == e);
+      const int64_t wo = want_expert == -1 ? e * egu : 0;
+      dg[k] = swiglu_backward(W->w_gate, W->w_up, W->w_down, L->act, e * egu, e * egu, d, f, xv,
+                              dy, g[k], dv, mine && dw_gate ? dw_gate + wo : NULL,
+                              mine && dw_up ? dw_up + wo : NULL,
+                              mine && dw_down ? dw_down + wo : NULL, buf);
+    }
+    if (ds > 0)
+      swiglu_backward(W->ws_gate, W->ws_up, W->ws_down, L->act, 0, 0, d, ds, xv, dy, 1.0, dv,
+                      dws_gate, dws_up, dws_down, buf);
+    route_grad(L, W, xv, idx, dg, dr);
+    for (int e = 0; e < E; ++e) {
+      if (dr[e] == 0.0) continue;
+      for (int i = 0; i < d; ++i) {
+        dv[i] += (double)W->w_router[(int64_t)e * d + i] * dr[e];
+        if (dw_router) dw_router[(int64_t)e * d + i] += dr[e] * xv[i];
+      }
+    }
+    if (dx) memcpy(dx + j * d, dv, sizeof(double) * (size_t)d);
+    free(idx);
+    free(dr);
+    free(g);
+    free(buf);
+    free(dv);
+    free(xv);
+  }
   return 0;
 }

@@ -669,3 +669,93 @@ def test_router_losses_uniform_closed_form():
     aux, z = oracle.Oracle(w, a).router_losses(counts, 0.01, 0.001)
     assert abs(aux - 0.01) < 1e-15
     assert abs(z - 0.001 * math.log(E) ** 2) < 1e-15
+
+
+# ---------------------------------------------------------------- backward
+# The oracle's backward is pinned by central finite differences of its own
+# (already pinned) forward pass: L(theta) = sum_t <c_t, y_t(theta)>, and
+# (L(theta + hV) - L(theta - hV)) / 2h must equal <dL/dtheta, V> along random
+# directions V of every input and weight. All tensors sit on a 2^-8 grid and
+# h V on a 2^-12 grid, so theta +- hV is exact in fp32: the difference sees
+# only the function, and its O(h^2) error is far below the tolerance.
+_FD_H = 2.0 ** -10
+_FD_KEYS = ("x", "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+
+
+def _fd_layer(route, seed, renorm=False, scale=1.0, E=5, K=2, T=6):
+    w = custom(f"fd_{route}_{seed}", config_no=800 + seed, T=T, d=8, d_ff=6, E=E, K=K,
+               n_shared=1, d_ff_shared=4, act="f32", route=route, renormalize=renorm,
+               routed_scale=scale, bias_std=0.2 if route != "softmax_topk" else 0.0)
+    a = moe_synth.generate(w)
+    for k in _FD_KEYS + ("bias",):
+        if a.get(k) is not None:
+            a[k] = (np.round(np.asarray(a[k], np.float64) * 256) / 256).astype(np.float32)
+    return w, a
+
+
+def _fd_loss(w, a, c):
+    out, idx, _, _ = oracle.Oracle(w, a).forward()
+    return float(np.sum(out * c)), idx
+
+
+@pytest.mark.parametrize("route,renorm,scale,seed", [
+    ("topk_softmax", False, 1.0, 1), ("topk_softmax", False, 1.0, 2),
+    ("softmax_topk", False, 1.0, 3), ("sigmoid_bias", False, 1.0, 4),
+    ("sigmoid_bias", True, 2.5, 5), ("topk_softmax", False, 1.0, 6),
+])
+def test_backward_matches_finite_differences(route, renorm, scale, seed):
+    w, a = _fd_layer(route, seed, renorm, scale, K=5 if seed == 6 else 2)
+    rng = np.random.default_rng(seed)
+    c = np.round(rng.standard_normal((w.T, w.d)) * 256) / 256
+    grads = oracle.Oracle(w, a).backward(c)
+    gmap = {"x": grads["dx"], "w_router": grads["w_router"], "w_gate": grads["w_gate"],
+            "w_up": grads["w_up"], "w_down": grads["w_down"], "ws_gate": grads["ws_gate"],
+            "ws_up": grads["ws_up"], "ws_down": grads["ws_down"]}
+    _, idx0 = _fd_loss(w, a, c)
+    for key in _FD_KEYS:
+        V = rng.integers(-1, 2, size=np.shape(a[key])).astype(np.float64) / 4
+        ap, am = dict(a), dict(a)
+        ap[key] = (np.asarray(a[key], np.float64) + _FD_H * V).astype(np.float32)
+        am[key] = (np.asarray(a[key], np.float64) - _FD_H * V).astype(np.float32)
+        assert np.array_equal(np.asarray(ap[key], np.float64) - a[key], _FD_H * V)  # exact
+        lp, ip = _fd_loss(w, ap, c)
+        lm, im = _fd_loss(w, am, c)
+        assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "selection moved"
+        fd = (lp - lm) / (2 * _FD_H)
+        an = float(np.sum(gmap[key] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, fd, an)
+
+
+def test_backward_inactive_experts_get_no_gradient():
+    """Only experts some token selects receive weight gradients (the
+    StableLatentMoE page: inactive experts' gradients stay unset)."""
+    w, a = _fd_layer("topk_softmax", 7, E=6, K=1, T=3)
+    c = np.ones((w.T, w.d))
+    g = oracle.Oracle(w, a).backward(c)
+    idx, _, _, _ = oracle.Oracle(w, a).route()
+    used = set(idx.ravel().tolist())
+    assert len(used) < w.E
+    for e in range(w.E):
+        nz = np.abs(g["w_gate"][e]).sum() + np.abs(g["w_up"][e]).sum() + np.abs(g["w_down"][e]).sum()
+        assert (nz > 0) == (e in used)
+        if e not in used:  # the router's logit of an unselected expert gets none either
+            assert not np.any(g["w_router"][e])
+
+
+def test_backward_token_subsets_and_single_expert():
+    """Per-token input gradients do not depend on the other tokens; one
+    expert's weight gradient over its tokens equals its slice of the full one."""
+    w, a = _fd_layer("sigmoid_bias", 8, E=5, K=2, T=9)
+    rng = np.random.default_rng(8)
+    c = rng.standard_normal((w.T, w.d))
+    orc = oracle.Oracle(w, a)
+    full = orc.backward(c)
+    toks = np.array([7, 2, 4])
+    sub = orc.backward(c[toks], tokens=toks, experts=None, router=False, shared=False)
+    assert np.allclose(sub["dx"], full["dx"][toks], rtol=0, atol=1e-13)
+    idx, _, _, _ = orc.route()
+    e = int(idx[0, 0])
+    mine = np.nonzero((idx == e).any(1))[0]
+    one = orc.backward(c[mine], tokens=mine, experts=e, router=False, shared=False)
+    for k in ("w_gate", "w_up", "w_down"):
+        assert np.allclose(one[k][0], full[k][e], rtol=0, atol=1e-12)
