@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass timing (bf16 non-latent layers)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -238,6 +240,34 @@ def main():
     rl = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E,
           "load_balancing_loss": round(float(losses[0]), 7),
           "z_loss": round(float(losses[1]), 7)}
+    # backward pass (bf16 layers without the latent projection): input and all
+    # weight gradients for an output gradient of ones
+    bwd = None
+    if not args.no_backward and w.act == "bf16" and not w.latent:
+        dy = torch.ones((w.T, w.d), dtype=layer.act, device=dev)
+        shapes = {"w_router": (w.E, w.d), "w_gate": (w.E, w.d_ff, w.d),
+                  "w_up": (w.E, w.d_ff, w.d), "w_down": (w.E, w.d, w.d_ff)}
+        if w.d_shared:
+            shapes.update(ws_gate=(w.d_shared, w.d), ws_up=(w.d_shared, w.d),
+                          ws_down=(w.d, w.d_shared))
+        grads = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+        d_x = torch.empty_like(x)
+        layer.backward(x, dy, d_x=d_x, grads=grads, stream=stream)
+        b_ev.record(stream)
+        for _ in range(3):
+            layer.backward(x, dy, d_x=d_x, grads=grads, stream=stream)
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        bms = b_ev.elapsed_time(e_ev) / 3
+        # routed + shared: forward gate/up recomputed, d(h), d(x), 3 weight gradients
+        fl = 2.0 * (w.T * w.K * w.d * w.d_ff + w.T * w.d * w.d_shared) * (2 + 1 + 2 + 3)
+        bwd = {"ms_per_call": round(bms, 4), "tokens_per_s": round(w.T / (bms / 1e3), 1),
+               "tflops": round(fl / (bms / 1e3) / 1e12, 2),
+               "note": "moe_backward: input, router, expert and shared weight gradients "
+                       "(routing recomputed), output gradient of ones"}
+        del grads, d_x, dy
+        layer.ws_bwd = None
+        torch.cuda.empty_cache()
     tok_s = w.T / (ms / 1e3)
     peak_tf = PEAK[w.act]
     intensity = alg["gu_flops"] / alg["gu_bytes"]
@@ -293,6 +323,7 @@ def main():
                          "note": "one bias-based balancer step, back-to-back launches"},
         "quantile_balance": qb,
         "router_losses": rl,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

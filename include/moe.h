@@ -258,6 +258,45 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream);
 
+/* Gradients of the layer's parameters (fp32 DEVICE arrays, caller-owned; a
+ * NULL member is not computed). Shapes as in moe_weights. */
+typedef struct moe_grads {
+  float *w_router;        /* [E, d_model]                              */
+  float *w_gate, *w_up;   /* [E, d_ff, d_model]                        */
+  float *w_down;          /* [E, d_model, d_ff]                        */
+  float *ws_gate, *ws_up; /* [d_shared, d_model]                       */
+  float *ws_down;         /* [d_model, d_shared]                       */
+} moe_grads;
+
+/* Device workspace, in bytes, that moe_backward needs for this layer (more
+ * than moe_workspace_size: transposed weights of the experts and per-row
+ * gradients). Errors as moe_backward's shape/mode checks. */
+MOE_API int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
+
+/* Backward pass of the layer for an output gradient d_out [T, d_model] (act
+ * dtype): the gradient of sum_t <d_out[t], MoE(x)[t]> with respect to x
+ * (d_x [T, d_model], act dtype; NULL: not computed) and to the weights
+ * (grads, fp32). The forward's routing and dispatch are recomputed from x
+ * (nothing is kept from a forward call). Rules ("StableLatentMoE and
+ * QuantileBalancer": gradients flow only into active experts):
+ *  - the top-K selection is piecewise constant and passes no gradient; the
+ *    routing weights pass theirs to the router logits (softmax over the
+ *    selected, or sigmoid, as routed) and so to W_router and x; the balance
+ *    bias gets none;
+ *  - experts that no token selects get no weight gradient: their slices of
+ *    grads->w_gate / w_up / w_down are left untouched; every other requested
+ *    array is overwritten (not accumulated);
+ *  - intermediate products are bf16 operands with fp32 accumulation, like
+ *    the forward; router gradients are fp32.
+ * Supported: bf16 layers without the latent projection, d_model, d_ff and
+ * d_shared multiples of 32. Errors: MOE_ERR_MODE (fp32 or latent layers),
+ * MOE_ERR_SHAPE (other widths, or operands beyond 4 GiB), MOE_ERR_NULL,
+ * MOE_ERR_WORKSPACE (below moe_backward_workspace_size), MOE_ERR_HIP.
+ * T == 0 is a no-op. */
+MOE_API int moe_backward(const moe_desc *desc, const moe_weights *w, const void *x,
+                         const void *d_out, void *d_x, const moe_grads *grads, void *ws,
+                         size_t ws_bytes, void *stream);
+
 /* The kernel plan moe_forward uses for this layer (it depends on the
  * descriptor only). Errors: a bad descriptor, MOE_ERR_NULL. */
 MOE_API int moe_plan(const moe_desc *desc, moe_plan_info *info);

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
-           "moe_balance_bias", "moe_router_losses", "moe_plan")
+           "moe_balance_bias", "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
+           "moe_backward")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -51,6 +52,11 @@ class MoePlanInfo(C.Structure):
         "dispatch_one_workgroup")]
 
 
+class MoeGrads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+
+
 class MoeProbe(C.Structure):
     _fields_ = [("stage", C.c_int32), ("repeat", C.c_int32), ("ev_begin", C.c_void_p),
                 ("ev_end", C.c_void_p)]
@@ -82,9 +88,12 @@ def lib():
         L.moe_quantile_balance.argtypes = [P, P, P, P, P, S, P]
         L.moe_router_losses.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, S, P]
         L.moe_plan.argtypes = [P, P]
+        L.moe_backward_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
+        L.moe_backward.argtypes = [P, P, P, P, P, P, P, S, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                   "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance",
-                  "moe_router_losses", "moe_plan"):
+                  "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
+                  "moe_backward"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -135,6 +144,22 @@ def moe_plan(desc: MoeDesc) -> dict:
     info = MoePlanInfo()
     _ok(lib().moe_plan(C.byref(desc), C.byref(info)), "moe_plan")
     return {n: int(getattr(info, n)) for n, _ in MoePlanInfo._fields_}
+
+
+def moe_backward_workspace_size(desc: MoeDesc) -> int:
+    n = C.c_size_t(0)
+    _ok(lib().moe_backward_workspace_size(C.byref(desc), C.byref(n)),
+        "moe_backward_workspace_size")
+    return n.value
+
+
+def moe_backward(desc, weights, x, d_out, d_x, grads: dict, ws, stream=None):
+    """Backward of the layer: d_x (act dtype) and fp32 weight gradients into
+    the device tensors of `grads` (keys as MoeGrads; missing keys are not
+    computed)."""
+    g = MoeGrads(**{k: _ptr(grads.get(k)) for k, _ in MoeGrads._fields_})
+    _ok(lib().moe_backward(C.byref(desc), C.byref(weights), _ptr(x), _ptr(d_out), _ptr(d_x),
+                           C.byref(g), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_backward")
 
 
 def moe_workspace_size(desc: MoeDesc) -> int:
@@ -241,3 +266,15 @@ class Layer:
             out = torch.empty((self.spec.T, self.spec.d), dtype=self.act, device=self.device)
         moe_forward(self.desc, self.weights, x, out, counts, n_near_ties, self.ws, probe, stream)
         return out
+
+    def backward(self, x, d_out, d_x=None, grads=None, stream=None):
+        """moe_backward with a workspace of its own (allocated on first use);
+        grads: dict of fp32 device tensors to fill (keys as MoeGrads)."""
+        import torch
+        if getattr(self, "ws_bwd", None) is None:
+            self.ws_bwd = torch.empty(max(1, moe_backward_workspace_size(self.desc)),
+                                      dtype=torch.uint8, device=self.device)
+        if d_x is None:
+            d_x = torch.empty((self.spec.T, self.spec.d), dtype=self.act, device=self.device)
+        moe_backward(self.desc, self.weights, x, d_out, d_x, grads or {}, self.ws_bwd, stream)
+        return d_x

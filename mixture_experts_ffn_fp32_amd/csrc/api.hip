@@ -163,10 +163,10 @@ struct Probe {
   const moe_probe *p;
   hipStream_t s;
   void begin(int stage) const {
-    if (p && p->stage == stage) hipEventRecord(static_cast<hipEvent_t>(p->ev_begin), s);
+    if (p && p->stage == stage) (void)hipEventRecord(static_cast<hipEvent_t>(p->ev_begin), s);
   }
   void end(int stage) const {
-    if (p && p->stage == stage) hipEventRecord(static_cast<hipEvent_t>(p->ev_end), s);
+    if (p && p->stage == stage) (void)hipEventRecord(static_cast<hipEvent_t>(p->ev_end), s);
   }
   // passes of a GEMM stage to enqueue (repeat > 1 on the probed stage only)
   int reps(int stage) const {
@@ -397,6 +397,92 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
   pr.begin(MOE_STAGE_COMBINE);
   MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, 1, s, static_cast<const float *>(sh)));
   pr.end(MOE_STAGE_COMBINE);
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ backward
+// Workspace of moe_backward beyond the forward layout: transposed weights of
+// the active experts, per-row fp32 pre-activations and gradients, and the
+// activations in expert-contiguous, 64-padded columns for the K-grouped
+// weight-gradient GEMMs.
+struct BwdLayout {
+  size_t poff, kt1, kn1, kt2, kn2, tiles, ntiles;
+  size_t wguT, wdT, wsguT, wsdT;
+  size_t apre, upre, dhu, h, dau, dg, dr, dxs;
+  size_t apre_s, upre_s, dhu_s, h_s, dau_s, dxsh;
+  size_t cols, cols_bytes;  // contiguous block of transposed activations (zeroed)
+  size_t xsT, dysT, daT, duT, hT, xT, dyT, dashT, dushT, hshT;
+  size_t total;
+  int64_t RP, TP, kt_cap;
+};
+
+BwdLayout bwd_layout_of(const moe_desc *d) {
+  BwdLayout B{};
+  const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
+  const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared;
+  size_t o = layout_of(d).total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  B.RP = rows + 64 * E;        // padded expert columns (upper bound)
+  B.TP = (T + 63) / 64 * 64;
+  B.kt_cap = E * ((f > dm ? f : dm) + 63) / 64 + 1;
+  B.poff = take((E + 1) * 4);
+  B.kt1 = take(B.kt_cap * kTileInts * 4);
+  B.kn1 = take(4);
+  B.kt2 = take(B.kt_cap * kTileInts * 4);
+  B.kn2 = take(4);
+  B.tiles = take(static_cast<size_t>(grouped_tile_bound(rows, E, 64)) * kTileInts * 4);
+  B.ntiles = take(4);
+  B.wguT = take(E * dm * 2 * f * 2);  // [E, d, 2 f]: W_gate^T | W_up^T
+  B.wdT = take(E * f * dm * 2);       // [E, f, d]
+  B.wsguT = take(dm * 2 * ds * 2);
+  B.wsdT = take(ds * dm * 2);
+  B.apre = take(rows * f * 4);
+  B.upre = take(rows * f * 4);
+  B.dhu = take(rows * f * 4);
+  B.h = take(rows * f * 2);
+  B.dau = take(rows * 2 * f * 2);
+  B.dg = take(rows * 4);
+  B.dr = take(rows * 4);
+  B.dxs = take(rows * dm * 4);
+  B.apre_s = take(T * ds * 4);
+  B.upre_s = take(T * ds * 4);
+  B.dhu_s = take(T * ds * 4);
+  B.h_s = take(T * ds * 2);
+  B.dau_s = take(T * 2 * ds * 2);
+  B.dxsh = take(T * dm * 4);
+  B.cols = o;
+  B.xsT = take(dm * B.RP * 2);
+  B.dysT = take(dm * B.RP * 2);
+  B.daT = take(f * B.RP * 2);
+  B.duT = take(f * B.RP * 2);
+  B.hT = take(f * B.RP * 2);
+  B.xT = take(dm * B.TP * 2);
+  B.dyT = take(dm * B.TP * 2);
+  B.dashT = take(ds * B.TP * 2);
+  B.dushT = take(ds * B.TP * 2);
+  B.hshT = take(ds * B.TP * 2);
+  B.cols_bytes = o - B.cols;
+  B.total = o;
+  return B;
+}
+
+int check_backward(const moe_desc *d) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->act_dtype != MOE_BF16 || d->latent) return MOE_ERR_MODE;
+  if (d->d_model % 32 || d->d_ff % 32 || d->d_shared % 32) return MOE_ERR_SHAPE;
+  constexpr int64_t kLim = int64_t(1) << 32;  // 32-bit operand offsets of the GEMMs
+  const int64_t T = d->T, rows = T * d->top_k, E = d->n_experts;
+  const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared;
+  const int64_t RP = rows + 64 * E, mx = (dm > f ? dm : f) + 256;
+  if (T * dm * 2 >= kLim || rows * 2 * f * 2 >= kLim || mx * RP * 2 >= kLim ||
+      (f + 256) * 2 * f * 2 >= kLim || mx * 2 * (ds > f ? ds : f) * 2 >= kLim ||
+      T * 2 * ds * 2 >= kLim || mx * ((T + 63) / 64 * 64) * 2 >= kLim)
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -736,6 +822,263 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
   if ((rc = expert_gemms(d, w, rsrc, stok, tb, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
     return rc;
   return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
+}
+
+int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes) {
+  const int rc = check_backward(desc);
+  if (rc) return rc;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = bwd_layout_of(desc).total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const void *d_out,
+                 void *d_x, const moe_grads *gr, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_backward(d);
+  if (rc) return rc;
+  if (!w || !w->w_router || !gr) return MOE_ERR_NULL;
+  if ((rc = check_expert_weights(d, w)) || (rc = check_combine_weights(d, w))) return rc;
+  if (!ws || (d->T > 0 && (!x || !d_out))) return MOE_ERR_NULL;
+  const BwdLayout B = bwd_layout_of(d);
+  if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  const Layout L = layout_of(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *wsb = static_cast<char *>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float *>(wsb + off); };
+  auto I = [&](size_t off) { return reinterpret_cast<int32_t *>(wsb + off); };
+  const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
+  const int dm = d->d_model, f = d->d_ff, ds = d->d_shared;
+  int32_t *idx = I(L.idx), *counts = I(L.counts), *offsets = I(L.offsets);
+  int32_t *stok = I(L.stok), *inv = I(L.inv);
+  float *sw = F(L.sw);
+
+  // 1. the forward's routing and dispatch (the selection defines the graph)
+  RouterArgs ra{};
+  ra.x = x;
+  ra.w = w->w_router;
+  ra.w_split = wsb + L.wsplit;
+  ra.logits = F(L.logits);
+  ra.bias = w->bias;
+  ra.T = T;
+  ra.d = dm;
+  ra.E = static_cast<int>(E);
+  ra.K = static_cast<int>(K);
+  ra.mode = d->route_mode;
+  ra.renormalize = d->renormalize;
+  ra.routed_scale = d->routed_scale;
+  ra.idx = idx;
+  ra.g = F(L.g);
+  ra.gap = F(L.gap);
+  MOE_TRY(launch_router(ra, 1, s));
+  ScanArgs sa{};
+  sa.chunk_hist = I(L.chunk);
+  sa.chunk_base = I(L.chunk);
+  sa.slots = rows;
+  sa.E = static_cast<int>(E);
+  sa.counts = counts;
+  sa.offsets = offsets;
+  ScatterArgs sc{};
+  sc.idx = idx;
+  sc.g = ra.g;
+  sc.chunk_base = I(L.chunk);
+  sc.slots = rows;
+  sc.K = static_cast<int>(K);
+  sc.E = static_cast<int>(E);
+  sc.perm = I(L.perm);
+  sc.sorted_token = stok;
+  sc.inv = inv;
+  sc.sorted_w = sw;
+  MOE_TRY(run_dispatch(sa, sc, s));
+  const int cfg = gemm2_pick(rows, E, dm, f, 0, rows, f);
+  const int bm = gemm2_bm(cfg);
+  MOE_TRY(launch_tiles(offsets, static_cast<int>(E), bm, I(B.tiles), I(B.ntiles), s));
+  const int64_t mt_bound = grouped_tile_bound(rows, E, bm);
+
+  // 2. transposed weights of the active experts (and the shared FFN)
+  MOE_TRY(launch_transpose(w->w_gate, E, f, dm, counts, wsb + B.wguT, 2 * f, dm * 2 * f, 0, s));
+  MOE_TRY(launch_transpose(w->w_up, E, f, dm, counts, wsb + B.wguT, 2 * f, dm * 2 * f, f, s));
+  MOE_TRY(launch_transpose(w->w_down, E, dm, f, counts, wsb + B.wdT, dm, f * dm, 0, s));
+  if (ds) {
+    MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, s));
+    MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, s));
+    MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, s));
+  }
+
+  // grouped GEMM over the sorted rows (tile table of this call)
+  auto grouped = [&](const void *a, int64_t lda, const int32_t *a_rows, int64_t a_extent,
+                     const void *b, int64_t ldb, int64_t b_stride, int Kd, int N, void *out,
+                     int64_t ldo) {
+    GemmArgs g{};
+    g.a = a;
+    g.lda = lda;
+    g.a_rows = a_rows;
+    g.a_extent = a_extent;
+    g.b0 = b;
+    g.ldb = ldb;
+    g.b_stride = b_stride;
+    g.K = Kd;
+    g.N = N;
+    g.M = rows;
+    g.tiles = I(B.tiles);
+    g.n_tiles = I(B.ntiles);
+    g.max_mtiles = mt_bound;
+    g.out = out;
+    g.ldo = ldo;
+    return g;
+  };
+  auto dense = [&](const void *a, int64_t lda, const void *b, int64_t ldb, int Kd, int N,
+                   int64_t M, void *out, int64_t ldo) {
+    GemmArgs g{};
+    g.a = a;
+    g.lda = lda;
+    g.b0 = b;
+    g.ldb = ldb;
+    g.K = Kd;
+    g.N = N;
+    g.M = M;
+    g.out = out;
+    g.ldo = ldo;
+    return g;
+  };
+  auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c) {
+    if (!gemm2_applicable(a, EPI_STORE_F32) || (b && !gemm2_applicable(*b, EPI_STORE_F32)))
+      return MOE_ERR_SHAPE;
+    return launch_gemm2(a, EPI_STORE_F32, c, s, b) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  };
+  const int cfg_s = ds ? gemm2_pick(T, 0, dm, ds, 0, T, ds) : cfg;
+
+  // 3. pre-activations a = W_gate x, u = W_up x (fp32), routed and shared
+  {
+    const GemmArgs ga = grouped(x, dm, stok, T, w->w_gate, dm, static_cast<int64_t>(f) * dm, dm,
+                                f, F(B.apre), f);
+    const GemmArgs gu = grouped(x, dm, stok, T, w->w_up, dm, static_cast<int64_t>(f) * dm, dm, f,
+                                F(B.upre), f);
+    if ((rc = gemm(ga, &gu, cfg))) return rc;
+    if (ds) {
+      const GemmArgs sa2 = dense(x, dm, w->ws_gate, dm, dm, ds, T, F(B.apre_s), ds);
+      const GemmArgs su = dense(x, dm, w->ws_up, dm, dm, ds, T, F(B.upre_s), ds);
+      if ((rc = gemm(sa2, &su, cfg_s))) return rc;
+    }
+  }
+  // 4. W_down^T dy per sorted row (unscaled) and per token for the shared FFN
+  {
+    const GemmArgs gd = grouped(d_out, dm, stok, T, wsb + B.wdT, dm,
+                                static_cast<int64_t>(f) * dm, dm, f, F(B.dhu), f);
+    if (ds) {
+      const GemmArgs sd = dense(d_out, dm, wsb + B.wsdT, dm, dm, ds, T, F(B.dhu_s), ds);
+      if ((rc = gemm(gd, &sd, cfg))) return rc;
+    } else if ((rc = gemm(gd, nullptr, cfg))) {
+      return rc;
+    }
+  }
+  // 5. h, [da | du], dg per row; the router's logit gradients
+  MOE_TRY(launch_bwd_rows(F(B.apre), F(B.upre), F(B.dhu), sw, rows, f, wsb + B.h, wsb + B.dau,
+                          F(B.dg), s));
+  if (ds)
+    MOE_TRY(launch_bwd_rows(F(B.apre_s), F(B.upre_s), F(B.dhu_s), nullptr, T, ds, wsb + B.h_s,
+                            wsb + B.dau_s, nullptr, s));
+  MOE_TRY(launch_router_backward(ra, 1, inv, F(B.dg), F(B.dr), s));
+
+  // 6. input gradient: [da | du] [W_gate^T | W_up^T]^T per row, shared, router
+  if (d_x) {
+    const GemmArgs gx = grouped(wsb + B.dau, 2 * f, nullptr, rows, wsb + B.wguT, 2 * f,
+                                static_cast<int64_t>(dm) * 2 * f, 2 * f, dm, F(B.dxs), dm);
+    if (ds) {
+      const GemmArgs sx = dense(wsb + B.dau_s, 2 * ds, wsb + B.wsguT, 2 * ds, 2 * ds, dm, T,
+                                F(B.dxsh), dm);
+      if ((rc = gemm(gx, &sx, cfg))) return rc;
+    } else if ((rc = gemm(gx, nullptr, cfg))) {
+      return rc;
+    }
+    MOE_TRY(launch_bwd_dx(F(B.dxs), ds ? F(B.dxsh) : nullptr, inv, idx, F(B.dr), w->w_router, T,
+                          static_cast<int>(K), dm, d_x, s));
+  }
+
+  // 7. weight gradients
+  if (gr->w_router)
+    MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, gr->w_router, s));
+  const bool want_e = gr->w_gate || gr->w_up || gr->w_down;
+  const bool want_s = ds && (gr->ws_gate || gr->ws_up || gr->ws_down);
+  if (!want_e && !want_s) return MOE_OK;
+  MOE_TRY(launch_fill0(wsb + B.cols, B.cols_bytes, s));
+  const int cfg_k = gemm2_pick(E * (f > dm ? f : dm), 0, rows / E + 64, f < dm ? f : dm, 0);
+  if (want_e) {
+    MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, dm, gemm2_bm(cfg_k), I(B.poff),
+                          I(B.kt1), I(B.kn1), I(B.kt2), I(B.kn2), s));
+    const int G = static_cast<int>(E);
+    const int32_t *po = I(B.poff);
+    MOE_TRY(launch_cols(x, dm, stok, nullptr, rows, dm, offsets, po, G, wsb + B.xsT, B.RP, s));
+    MOE_TRY(launch_cols(d_out, dm, stok, sw, rows, dm, offsets, po, G, wsb + B.dysT, B.RP, s));
+    MOE_TRY(launch_cols(wsb + B.dau, 2 * f, nullptr, nullptr, rows, f, offsets, po, G,
+                        wsb + B.daT, B.RP, s));
+    MOE_TRY(launch_cols(wsb + B.dau + static_cast<size_t>(f) * 2, 2 * f, nullptr, nullptr, rows,
+                        f, offsets, po, G, wsb + B.duT, B.RP, s));
+    MOE_TRY(launch_cols(wsb + B.h, f, nullptr, nullptr, rows, f, offsets, po, G, wsb + B.hT,
+                        B.RP, s));
+    auto kgrouped = [&](const void *a, int64_t M, const void *b, int N, int32_t *tab,
+                        int32_t *ntab, void *out) {
+      GemmArgs g{};
+      g.a = a;
+      g.lda = B.RP;
+      g.a_extent = M;
+      g.b0 = b;
+      g.ldb = B.RP;
+      g.K = 64;
+      g.N = N;
+      g.tiles = tab;
+      g.n_tiles = ntab;
+      g.max_mtiles = E * ((M + gemm2_bm(cfg_k) - 1) / gemm2_bm(cfg_k));
+      g.k_offsets = I(B.poff);
+      g.out = out;
+      g.ldo = N;
+      g.out_stride = M * N;
+      return g;
+    };
+    if (gr->w_gate || gr->w_up) {
+      // a scratch target for a missing one keeps both in one launch
+      void *og = gr->w_gate ? static_cast<void *>(gr->w_gate) : F(B.dxs);
+      void *ou = gr->w_up ? static_cast<void *>(gr->w_up) : F(B.dxs);
+      const GemmArgs kg = kgrouped(wsb + B.daT, f, wsb + B.xsT, dm, I(B.kt1), I(B.kn1), og);
+      const GemmArgs ku = kgrouped(wsb + B.duT, f, wsb + B.xsT, dm, I(B.kt1), I(B.kn1), ou);
+      if (gr->w_gate && gr->w_up) {
+        if ((rc = gemm(kg, &ku, cfg_k))) return rc;
+      } else if ((rc = gemm(gr->w_gate ? kg : ku, nullptr, cfg_k))) {
+        return rc;
+      }
+    }
+    if (gr->w_down) {
+      const GemmArgs kd = kgrouped(wsb + B.dysT, dm, wsb + B.hT, f, I(B.kt2), I(B.kn2),
+                                   gr->w_down);
+      if ((rc = gemm(kd, nullptr, cfg_k))) return rc;
+    }
+  }
+  if (want_s) {
+    MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, wsb + B.xT, B.TP, s));
+    MOE_TRY(launch_cols(d_out, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, wsb + B.dyT,
+                        B.TP, s));
+    MOE_TRY(launch_cols(wsb + B.dau_s, 2 * ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0,
+                        wsb + B.dashT, B.TP, s));
+    MOE_TRY(launch_cols(wsb + B.dau_s + static_cast<size_t>(ds) * 2, 2 * ds, nullptr, nullptr, T,
+                        ds, nullptr, nullptr, 0, wsb + B.dushT, B.TP, s));
+    MOE_TRY(launch_cols(wsb + B.h_s, ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0,
+                        wsb + B.hshT, B.TP, s));
+    const int TPk = static_cast<int>(B.TP);
+    const int cfg_w = gemm2_pick(ds, 0, TPk, dm, 0, ds, dm);
+    if (gr->ws_gate) {
+      const GemmArgs g1 = dense(wsb + B.dashT, B.TP, wsb + B.xT, B.TP, TPk, dm, ds, gr->ws_gate, dm);
+      if ((rc = gemm(g1, nullptr, cfg_w))) return rc;
+    }
+    if (gr->ws_up) {
+      const GemmArgs g2 = dense(wsb + B.dushT, B.TP, wsb + B.xT, B.TP, TPk, dm, ds, gr->ws_up, dm);
+      if ((rc = gemm(g2, nullptr, cfg_w))) return rc;
+    }
+    if (gr->ws_down) {
+      const GemmArgs g3 = dense(wsb + B.dyT, B.TP, wsb + B.hshT, B.TP, TPk, ds, dm, gr->ws_down, ds);
+      if ((rc = gemm(g3, nullptr, gemm2_pick(dm, 0, TPk, ds, 0)))) return rc;
+    }
+  }
+  return MOE_OK;
 }
 
 int moe_plan(const moe_desc *d, moe_plan_info *info) {

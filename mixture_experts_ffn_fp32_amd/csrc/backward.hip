@@ -1,0 +1,273 @@
+// Backward pass of the layer (non-latent, bf16): the elementwise, transpose
+// and reduction kernels around the GEMMs that api.hip enqueues.
+//
+// The layer (APEX-1 Mathematical Reference - Part 3, 13.2 and 12.2) is
+// y_t = sum_s FFN_s(x_t) + sum_k g_k FFN_{e_k}(x_t), FFN(x) = W_down h,
+// h = SiLU(a) * u, a = W_gate x, u = W_up x. For an output gradient dy:
+//   dh = g W_down^T dy,   dg_k = <dy, FFN_{e_k}(x)> = <W_down^T dy, h>,
+//   da = dh * u * SiLU'(a),  du = dh * SiLU(a),  SiLU' = s (1 + a (1 - s)),
+//   dx += W_gate^T da + W_up^T du,
+//   dW_down += (g dy) h^T,  dW_gate += da x^T,  dW_up += du x^T,
+// and the router gradient from dg (router.hip). The selection passes no
+// gradient and the balance bias gets none; experts no token selected get no
+// weight gradient ("StableLatentMoE and QuantileBalancer": inactive experts'
+// gradients stay unset).
+//
+// Every product runs on the pipelined NT GEMM (C = A B^T, both operands
+// K-contiguous). Products whose natural operand is K-strided use transposed
+// copies: the weights of active experts (W_down^T, W_gate^T, W_up^T) and, for
+// the weight gradients, the activations in expert-contiguous columns whose
+// per-expert runs are padded to multiples of 64 with zeros (the K-grouped
+// GEMM reduces each expert over its own run).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void fill0_kernel(uint4 *p, int64_t n16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16), 64 x 64
+// tiles through LDS; batches b with active && !active[b] are skipped.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t R, int64_t C,
+                                                        const int32_t *active, uint16_t *dst,
+                                                        int64_t dst_ld, int64_t dst_bstride,
+                                                        int64_t col0) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t b = blockIdx.z;
+  if (active && active[b] == 0) return;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const uint16_t *s = src + b * R * C;
+  uint16_t *d = dst + b * dst_bstride + col0;
+  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
+  for (int r = ly; r < 64; r += 4)
+    if (r0 + r < R && c0 + lx < C) tile[r][lx] = s[(r0 + r) * C + c0 + lx];
+  __syncthreads();
+  for (int c = ly; c < 64; c += 4)
+    if (c0 + c < C && r0 + lx < R) d[(c0 + c) * dst_ld + r0 + lx] = tile[lx][c];
+}
+
+// Rows of a bf16 matrix (row r read from row_index[r] if given, times
+// row_scale[r] if given) written as columns: dst[c * ldd + col(r)], col(r) = r,
+// or, grouped, poff[e] + r - off[e] for the group e holding r (off, poff:
+// [G + 1] row and padded-column offsets). Columns not written stay as they
+// are (the caller zeroes the padding).
+__global__ __launch_bounds__(256) void cols_kernel(const uint16_t *src, int64_t ld_src,
+                                                   const int32_t *row_index,
+                                                   const float *row_scale, int64_t R, int64_t C,
+                                                   const int32_t *off, const int32_t *poff, int G,
+                                                   uint16_t *dst, int64_t ldd) {
+  __shared__ uint16_t tile[64][66];
+  __shared__ int64_t col[64];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
+  if (ly == 0) {
+    const int64_t r = r0 + lx;
+    int64_t cc = r;
+    if (off && r < R) {
+      int lo = 0, hi = G;  // group e with off[e] <= r < off[e + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+      }
+      cc = poff[lo] + (r - off[lo]);
+    }
+    col[lx] = cc;
+  }
+  for (int r = ly; r < 64; r += 4) {
+    const int64_t rr = r0 + r;
+    if (rr < R && c0 + lx < C) {
+      const int64_t sr = row_index ? row_index[rr] : rr;
+      uint16_t v = src[sr * ld_src + c0 + lx];
+      if (row_scale) v = f32_to_bf16(bf16_to_f32(v) * row_scale[rr]);
+      tile[r][lx] = v;
+    }
+  }
+  __syncthreads();
+  for (int c = ly; c < 64; c += 4)
+    if (c0 + c < C && r0 + lx < R) dst[(c0 + c) * ldd + col[lx]] = tile[lx][c];
+}
+
+// Padded expert column offsets poff[e] = sum of round64(counts) before e, and
+// the K-grouped m-tile table of each output height M (bm rows per tile): one
+// run of ceil(M / bm) tiles per active expert, grouped per expert.
+__global__ __launch_bounds__(1024) void kgroup_kernel(const int32_t *counts, int E, int M1, int M2,
+                                                      int bm, int32_t *poff, int32_t *t1,
+                                                      int32_t *n1, int32_t *t2, int32_t *n2) {
+  __shared__ int tmp[1024];
+  const int t = threadIdx.x;
+  const int c = t < E ? counts[t] : 0;
+  int total;
+  const int ex = block_exscan_1024((c + 63) / 64 * 64, tmp, &total);
+  if (t < E) poff[t] = ex;
+  if (t == 0) poff[E] = total;
+  for (int w = 0; w < 2; ++w) {
+    const int M = w ? M2 : M1;
+    int32_t *tab = w ? t2 : t1;
+    const int per = (M + bm - 1) / bm;
+    int ntot;
+    const int start = block_exscan_1024(c > 0 ? per : 0, tmp, &ntot);
+    if (t < E && c > 0) {
+      for (int i = 0; i < per; ++i) {
+        int32_t *ti = tab + kTileInts * static_cast<int64_t>(start + i);
+        ti[0] = t;
+        ti[1] = i * bm;
+        ti[2] = min((i + 1) * bm, M);
+        ti[3] = start + i / kTileGroup * kTileGroup;
+        ti[4] = min(kTileGroup, per - i / kTileGroup * kTileGroup);
+      }
+    }
+    if (t == 0) *(w ? n2 : n1) = ntot;
+    __syncthreads();
+  }
+}
+
+// Per row p (one wavefront): from the pre-activations a, u and the unscaled
+// W_down^T dy (fp32 [R, f]) and the routing weight g[p] (1 if null): h =
+// SiLU(a) u, dh = g W_down^T dy, da = dh u SiLU'(a), du = dh SiLU(a) as bf16
+// (dAU row p = [da | du], 2 f wide), and dg[p] = <W_down^T dy, h> (if dg).
+__global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *U, const float *D,
+                                                   const float *gw, int64_t R, int f,
+                                                   uint16_t *H, uint16_t *dAU, float *dg) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (p >= R) return;
+  const int lane = threadIdx.x & 63;
+  const float g = gw ? gw[p] : 1.0f;
+  float acc = 0.f;
+  const int64_t o = p * f;
+  for (int j = lane; j < f; j += 64) {
+    const float a = A[o + j], u = U[o + j], dd = D[o + j];
+    const float s = 1.0f / (1.0f + expf(-a));
+    const float si = a * s;
+    const float h = si * u;
+    acc += dd * h;
+    const float dh = g * dd;
+    H[o + j] = f32_to_bf16(h);
+    dAU[2 * o + j] = f32_to_bf16(dh * u * s * (1.0f + a * (1.0f - s)));
+    dAU[2 * o + f + j] = f32_to_bf16(dh * si);
+  }
+  if (dg) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) dg[p] = acc;
+  }
+}
+
+// dx[t] = sum_k dXs[inv[t K + k]] + dXsh[t] + sum_k dr[inv[t K + k]] W_router[idx[t K + k]]
+// (fp32, k in order, then rounded to bf16); one wavefront per token.
+__global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *dXsh,
+                                                 const int32_t *inv, const int32_t *idx,
+                                                 const float *dr, const float *wr, int64_t T,
+                                                 int K, int d, uint16_t *dx) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < K; ++k) {
+      const int64_t q = inv[t * K + k];
+      const float4 v = *reinterpret_cast<const float4 *>(dXs + q * d + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (dXsh) {
+      const float4 v = *reinterpret_cast<const float4 *>(dXsh + t * d + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (dr) {
+      for (int k = 0; k < K; ++k) {
+        const float c = dr[inv[t * K + k]];
+        const float4 w = *reinterpret_cast<const float4 *>(wr + static_cast<int64_t>(idx[t * K + k]) * d + i);
+        acc.x += c * w.x; acc.y += c * w.y; acc.z += c * w.z; acc.w += c * w.w;
+      }
+    }
+    const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+    uint2 o;
+    o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2 *>(dx + t * d + i) = o;
+  }
+}
+
+// dW_router[e, i] = sum over the rows p of expert e (sorted order) of
+// dr[p] x[sorted_token[p], i], fp32 in row order; one thread per (e, i).
+__global__ __launch_bounds__(256) void dwr_kernel(const float *dr, const int32_t *stok,
+                                                  const int32_t *offsets, const uint16_t *x,
+                                                  int d, float *dwr) {
+  const int e = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  float acc = 0.f;
+  for (int p = offsets[e]; p < offsets[e + 1]; ++p)
+    acc += dr[p] * bf16_to_f32(x[static_cast<int64_t>(stok[p]) * d + i]);
+  dwr[static_cast<int64_t>(e) * d + i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_fill0(void *p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  fill0_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(static_cast<uint4 *>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t C,
+                            const int32_t *active, void *dst, int64_t dst_ld, int64_t dst_bstride,
+                            int64_t col0, hipStream_t s) {
+  if (batches == 0 || R == 0 || C == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64),
+            static_cast<unsigned>(batches));
+  transpose_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), R, C, active,
+                                        static_cast<uint16_t *>(dst), dst_ld, dst_bstride, col0);
+  return hipGetLastError();
+}
+
+hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
+                       const float *row_scale, int64_t R, int64_t C, const int32_t *off,
+                       const int32_t *poff, int G, void *dst, int64_t ldd, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64));
+  cols_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), ld_src, row_index,
+                                   row_scale, R, C, off, poff, G, static_cast<uint16_t *>(dst),
+                                   ldd);
+  return hipGetLastError();
+}
+
+hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, int32_t *poff,
+                         int32_t *t1, int32_t *n1, int32_t *t2, int32_t *n2, hipStream_t s) {
+  kgroup_kernel<<<1, 1024, 0, s>>>(counts, E, M1, M2, bm, poff, t1, n1, t2, n2);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const float *gw,
+                           int64_t R, int f, void *H, void *dAU, float *dg, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  rows_kernel<<<static_cast<unsigned>((R + 3) / 4), 256, 0, s>>>(
+      A, U, D, gw, R, f, static_cast<uint16_t *>(H), static_cast<uint16_t *>(dAU), dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const int32_t *inv,
+                         const int32_t *idx, const float *dr, const float *wr, int64_t T, int K,
+                         int d, void *dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dx_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(dXs, dXsh, inv, idx, dr, wr, T, K,
+                                                               d, static_cast<uint16_t *>(dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
+                          const void *x, int E, int d, float *dwr, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E));
+  dwr_kernel<<<grid, 256, 0, s>>>(dr, stok, offsets, static_cast<const uint16_t *>(x), d, dwr);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -180,6 +180,13 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     m_end = min<int64_t>(m_begin + BM, p.M);
   }
   const int n_begin = nt * NOUT;
+  // K-grouped: this expert's reduction columns and output block
+  int64_t kbeg = 0, kseg = p.K;
+  if (p.k_offsets) {
+    kbeg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert]);
+    kseg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert + 1]) - kbeg;
+  }
+  const int64_t obase = p.k_offsets ? expert * p.out_stride : 0;
 
   // ------------------------------------------------------------ loads
   // load j of a thread: tile row ROWS j + lrow, in the 1 KB block starting at
@@ -202,30 +209,31 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       int64_t m = m_begin + ROWS * j + lrow;
       if (m >= m_end) m = m_begin;
       const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
-      aoff[j] = static_cast<uint32_t>((src * lda + lchunk * 8) * 2);
+      aoff[j] = static_cast<uint32_t>((src * lda + (seg ? 0 : kbeg) + lchunk * 8) * 2);
     }
   };
   auto setup_b = [&](int seg) {
     if (seg && !p.a2) return;
     const int64_t ldb = seg ? p.ldb2 : p.ldb, bytes = static_cast<int64_t>(p.N) * ldb * 2;
     if (seg) {
-      br0 = br1 = rsrc(p.b2, bytes);
+      br0 = br1 = rsrc(static_cast<const char *>(p.b2) + expert * p.b2_stride * 2, bytes);
     } else {
       const int64_t eoff = expert * p.b_stride * 2;
       br0 = rsrc(static_cast<const char *>(p.b0) + eoff, bytes);
       br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, bytes) : br0;
     }
-    boff0 = static_cast<uint32_t>((static_cast<int64_t>(n_begin + lrow) * ldb + lchunk * 8) * 2);
+    boff0 = static_cast<uint32_t>(
+        (static_cast<int64_t>(n_begin + lrow) * ldb + (seg ? 0 : kbeg) + lchunk * 8) * 2);
     bstep = static_cast<uint32_t>(ROWS * ldb * 2);
   };
 
   // a last K segment that ends 32 columns into a stage runs only that
   // stage's first k-step (the other half of its buffers holds columns past
   // the row: the next row's, or zeros past the operand's extent)
-  const int steps1 = (p.K + 63) / 64;
+  const int steps1 = static_cast<int>((kseg + 63) / 64);
   const int steps = steps1 + (p.a2 ? (p.K2 + 63) / 64 : 0);
   const int last = steps - 1;
-  const bool half_last = ((p.a2 ? p.K2 : p.K) & 63) != 0;
+  const bool half_last = ((p.a2 ? p.K2 : kseg) & 63) != 0;
   auto kbytes = [&](int st) {
     return __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * kRowBytes);
   };
@@ -408,11 +416,11 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
         for (int e = 0; e < 8; ++e) v[e] += rs[e];
       }
       if (EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32)) {
-        float *o = static_cast<float *>(p.out) + m * p.ldo + col;
+        float *o = static_cast<float *>(p.out) + obase + m * p.ldo + col;
         *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
       } else {
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + m * p.ldo + col) =
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + obase + m * p.ldo + col) =
             Chunk<bf16_t>::pack(v);
       }
     }
@@ -465,7 +473,8 @@ bool gemm2_applicable(const GemmArgs &a, int epi) {
     return false;
   if (a.a2 && (a.M * a.lda2 * 2 >= kLim || (a.N + 256LL) * a.ldb2 * 2 >= kLim)) return false;
   // K a multiple of 32 (64 for the first of two segments)
-  if (a.K % 32 || (a.a2 && (a.K % 64 || a.K2 % 32))) return false;
+  if (!a.k_offsets && (a.K % 32 || (a.a2 && (a.K % 64 || a.K2 % 32)))) return false;
+  if (a.k_offsets && (!a.tiles || a.a2 || a.a_rows)) return false;
   if (a.N % 8) return false;
   if (epi == EPI_COMBINE && a.ldy % 8) return false;
   return a.ldo % 8 == 0;

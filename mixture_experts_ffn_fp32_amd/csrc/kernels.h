@@ -150,6 +150,13 @@ struct GemmArgs {
   int k_split;               // fp32-store only: K split count (0 or 1 = none);
   int64_t split_stride;      // elements between the splits' partial outputs
   int out_f32;               // SCALE, pipelined kernel: fp32 output instead of act dtype
+  int64_t b2_stride;         // elements between experts' B matrices of the second K segment
+  // K-grouped (pipelined kernel): tile table entries {expert, m_begin, m_end}
+  // over the output rows; expert e reduces over columns [k_offsets[e],
+  // k_offsets[e+1]) of A and B (multiples of 64, shared by all experts) and
+  // writes its output at out + e * out_stride.
+  const int32_t *k_offsets;
+  int64_t out_stride;
 };
 
 // Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,
@@ -203,6 +210,37 @@ hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int 
 hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, int K, int L,
                                  int has_rmsnorm, float eps, const float *gamma, void *r,
                                  int act_bf16, hipStream_t s);
+
+// ------------------------------------------------------------------ backward
+// Router gradient (router.hip): dr[p] for the sorted rows p of each token's
+// selected experts from dg[p] (the routing weights' gradients), with a.idx,
+// a.logits (of a router pass on the same x), bias, mode, scale as routed.
+hipError_t launch_router_backward(const RouterArgs &a, int act_bf16, const int32_t *inv,
+                                  const float *dg, float *dr, hipStream_t s);
+// backward.hip
+hipError_t launch_fill0(void *p, size_t bytes, hipStream_t s);
+// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16) for batches
+// b with active[b] != 0 (all if null)
+hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t C,
+                            const int32_t *active, void *dst, int64_t dst_ld, int64_t dst_bstride,
+                            int64_t col0, hipStream_t s);
+// bf16 rows (gathered by row_index, scaled by row_scale, either optional) to
+// columns of dst (ld ldd), at column r, or grouped: poff[e] + r - off[e]
+hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
+                       const float *row_scale, int64_t R, int64_t C, const int32_t *off,
+                       const int32_t *poff, int G, void *dst, int64_t ldd, hipStream_t s);
+// padded expert offsets and the K-grouped m-tile tables of heights M1, M2
+hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, int32_t *poff,
+                         int32_t *t1, int32_t *n1, int32_t *t2, int32_t *n2, hipStream_t s);
+// h = SiLU(a) u and [da | du] (bf16 [R, 2f]) from a, u and W_down^T dy (fp32
+// [R, f]) and the row weights gw (1 if null); dg[p] = <W_down^T dy, h> if dg
+hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const float *gw,
+                           int64_t R, int f, void *H, void *dAU, float *dg, hipStream_t s);
+hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const int32_t *inv,
+                         const int32_t *idx, const float *dr, const float *wr, int64_t T, int K,
+                         int d, void *dx, hipStream_t s);
+hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
+                          const void *x, int E, int d, float *dwr, hipStream_t s);
 
 // Bias-based balancer step (balance.hip); nk = tokens x top-k.
 hipError_t launch_balance(int E, int64_t nk, const int32_t *counts, float alpha, float *bias,

@@ -272,6 +272,62 @@ __global__ __launch_bounds__(256) void router_valu_kernel(RouterArgs a, int sele
   }
 }
 
+// ------------------------------------------------------------ backward
+// Router gradient of one token (one wavefront, lane k < K for slot k): from
+// the gradients dg of its routing weights (stored per sorted row, found
+// through inv) to the gradients dr of its selected logits, written per
+// sorted row. With c = routed_scale:
+//  - softmax over the selected (and the softmax-first rule, the same function
+//    of the selected logits): q = softmax(logits + bias) over the selected,
+//    g = c q, dr_k = q_k (c dg_k - sum_j q_j c dg_j);
+//  - sigmoid rule: s = sigmoid(logit), g = c s (or c s / sum s when
+//    renormalised), dr_k = ds_k s_k (1 - s_k).
+__global__ __launch_bounds__(256) void route_bwd_kernel(RouterArgs a, int parts, int splits,
+                                                        int64_t ss, const int32_t *inv,
+                                                        const float *dg, float *dr) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int lane = threadIdx.x & 63;
+  const bool on = lane < a.K;
+  int e = 0;
+  int64_t p = 0;
+  float l = 0.f, g = 0.f;
+  if (on) {
+    e = a.idx[t * a.K + lane];
+    p = inv[t * a.K + lane];
+    g = dg[p];
+    l = logit_of(a.logits + t * static_cast<int64_t>(parts) * a.E, e, a.E, parts, splits, ss);
+  }
+  const float c = a.routed_scale;
+  float out;
+  if (a.mode == 2) {
+    const float sg = on ? sigmoidf_(l) : 0.f;
+    float S = sg, sdg = g * sg;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      S += __shfl_xor(S, off);
+      sdg += __shfl_xor(sdg, off);
+    }
+    const float ds = a.renormalize ? c * (g / S - sdg / (S * S)) : c * g;
+    out = ds * sg * (1.0f - sg);
+  } else {
+    const float z = on ? l + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
+    float m = z;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float ex = on ? expf(z - m) : 0.f;
+    float Z = ex;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
+    const float q = ex / Z;
+    float qdg = q * c * g;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) qdg += __shfl_xor(qdg, off);
+    out = q * (c * g - qdg);
+  }
+  if (on) dr[p] = out;
+}
+
 // ------------------------------------------------------------ QuantileBalancer
 // d[e][t] = thresh_t - sigmoid(logit[t, e]), thresh_t = the token's (K+1)-th
 // corrected score (top[t, K]). 64 tokens x 64 experts per workgroup,
@@ -550,6 +606,16 @@ hipError_t launch_router(const RouterArgs &a, int act_bf16, hipStream_t s) {
 int router_loss_chunk_tokens(int64_t T) {
   int64_t c = (T / kLossChunks + 3) / 4 * 4;
   return static_cast<int>(c < kLossMinTokens ? kLossMinTokens : (c > kLossMaxTokens ? kLossMaxTokens : c));
+}
+
+hipError_t launch_router_backward(const RouterArgs &a, int act_bf16, const int32_t *inv,
+                                  const float *dg, float *dr, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  int parts, splits;
+  logit_layout(a, act_bf16, &parts, &splits);
+  route_bwd_kernel<<<static_cast<unsigned>((a.T + 3) / 4), 256, 0, s>>>(
+      a, parts, splits, a.T * parts * a.E, inv, dg, dr);
+  return hipGetLastError();
 }
 
 int64_t router_loss_chunks(int64_t T) {

@@ -183,3 +183,30 @@ def test_plan_paths_of_the_workloads():
     assert P["large_decode"]["dispatch_one_workgroup"] == 1
     with pytest.raises(moe.MoeError):
         moe.moe_plan(_desc(T=-1))
+
+
+def test_backward_checked_before_launch():
+    """moe_backward: bf16 non-latent layers with widths that are multiples of
+    32; NULLs and a short workspace are reported before anything runs."""
+    fake = C.c_void_p(1 << 20)
+    w = moe.MoeWeights(**{k: fake.value for k, _ in moe.MoeWeights._fields_})
+    g = moe.MoeGrads()
+    L = moe.lib()
+    d = _desc(T=64)
+    n = moe.moe_backward_workspace_size(d)
+    assert n > moe.moe_workspace_size(d)
+    assert L.moe_backward(C.byref(_desc(T=64, act_dtype=0)), C.byref(w), fake, fake, fake,
+                          C.byref(g), fake, 1 << 40, None) == -3
+    w8 = moe_synth.get("latent")
+    assert L.moe_backward(C.byref(moe.make_desc(w8)), C.byref(w), fake, fake, fake, C.byref(g),
+                          fake, 1 << 40, None) == -3
+    assert L.moe_backward(C.byref(_desc(T=64, d_model=520)), C.byref(w), fake, fake, fake,
+                          C.byref(g), fake, 1 << 40, None) == -2
+    assert L.moe_backward(C.byref(d), C.byref(w), fake, fake, fake, None, fake, n, None) == -1
+    assert L.moe_backward(C.byref(d), C.byref(w), None, fake, fake, C.byref(g), fake, n,
+                          None) == -1
+    assert L.moe_backward(C.byref(d), C.byref(w), fake, fake, fake, C.byref(g), fake, n - 1,
+                          None) == -4
+    d0 = _desc(T=0)
+    assert L.moe_backward(C.byref(d0), C.byref(w), None, None, None, C.byref(g), fake,
+                          moe.moe_backward_workspace_size(d0), None) == 0

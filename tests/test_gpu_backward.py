@@ -1,0 +1,162 @@
+"""GPU parity of moe_backward against the CPU oracle's backward: input
+gradient, router, expert and shared weight gradients, on the same seeded
+inputs and output gradient; inactive experts' gradients left untouched."""
+import numpy as np
+import pytest
+
+import mixture_experts_ffn_fp32_amd as moe
+import moe_synth
+import oracle
+from _gpu import f64, gpu_route, layer_of, need_gpu, sample_tokens, say, torch
+from _layers import custom, max_abs_rel
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2  # max-abs-rel per gradient tensor: bf16 operands, fp32 accumulation
+
+SHAPES = {"w_router": ("E", "d"), "w_gate": ("E", "d_ff", "d"), "w_up": ("E", "d_ff", "d"),
+          "w_down": ("E", "d", "d_ff"), "ws_gate": ("d_shared", "d"),
+          "ws_up": ("d_shared", "d"), "ws_down": ("d", "d_shared")}
+
+
+def _grad_buffers(w, keys):
+    dims = {"E": w.E, "d": w.d, "d_ff": w.d_ff, "d_shared": w.d_shared}
+    return {k: torch.full(tuple(dims[s] for s in SHAPES[k]), float("nan"), dtype=torch.float32,
+                          device="cuda") for k in keys}
+
+
+def _d_out(w, seed):
+    bits = moe_synth.draw_rows(seed, (w.T, w.d), "bf16")
+    return bits, torch.from_numpy(bits).view(torch.bfloat16).cuda()
+
+
+def run_backward(w, a, layer, keys, seed=11):
+    bits, dy = _d_out(w, seed)
+    grads = _grad_buffers(w, keys)
+    dx = layer.backward(layer.dev["x"], dy, grads=grads)
+    torch.cuda.synchronize()
+    g_idx = gpu_route(layer)[0]
+    return bits, f64(dx), {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}, g_idx
+
+
+def oracle_selection(orc, g_idx):
+    """The oracle's selection, with the GPU's on near-tied tokens (both are
+    correct there)."""
+    o_idx, _, gap, _ = orc.route()
+    use = o_idx.copy()
+    near = gap < moe.TIE_EPS
+    use[near] = g_idx[near]
+    return use, int(near.sum())
+
+
+def check_all(w, a, layer, keys=tuple(SHAPES), seed=11, tol=TOL):
+    keys = [k for k in keys if w.d_shared or not k.startswith("ws_")]
+    bits, dx, grads, g_idx = run_backward(w, a, layer, keys, seed)
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    ref = orc.backward(moe_synth.as_f64(bits, "bf16"), idx_override=use,
+                       shared=bool(w.d_shared))
+    errs = {"dx": max_abs_rel(dx, ref["dx"])}
+    active = np.bincount(use.ravel(), minlength=w.E) > 0
+    for k in keys:
+        got = grads[k]
+        if k in ("w_gate", "w_up", "w_down"):
+            assert np.all(np.isnan(got[~active])), f"{k}: inactive experts were written"
+            assert np.all(np.isfinite(got[active])), k
+            errs[k] = max_abs_rel(got[active], ref[k][active])
+        else:
+            assert np.all(np.isfinite(got)), k
+            errs[k] = max_abs_rel(got, ref[k])
+    say(f"  backward {w.name}: T={w.T} near-ties={n_near} active={int(active.sum())}/{w.E} "
+        + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    return errs
+
+
+LAYERS = {
+    "small_256": None,
+    "topk_e16": dict(T=512, d=256, d_ff=384, E=16, K=4, act="bf16", n_shared=1,
+                     d_ff_shared=256, w_std=0.05, router_std=0.05, bias_std=0.01),
+    "softmax_first": dict(T=300, d=128, d_ff=160, E=8, K=2, act="bf16", route="softmax_topk",
+                          n_shared=1, d_ff_shared=96, w_std=0.08, router_std=0.08),
+    "sigmoid_renorm": dict(T=300, d=128, d_ff=96, E=12, K=3, act="bf16", route="sigmoid_bias",
+                           renormalize=True, routed_scale=2.5, bias_std=0.1, n_shared=0,
+                           d_ff_shared=0, w_std=0.08, router_std=0.08),
+    "sigmoid_raw": dict(T=200, d=96, d_ff=64, E=6, K=2, act="bf16", route="sigmoid_bias",
+                        bias_std=0.1, n_shared=2, d_ff_shared=32, w_std=0.1, router_std=0.1),
+    "one_expert": dict(T=100, d=64, d_ff=96, E=1, K=1, act="bf16", n_shared=1, d_ff_shared=64,
+                       w_std=0.1, router_std=0.1),
+    "inactive": dict(T=6, d=64, d_ff=64, E=32, K=1, act="bf16", n_shared=0, d_ff_shared=0,
+                     w_std=0.1, router_std=0.1),
+    "k_eq_e": dict(T=150, d=64, d_ff=64, E=4, K=4, act="bf16", w_std=0.1, router_std=0.1,
+                   n_shared=1, d_ff_shared=32),
+}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("name", sorted(LAYERS))
+def test_backward_matches_oracle(name):
+    if name == "small_256":
+        w = moe_synth.get("small").with_T(256)
+    else:
+        w = custom(name, config_no=950 + sorted(LAYERS).index(name), **LAYERS[name])
+    say(f"case backward {name} T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K} route={w.route}")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    check_all(w, a, layer)
+
+
+def test_backward_is_deterministic_and_partial_requests():
+    """Two calls give the same bits; gradients not asked for are not
+    written, the ones asked for are unchanged."""
+    w = custom("bwd_det", config_no=990, **LAYERS["topk_e16"])
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    _, dy = _d_out(w, 3)
+    g1 = _grad_buffers(w, SHAPES)
+    g2 = _grad_buffers(w, ["w_down", "ws_up"])
+    dx1 = layer.backward(layer.dev["x"], dy, grads=g1).clone()
+    dx2 = layer.backward(layer.dev["x"], dy, grads=g2)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2)
+    assert torch.equal(g1["w_down"].nan_to_num(7.0), g2["w_down"].nan_to_num(7.0))
+    assert torch.equal(g1["ws_up"], g2["ws_up"])
+
+
+@pytest.mark.timeout(900)
+def test_backward_medium_sampled():
+    """Full-size medium layer (skewed loads, empty experts): input gradients on
+    a seeded token sample, and the weight gradients of the smallest non-empty
+    expert over all of its tokens."""
+    w = moe_synth.get("medium")
+    say("case backward medium: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    bits, dx, grads, g_idx = run_backward(w, a, layer, ["w_gate", "w_up", "w_down"])
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    dy = moe_synth.as_f64(bits, "bf16")
+    toks = sample_tokens(use, w.E, 256, seed=5)
+    ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
+                       router=False, shared=False)
+    err = max_abs_rel(dx[toks], ref["dx"])
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    nz = np.nonzero(counts)[0]
+    e = int(nz[np.argmin(counts[nz])])
+    mine = np.nonzero((use == e).any(1))[0]
+    one = orc.backward(dy[mine], tokens=mine, idx_override=use[mine], experts=e, router=False,
+                       shared=False)
+    errs = {k: max_abs_rel(grads[k][e], one[k][0]) for k in ("w_gate", "w_up", "w_down")}
+    assert np.all(np.isnan(grads["w_gate"][counts == 0]))
+    say(f"  medium: near-ties={n_near} dx(sample {len(toks)})={err:.2e} expert {e} "
+        f"({counts[e]} rows): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert err <= TOL
+    for v in errs.values():
+        assert v <= TOL
+    del layer, a
+    torch.cuda.empty_cache()
