@@ -263,7 +263,8 @@ def main():
         fl = 2.0 * (w.T * w.K * w.d * w.d_ff + w.T * w.d * w.d_shared) * (2 + 1 + 2 + 3)
         bwd = {"ms_per_call": round(bms, 4), "tokens_per_s": round(w.T / (bms / 1e3), 1),
                "tflops": round(fl / (bms / 1e3) / 1e12, 2),
-               "note": "moe_backward: input, router, expert and shared weight gradients "
+               "note": "moe_backward: input, router, expert and shared weight gradients; tflops "
+                        "counts the recomputed gate/up GEMM; "
                        "(routing recomputed), output gradient of ones"}
         del grads, d_x, dy
         layer.ws_bwd = None

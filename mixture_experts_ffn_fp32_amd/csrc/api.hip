@@ -410,7 +410,7 @@ struct BwdLayout {
   size_t wguT, wdT, wsguT, wsdT;
   size_t apre, upre, dhu, h, dau, dg, dr, dxs;
   size_t apre_s, upre_s, dhu_s, h_s, dau_s, dxsh;
-  size_t cols, cols_bytes;  // contiguous block of transposed activations (zeroed)
+  size_t cols, cols_bytes;  // block of transposed activations
   size_t xsT, dysT, daT, duT, hT, xT, dyT, dashT, dushT, hshT;
   size_t total;
   int64_t RP, TP, kt_cap;
@@ -426,7 +426,7 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
     o += align256(bytes);
     return at;
   };
-  B.RP = rows + 64 * E;        // padded expert columns (upper bound)
+  B.RP = (rows + 63) / 64 * 64 + 64 * E;  // padded expert columns (upper bound)
   B.TP = (T + 63) / 64 * 64;
   B.kt_cap = E * ((f > dm ? f : dm) + 63) / 64 + 1;
   B.poff = take((E + 1) * 4);
@@ -1001,21 +1001,21 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const bool want_e = gr->w_gate || gr->w_up || gr->w_down;
   const bool want_s = ds && (gr->ws_gate || gr->ws_up || gr->ws_down);
   if (!want_e && !want_s) return MOE_OK;
-  MOE_TRY(launch_fill0(wsb + B.cols, B.cols_bytes, s));
   const int cfg_k = gemm2_pick(E * (f > dm ? f : dm), 0, rows / E + 64, f < dm ? f : dm, 0);
   if (want_e) {
     MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, dm, gemm2_bm(cfg_k), I(B.poff),
                           I(B.kt1), I(B.kn1), I(B.kt2), I(B.kn2), s));
     const int G = static_cast<int>(E);
     const int32_t *po = I(B.poff);
-    MOE_TRY(launch_cols(x, dm, stok, nullptr, rows, dm, offsets, po, G, wsb + B.xsT, B.RP, s));
-    MOE_TRY(launch_cols(d_out, dm, stok, sw, rows, dm, offsets, po, G, wsb + B.dysT, B.RP, s));
-    MOE_TRY(launch_cols(wsb + B.dau, 2 * f, nullptr, nullptr, rows, f, offsets, po, G,
-                        wsb + B.daT, B.RP, s));
+    const int64_t RP = B.RP;
+    MOE_TRY(launch_cols(x, dm, stok, nullptr, rows, dm, offsets, po, G, RP, wsb + B.xsT, RP, s));
+    MOE_TRY(launch_cols(d_out, dm, stok, sw, rows, dm, offsets, po, G, RP, wsb + B.dysT, RP, s));
+    MOE_TRY(launch_cols(wsb + B.dau, 2 * f, nullptr, nullptr, rows, f, offsets, po, G, RP,
+                        wsb + B.daT, RP, s));
     MOE_TRY(launch_cols(wsb + B.dau + static_cast<size_t>(f) * 2, 2 * f, nullptr, nullptr, rows,
-                        f, offsets, po, G, wsb + B.duT, B.RP, s));
-    MOE_TRY(launch_cols(wsb + B.h, f, nullptr, nullptr, rows, f, offsets, po, G, wsb + B.hT,
-                        B.RP, s));
+                        f, offsets, po, G, RP, wsb + B.duT, RP, s));
+    MOE_TRY(launch_cols(wsb + B.h, f, nullptr, nullptr, rows, f, offsets, po, G, RP, wsb + B.hT,
+                        RP, s));
     auto kgrouped = [&](const void *a, int64_t M, const void *b, int N, int32_t *tab,
                         int32_t *ntab, void *out) {
       GemmArgs g{};
@@ -1054,15 +1054,16 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     }
   }
   if (want_s) {
-    MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, wsb + B.xT, B.TP, s));
-    MOE_TRY(launch_cols(d_out, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, wsb + B.dyT,
-                        B.TP, s));
-    MOE_TRY(launch_cols(wsb + B.dau_s, 2 * ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0,
-                        wsb + B.dashT, B.TP, s));
+    const int64_t TP = B.TP;
+    MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.xT, TP, s));
+    MOE_TRY(launch_cols(d_out, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.dyT,
+                        TP, s));
+    MOE_TRY(launch_cols(wsb + B.dau_s, 2 * ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
+                        wsb + B.dashT, TP, s));
     MOE_TRY(launch_cols(wsb + B.dau_s + static_cast<size_t>(ds) * 2, 2 * ds, nullptr, nullptr, T,
-                        ds, nullptr, nullptr, 0, wsb + B.dushT, B.TP, s));
-    MOE_TRY(launch_cols(wsb + B.h_s, ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0,
-                        wsb + B.hshT, B.TP, s));
+                        ds, nullptr, nullptr, 0, TP, wsb + B.dushT, TP, s));
+    MOE_TRY(launch_cols(wsb + B.h_s, ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
+                        wsb + B.hshT, TP, s));
     const int TPk = static_cast<int>(B.TP);
     const int cfg_w = gemm2_pick(ds, 0, TPk, dm, 0, ds, dm);
     if (gr->ws_gate) {

@@ -32,65 +32,105 @@ __global__ __launch_bounds__(256) void fill0_kernel(uint4 *p, int64_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16), 64 x 64
-// tiles through LDS; batches b with active && !active[b] are skipped.
+// 64 x 64 bf16 tiles through LDS with 16-byte global accesses on both sides:
+// tile row i holds 64 consecutive columns of one source row (8 chunks of 8);
+// a destination row takes 8 tile rows of one column per 16-byte chunk.
+// Widths and offsets are multiples of 8 elements.
+constexpr int kTP = 64 + 8;  // tile pitch (elements): rows stay 16-byte aligned
+
+__device__ __forceinline__ void tile_store_cols(const uint16_t (*tile)[kTP], int64_t c0,
+                                                int64_t C, int64_t q0, int64_t Q,
+                                                uint16_t *dst, int64_t dst_ld) {
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, qc = i & 7;
+    if (c0 + c >= C || q0 + 8 * qc >= Q) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(tile[8 * qc + 2 * j][c]) |
+             (static_cast<uint32_t>(tile[8 * qc + 2 * j + 1][c]) << 16);
+    *reinterpret_cast<uint4 *>(dst + (c0 + c) * dst_ld + q0 + 8 * qc) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16); batches
+// b with active && !active[b] are skipped.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t R, int64_t C,
                                                         const int32_t *active, uint16_t *dst,
                                                         int64_t dst_ld, int64_t dst_bstride,
                                                         int64_t col0) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kTP];
   const int64_t b = blockIdx.z;
   if (active && active[b] == 0) return;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, r0 = static_cast<int64_t>(blockIdx.y) * 64;
   const uint16_t *s = src + b * R * C;
-  uint16_t *d = dst + b * dst_bstride + col0;
-  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
-  for (int r = ly; r < 64; r += 4)
-    if (r0 + r < R && c0 + lx < C) tile[r][lx] = s[(r0 + r) * C + c0 + lx];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, cc = i & 7;
+    if (r0 + r < R && c0 + 8 * cc < C)
+      *reinterpret_cast<uint4 *>(&tile[r][8 * cc]) =
+          *reinterpret_cast<const uint4 *>(s + (r0 + r) * C + c0 + 8 * cc);
+  }
   __syncthreads();
-  for (int c = ly; c < 64; c += 4)
-    if (c0 + c < C && r0 + lx < R) d[(c0 + c) * dst_ld + r0 + lx] = tile[lx][c];
+  tile_store_cols(tile, c0, C, r0, R, dst + b * dst_bstride + col0, dst_ld);
 }
 
-// Rows of a bf16 matrix (row r read from row_index[r] if given, times
-// row_scale[r] if given) written as columns: dst[c * ldd + col(r)], col(r) = r,
-// or, grouped, poff[e] + r - off[e] for the group e holding r (off, poff:
-// [G + 1] row and padded-column offsets). Columns not written stay as they
-// are (the caller zeroes the padding).
+// Rows of a bf16 matrix as columns of dst (ld ldd): destination column q
+// holds source row r(q) (read from row_index[r] if given, times row_scale[r]
+// if given); dense: r(q) = q, valid below R; grouped: column runs of
+// padded length per group, r(q) = off[e] + q - poff[e] for
+// poff[e] <= q < poff[e + 1], valid below off[e + 1]. Invalid columns (the
+// padding) are written as zeros, up to Q columns (grouped: poff[G]).
 __global__ __launch_bounds__(256) void cols_kernel(const uint16_t *src, int64_t ld_src,
                                                    const int32_t *row_index,
                                                    const float *row_scale, int64_t R, int64_t C,
                                                    const int32_t *off, const int32_t *poff, int G,
-                                                   uint16_t *dst, int64_t ldd) {
-  __shared__ uint16_t tile[64][66];
-  __shared__ int64_t col[64];
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
-  if (ly == 0) {
-    const int64_t r = r0 + lx;
-    int64_t cc = r;
-    if (off && r < R) {
-      int lo = 0, hi = G;  // group e with off[e] <= r < off[e + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (off[mid] <= r) lo = mid; else hi = mid;
+                                                   int64_t Q, uint16_t *dst, int64_t ldd) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kTP];
+  __shared__ int64_t srow[64];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, q0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int64_t qend = off ? poff[G] : Q;
+  if (q0 >= qend) return;
+  if (threadIdx.x < 64) {
+    const int64_t q = q0 + threadIdx.x;
+    int64_t r = -1;
+    if (q < qend) {
+      if (off) {
+        int lo = 0, hi = G;  // group e with poff[e] <= q < poff[e + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (poff[mid] <= q) lo = mid; else hi = mid;
+        }
+        const int64_t rr = off[lo] + (q - poff[lo]);
+        r = rr < off[lo + 1] ? rr : -1;
+      } else {
+        r = q < R ? q : -1;
       }
-      cc = poff[lo] + (r - off[lo]);
     }
-    col[lx] = cc;
-  }
-  for (int r = ly; r < 64; r += 4) {
-    const int64_t rr = r0 + r;
-    if (rr < R && c0 + lx < C) {
-      const int64_t sr = row_index ? row_index[rr] : rr;
-      uint16_t v = src[sr * ld_src + c0 + lx];
-      if (row_scale) v = f32_to_bf16(bf16_to_f32(v) * row_scale[rr]);
-      tile[r][lx] = v;
-    }
+    srow[threadIdx.x] = r;
   }
   __syncthreads();
-  for (int c = ly; c < 64; c += 4)
-    if (c0 + c < C && r0 + lx < R) dst[(c0 + c) * ldd + col[lx]] = tile[lx][c];
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int qi = i >> 3, cc = i & 7;
+    if (c0 + 8 * cc >= C) continue;
+    const int64_t r = srow[qi];
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r >= 0) {
+      const int64_t sr = row_index ? row_index[r] : r;
+      v = *reinterpret_cast<const uint4 *>(src + sr * ld_src + c0 + 8 * cc);
+      if (row_scale) {
+        float f[8];
+        Chunk<bf16_t>::unpack(v, f);
+        const float sc = row_scale[r];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] *= sc;
+        v = Chunk<bf16_t>::pack(f);
+      }
+    }
+    *reinterpret_cast<uint4 *>(&tile[qi][8 * cc]) = v;
+  }
+  __syncthreads();
+  tile_store_cols(tile, c0, C, q0, qend, dst, ldd);
 }
 
 // Padded expert column offsets poff[e] = sum of round64(counts) before e, and
@@ -231,12 +271,13 @@ hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t
 
 hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
                        const float *row_scale, int64_t R, int64_t C, const int32_t *off,
-                       const int32_t *poff, int G, void *dst, int64_t ldd, hipStream_t s) {
-  if (R == 0 || C == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64));
+                       const int32_t *poff, int G, int64_t Q, void *dst, int64_t ldd,
+                       hipStream_t s) {
+  if (Q == 0 || C == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((Q + 63) / 64));
   cols_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), ld_src, row_index,
-                                   row_scale, R, C, off, poff, G, static_cast<uint16_t *>(dst),
-                                   ldd);
+                                   row_scale, R, C, off, poff, G, Q,
+                                   static_cast<uint16_t *>(dst), ldd);
   return hipGetLastError();
 }
 

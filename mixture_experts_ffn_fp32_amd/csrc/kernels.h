@@ -224,11 +224,15 @@ hipError_t launch_fill0(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t C,
                             const int32_t *active, void *dst, int64_t dst_ld, int64_t dst_bstride,
                             int64_t col0, hipStream_t s);
-// bf16 rows (gathered by row_index, scaled by row_scale, either optional) to
-// columns of dst (ld ldd), at column r, or grouped: poff[e] + r - off[e]
+// bf16 rows (gathered by row_index, scaled by row_scale, either optional) as
+// columns of dst (ld ldd, a multiple of 8): column q = row q (dense, zeros
+// from R up to Q, a bound of the columns written) or, grouped, the runs
+// [poff[e], poff[e+1]) hold rows [off[e], off[e+1]) then zeros (Q bounds
+// poff[G]); widths multiples of 8
 hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
                        const float *row_scale, int64_t R, int64_t C, const int32_t *off,
-                       const int32_t *poff, int G, void *dst, int64_t ldd, hipStream_t s);
+                       const int32_t *poff, int G, int64_t Q, void *dst, int64_t ldd,
+                       hipStream_t s);
 // padded expert offsets and the K-grouped m-tile tables of heights M1, M2
 hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, int32_t *poff,
                          int32_t *t1, int32_t *n1, int32_t *t2, int32_t *n2, hipStream_t s);
