@@ -107,18 +107,21 @@ struct Plan {
 };
 
 // The pipelined kernel when it applies (bf16, K a multiple of 32, 32-bit
-// operand extents, more than ~32 rows per expert); else the generic kernel:
-// 16-row tiles for few rows per expert, 128x128 otherwise (128x64 for bf16
-// down projections that would give fewer than 256 workgroups).
+// operand extents): 32 x 256 tiles streaming the weights for ~32 rows per
+// expert or fewer (decode), else the tile gemm2_pick chooses; otherwise the
+// generic kernel: 16-row tiles for few rows per expert, 128x128 otherwise
+// (128x64 for bf16 down projections that would give fewer than 256
+// workgroups).
 // (a_rows: rows the GEMM's A operand spans; the pipelined kernel addresses
 // A and each expert's B with 32-bit offsets.)
 GemmPlan plan_one(int64_t rows, int64_t E, int64_t K, int64_t n_out, int glu, int bf,
                   int64_t a_rows) {
-  if (rows <= 32 * E) return {0, TILE_SMALL_M};  // ~32 rows per expert or fewer
   constexpr int64_t kLim = int64_t(1) << 32;
   const bool small_extent = a_rows * K * 2 < kLim && (n_out + 256) * K * 2 < kLim;
-  if (bf && K % 32 == 0 && n_out % 8 == 0 && small_extent)
-    return {1, gemm2_pick(rows, E, K, n_out, glu)};
+  const bool v2 = bf && K % 32 == 0 && n_out % 8 == 0 && small_extent;
+  if (rows <= 32 * E)  // ~32 rows per expert or fewer: weight streaming
+    return v2 ? GemmPlan{1, TILE2_32x256_D2} : GemmPlan{0, TILE_SMALL_M};
+  if (v2) return {1, gemm2_pick(rows, E, K, n_out, glu)};
   const int64_t mt = rows / tile_bm(TILE_LARGE) + (rows < E ? rows : E);
   if (!bf || glu || mt * tile_count(TILE_LARGE, 1, n_out, glu) >= 256) return {0, TILE_LARGE};
   return {0, TILE_TALL_N64};  // few down tiles (narrow model, few experts)
@@ -140,8 +143,10 @@ Plan plan_grouped(const moe_desc *d) {
       dm % 32 == 0 && ds % 32 == 0 && T * dm * 2 < kLim && T * ds * 2 < kLim &&
       (ds + 256) * dm * 2 < kLim && (dm + 256) * ds * 2 < kLim) {
     pl.merged = true;
-    pl.gu.cfg = gemm2_pick(rows, E, dm, d->d_ff, 1, T, ds);
-    pl.dn.cfg = gemm2_pick(rows, E, d->d_ff > ds ? d->d_ff : ds, dm, 0, T, dm);
+    if (rows > 32 * E) {  // (weight-streaming tiles stay as they are)
+      pl.gu.cfg = gemm2_pick(rows, E, dm, d->d_ff, 1, T, ds);
+      pl.dn.cfg = gemm2_pick(rows, E, d->d_ff > ds ? d->d_ff : ds, dm, 0, T, dm);
+    }
   }
   return pl;
 }

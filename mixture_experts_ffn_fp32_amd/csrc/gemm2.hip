@@ -485,6 +485,7 @@ int gemm2_bm(int cfg) {
     case TILE2_128x256: case TILE2_128x128: case TILE2_128x64: case TILE2_128x128_D4:
     case TILE2_128x128_W8D4: case TILE2_128x256_W8: return 128;
     case TILE2_64x128: case TILE2_64x128_D4: return 64;
+    case TILE2_32x256_D3: case TILE2_32x256_D2: return 32;
   }
   return 256;
 }
@@ -559,6 +560,8 @@ hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, cons
     case TILE2_256x128_W8D3: return dispatch2<256, 128, 4, 2, 3>(a, b, epi, s);
     case TILE2_128x256_W8: return dispatch2<128, 256, 2, 4>(a, b, epi, s);
     case TILE2_64x128_D4: return dispatch2<64, 128, 2, 2, 4>(a, b, epi, s);
+    case TILE2_32x256_D3: return dispatch2<32, 256, 1, 4, 3>(a, b, epi, s);
+    case TILE2_32x256_D2: return dispatch2<32, 256, 1, 4, 2>(a, b, epi, s);
   }
   return hipErrorInvalidValue;
 }

@@ -183,7 +183,9 @@ enum Tile2Cfg {
   TILE2_256x256_TALLW = 4, TILE2_128x128 = 5, TILE2_64x128 = 6, TILE2_128x64 = 7,
   // deeper look-ahead (A NA stages ahead, B NA + 1) for tiles that leave LDS room:
   TILE2_128x128_D4 = 8, TILE2_128x128_W8D4 = 9, TILE2_256x128_W8D3 = 10, TILE2_128x256_W8 = 11,
-  TILE2_64x128_D4 = 12
+  TILE2_64x128_D4 = 12,
+  // few rows per expert (weight streaming): 32 rows x 256 weight rows, 4 wavefronts
+  TILE2_32x256_D3 = 13, TILE2_32x256_D2 = 14
 };
 bool gemm2_applicable(const GemmArgs &a, int epi);
 int gemm2_bm(int cfg);

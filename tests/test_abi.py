@@ -179,7 +179,8 @@ def test_plan_paths_of_the_workloads():
         assert (P[n]["gate_up_tile_m"], P[n]["gate_up_tile_n"]) == (256, 256)
         assert P[n]["router_per_token"] == 0 and P[n]["dispatch_one_workgroup"] == 0
     assert P["tiny"]["gate_up_pipelined"] == 0  # fp32: generic kernel
-    assert P["large_decode"]["gate_up_tile_m"] == 16 and P["large_decode"]["merged_shared"] == 0
+    assert (P["large_decode"]["gate_up_tile_m"], P["large_decode"]["gate_up_tile_n"]) == (32, 256)
+    assert P["large_decode"]["merged_shared"] == 1
     assert P["large_decode"]["dispatch_one_workgroup"] == 1
     with pytest.raises(moe.MoeError):
         moe.moe_plan(_desc(T=-1))
