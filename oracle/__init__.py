@@ -67,7 +67,7 @@ def lib():
         L.or_balance_bias.argtypes = [C.c_int32, C.c_int32, C.c_int64, P, C.c_float, P]
         L.or_quantile_balance.argtypes = [P, P, P]
         L.or_router_losses.argtypes = [P, P, P, C.c_double, C.c_double, P]
-        L.or_backward.argtypes = [P, P, P, P, C.c_int64, P, C.c_int32] + [P] * 8
+        L.or_backward.argtypes = [P, P, P, P, C.c_int64, P, C.c_int32] + [P] * 11
         L.or_backward.restype = C.c_int
         for f in ("or_route", "or_forward", "or_expert_rows", "or_combine", "or_dispatch"):
             getattr(L, f).restype = C.c_int
@@ -181,13 +181,15 @@ class Oracle:
         return float(out[0]), float(out[1])
 
     def backward(self, d_out, tokens=None, idx_override=None, experts="all",
-                 router=True, shared=True):
-        """Backward of the (non-latent) layer in fp64 for output gradients
+                 router=True, shared=True, latent=True):
+        """Backward of the layer in fp64 for output gradients
         d_out [n, d] of the listed tokens (all if None). Returns a dict: dx
         [n, d]; w_router [E, d] (router=True); w_gate / w_up [E or 1, d_ff, d]
         and w_down [E or 1, d, d_ff] for experts="all", one expert id, or None;
-        ws_gate / ws_up [d_shared, d], ws_down [d, d_shared] (shared=True).
-        Weight gradients are summed over the listed tokens only."""
+        ws_gate / ws_up [d_shared, d], ws_down [d, d_shared] (shared=True);
+        latent layers: w_lat_down [L, d], w_lat_up [d, L], rms_gamma [L]
+        (latent=True; expert gradients then at width L). Weight gradients are
+        summed over the listed tokens only."""
         sp = self.spec
         t, n = self._tokens(tokens)
         dy = np.ascontiguousarray(d_out, np.float64)
@@ -198,19 +200,26 @@ class Oracle:
         out = {"dx": np.empty((n, sp.d))}
         if router:
             out["w_router"] = np.empty((sp.E, sp.d))
+        de = sp.latent or sp.d
         if want >= -1:
-            out["w_gate"] = np.empty((ne, sp.d_ff, sp.d))
-            out["w_up"] = np.empty((ne, sp.d_ff, sp.d))
-            out["w_down"] = np.empty((ne, sp.d, sp.d_ff))
+            out["w_gate"] = np.empty((ne, sp.d_ff, de))
+            out["w_up"] = np.empty((ne, sp.d_ff, de))
+            out["w_down"] = np.empty((ne, de, sp.d_ff))
         if shared and sp.d_shared:
             out["ws_gate"] = np.empty((sp.d_shared, sp.d))
             out["ws_up"] = np.empty((sp.d_shared, sp.d))
             out["ws_down"] = np.empty((sp.d, sp.d_shared))
+        if latent and sp.latent:
+            out["w_lat_down"] = np.empty((sp.latent, sp.d))
+            out["w_lat_up"] = np.empty((sp.d, sp.latent))
+            if sp.has_rmsnorm:
+                out["rms_gamma"] = np.empty(sp.latent)
         g = out.get
         _check(lib().or_backward(C.byref(self.layer), C.byref(self.tensors), _p(dy), _p(t), n,
                                  _p(ov), want, _p(g("dx")), _p(g("w_router")), _p(g("w_gate")),
                                  _p(g("w_up")), _p(g("w_down")), _p(g("ws_gate")),
-                                 _p(g("ws_up")), _p(g("ws_down"))), "or_backward")
+                                 _p(g("ws_up")), _p(g("ws_down")), _p(g("w_lat_down")),
+                                 _p(g("w_lat_up")), _p(g("rms_gamma"))), "or_backward")
         return out
 
     def expert_rows(self, rows, expert, scale=None):

@@ -615,7 +615,7 @@ static double swiglu_backward(const void *wg, const void *wu, const void *wd, in
   return dg;
 }
 
-/* Backward of the layer (non-latent) for the listed tokens (all if NULL)
+/* Backward of the layer for the listed tokens (all if NULL)
  * with output gradients d_out[n, d] (row j belongs to token tokens[j]):
  *  - dx[n, d] (may be NULL): input gradients (routed experts, shared
  *    experts, router);
@@ -624,7 +624,9 @@ static double swiglu_backward(const void *wg, const void *wu, const void *wd, in
  *    expert if want_expert == -1 (dw_gate / dw_up [E, d_ff, d], dw_down
  *    [E, d, d_ff]), for expert want_expert only (one expert's shape), or
  *    none if want_expert < -1 (the three may also be NULL);
- *  - dws_gate / dws_up [d_shared, d], dws_down [d, d_shared] (may be NULL).
+ *  - dws_gate / dws_up [d_shared, d], dws_down [d, d_shared] (may be NULL);
+ *  - latent layers: dw_lat_down [L, d], dw_lat_up [d, L], d_rms_gamma [L]
+ *    (may be NULL; expert weight gradients are then at the routed width L).
  * Gradient outputs are zeroed first. Experts no listed token selects keep
  * zero gradients. idx_override [n, K] replaces the selection (near ties).
  * Tokens run in parallel when no weight gradient is requested. */
@@ -632,14 +634,16 @@ int or_backward(const or_layer *L, const or_tensors *W, const double *d_out,
                 const int64_t *tokens, int64_t n, const int32_t *idx_override,
                 int32_t want_expert, double *dx, double *dw_router, double *dw_gate,
                 double *dw_up, double *dw_down, double *dws_gate, double *dws_up,
-                double *dws_down) {
+                double *dws_down, double *dw_lat_down, double *dw_lat_up,
+                double *d_rms_gamma) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if (L->latent) return -3;
   const int d = L->d, f = L->d_ff, E = L->E, K = L->K, ds = L->d_shared;
-  const int64_t egu = (int64_t)f * d;
+  const int de = L->latent ? L->latent : d; /* routed width */
+  const int64_t egu = (int64_t)f * de;
   const int want_w = want_expert >= -1 && (dw_gate || dw_up || dw_down);
-  const int serial = want_w || dw_router || dws_gate || dws_up || dws_down;
+  const int serial = want_w || dw_router || dws_gate || dws_up || dws_down || dw_lat_down ||
+                     dw_lat_up || d_rms_gamma;
   if (dx) memset(dx, 0, sizeof(double) * (size_t)(n * d));
   if (dw_router) memset(dw_router, 0, sizeof(double) * (size_t)E * d);
   const int64_t n_exp = want_expert == -1 ? E : 1;
@@ -653,6 +657,11 @@ int or_backward(const or_layer *L, const or_tensors *W, const double *d_out,
     if (dws_up) memset(dws_up, 0, sizeof(double) * (size_t)ds * d);
     if (dws_down) memset(dws_down, 0, sizeof(double) * (size_t)ds * d);
   }
+  if (L->latent) {
+    if (dw_lat_down) memset(dw_lat_down, 0, sizeof(double) * (size_t)de * d);
+    if (dw_lat_up) memset(dw_lat_up, 0, sizeof(double) * (size_t)de * d);
+    if (d_rms_gamma) memset(d_rms_gamma, 0, sizeof(double) * (size_t)de);
+  }
 #pragma omp parallel for schedule(dynamic, 1) if (!serial)
   for (int64_t j = 0; j < n; ++j) {
     const int64_t t = tokens ? tokens[j] : j;
@@ -664,18 +673,71 @@ int or_backward(const or_layer *L, const or_tensors *W, const double *d_out,
     double *dg = g + K;
     double *dr = (double *)malloc(sizeof(double) * (size_t)E);
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    /* routed input and its gradient (latent: z = W_lat_down x, else x) */
+    double *zv = (double *)malloc(sizeof(double) * (size_t)de);
+    double *dz = (double *)calloc((size_t)de, sizeof(double));
+    double *dR = (double *)malloc(sizeof(double) * (size_t)de);
     double gap;
     const double *dy = d_out + j * d;
     load_row(W->x, L->act, t, d, xv);
     route_one(L, W, xv, idx_override ? idx_override + j * K : NULL, idx, g, &gap, NULL);
+    if (L->latent) {
+      /* StableLatentMoE "Return to model width": y = W_lat_up R' + shared,
+       * R' = R / sqrt(mean(R^2) + eps) * gamma (or R' = R without the norm),
+       * R = sum_k g_k FFN_{e_k}(z), z = W_lat_down x. */
+      for (int l = 0; l < de; ++l) zv[l] = dot(W->w_lat_down, L->act, (int64_t)l * d, xv, d);
+      double *R = (double *)calloc((size_t)de, sizeof(double));
+      double *hb = (double *)malloc(sizeof(double) * (size_t)f);
+      for (int k = 0; k < K; ++k) {
+        const int64_t e = idx[k];
+        swiglu_acc(W->w_gate, W->w_up, W->w_down, L->act, e * egu, e * egu, de, f, zv, g[k], R,
+                   hb);
+      }
+      double inv = 1.0;
+      if (L->has_rmsnorm) {
+        double ms = 0.0;
+        for (int l = 0; l < de; ++l) ms += R[l] * R[l];
+        inv = 1.0 / sqrt(ms / de + L->rms_eps);
+      }
+      /* dR' = W_lat_up^T dy; dW_lat_up += dy R'^T */
+      double sR = 0.0;
+      for (int l = 0; l < de; ++l) {
+        double s2 = 0.0;
+        for (int i = 0; i < d; ++i) s2 += ld(W->w_lat_up, L->act, (int64_t)i * de + l) * dy[i];
+        const double gam = (L->has_rmsnorm && W->rms_gamma) ? (double)W->rms_gamma[l] : 1.0;
+        const double Rn = L->has_rmsnorm ? R[l] * inv * gam : R[l];
+        if (dw_lat_up)
+          for (int i = 0; i < d; ++i) dw_lat_up[(int64_t)i * de + l] += dy[i] * Rn;
+        if (L->has_rmsnorm && d_rms_gamma) d_rms_gamma[l] += s2 * R[l] * inv;
+        dR[l] = L->has_rmsnorm ? s2 * gam : s2; /* gamma-weighted dR' for the norm */
+        sR += dR[l] * R[l];
+      }
+      /* RMSNorm: dR = inv (gamma dR') - R inv^3 <gamma dR', R> / L */
+      if (L->has_rmsnorm)
+        for (int l = 0; l < de; ++l) dR[l] = inv * dR[l] - R[l] * inv * inv * inv * sR / de;
+      free(hb);
+      free(R);
+    } else {
+      memcpy(zv, xv, sizeof(double) * (size_t)d);
+      memcpy(dR, dy, sizeof(double) * (size_t)d);
+    }
     for (int k = 0; k < K; ++k) {
       const int64_t e = idx[k];
       const int mine = want_w && (want_expert == -1 || want_expert == e);
       const int64_t wo = want_expert == -1 ? e * egu : 0;
-      dg[k] = swiglu_backward(W->w_gate, W->w_up, W->w_down, L->act, e * egu, e * egu, d, f, xv,
-                              dy, g[k], dv, mine && dw_gate ? dw_gate + wo : NULL,
+      dg[k] = swiglu_backward(W->w_gate, W->w_up, W->w_down, L->act, e * egu, e * egu, de, f, zv,
+                              dR, g[k], L->latent ? dz : dv,
+                              mine && dw_gate ? dw_gate + wo : NULL,
                               mine && dw_up ? dw_up + wo : NULL,
                               mine && dw_down ? dw_down + wo : NULL, buf);
+    }
+    if (L->latent) { /* dx += W_lat_down^T dz; dW_lat_down += dz x^T */
+      for (int l = 0; l < de; ++l) {
+        for (int i = 0; i < d; ++i) {
+          dv[i] += ld(W->w_lat_down, L->act, (int64_t)l * d + i) * dz[l];
+          if (dw_lat_down) dw_lat_down[(int64_t)l * d + i] += dz[l] * xv[i];
+        }
+      }
     }
     if (ds > 0)
       swiglu_backward(W->ws_gate, W->ws_up, W->ws_down, L->act, 0, 0, d, ds, xv, dy, 1.0, dv,
@@ -689,6 +751,9 @@ int or_backward(const or_layer *L, const or_tensors *W, const double *d_out,
       }
     }
     if (dx) memcpy(dx + j * d, dv, sizeof(double) * (size_t)d);
+    free(dR);
+    free(dz);
+    free(zv);
     free(idx);
     free(dr);
     free(g);

@@ -693,6 +693,56 @@ def _fd_layer(route, seed, renorm=False, scale=1.0, E=5, K=2, T=6):
     return w, a
 
 
+_FD_LAT_KEYS = ("x", "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+                "w_lat_down", "w_lat_up", "rms_gamma")
+
+
+def _fd_latent_layer(route, seed, norm=True, renorm=False):
+    w = custom(f"fdl_{route}_{seed}", config_no=850 + seed, T=5, d=8, latent=6, d_ff=5, E=5,
+               K=2, n_shared=1, d_ff_shared=4, act="f32", route=route, renormalize=renorm,
+               has_rmsnorm=norm, bias_std=0.2 if route == "sigmoid_bias" else 0.0)
+    a = moe_synth.generate(w)
+    rng = np.random.default_rng(seed)
+    if norm:  # a gain away from one, so its gradient and role are visible
+        a["rms_gamma"] = (0.5 + rng.integers(0, 257, size=w.latent) / 256).astype(np.float32)
+    for k in _FD_LAT_KEYS + ("bias",):
+        if a.get(k) is not None:
+            a[k] = (np.round(np.asarray(a[k], np.float64) * 256) / 256).astype(np.float32)
+    return w, a
+
+
+@pytest.mark.parametrize("route,norm,renorm,seed", [
+    ("sigmoid_bias", True, False, 1), ("sigmoid_bias", True, True, 2),
+    ("topk_softmax", False, False, 3), ("topk_softmax", True, False, 4),
+])
+def test_backward_latent_matches_finite_differences(route, norm, renorm, seed):
+    """StableLatentMoE layer (down-projection to L, routed experts in L,
+    optional RMSNorm, up-projection): every gradient, incl. the latent
+    projections and the RMSNorm gain, against central differences."""
+    w, a = _fd_latent_layer(route, seed, norm, renorm)
+    h = 2.0 ** -12  # the norm curves the loss more: a smaller step (still exact in fp32)
+    rng = np.random.default_rng(100 + seed)
+    c = np.round(rng.standard_normal((w.T, w.d)) * 256) / 256
+    grads = oracle.Oracle(w, a).backward(c)
+    gmap = dict(grads)
+    gmap["x"] = grads["dx"]
+    _, idx0 = _fd_loss(w, a, c)
+    for key in _FD_LAT_KEYS:
+        if key == "rms_gamma" and not norm:
+            continue
+        V = rng.integers(-1, 2, size=np.shape(a[key])).astype(np.float64) / 4
+        ap, am = dict(a), dict(a)
+        ap[key] = (np.asarray(a[key], np.float64) + h * V).astype(np.float32)
+        am[key] = (np.asarray(a[key], np.float64) - h * V).astype(np.float32)
+        assert np.array_equal(np.asarray(ap[key], np.float64) - a[key], h * V)
+        lp, ip = _fd_loss(w, ap, c)
+        lm, im = _fd_loss(w, am, c)
+        assert np.array_equal(ip, idx0) and np.array_equal(im, idx0), "selection moved"
+        fd = (lp - lm) / (2 * h)
+        an = float(np.sum(gmap[key] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, fd, an)
+
+
 def _fd_loss(w, a, c):
     out, idx, _, _ = oracle.Oracle(w, a).forward()
     return float(np.sum(out * c)), idx
