@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward-pass timing (bf16 non-latent layers)")
+                    help="skip the backward-pass timing (bf16 layers)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -240,16 +240,21 @@ def main():
     rl = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E,
           "load_balancing_loss": round(float(losses[0]), 7),
           "z_loss": round(float(losses[1]), 7)}
-    # backward pass (bf16 layers without the latent projection): input and all
-    # weight gradients for an output gradient of ones
+    # backward pass (bf16 layers): input and all weight gradients for an output
+    # gradient of ones
     bwd = None
-    if not args.no_backward and w.act == "bf16" and not w.latent:
+    if not args.no_backward and w.act == "bf16":
         dy = torch.ones((w.T, w.d), dtype=layer.act, device=dev)
-        shapes = {"w_router": (w.E, w.d), "w_gate": (w.E, w.d_ff, w.d),
-                  "w_up": (w.E, w.d_ff, w.d), "w_down": (w.E, w.d, w.d_ff)}
+        de = w.d_e
+        shapes = {"w_router": (w.E, w.d), "w_gate": (w.E, w.d_ff, de),
+                  "w_up": (w.E, w.d_ff, de), "w_down": (w.E, de, w.d_ff)}
         if w.d_shared:
             shapes.update(ws_gate=(w.d_shared, w.d), ws_up=(w.d_shared, w.d),
                           ws_down=(w.d, w.d_shared))
+        if w.latent:
+            shapes.update(w_lat_down=(w.latent, w.d), w_lat_up=(w.d, w.latent))
+            if w.has_rmsnorm:
+                shapes["rms_gamma"] = (w.latent,)
         grads = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
         d_x = torch.empty_like(x)
         layer.backward(x, dy, d_x=d_x, grads=grads, stream=stream)
@@ -259,8 +264,11 @@ def main():
         e_ev.record(stream)
         torch.cuda.synchronize()
         bms = b_ev.elapsed_time(e_ev) / 3
-        # routed + shared: forward gate/up recomputed, d(h), d(x), 3 weight gradients
-        fl = 2.0 * (w.T * w.K * w.d * w.d_ff + w.T * w.d * w.d_shared) * (2 + 1 + 2 + 3)
+        # routed + shared: forward gate/up recomputed, d(h), d(x), 3 weight gradients;
+        # latent: + the routed down GEMM recomputed, the two projections' three
+        fl = 2.0 * (w.T * w.K * de * w.d_ff + w.T * w.d * w.d_shared) * (2 + 1 + 2 + 3)
+        if w.latent:
+            fl += 2.0 * w.T * w.K * de * w.d_ff + 2.0 * w.T * w.d * w.latent * 5
         bwd = {"ms_per_call": round(bms, 4), "tokens_per_s": round(w.T / (bms / 1e3), 1),
                "tflops": round(fl / (bms / 1e3) / 1e12, 2),
                "note": "moe_backward: input, router, expert and shared weight gradients; tflops "

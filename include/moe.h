@@ -262,10 +262,13 @@ MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *
  * NULL member is not computed). Shapes as in moe_weights. */
 typedef struct moe_grads {
   float *w_router;        /* [E, d_model]                              */
-  float *w_gate, *w_up;   /* [E, d_ff, d_model]                        */
-  float *w_down;          /* [E, d_model, d_ff]                        */
+  float *w_gate, *w_up;   /* [E, d_ff, d_e]  (d_e = latent ? L : d_model) */
+  float *w_down;          /* [E, d_e, d_ff]                            */
   float *ws_gate, *ws_up; /* [d_shared, d_model]                       */
   float *ws_down;         /* [d_model, d_shared]                       */
+  float *w_lat_down;      /* [L, d_model]   (latent layers)            */
+  float *w_lat_up;        /* [d_model, L]   (latent layers)            */
+  float *rms_gamma;       /* [L]            (latent layers with RMSNorm) */
 } moe_grads;
 
 /* Device workspace, in bytes, that moe_backward needs for this layer (more
@@ -288,9 +291,13 @@ MOE_API int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
  *    array is overwritten (not accumulated);
  *  - intermediate products are bf16 operands with fp32 accumulation, like
  *    the forward; router gradients are fp32.
- * Supported: bf16 layers without the latent projection, d_model, d_ff and
- * d_shared multiples of 32. Errors: MOE_ERR_MODE (fp32 or latent layers),
- * MOE_ERR_SHAPE (other widths, or operands beyond 4 GiB), MOE_ERR_NULL,
+ *  - latent layers ("StableLatentMoE and QuantileBalancer"): the routed sum
+ *    and its RMSNorm are recomputed; gradients also reach W_lat_down,
+ *    W_lat_up and the RMSNorm gain (rms_gamma NULL in w: a gain of ones,
+ *    whose gradient is still reported if grads->rms_gamma is given).
+ * Supported: bf16 layers with d_model, d_ff, d_shared and L multiples of
+ * 32. Errors: MOE_ERR_MODE (fp32 layers), MOE_ERR_SHAPE (other widths, or
+ * operands beyond 4 GiB), MOE_ERR_NULL,
  * MOE_ERR_WORKSPACE (below moe_backward_workspace_size), MOE_ERR_HIP.
  * T == 0 is a no-op. */
 MOE_API int moe_backward(const moe_desc *desc, const moe_weights *w, const void *x,

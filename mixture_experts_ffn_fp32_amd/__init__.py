@@ -54,7 +54,8 @@ class MoePlanInfo(C.Structure):
 
 class MoeGrads(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
-        "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+        "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_lat_down",
+        "w_lat_up", "rms_gamma")]
 
 
 class MoeProbe(C.Structure):

@@ -407,16 +407,18 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
 
 // ------------------------------------------------------------ backward
 // Workspace of moe_backward beyond the forward layout: transposed weights of
-// the active experts, per-row fp32 pre-activations and gradients, and the
+// the active experts, per-row fp32 pre-activations and gradients, the
 // activations in expert-contiguous, 64-padded columns for the K-grouped
-// weight-gradient GEMMs.
+// weight-gradient GEMMs, and (latent layers) the recomputed routed sum and
+// the projections' buffers. de is the routed width (d_model, or L).
 struct BwdLayout {
   size_t poff, kt1, kn1, kt2, kn2, tiles, ntiles;
   size_t wguT, wdT, wsguT, wsdT;
   size_t apre, upre, dhu, h, dau, dg, dr, dxs;
   size_t apre_s, upre_s, dhu_s, h_s, dau_s, dxsh;
-  size_t cols, cols_bytes;  // block of transposed activations
   size_t xsT, dysT, daT, duT, hT, xT, dyT, dashT, dushT, hshT;
+  // latent
+  size_t wluT, wldT, yf, R, rinv, Rp, dRp, dR, dz, dxl, gpart, RpT, dzT;
   size_t total;
   int64_t RP, TP, kt_cap;
 };
@@ -424,7 +426,8 @@ struct BwdLayout {
 BwdLayout bwd_layout_of(const moe_desc *d) {
   BwdLayout B{};
   const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
-  const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared;
+  const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
+  const int64_t de = Lt ? Lt : dm;
   size_t o = layout_of(d).total;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -433,16 +436,16 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   };
   B.RP = (rows + 63) / 64 * 64 + 64 * E;  // padded expert columns (upper bound)
   B.TP = (T + 63) / 64 * 64;
-  B.kt_cap = E * ((f > dm ? f : dm) + 63) / 64 + 1;
+  B.kt_cap = E * ((f > de ? f : de) + 63) / 64 + 1;
   B.poff = take((E + 1) * 4);
   B.kt1 = take(B.kt_cap * kTileInts * 4);
   B.kn1 = take(4);
   B.kt2 = take(B.kt_cap * kTileInts * 4);
   B.kn2 = take(4);
-  B.tiles = take(static_cast<size_t>(grouped_tile_bound(rows, E, 64)) * kTileInts * 4);
+  B.tiles = take(static_cast<size_t>(grouped_tile_bound(rows, E, 32)) * kTileInts * 4);
   B.ntiles = take(4);
-  B.wguT = take(E * dm * 2 * f * 2);  // [E, d, 2 f]: W_gate^T | W_up^T
-  B.wdT = take(E * f * dm * 2);       // [E, f, d]
+  B.wguT = take(E * de * 2 * f * 2);  // [E, de, 2 f]: W_gate^T | W_up^T
+  B.wdT = take(E * f * de * 2);       // [E, f, de]
   B.wsguT = take(dm * 2 * ds * 2);
   B.wsdT = take(ds * dm * 2);
   B.apre = take(rows * f * 4);
@@ -452,16 +455,15 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.dau = take(rows * 2 * f * 2);
   B.dg = take(rows * 4);
   B.dr = take(rows * 4);
-  B.dxs = take(rows * dm * 4);
+  B.dxs = take(rows * de * 4);
   B.apre_s = take(T * ds * 4);
   B.upre_s = take(T * ds * 4);
   B.dhu_s = take(T * ds * 4);
   B.h_s = take(T * ds * 2);
   B.dau_s = take(T * 2 * ds * 2);
   B.dxsh = take(T * dm * 4);
-  B.cols = o;
-  B.xsT = take(dm * B.RP * 2);
-  B.dysT = take(dm * B.RP * 2);
+  B.xsT = take(de * B.RP * 2);
+  B.dysT = take(de * B.RP * 2);
   B.daT = take(f * B.RP * 2);
   B.duT = take(f * B.RP * 2);
   B.hT = take(f * B.RP * 2);
@@ -470,7 +472,21 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.dashT = take(ds * B.TP * 2);
   B.dushT = take(ds * B.TP * 2);
   B.hshT = take(ds * B.TP * 2);
-  B.cols_bytes = o - B.cols;
+  if (Lt) {
+    B.wluT = take(Lt * dm * 2);
+    B.wldT = take(dm * Lt * 2);
+    B.yf = take(rows * Lt * 4);
+    B.R = take(T * Lt * 4);
+    B.rinv = take(T * 4);
+    B.Rp = take(T * Lt * 2);
+    B.dRp = take(T * Lt * 4);
+    B.dR = take(T * Lt * 2);
+    B.dz = take(T * Lt * 2);
+    B.dxl = take(T * dm * 4);
+    B.gpart = take(static_cast<size_t>(colsum_blocks(T)) * Lt * 4);
+    B.RpT = take(Lt * B.TP * 2);
+    B.dzT = take(Lt * B.TP * 2);
+  }
   B.total = o;
   return B;
 }
@@ -478,15 +494,17 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
 int check_backward(const moe_desc *d) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (d->act_dtype != MOE_BF16 || d->latent) return MOE_ERR_MODE;
-  if (d->d_model % 32 || d->d_ff % 32 || d->d_shared % 32) return MOE_ERR_SHAPE;
+  if (d->act_dtype != MOE_BF16) return MOE_ERR_MODE;
+  if (d->d_model % 32 || d->d_ff % 32 || d->d_shared % 32 || d->latent % 32) return MOE_ERR_SHAPE;
   constexpr int64_t kLim = int64_t(1) << 32;  // 32-bit operand offsets of the GEMMs
   const int64_t T = d->T, rows = T * d->top_k, E = d->n_experts;
   const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared;
-  const int64_t RP = rows + 64 * E, mx = (dm > f ? dm : f) + 256;
-  if (T * dm * 2 >= kLim || rows * 2 * f * 2 >= kLim || mx * RP * 2 >= kLim ||
+  const int64_t de = d->latent ? d->latent : dm, wm = dm > de ? dm : de;
+  const int64_t RP = (rows + 63) / 64 * 64 + 64 * E, mx = (wm > f ? wm : f) + 256;
+  const int64_t TP = (T + 63) / 64 * 64;
+  if (T * wm * 2 >= kLim || rows * 2 * f * 2 >= kLim || mx * RP * 2 >= kLim ||
       (f + 256) * 2 * f * 2 >= kLim || mx * 2 * (ds > f ? ds : f) * 2 >= kLim ||
-      T * 2 * ds * 2 >= kLim || mx * ((T + 63) / 64 * 64) * 2 >= kLim)
+      T * 2 * ds * 2 >= kLim || mx * TP * 2 >= kLim || mx * wm * 2 >= kLim)
     return MOE_ERR_SHAPE;
   return MOE_OK;
 }
@@ -688,7 +706,6 @@ int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
   if (d->T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *wsb = static_cast<char *>(ws);
-  const int64_t rows_n = d->T * d->top_k;
   const Plan pl = plan_grouped(d);
   const Tables tb = tables_of(wsb, L, pl);
   MOE_TRY(launch_tiles(offsets, d->n_experts, pl.gu.bm(), const_cast<int32_t *>(tb.gu),
@@ -843,6 +860,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   if (rc) return rc;
   if (!w || !w->w_router || !gr) return MOE_ERR_NULL;
   if ((rc = check_expert_weights(d, w)) || (rc = check_combine_weights(d, w))) return rc;
+  if (d->latent && !w->w_lat_down) return MOE_ERR_NULL;
   if (!ws || (d->T > 0 && (!x || !d_out))) return MOE_ERR_NULL;
   const BwdLayout B = bwd_layout_of(d);
   if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
@@ -853,7 +871,8 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   auto F = [&](size_t off) { return reinterpret_cast<float *>(wsb + off); };
   auto I = [&](size_t off) { return reinterpret_cast<int32_t *>(wsb + off); };
   const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
-  const int dm = d->d_model, f = d->d_ff, ds = d->d_shared;
+  const int dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
+  const int de = Lt ? Lt : dm;  // routed width
   int32_t *idx = I(L.idx), *counts = I(L.counts), *offsets = I(L.offsets);
   int32_t *stok = I(L.stok), *inv = I(L.inv);
   float *sw = F(L.sw);
@@ -895,22 +914,26 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   sc.inv = inv;
   sc.sorted_w = sw;
   MOE_TRY(run_dispatch(sa, sc, s));
-  const int cfg = gemm2_pick(rows, E, dm, f, 0, rows, f);
+  const int cfg = gemm2_pick(rows, E, de, f, 0, rows, f);
   const int bm = gemm2_bm(cfg);
   MOE_TRY(launch_tiles(offsets, static_cast<int>(E), bm, I(B.tiles), I(B.ntiles), s));
   const int64_t mt_bound = grouped_tile_bound(rows, E, bm);
 
-  // 2. transposed weights of the active experts (and the shared FFN)
-  MOE_TRY(launch_transpose(w->w_gate, E, f, dm, counts, wsb + B.wguT, 2 * f, dm * 2 * f, 0, s));
-  MOE_TRY(launch_transpose(w->w_up, E, f, dm, counts, wsb + B.wguT, 2 * f, dm * 2 * f, f, s));
-  MOE_TRY(launch_transpose(w->w_down, E, dm, f, counts, wsb + B.wdT, dm, f * dm, 0, s));
+  // 2. transposed weights of the active experts (and the shared FFN, the
+  //    latent projections)
+  MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, s));
+  MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, s));
+  MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, s));
   if (ds) {
     MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, s));
     MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, s));
     MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, s));
   }
+  if (Lt) {
+    MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, s));
+    MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, s));
+  }
 
-  // grouped GEMM over the sorted rows (tile table of this call)
   auto grouped = [&](const void *a, int64_t lda, const int32_t *a_rows, int64_t a_extent,
                      const void *b, int64_t ldb, int64_t b_stride, int Kd, int N, void *out,
                      int64_t ldo) {
@@ -946,19 +969,27 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     g.ldo = ldo;
     return g;
   };
-  auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c) {
-    if (!gemm2_applicable(a, EPI_STORE_F32) || (b && !gemm2_applicable(*b, EPI_STORE_F32)))
-      return MOE_ERR_SHAPE;
-    return launch_gemm2(a, EPI_STORE_F32, c, s, b) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c, int epi = EPI_STORE_F32) {
+    if (!gemm2_applicable(a, epi) || (b && !gemm2_applicable(*b, epi))) return MOE_ERR_SHAPE;
+    return launch_gemm2(a, epi, c, s, b) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   };
+  auto pick_dense = [&](int64_t M, int Kd, int N) { return gemm2_pick(M, 0, Kd, N, 0); };
   const int cfg_s = ds ? gemm2_pick(T, 0, dm, ds, 0, T, ds) : cfg;
 
-  // 3. pre-activations a = W_gate x, u = W_up x (fp32), routed and shared
+  // routed input rows (x, or z = x W_lat_down^T as the forward computes it)
+  const void *rin = x;
+  if (Lt) {
+    GemmArgs gz = dense(x, dm, w->w_lat_down, dm, dm, Lt, T, wsb + L.z, Lt);
+    MOE_TRY(launch_dense(gz, EPI_STORE, 1, s));
+    rin = wsb + L.z;
+  }
+
+  // 3. pre-activations a, u (fp32), routed and shared
   {
-    const GemmArgs ga = grouped(x, dm, stok, T, w->w_gate, dm, static_cast<int64_t>(f) * dm, dm,
+    const GemmArgs ga = grouped(rin, de, stok, T, w->w_gate, de, static_cast<int64_t>(f) * de, de,
                                 f, F(B.apre), f);
-    const GemmArgs gu = grouped(x, dm, stok, T, w->w_up, dm, static_cast<int64_t>(f) * dm, dm, f,
-                                F(B.upre), f);
+    const GemmArgs gu = grouped(rin, de, stok, T, w->w_up, de, static_cast<int64_t>(f) * de, de,
+                                f, F(B.upre), f);
     if ((rc = gemm(ga, &gu, cfg))) return rc;
     if (ds) {
       const GemmArgs sa2 = dense(x, dm, w->ws_gate, dm, dm, ds, T, F(B.apre_s), ds);
@@ -966,10 +997,31 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
       if ((rc = gemm(sa2, &su, cfg_s))) return rc;
     }
   }
+
+  // routed output gradient per token: d_out, or (latent) the RMSNorm
+  // backward of W_lat_up^T d_out on the recomputed routed sum
+  const void *rdy = d_out;
+  if (Lt) {
+    MOE_TRY(launch_bwd_rows(F(B.apre), F(B.upre), nullptr, nullptr, rows, f, wsb + B.h, nullptr,
+                            nullptr, s));
+    GemmArgs gy = grouped(wsb + B.h, f, nullptr, rows, w->w_down, f,
+                          static_cast<int64_t>(Lt) * f, f, Lt, F(B.yf), Lt);
+    gy.row_scale = sw;
+    gy.out_f32 = 1;
+    if ((rc = gemm(gy, nullptr, cfg, EPI_SCALE))) return rc;
+    MOE_TRY(launch_latent_fwd(F(B.yf), inv, T, static_cast<int>(K), Lt, d->has_rmsnorm,
+                              d->rms_eps, w->rms_gamma, F(B.R), F(B.rinv), wsb + B.Rp, s));
+    const GemmArgs gp = dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
+    if ((rc = gemm(gp, nullptr, pick_dense(T, dm, Lt)))) return rc;
+    MOE_TRY(launch_latent_bwd(F(B.dRp), F(B.R), F(B.rinv), w->rms_gamma, T, Lt,
+                              d->has_rmsnorm, wsb + B.dR, s));
+    rdy = wsb + B.dR;
+  }
+
   // 4. W_down^T dy per sorted row (unscaled) and per token for the shared FFN
   {
-    const GemmArgs gd = grouped(d_out, dm, stok, T, wsb + B.wdT, dm,
-                                static_cast<int64_t>(f) * dm, dm, f, F(B.dhu), f);
+    const GemmArgs gd = grouped(rdy, de, stok, T, wsb + B.wdT, de, static_cast<int64_t>(f) * de,
+                                de, f, F(B.dhu), f);
     if (ds) {
       const GemmArgs sd = dense(d_out, dm, wsb + B.wsdT, dm, dm, ds, T, F(B.dhu_s), ds);
       if ((rc = gemm(gd, &sd, cfg))) return rc;
@@ -985,10 +1037,12 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
                             wsb + B.dau_s, nullptr, s));
   MOE_TRY(launch_router_backward(ra, 1, inv, F(B.dg), F(B.dr), s));
 
-  // 6. input gradient: [da | du] [W_gate^T | W_up^T]^T per row, shared, router
-  if (d_x) {
+  // 6. input gradient: [da | du] [W_gate^T | W_up^T]^T per row (to x, or to z
+  //    and through W_lat_down), shared, router
+  const bool need_dz = d_x || (Lt && gr->w_lat_down);
+  if (need_dz) {
     const GemmArgs gx = grouped(wsb + B.dau, 2 * f, nullptr, rows, wsb + B.wguT, 2 * f,
-                                static_cast<int64_t>(dm) * 2 * f, 2 * f, dm, F(B.dxs), dm);
+                                static_cast<int64_t>(de) * 2 * f, 2 * f, de, F(B.dxs), de);
     if (ds) {
       const GemmArgs sx = dense(wsb + B.dau_s, 2 * ds, wsb + B.wsguT, 2 * ds, 2 * ds, dm, T,
                                 F(B.dxsh), dm);
@@ -996,25 +1050,37 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     } else if ((rc = gemm(gx, nullptr, cfg))) {
       return rc;
     }
-    MOE_TRY(launch_bwd_dx(F(B.dxs), ds ? F(B.dxsh) : nullptr, inv, idx, F(B.dr), w->w_router, T,
-                          static_cast<int>(K), dm, d_x, s));
   }
+  if (Lt && need_dz) {  // dz = sum_k dX rows (bf16), dx_lat = dz W_lat_down
+    MOE_TRY(launch_bwd_dx(F(B.dxs), nullptr, nullptr, inv, idx, nullptr, nullptr, T,
+                          static_cast<int>(K), Lt, wsb + B.dz, s));
+    if (d_x) {
+      const GemmArgs gl = dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
+      if ((rc = gemm(gl, nullptr, pick_dense(T, Lt, dm)))) return rc;
+    }
+  }
+  if (d_x)
+    MOE_TRY(launch_bwd_dx(Lt ? nullptr : F(B.dxs), ds ? F(B.dxsh) : nullptr,
+                          Lt ? F(B.dxl) : nullptr, inv, idx, F(B.dr), w->w_router, T,
+                          static_cast<int>(K), dm, d_x, s));
 
   // 7. weight gradients
   if (gr->w_router)
     MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, gr->w_router, s));
+  if (Lt && d->has_rmsnorm && gr->rms_gamma)
+    MOE_TRY(launch_colsum(F(B.dRp), F(B.R), F(B.rinv), T, Lt, F(B.gpart), gr->rms_gamma, s));
   const bool want_e = gr->w_gate || gr->w_up || gr->w_down;
   const bool want_s = ds && (gr->ws_gate || gr->ws_up || gr->ws_down);
-  if (!want_e && !want_s) return MOE_OK;
-  const int cfg_k = gemm2_pick(E * (f > dm ? f : dm), 0, rows / E + 64, f < dm ? f : dm, 0);
+  const bool want_l = Lt && (gr->w_lat_up || gr->w_lat_down);
+  const int cfg_k = gemm2_pick(E * (f > de ? f : de), 0, rows / E + 64, f < de ? f : de, 0);
   if (want_e) {
-    MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, dm, gemm2_bm(cfg_k), I(B.poff),
+    MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, de, gemm2_bm(cfg_k), I(B.poff),
                           I(B.kt1), I(B.kn1), I(B.kt2), I(B.kn2), s));
     const int G = static_cast<int>(E);
     const int32_t *po = I(B.poff);
     const int64_t RP = B.RP;
-    MOE_TRY(launch_cols(x, dm, stok, nullptr, rows, dm, offsets, po, G, RP, wsb + B.xsT, RP, s));
-    MOE_TRY(launch_cols(d_out, dm, stok, sw, rows, dm, offsets, po, G, RP, wsb + B.dysT, RP, s));
+    MOE_TRY(launch_cols(rin, de, stok, nullptr, rows, de, offsets, po, G, RP, wsb + B.xsT, RP, s));
+    MOE_TRY(launch_cols(rdy, de, stok, sw, rows, de, offsets, po, G, RP, wsb + B.dysT, RP, s));
     MOE_TRY(launch_cols(wsb + B.dau, 2 * f, nullptr, nullptr, rows, f, offsets, po, G, RP,
                         wsb + B.daT, RP, s));
     MOE_TRY(launch_cols(wsb + B.dau + static_cast<size_t>(f) * 2, 2 * f, nullptr, nullptr, rows,
@@ -1041,11 +1107,10 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
       return g;
     };
     if (gr->w_gate || gr->w_up) {
-      // a scratch target for a missing one keeps both in one launch
-      void *og = gr->w_gate ? static_cast<void *>(gr->w_gate) : F(B.dxs);
-      void *ou = gr->w_up ? static_cast<void *>(gr->w_up) : F(B.dxs);
-      const GemmArgs kg = kgrouped(wsb + B.daT, f, wsb + B.xsT, dm, I(B.kt1), I(B.kn1), og);
-      const GemmArgs ku = kgrouped(wsb + B.duT, f, wsb + B.xsT, dm, I(B.kt1), I(B.kn1), ou);
+      const GemmArgs kg = kgrouped(wsb + B.daT, f, wsb + B.xsT, de, I(B.kt1), I(B.kn1),
+                                   gr->w_gate ? static_cast<void *>(gr->w_gate) : nullptr);
+      const GemmArgs ku = kgrouped(wsb + B.duT, f, wsb + B.xsT, de, I(B.kt1), I(B.kn1),
+                                   gr->w_up ? static_cast<void *>(gr->w_up) : nullptr);
       if (gr->w_gate && gr->w_up) {
         if ((rc = gemm(kg, &ku, cfg_k))) return rc;
       } else if ((rc = gemm(gr->w_gate ? kg : ku, nullptr, cfg_k))) {
@@ -1053,35 +1118,51 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
       }
     }
     if (gr->w_down) {
-      const GemmArgs kd = kgrouped(wsb + B.dysT, dm, wsb + B.hT, f, I(B.kt2), I(B.kn2),
+      const GemmArgs kd = kgrouped(wsb + B.dysT, de, wsb + B.hT, f, I(B.kt2), I(B.kn2),
                                    gr->w_down);
       if ((rc = gemm(kd, nullptr, cfg_k))) return rc;
     }
   }
-  if (want_s) {
-    const int64_t TP = B.TP;
+  const int64_t TP = B.TP;
+  const int TPk = static_cast<int>(TP);
+  if (want_s || want_l) {
     MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.xT, TP, s));
     MOE_TRY(launch_cols(d_out, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.dyT,
                         TP, s));
+  }
+  if (want_s) {
     MOE_TRY(launch_cols(wsb + B.dau_s, 2 * ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
                         wsb + B.dashT, TP, s));
     MOE_TRY(launch_cols(wsb + B.dau_s + static_cast<size_t>(ds) * 2, 2 * ds, nullptr, nullptr, T,
                         ds, nullptr, nullptr, 0, TP, wsb + B.dushT, TP, s));
     MOE_TRY(launch_cols(wsb + B.h_s, ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
                         wsb + B.hshT, TP, s));
-    const int TPk = static_cast<int>(B.TP);
     const int cfg_w = gemm2_pick(ds, 0, TPk, dm, 0, ds, dm);
     if (gr->ws_gate) {
-      const GemmArgs g1 = dense(wsb + B.dashT, B.TP, wsb + B.xT, B.TP, TPk, dm, ds, gr->ws_gate, dm);
+      const GemmArgs g1 = dense(wsb + B.dashT, TP, wsb + B.xT, TP, TPk, dm, ds, gr->ws_gate, dm);
       if ((rc = gemm(g1, nullptr, cfg_w))) return rc;
     }
     if (gr->ws_up) {
-      const GemmArgs g2 = dense(wsb + B.dushT, B.TP, wsb + B.xT, B.TP, TPk, dm, ds, gr->ws_up, dm);
+      const GemmArgs g2 = dense(wsb + B.dushT, TP, wsb + B.xT, TP, TPk, dm, ds, gr->ws_up, dm);
       if ((rc = gemm(g2, nullptr, cfg_w))) return rc;
     }
     if (gr->ws_down) {
-      const GemmArgs g3 = dense(wsb + B.dyT, B.TP, wsb + B.hshT, B.TP, TPk, ds, dm, gr->ws_down, ds);
-      if ((rc = gemm(g3, nullptr, gemm2_pick(dm, 0, TPk, ds, 0)))) return rc;
+      const GemmArgs g3 = dense(wsb + B.dyT, TP, wsb + B.hshT, TP, TPk, ds, dm, gr->ws_down, ds);
+      if ((rc = gemm(g3, nullptr, pick_dense(dm, TPk, ds)))) return rc;
+    }
+  }
+  if (want_l) {
+    if (gr->w_lat_up) {  // dW_lat_up = dy^T R' (d x L)
+      MOE_TRY(launch_cols(wsb + B.Rp, Lt, nullptr, nullptr, T, Lt, nullptr, nullptr, 0, TP,
+                          wsb + B.RpT, TP, s));
+      const GemmArgs gu = dense(wsb + B.dyT, TP, wsb + B.RpT, TP, TPk, Lt, dm, gr->w_lat_up, Lt);
+      if ((rc = gemm(gu, nullptr, pick_dense(dm, TPk, Lt)))) return rc;
+    }
+    if (gr->w_lat_down) {  // dW_lat_down = dz^T x (L x d)
+      MOE_TRY(launch_cols(wsb + B.dz, Lt, nullptr, nullptr, T, Lt, nullptr, nullptr, 0, TP,
+                          wsb + B.dzT, TP, s));
+      const GemmArgs gd = dense(wsb + B.dzT, TP, wsb + B.xT, TP, TPk, dm, Lt, gr->w_lat_down, dm);
+      if ((rc = gemm(gd, nullptr, pick_dense(Lt, TPk, dm)))) return rc;
     }
   }
   return MOE_OK;

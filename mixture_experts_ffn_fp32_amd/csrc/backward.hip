@@ -180,6 +180,13 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
   const float g = gw ? gw[p] : 1.0f;
   float acc = 0.f;
   const int64_t o = p * f;
+  if (!D) {  // h only (a forward recompute)
+    for (int j = lane; j < f; j += 64) {
+      const float a = A[o + j];
+      H[o + j] = f32_to_bf16(a / (1.0f + expf(-a)) * U[o + j]);
+    }
+    return;
+  }
   for (int j = lane; j < f; j += 64) {
     const float a = A[o + j], u = U[o + j], dd = D[o + j];
     const float s = 1.0f / (1.0f + expf(-a));
@@ -198,24 +205,33 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
   }
 }
 
-// dx[t] = sum_k dXs[inv[t K + k]] + dXsh[t] + sum_k dr[inv[t K + k]] W_router[idx[t K + k]]
-// (fp32, k in order, then rounded to bf16); one wavefront per token.
+// dx[t] = sum_k dXs[inv[t K + k]] + add1[t] + add2[t]
+//         + sum_k dr[inv[t K + k]] W_router[idx[t K + k]]
+// (each term optional; fp32, k in order, then rounded to bf16); one wavefront
+// per token.
 __global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *dXsh,
-                                                 const int32_t *inv, const int32_t *idx,
-                                                 const float *dr, const float *wr, int64_t T,
-                                                 int K, int d, uint16_t *dx) {
+                                                 const float *add2, const int32_t *inv,
+                                                 const int32_t *idx, const float *dr,
+                                                 const float *wr, int64_t T, int K, int d,
+                                                 uint16_t *dx) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   for (int i = lane * 4; i < d; i += 256) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const int64_t q = inv[t * K + k];
-      const float4 v = *reinterpret_cast<const float4 *>(dXs + q * d + i);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    if (dXs) {
+      for (int k = 0; k < K; ++k) {
+        const int64_t q = inv[t * K + k];
+        const float4 v = *reinterpret_cast<const float4 *>(dXs + q * d + i);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
     }
     if (dXsh) {
       const float4 v = *reinterpret_cast<const float4 *>(dXsh + t * d + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (add2) {
+      const float4 v = *reinterpret_cast<const float4 *>(add2 + t * d + i);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     if (dr) {
@@ -245,6 +261,81 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float *dr, const int32_t
   for (int p = offsets[e]; p < offsets[e + 1]; ++p)
     acc += dr[p] * bf16_to_f32(x[static_cast<int64_t>(stok[p]) * d + i]);
   dwr[static_cast<int64_t>(e) * d + i] = acc;
+}
+
+// Latent layer ("StableLatentMoE and QuantileBalancer", "Return to model
+// width"), one wavefront per token. Forward recompute: R = sum_k Y[inv[t K +
+// k]] (fp32, k in order), rinv = 1 / sqrt(mean(R^2) + eps) (1 without the
+// norm), R' = R rinv gamma as bf16 (gamma = 1 if null).
+__global__ __launch_bounds__(256) void latent_fwd_kernel(const float *Y, const int32_t *inv,
+                                                         int64_t T, int K, int L, int norm,
+                                                         float eps, const float *gamma, float *R,
+                                                         float *rinv, uint16_t *Rp) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  float ss = 0.f;
+  for (int l = lane; l < L; l += 64) {
+    float v = 0.f;
+    for (int k = 0; k < K; ++k) v += Y[static_cast<int64_t>(inv[t * K + k]) * L + l];
+    R[t * L + l] = v;
+    ss += v * v;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float r = norm ? 1.0f / sqrtf(ss / static_cast<float>(L) + eps) : 1.0f;
+  if (lane == 0) rinv[t] = r;
+  for (int l = lane; l < L; l += 64) {
+    const float gm = (norm && gamma) ? gamma[l] : 1.0f;
+    Rp[t * L + l] = f32_to_bf16(R[t * L + l] * r * gm);
+  }
+}
+
+// RMSNorm backward per token: s = gamma dR' (dR' = W_lat_up^T dy, fp32),
+// dR = rinv s - R rinv^3 <s, R> / L (dR = dR' without the norm), as bf16.
+__global__ __launch_bounds__(256) void latent_bwd_kernel(const float *dRp, const float *R,
+                                                         const float *rinv, const float *gamma,
+                                                         int64_t T, int L, int norm,
+                                                         uint16_t *dR) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t o = t * L;
+  if (!norm) {
+    for (int l = lane; l < L; l += 64) dR[o + l] = f32_to_bf16(dRp[o + l]);
+    return;
+  }
+  float sR = 0.f;
+  for (int l = lane; l < L; l += 64) sR += dRp[o + l] * (gamma ? gamma[l] : 1.0f) * R[o + l];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sR += __shfl_xor(sR, off);
+  const float r = rinv[t];
+  const float c = r * r * r * sR / static_cast<float>(L);
+  for (int l = lane; l < L; l += 64)
+    dR[o + l] = f32_to_bf16(r * dRp[o + l] * (gamma ? gamma[l] : 1.0f) - R[o + l] * c);
+}
+
+// Column sums sum_t A[t, l] B[t, l] s[t] in two passes (fixed order): per
+// block of 256 tokens into part[blk, l], then the blocks in order.
+__global__ __launch_bounds__(256) void colsum_part_kernel(const float *A, const float *B,
+                                                          const float *sc, int64_t T, int L,
+                                                          float *part) {
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l >= L) return;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 256;
+  const int64_t t1 = t0 + 256 < T ? t0 + 256 : T;
+  float acc = 0.f;
+  for (int64_t t = t0; t < t1; ++t) acc += A[t * L + l] * B[t * L + l] * sc[t];
+  part[static_cast<int64_t>(blockIdx.y) * L + l] = acc;
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float *part, int64_t nblk, int L,
+                                                           float *out) {
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l >= L) return;
+  float acc = 0.f;
+  for (int64_t b = 0; b < nblk; ++b) acc += part[b * L + l];
+  out[l] = acc;
 }
 
 }  // namespace
@@ -295,12 +386,12 @@ hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const int32_t *inv,
-                         const int32_t *idx, const float *dr, const float *wr, int64_t T, int K,
-                         int d, void *dx, hipStream_t s) {
+hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
+                         const int32_t *inv, const int32_t *idx, const float *dr, const float *wr,
+                         int64_t T, int K, int d, void *dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dx_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(dXs, dXsh, inv, idx, dr, wr, T, K,
-                                                               d, static_cast<uint16_t *>(dx));
+  dx_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
+      dXs, dXsh, add2, inv, idx, dr, wr, T, K, d, static_cast<uint16_t *>(dx));
   return hipGetLastError();
 }
 
@@ -308,6 +399,38 @@ hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *o
                           const void *x, int E, int d, float *dwr, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E));
   dwr_kernel<<<grid, 256, 0, s>>>(dr, stok, offsets, static_cast<const uint16_t *>(x), d, dwr);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_fwd(const float *Y, const int32_t *inv, int64_t T, int K, int L,
+                             int norm, float eps, const float *gamma, float *R, float *rinv,
+                             void *Rp, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  latent_fwd_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
+      Y, inv, T, K, L, norm, eps, gamma, R, rinv, static_cast<uint16_t *>(Rp));
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_bwd(const float *dRp, const float *R, const float *rinv,
+                             const float *gamma, int64_t T, int L, int norm, void *dR,
+                             hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  latent_bwd_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
+      dRp, R, rinv, gamma, T, L, norm, static_cast<uint16_t *>(dR));
+  return hipGetLastError();
+}
+
+int64_t colsum_blocks(int64_t T) { return (T + 255) / 256; }
+
+hipError_t launch_colsum(const float *A, const float *B, const float *sc, int64_t T, int L,
+                         float *part, float *out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 g1(static_cast<unsigned>((L + 255) / 256), static_cast<unsigned>(colsum_blocks(T)));
+  colsum_part_kernel<<<g1, 256, 0, s>>>(A, B, sc, T, L, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  colsum_final_kernel<<<static_cast<unsigned>((L + 255) / 256), 256, 0, s>>>(
+      part, colsum_blocks(T), L, out);
   return hipGetLastError();
 }
 

@@ -239,12 +239,26 @@ hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index
 hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, int32_t *poff,
                          int32_t *t1, int32_t *n1, int32_t *t2, int32_t *n2, hipStream_t s);
 // h = SiLU(a) u and [da | du] (bf16 [R, 2f]) from a, u and W_down^T dy (fp32
-// [R, f]) and the row weights gw (1 if null); dg[p] = <W_down^T dy, h> if dg
+// [R, f]) and the row weights gw (1 if null); dg[p] = <W_down^T dy, h> if dg;
+// with D null, h only
 hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const float *gw,
                            int64_t R, int f, void *H, void *dAU, float *dg, hipStream_t s);
-hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const int32_t *inv,
-                         const int32_t *idx, const float *dr, const float *wr, int64_t T, int K,
-                         int d, void *dx, hipStream_t s);
+// dx = sum_k dXs[inv] + dXsh + add2 + sum_k dr W_router rows (terms optional)
+hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
+                         const int32_t *inv, const int32_t *idx, const float *dr, const float *wr,
+                         int64_t T, int K, int d, void *dx, hipStream_t s);
+// latent: R = sum_k Y[inv] (fp32), rinv, R' = R rinv gamma (bf16)
+hipError_t launch_latent_fwd(const float *Y, const int32_t *inv, int64_t T, int K, int L,
+                             int norm, float eps, const float *gamma, float *R, float *rinv,
+                             void *Rp, hipStream_t s);
+// latent: RMSNorm backward dR (bf16) from dR' (fp32)
+hipError_t launch_latent_bwd(const float *dRp, const float *R, const float *rinv,
+                             const float *gamma, int64_t T, int L, int norm, void *dR,
+                             hipStream_t s);
+// out[l] = sum_t A[t, l] B[t, l] sc[t] (part: [colsum_blocks(T), L] scratch)
+int64_t colsum_blocks(int64_t T);
+hipError_t launch_colsum(const float *A, const float *B, const float *sc, int64_t T, int L,
+                         float *part, float *out, hipStream_t s);
 hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
                           const void *x, int E, int d, float *dwr, hipStream_t s);
 

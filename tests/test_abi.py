@@ -198,9 +198,10 @@ def test_backward_checked_before_launch():
     assert n > moe.moe_workspace_size(d)
     assert L.moe_backward(C.byref(_desc(T=64, act_dtype=0)), C.byref(w), fake, fake, fake,
                           C.byref(g), fake, 1 << 40, None) == -3
-    w8 = moe_synth.get("latent")
-    assert L.moe_backward(C.byref(moe.make_desc(w8)), C.byref(w), fake, fake, fake, C.byref(g),
-                          fake, 1 << 40, None) == -3
+    dl = moe.make_desc(moe_synth.get("latent"))
+    dl.latent = 40  # latent widths must be multiples of 32 as well
+    assert L.moe_backward(C.byref(dl), C.byref(w), fake, fake, fake, C.byref(g), fake, 1 << 40,
+                          None) == -2
     assert L.moe_backward(C.byref(_desc(T=64, d_model=520)), C.byref(w), fake, fake, fake,
                           C.byref(g), fake, 1 << 40, None) == -2
     assert L.moe_backward(C.byref(d), C.byref(w), fake, fake, fake, None, fake, n, None) == -1

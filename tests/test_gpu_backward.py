@@ -14,13 +14,21 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-2  # max-abs-rel per gradient tensor: bf16 operands, fp32 accumulation
 
-SHAPES = {"w_router": ("E", "d"), "w_gate": ("E", "d_ff", "d"), "w_up": ("E", "d_ff", "d"),
-          "w_down": ("E", "d", "d_ff"), "ws_gate": ("d_shared", "d"),
-          "ws_up": ("d_shared", "d"), "ws_down": ("d", "d_shared")}
+SHAPES = {"w_router": ("E", "d"), "w_gate": ("E", "d_ff", "de"), "w_up": ("E", "d_ff", "de"),
+          "w_down": ("E", "de", "d_ff"), "ws_gate": ("d_shared", "d"),
+          "ws_up": ("d_shared", "d"), "ws_down": ("d", "d_shared"),
+          "w_lat_down": ("L", "d"), "w_lat_up": ("d", "L"), "rms_gamma": ("L",)}
+
+
+def _keys(w):
+    return [k for k in SHAPES if (w.d_shared or not k.startswith("ws_"))
+            and (w.latent or k not in ("w_lat_down", "w_lat_up", "rms_gamma"))
+            and (w.has_rmsnorm or k != "rms_gamma")]
 
 
 def _grad_buffers(w, keys):
-    dims = {"E": w.E, "d": w.d, "d_ff": w.d_ff, "d_shared": w.d_shared}
+    dims = {"E": w.E, "d": w.d, "d_ff": w.d_ff, "d_shared": w.d_shared, "L": w.latent,
+            "de": w.latent or w.d}
     return {k: torch.full(tuple(dims[s] for s in SHAPES[k]), float("nan"), dtype=torch.float32,
                           device="cuda") for k in keys}
 
@@ -49,8 +57,8 @@ def oracle_selection(orc, g_idx):
     return use, int(near.sum())
 
 
-def check_all(w, a, layer, keys=tuple(SHAPES), seed=11, tol=TOL):
-    keys = [k for k in keys if w.d_shared or not k.startswith("ws_")]
+def check_all(w, a, layer, keys=None, seed=11, tol=TOL):
+    keys = _keys(w) if keys is None else keys
     bits, dx, grads, g_idx = run_backward(w, a, layer, keys, seed)
     orc = oracle.Oracle(w, a)
     use, n_near = oracle_selection(orc, g_idx)
@@ -91,6 +99,13 @@ LAYERS = {
                      w_std=0.1, router_std=0.1),
     "k_eq_e": dict(T=150, d=64, d_ff=64, E=4, K=4, act="bf16", w_std=0.1, router_std=0.1,
                    n_shared=1, d_ff_shared=32),
+    # StableLatentMoE layers: routed experts in width L between the projections
+    "latent_norm_sigmoid": dict(T=300, d=128, latent=64, d_ff=96, E=8, K=3, act="bf16",
+                                route="sigmoid_bias", bias_std=0.05, has_rmsnorm=True,
+                                n_shared=1, d_ff_shared=160, w_std=0.08, router_std=0.08),
+    "latent_nonorm_topk": dict(T=200, d=96, latent=64, d_ff=64, E=6, K=2, act="bf16",
+                               has_rmsnorm=False, n_shared=0, d_ff_shared=0, w_std=0.1,
+                               router_std=0.1),
 }
 
 
@@ -118,7 +133,7 @@ def test_backward_is_deterministic_and_partial_requests():
     a = moe_synth.generate(w)
     layer = layer_of(w, a)
     _, dy = _d_out(w, 3)
-    g1 = _grad_buffers(w, SHAPES)
+    g1 = _grad_buffers(w, _keys(w))
     g2 = _grad_buffers(w, ["w_down", "ws_up"])
     dx1 = layer.backward(layer.dev["x"], dy, grads=g1).clone()
     dx2 = layer.backward(layer.dev["x"], dy, grads=g2)
@@ -154,6 +169,41 @@ def test_backward_medium_sampled():
     errs = {k: max_abs_rel(grads[k][e], one[k][0]) for k in ("w_gate", "w_up", "w_down")}
     assert np.all(np.isnan(grads["w_gate"][counts == 0]))
     say(f"  medium: near-ties={n_near} dx(sample {len(toks)})={err:.2e} expert {e} "
+        f"({counts[e]} rows): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert err <= TOL
+    for v in errs.values():
+        assert v <= TOL
+    del layer, a
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_backward_latent_full_size_sampled():
+    """Full-size latent layer (sigmoid routing, RMSNorm in L): input gradients
+    on a seeded token sample and the weight gradients of the smallest
+    non-empty expert over its tokens. (The projections' and the gain's
+    gradients, sums over all tokens, are checked element by element on the
+    small latent layers above.)"""
+    w = moe_synth.get("latent")
+    say("case backward latent: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    bits, dx, grads, g_idx = run_backward(w, a, layer, ["w_gate", "w_up", "w_down"])
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    dy = moe_synth.as_f64(bits, "bf16")
+    toks = sample_tokens(use, w.E, 128, seed=6)
+    ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
+                       router=False, shared=False, latent=False)
+    err = max_abs_rel(dx[toks], ref["dx"])
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    nz = np.nonzero(counts)[0]
+    e = int(nz[np.argmin(counts[nz])])
+    mine = np.nonzero((use == e).any(1))[0]
+    one = orc.backward(dy[mine], tokens=mine, idx_override=use[mine], experts=e, router=False,
+                       shared=False, latent=False)
+    errs = {k: max_abs_rel(grads[k][e], one[k][0]) for k in ("w_gate", "w_up", "w_down")}
+    say(f"  latent: near-ties={n_near} dx(sample {len(toks)})={err:.2e} expert {e} "
         f"({counts[e]} rows): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert err <= TOL
     for v in errs.values():
