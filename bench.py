@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward-pass timing (bf16 layers)")
+                    help="skip the backward-pass timing")
     ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -240,10 +240,9 @@ def main():
     rl = {"ms_per_call": round(b_ev.elapsed_time(e_ev) / 10, 4), "tokens": w.T, "experts": w.E,
           "load_balancing_loss": round(float(losses[0]), 7),
           "z_loss": round(float(losses[1]), 7)}
-    # backward pass (bf16 layers): input and all weight gradients for an output
-    # gradient of ones
+    # backward pass: input and all weight gradients for an output gradient of ones
     bwd = None
-    if not args.no_backward and w.act == "bf16":
+    if not args.no_backward:
         dy = torch.ones((w.T, w.d), dtype=layer.act, device=dev)
         de = w.d_e
         shapes = {"w_router": (w.E, w.d), "w_gate": (w.E, w.d_ff, de),
@@ -271,9 +270,9 @@ def main():
             fl += 2.0 * w.T * w.K * de * w.d_ff + 2.0 * w.T * w.d * w.latent * 5
         bwd = {"ms_per_call": round(bms, 4), "tokens_per_s": round(w.T / (bms / 1e3), 1),
                "tflops": round(fl / (bms / 1e3) / 1e12, 2),
-               "note": "moe_backward: input, router, expert and shared weight gradients; tflops "
-                        "counts the recomputed gate/up GEMM; "
-                       "(routing recomputed), output gradient of ones"}
+               "note": "moe_backward: input, router, expert and shared weight gradients "
+                       "(routing recomputed), output gradient of ones; tflops counts the "
+                       "recomputed gate/up GEMM"}
         del grads, d_x, dy
         layer.ws_bwd = None
         torch.cuda.empty_cache()

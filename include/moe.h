@@ -289,15 +289,15 @@ MOE_API int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
  *  - experts that no token selects get no weight gradient: their slices of
  *    grads->w_gate / w_up / w_down are left untouched; every other requested
  *    array is overwritten (not accumulated);
- *  - intermediate products are bf16 operands with fp32 accumulation, like
- *    the forward; router gradients are fp32.
+ *  - intermediate products are in the layer's dtype with fp32
+ *    accumulation, like the forward (bf16 layers: bf16 operands; fp32
+ *    layers: every product in fp32); router gradients are fp32.
  *  - latent layers ("StableLatentMoE and QuantileBalancer"): the routed sum
  *    and its RMSNorm are recomputed; gradients also reach W_lat_down,
  *    W_lat_up and the RMSNorm gain (rms_gamma NULL in w: a gain of ones,
  *    whose gradient is still reported if grads->rms_gamma is given).
- * Supported: bf16 layers with d_model, d_ff, d_shared and L multiples of
- * 32. Errors: MOE_ERR_MODE (fp32 layers), MOE_ERR_SHAPE (other widths, or
- * operands beyond 4 GiB), MOE_ERR_NULL,
+ * Supported: d_model, d_ff, d_shared and L multiples of 32. Errors:
+ * MOE_ERR_SHAPE (other widths, or operands beyond 4 GiB), MOE_ERR_NULL,
  * MOE_ERR_WORKSPACE (below moe_backward_workspace_size), MOE_ERR_HIP.
  * T == 0 is a no-op. */
 MOE_API int moe_backward(const moe_desc *desc, const moe_weights *w, const void *x,

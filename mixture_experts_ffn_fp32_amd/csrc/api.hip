@@ -428,6 +428,7 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
   const int64_t dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
   const int64_t de = Lt ? Lt : dm;
+  const int64_t es = d->act_dtype == MOE_BF16 ? 2 : 4;  // act element size
   size_t o = layout_of(d).total;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -444,48 +445,48 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.kn2 = take(4);
   B.tiles = take(static_cast<size_t>(grouped_tile_bound(rows, E, 32)) * kTileInts * 4);
   B.ntiles = take(4);
-  B.wguT = take(E * de * 2 * f * 2);  // [E, de, 2 f]: W_gate^T | W_up^T
-  B.wdT = take(E * f * de * 2);       // [E, f, de]
-  B.wsguT = take(dm * 2 * ds * 2);
-  B.wsdT = take(ds * dm * 2);
+  B.wguT = take(E * de * 2 * f * es);  // [E, de, 2 f]: W_gate^T | W_up^T
+  B.wdT = take(E * f * de * es);       // [E, f, de]
+  B.wsguT = take(dm * 2 * ds * es);
+  B.wsdT = take(ds * dm * es);
   B.apre = take(rows * f * 4);
   B.upre = take(rows * f * 4);
   B.dhu = take(rows * f * 4);
-  B.h = take(rows * f * 2);
-  B.dau = take(rows * 2 * f * 2);
+  B.h = take(rows * f * es);
+  B.dau = take(rows * 2 * f * es);
   B.dg = take(rows * 4);
   B.dr = take(rows * 4);
   B.dxs = take(rows * de * 4);
   B.apre_s = take(T * ds * 4);
   B.upre_s = take(T * ds * 4);
   B.dhu_s = take(T * ds * 4);
-  B.h_s = take(T * ds * 2);
-  B.dau_s = take(T * 2 * ds * 2);
+  B.h_s = take(T * ds * es);
+  B.dau_s = take(T * 2 * ds * es);
   B.dxsh = take(T * dm * 4);
-  B.xsT = take(de * B.RP * 2);
-  B.dysT = take(de * B.RP * 2);
-  B.daT = take(f * B.RP * 2);
-  B.duT = take(f * B.RP * 2);
-  B.hT = take(f * B.RP * 2);
-  B.xT = take(dm * B.TP * 2);
-  B.dyT = take(dm * B.TP * 2);
-  B.dashT = take(ds * B.TP * 2);
-  B.dushT = take(ds * B.TP * 2);
-  B.hshT = take(ds * B.TP * 2);
+  B.xsT = take(de * B.RP * es);
+  B.dysT = take(de * B.RP * es);
+  B.daT = take(f * B.RP * es);
+  B.duT = take(f * B.RP * es);
+  B.hT = take(f * B.RP * es);
+  B.xT = take(dm * B.TP * es);
+  B.dyT = take(dm * B.TP * es);
+  B.dashT = take(ds * B.TP * es);
+  B.dushT = take(ds * B.TP * es);
+  B.hshT = take(ds * B.TP * es);
   if (Lt) {
-    B.wluT = take(Lt * dm * 2);
-    B.wldT = take(dm * Lt * 2);
+    B.wluT = take(Lt * dm * es);
+    B.wldT = take(dm * Lt * es);
     B.yf = take(rows * Lt * 4);
     B.R = take(T * Lt * 4);
     B.rinv = take(T * 4);
-    B.Rp = take(T * Lt * 2);
+    B.Rp = take(T * Lt * es);
     B.dRp = take(T * Lt * 4);
-    B.dR = take(T * Lt * 2);
-    B.dz = take(T * Lt * 2);
+    B.dR = take(T * Lt * es);
+    B.dz = take(T * Lt * es);
     B.dxl = take(T * dm * 4);
     B.gpart = take(static_cast<size_t>(colsum_blocks(T)) * Lt * 4);
-    B.RpT = take(Lt * B.TP * 2);
-    B.dzT = take(Lt * B.TP * 2);
+    B.RpT = take(Lt * B.TP * es);
+    B.dzT = take(Lt * B.TP * es);
   }
   B.total = o;
   return B;
@@ -494,7 +495,6 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
 int check_backward(const moe_desc *d) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (d->act_dtype != MOE_BF16) return MOE_ERR_MODE;
   if (d->d_model % 32 || d->d_ff % 32 || d->d_shared % 32 || d->latent % 32) return MOE_ERR_SHAPE;
   constexpr int64_t kLim = int64_t(1) << 32;  // 32-bit operand offsets of the GEMMs
   const int64_t T = d->T, rows = T * d->top_k, E = d->n_experts;
@@ -873,6 +873,8 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const int64_t T = d->T, K = d->top_k, E = d->n_experts, rows = T * K;
   const int dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
   const int de = Lt ? Lt : dm;  // routed width
+  const int bf = d->act_dtype == MOE_BF16;
+  const size_t es = bf ? 2 : 4;  // act element size
   int32_t *idx = I(L.idx), *counts = I(L.counts), *offsets = I(L.offsets);
   int32_t *stok = I(L.stok), *inv = I(L.inv);
   float *sw = F(L.sw);
@@ -894,7 +896,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   ra.idx = idx;
   ra.g = F(L.g);
   ra.gap = F(L.gap);
-  MOE_TRY(launch_router(ra, 1, s));
+  MOE_TRY(launch_router(ra, bf, s));
   ScanArgs sa{};
   sa.chunk_hist = I(L.chunk);
   sa.chunk_base = I(L.chunk);
@@ -914,24 +916,26 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   sc.inv = inv;
   sc.sorted_w = sw;
   MOE_TRY(run_dispatch(sa, sc, s));
-  const int cfg = gemm2_pick(rows, E, de, f, 0, rows, f);
-  const int bm = gemm2_bm(cfg);
+  // bf16: the pipelined kernel (two problems per launch where they pair up);
+  // fp32: the generic kernel, 128 x 128 tiles, one problem per launch
+  const int cfg = bf ? gemm2_pick(rows, E, de, f, 0, rows, f) : TILE_LARGE;
+  const int bm = bf ? gemm2_bm(cfg) : tile_bm(TILE_LARGE);
   MOE_TRY(launch_tiles(offsets, static_cast<int>(E), bm, I(B.tiles), I(B.ntiles), s));
   const int64_t mt_bound = grouped_tile_bound(rows, E, bm);
 
   // 2. transposed weights of the active experts (and the shared FFN, the
   //    latent projections)
-  MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, s));
-  MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, s));
-  MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, s));
+  MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, bf, s));
+  MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, bf, s));
+  MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, bf, s));
   if (ds) {
-    MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, s));
-    MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, s));
-    MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, s));
+    MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, bf, s));
+    MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, bf, s));
+    MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, bf, s));
   }
   if (Lt) {
-    MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, s));
-    MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, s));
+    MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, bf, s));
+    MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, bf, s));
   }
 
   auto grouped = [&](const void *a, int64_t lda, const int32_t *a_rows, int64_t a_extent,
@@ -970,6 +974,11 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     return g;
   };
   auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c, int epi = EPI_STORE_F32) {
+    if (!bf) {  // generic kernel, one problem per launch
+      if (launch_gemm(a, epi, TILE_LARGE, 0, s) != hipSuccess) return MOE_ERR_HIP;
+      if (b && launch_gemm(*b, epi, TILE_LARGE, 0, s) != hipSuccess) return MOE_ERR_HIP;
+      return MOE_OK;
+    }
     if (!gemm2_applicable(a, epi) || (b && !gemm2_applicable(*b, epi))) return MOE_ERR_SHAPE;
     return launch_gemm2(a, epi, c, s, b) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   };
@@ -980,7 +989,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const void *rin = x;
   if (Lt) {
     GemmArgs gz = dense(x, dm, w->w_lat_down, dm, dm, Lt, T, wsb + L.z, Lt);
-    MOE_TRY(launch_dense(gz, EPI_STORE, 1, s));
+    MOE_TRY(launch_dense(gz, EPI_STORE, bf, s));
     rin = wsb + L.z;
   }
 
@@ -1003,18 +1012,18 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const void *rdy = d_out;
   if (Lt) {
     MOE_TRY(launch_bwd_rows(F(B.apre), F(B.upre), nullptr, nullptr, rows, f, wsb + B.h, nullptr,
-                            nullptr, s));
+                            nullptr, bf, s));
     GemmArgs gy = grouped(wsb + B.h, f, nullptr, rows, w->w_down, f,
                           static_cast<int64_t>(Lt) * f, f, Lt, F(B.yf), Lt);
     gy.row_scale = sw;
     gy.out_f32 = 1;
     if ((rc = gemm(gy, nullptr, cfg, EPI_SCALE))) return rc;
     MOE_TRY(launch_latent_fwd(F(B.yf), inv, T, static_cast<int>(K), Lt, d->has_rmsnorm,
-                              d->rms_eps, w->rms_gamma, F(B.R), F(B.rinv), wsb + B.Rp, s));
+                              d->rms_eps, w->rms_gamma, F(B.R), F(B.rinv), wsb + B.Rp, bf, s));
     const GemmArgs gp = dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
     if ((rc = gemm(gp, nullptr, pick_dense(T, dm, Lt)))) return rc;
     MOE_TRY(launch_latent_bwd(F(B.dRp), F(B.R), F(B.rinv), w->rms_gamma, T, Lt,
-                              d->has_rmsnorm, wsb + B.dR, s));
+                              d->has_rmsnorm, wsb + B.dR, bf, s));
     rdy = wsb + B.dR;
   }
 
@@ -1031,11 +1040,11 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   }
   // 5. h, [da | du], dg per row; the router's logit gradients
   MOE_TRY(launch_bwd_rows(F(B.apre), F(B.upre), F(B.dhu), sw, rows, f, wsb + B.h, wsb + B.dau,
-                          F(B.dg), s));
+                          F(B.dg), bf, s));
   if (ds)
     MOE_TRY(launch_bwd_rows(F(B.apre_s), F(B.upre_s), F(B.dhu_s), nullptr, T, ds, wsb + B.h_s,
-                            wsb + B.dau_s, nullptr, s));
-  MOE_TRY(launch_router_backward(ra, 1, inv, F(B.dg), F(B.dr), s));
+                            wsb + B.dau_s, nullptr, bf, s));
+  MOE_TRY(launch_router_backward(ra, bf, inv, F(B.dg), F(B.dr), s));
 
   // 6. input gradient: [da | du] [W_gate^T | W_up^T]^T per row (to x, or to z
   //    and through W_lat_down), shared, router
@@ -1053,7 +1062,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   }
   if (Lt && need_dz) {  // dz = sum_k dX rows (bf16), dx_lat = dz W_lat_down
     MOE_TRY(launch_bwd_dx(F(B.dxs), nullptr, nullptr, inv, idx, nullptr, nullptr, T,
-                          static_cast<int>(K), Lt, wsb + B.dz, s));
+                          static_cast<int>(K), Lt, wsb + B.dz, bf, s));
     if (d_x) {
       const GemmArgs gl = dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
       if ((rc = gemm(gl, nullptr, pick_dense(T, Lt, dm)))) return rc;
@@ -1062,31 +1071,33 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   if (d_x)
     MOE_TRY(launch_bwd_dx(Lt ? nullptr : F(B.dxs), ds ? F(B.dxsh) : nullptr,
                           Lt ? F(B.dxl) : nullptr, inv, idx, F(B.dr), w->w_router, T,
-                          static_cast<int>(K), dm, d_x, s));
+                          static_cast<int>(K), dm, d_x, bf, s));
 
   // 7. weight gradients
   if (gr->w_router)
-    MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, gr->w_router, s));
+    MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, gr->w_router, bf, s));
   if (Lt && d->has_rmsnorm && gr->rms_gamma)
     MOE_TRY(launch_colsum(F(B.dRp), F(B.R), F(B.rinv), T, Lt, F(B.gpart), gr->rms_gamma, s));
   const bool want_e = gr->w_gate || gr->w_up || gr->w_down;
   const bool want_s = ds && (gr->ws_gate || gr->ws_up || gr->ws_down);
   const bool want_l = Lt && (gr->w_lat_up || gr->w_lat_down);
-  const int cfg_k = gemm2_pick(E * (f > de ? f : de), 0, rows / E + 64, f < de ? f : de, 0);
+  const int cfg_k =
+      bf ? gemm2_pick(E * (f > de ? f : de), 0, rows / E + 64, f < de ? f : de, 0) : TILE_LARGE;
+  const int bm_k = bf ? gemm2_bm(cfg_k) : tile_bm(TILE_LARGE);
   if (want_e) {
-    MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, de, gemm2_bm(cfg_k), I(B.poff),
+    MOE_TRY(launch_kgroup(counts, static_cast<int>(E), f, de, bm_k, I(B.poff),
                           I(B.kt1), I(B.kn1), I(B.kt2), I(B.kn2), s));
     const int G = static_cast<int>(E);
     const int32_t *po = I(B.poff);
     const int64_t RP = B.RP;
-    MOE_TRY(launch_cols(rin, de, stok, nullptr, rows, de, offsets, po, G, RP, wsb + B.xsT, RP, s));
-    MOE_TRY(launch_cols(rdy, de, stok, sw, rows, de, offsets, po, G, RP, wsb + B.dysT, RP, s));
+    MOE_TRY(launch_cols(rin, de, stok, nullptr, rows, de, offsets, po, G, RP, wsb + B.xsT, RP, bf, s));
+    MOE_TRY(launch_cols(rdy, de, stok, sw, rows, de, offsets, po, G, RP, wsb + B.dysT, RP, bf, s));
     MOE_TRY(launch_cols(wsb + B.dau, 2 * f, nullptr, nullptr, rows, f, offsets, po, G, RP,
-                        wsb + B.daT, RP, s));
-    MOE_TRY(launch_cols(wsb + B.dau + static_cast<size_t>(f) * 2, 2 * f, nullptr, nullptr, rows,
-                        f, offsets, po, G, RP, wsb + B.duT, RP, s));
+                        wsb + B.daT, RP, bf, s));
+    MOE_TRY(launch_cols(wsb + B.dau + static_cast<size_t>(f) * es, 2 * f, nullptr, nullptr, rows,
+                        f, offsets, po, G, RP, wsb + B.duT, RP, bf, s));
     MOE_TRY(launch_cols(wsb + B.h, f, nullptr, nullptr, rows, f, offsets, po, G, RP, wsb + B.hT,
-                        RP, s));
+                        RP, bf, s));
     auto kgrouped = [&](const void *a, int64_t M, const void *b, int N, int32_t *tab,
                         int32_t *ntab, void *out) {
       GemmArgs g{};
@@ -1099,7 +1110,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
       g.N = N;
       g.tiles = tab;
       g.n_tiles = ntab;
-      g.max_mtiles = E * ((M + gemm2_bm(cfg_k) - 1) / gemm2_bm(cfg_k));
+      g.max_mtiles = E * ((M + bm_k - 1) / bm_k);
       g.k_offsets = I(B.poff);
       g.out = out;
       g.ldo = N;
@@ -1126,17 +1137,17 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const int64_t TP = B.TP;
   const int TPk = static_cast<int>(TP);
   if (want_s || want_l) {
-    MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.xT, TP, s));
+    MOE_TRY(launch_cols(x, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.xT, TP, bf, s));
     MOE_TRY(launch_cols(d_out, dm, nullptr, nullptr, T, dm, nullptr, nullptr, 0, TP, wsb + B.dyT,
-                        TP, s));
+                        TP, bf, s));
   }
   if (want_s) {
     MOE_TRY(launch_cols(wsb + B.dau_s, 2 * ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
-                        wsb + B.dashT, TP, s));
-    MOE_TRY(launch_cols(wsb + B.dau_s + static_cast<size_t>(ds) * 2, 2 * ds, nullptr, nullptr, T,
-                        ds, nullptr, nullptr, 0, TP, wsb + B.dushT, TP, s));
+                        wsb + B.dashT, TP, bf, s));
+    MOE_TRY(launch_cols(wsb + B.dau_s + static_cast<size_t>(ds) * es, 2 * ds, nullptr, nullptr, T,
+                        ds, nullptr, nullptr, 0, TP, wsb + B.dushT, TP, bf, s));
     MOE_TRY(launch_cols(wsb + B.h_s, ds, nullptr, nullptr, T, ds, nullptr, nullptr, 0, TP,
-                        wsb + B.hshT, TP, s));
+                        wsb + B.hshT, TP, bf, s));
     const int cfg_w = gemm2_pick(ds, 0, TPk, dm, 0, ds, dm);
     if (gr->ws_gate) {
       const GemmArgs g1 = dense(wsb + B.dashT, TP, wsb + B.xT, TP, TPk, dm, ds, gr->ws_gate, dm);
@@ -1154,13 +1165,13 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   if (want_l) {
     if (gr->w_lat_up) {  // dW_lat_up = dy^T R' (d x L)
       MOE_TRY(launch_cols(wsb + B.Rp, Lt, nullptr, nullptr, T, Lt, nullptr, nullptr, 0, TP,
-                          wsb + B.RpT, TP, s));
+                          wsb + B.RpT, TP, bf, s));
       const GemmArgs gu = dense(wsb + B.dyT, TP, wsb + B.RpT, TP, TPk, Lt, dm, gr->w_lat_up, Lt);
       if ((rc = gemm(gu, nullptr, pick_dense(dm, TPk, Lt)))) return rc;
     }
     if (gr->w_lat_down) {  // dW_lat_down = dz^T x (L x d)
       MOE_TRY(launch_cols(wsb + B.dz, Lt, nullptr, nullptr, T, Lt, nullptr, nullptr, 0, TP,
-                          wsb + B.dzT, TP, s));
+                          wsb + B.dzT, TP, bf, s));
       const GemmArgs gd = dense(wsb + B.dzT, TP, wsb + B.xT, TP, TPk, dm, Lt, gr->w_lat_down, dm);
       if ((rc = gemm(gd, nullptr, pick_dense(Lt, TPk, dm)))) return rc;
     }

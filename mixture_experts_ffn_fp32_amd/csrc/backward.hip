@@ -1,5 +1,5 @@
-// Backward pass of the layer (non-latent, bf16): the elementwise, transpose
-// and reduction kernels around the GEMMs that api.hip enqueues.
+// Backward pass of the layer (bf16 or fp32 activations): the elementwise,
+// transpose and reduction kernels around the GEMMs that api.hip enqueues.
 //
 // The layer (APEX-1 Mathematical Reference - Part 3, 13.2 and 12.2) is
 // y_t = sum_s FFN_s(x_t) + sum_k g_k FFN_{e_k}(x_t), FFN(x) = W_down h,
@@ -13,9 +13,10 @@
 // weight gradient ("StableLatentMoE and QuantileBalancer": inactive experts'
 // gradients stay unset).
 //
-// Every product runs on the pipelined NT GEMM (C = A B^T, both operands
-// K-contiguous). Products whose natural operand is K-strided use transposed
-// copies: the weights of active experts (W_down^T, W_gate^T, W_up^T) and, for
+// Every product runs as an NT GEMM (C = A B^T, both operands K-contiguous;
+// bf16: the pipelined kernel, fp32: the generic one). Products whose natural
+// operand is K-strided use transposed copies: the weights of active experts
+// (W_down^T, W_gate^T, W_up^T) and, for
 // the weight gradients, the activations in expert-contiguous columns whose
 // per-expert runs are padded to multiples of 64 with zeros (the K-grouped
 // GEMM reduces each expert over its own run).
@@ -32,61 +33,77 @@ __global__ __launch_bounds__(256) void fill0_kernel(uint4 *p, int64_t n16) {
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// 64 x 64 bf16 tiles through LDS with 16-byte global accesses on both sides:
-// tile row i holds 64 consecutive columns of one source row (8 chunks of 8);
-// a destination row takes 8 tile rows of one column per 16-byte chunk.
-// Widths and offsets are multiples of 8 elements.
-constexpr int kTP = 64 + 8;  // tile pitch (elements): rows stay 16-byte aligned
+// 64 x 64 element tiles (bf16 or fp32 bits: E = uint16_t or uint32_t) through
+// LDS with 16-byte global accesses on both sides: tile row i holds 64
+// consecutive columns of one source row; a destination row takes EPC tile
+// rows of one column per 16-byte chunk. Widths and offsets are multiples of
+// 8 elements.
+template <typename E>
+struct TileOf {
+  static constexpr int EPC = 16 / static_cast<int>(sizeof(E));  // elements per chunk
+  static constexpr int CPR = 64 / EPC;                           // chunks per tile row
+  static constexpr int P = 64 + EPC;                             // pitch: rows stay 16-byte aligned
+};
+template <typename E> struct ChunkT;
+template <> struct ChunkT<uint16_t> { using C = Chunk<bf16_t>; };
+template <> struct ChunkT<uint32_t> { using C = Chunk<float>; };
 
-__device__ __forceinline__ void tile_store_cols(const uint16_t (*tile)[kTP], int64_t c0,
-                                                int64_t C, int64_t q0, int64_t Q,
-                                                uint16_t *dst, int64_t dst_ld) {
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int c = i >> 3, qc = i & 7;
-    if (c0 + c >= C || q0 + 8 * qc >= Q) continue;
-    uint32_t w[4];
+template <typename E>
+__device__ __forceinline__ void tile_store_cols(const E (*tile)[TileOf<E>::P], int64_t c0,
+                                                int64_t C, int64_t q0, int64_t Q, E *dst,
+                                                int64_t dst_ld) {
+  constexpr int EPC = TileOf<E>::EPC, CPR = TileOf<E>::CPR;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int c = i / CPR, qc = i % CPR;
+    if (c0 + c >= C || q0 + EPC * qc >= Q) continue;
+    union {
+      uint4 v;
+      E e[EPC];
+    } u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = static_cast<uint32_t>(tile[8 * qc + 2 * j][c]) |
-             (static_cast<uint32_t>(tile[8 * qc + 2 * j + 1][c]) << 16);
-    *reinterpret_cast<uint4 *>(dst + (c0 + c) * dst_ld + q0 + 8 * qc) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    for (int j = 0; j < EPC; ++j) u.e[j] = tile[EPC * qc + j][c];
+    *reinterpret_cast<uint4 *>(dst + (c0 + c) * dst_ld + q0 + EPC * qc) = u.v;
   }
 }
 
-// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16); batches
-// b with active && !active[b] are skipped.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *src, int64_t R, int64_t C,
-                                                        const int32_t *active, uint16_t *dst,
+// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c]; batches b with
+// active && !active[b] are skipped.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E *src, int64_t R, int64_t C,
+                                                        const int32_t *active, E *dst,
                                                         int64_t dst_ld, int64_t dst_bstride,
                                                         int64_t col0) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kTP];
+  constexpr int EPC = TileOf<E>::EPC, CPR = TileOf<E>::CPR;
+  __shared__ __attribute__((aligned(16))) E tile[64][TileOf<E>::P];
   const int64_t b = blockIdx.z;
   if (active && active[b] == 0) return;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const uint16_t *s = src + b * R * C;
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int r = i >> 3, cc = i & 7;
-    if (r0 + r < R && c0 + 8 * cc < C)
-      *reinterpret_cast<uint4 *>(&tile[r][8 * cc]) =
-          *reinterpret_cast<const uint4 *>(s + (r0 + r) * C + c0 + 8 * cc);
+  const E *s = src + b * R * C;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, cc = i % CPR;
+    if (r0 + r < R && c0 + EPC * cc < C)
+      *reinterpret_cast<uint4 *>(&tile[r][EPC * cc]) =
+          *reinterpret_cast<const uint4 *>(s + (r0 + r) * C + c0 + EPC * cc);
   }
   __syncthreads();
-  tile_store_cols(tile, c0, C, r0, R, dst + b * dst_bstride + col0, dst_ld);
+  tile_store_cols<E>(tile, c0, C, r0, R, dst + b * dst_bstride + col0, dst_ld);
 }
 
-// Rows of a bf16 matrix as columns of dst (ld ldd): destination column q
-// holds source row r(q) (read from row_index[r] if given, times row_scale[r]
-// if given); dense: r(q) = q, valid below R; grouped: column runs of
-// padded length per group, r(q) = off[e] + q - poff[e] for
-// poff[e] <= q < poff[e + 1], valid below off[e + 1]. Invalid columns (the
-// padding) are written as zeros, up to Q columns (grouped: poff[G]).
-__global__ __launch_bounds__(256) void cols_kernel(const uint16_t *src, int64_t ld_src,
+// Rows of a matrix as columns of dst (ld ldd): destination column q holds
+// source row r(q) (read from row_index[r] if given, times row_scale[r] if
+// given); dense: r(q) = q, valid below R; grouped: column runs of padded
+// length per group, r(q) = off[e] + q - poff[e] for poff[e] <= q < poff[e+1],
+// valid below off[e + 1]. Invalid columns (the padding) are written as
+// zeros, up to Q columns (grouped: poff[G]).
+template <typename E>
+__global__ __launch_bounds__(256) void cols_kernel(const E *src, int64_t ld_src,
                                                    const int32_t *row_index,
                                                    const float *row_scale, int64_t R, int64_t C,
                                                    const int32_t *off, const int32_t *poff, int G,
-                                                   int64_t Q, uint16_t *dst, int64_t ldd) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kTP];
+                                                   int64_t Q, E *dst, int64_t ldd) {
+  constexpr int EPC = TileOf<E>::EPC, CPR = TileOf<E>::CPR;
+  using CK = typename ChunkT<E>::C;
+  __shared__ __attribute__((aligned(16))) E tile[64][TileOf<E>::P];
   __shared__ int64_t srow[64];
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64, q0 = static_cast<int64_t>(blockIdx.y) * 64;
   const int64_t qend = off ? poff[G] : Q;
@@ -110,27 +127,27 @@ __global__ __launch_bounds__(256) void cols_kernel(const uint16_t *src, int64_t 
     srow[threadIdx.x] = r;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 512; i += 256) {
-    const int qi = i >> 3, cc = i & 7;
-    if (c0 + 8 * cc >= C) continue;
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int qi = i / CPR, cc = i % CPR;
+    if (c0 + EPC * cc >= C) continue;
     const int64_t r = srow[qi];
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (r >= 0) {
       const int64_t sr = row_index ? row_index[r] : r;
-      v = *reinterpret_cast<const uint4 *>(src + sr * ld_src + c0 + 8 * cc);
+      v = *reinterpret_cast<const uint4 *>(src + sr * ld_src + c0 + EPC * cc);
       if (row_scale) {
-        float f[8];
-        Chunk<bf16_t>::unpack(v, f);
+        float f[EPC];
+        CK::unpack(v, f);
         const float sc = row_scale[r];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] *= sc;
-        v = Chunk<bf16_t>::pack(f);
+        for (int j = 0; j < EPC; ++j) f[j] *= sc;
+        v = CK::pack(f);
       }
     }
-    *reinterpret_cast<uint4 *>(&tile[qi][8 * cc]) = v;
+    *reinterpret_cast<uint4 *>(&tile[qi][EPC * cc]) = v;
   }
   __syncthreads();
-  tile_store_cols(tile, c0, C, q0, qend, dst, ldd);
+  tile_store_cols<E>(tile, c0, C, q0, qend, dst, ldd);
 }
 
 // Padded expert column offsets poff[e] = sum of round64(counts) before e, and
@@ -169,11 +186,12 @@ __global__ __launch_bounds__(1024) void kgroup_kernel(const int32_t *counts, int
 
 // Per row p (one wavefront): from the pre-activations a, u and the unscaled
 // W_down^T dy (fp32 [R, f]) and the routing weight g[p] (1 if null): h =
-// SiLU(a) u, dh = g W_down^T dy, da = dh u SiLU'(a), du = dh SiLU(a) as bf16
-// (dAU row p = [da | du], 2 f wide), and dg[p] = <W_down^T dy, h> (if dg).
+// SiLU(a) u, dh = g W_down^T dy, da = dh u SiLU'(a), du = dh SiLU(a) in the
+// activation type (dAU row p = [da | du], 2 f wide), and dg[p] = <W_down^T dy, h> (if dg).
+template <typename AT>
 __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *U, const float *D,
-                                                   const float *gw, int64_t R, int f,
-                                                   uint16_t *H, uint16_t *dAU, float *dg) {
+                                                   const float *gw, int64_t R, int f, void *H,
+                                                   void *dAU, float *dg) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (p >= R) return;
   const int lane = threadIdx.x & 63;
@@ -183,7 +201,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
   if (!D) {  // h only (a forward recompute)
     for (int j = lane; j < f; j += 64) {
       const float a = A[o + j];
-      H[o + j] = f32_to_bf16(a / (1.0f + expf(-a)) * U[o + j]);
+      Elem<AT>::store(H, o + j, a / (1.0f + expf(-a)) * U[o + j]);
     }
     return;
   }
@@ -194,9 +212,9 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
     const float h = si * u;
     acc += dd * h;
     const float dh = g * dd;
-    H[o + j] = f32_to_bf16(h);
-    dAU[2 * o + j] = f32_to_bf16(dh * u * s * (1.0f + a * (1.0f - s)));
-    dAU[2 * o + f + j] = f32_to_bf16(dh * si);
+    Elem<AT>::store(H, o + j, h);
+    Elem<AT>::store(dAU, 2 * o + j, dh * u * s * (1.0f + a * (1.0f - s)));
+    Elem<AT>::store(dAU, 2 * o + f + j, dh * si);
   }
   if (dg) {
 #pragma unroll
@@ -207,13 +225,15 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
 
 // dx[t] = sum_k dXs[inv[t K + k]] + add1[t] + add2[t]
 //         + sum_k dr[inv[t K + k]] W_router[idx[t K + k]]
-// (each term optional; fp32, k in order, then rounded to bf16); one wavefront
+// (each term optional; fp32, k in order, then stored in the activation type);
+// one wavefront
 // per token.
+template <typename AT>
 __global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *dXsh,
                                                  const float *add2, const int32_t *inv,
                                                  const int32_t *idx, const float *dr,
                                                  const float *wr, int64_t T, int K, int d,
-                                                 uint16_t *dx) {
+                                                 void *dx) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
@@ -241,36 +261,37 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *
         acc.x += c * w.x; acc.y += c * w.y; acc.z += c * w.z; acc.w += c * w.w;
       }
     }
-    const float v[4] = {acc.x, acc.y, acc.z, acc.w};
-    uint2 o;
-    o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    *reinterpret_cast<uint2 *>(dx + t * d + i) = o;
+    Elem<AT>::store(dx, t * d + i, acc.x);
+    Elem<AT>::store(dx, t * d + i + 1, acc.y);
+    Elem<AT>::store(dx, t * d + i + 2, acc.z);
+    Elem<AT>::store(dx, t * d + i + 3, acc.w);
   }
 }
 
 // dW_router[e, i] = sum over the rows p of expert e (sorted order) of
 // dr[p] x[sorted_token[p], i], fp32 in row order; one thread per (e, i).
+template <typename AT>
 __global__ __launch_bounds__(256) void dwr_kernel(const float *dr, const int32_t *stok,
-                                                  const int32_t *offsets, const uint16_t *x,
+                                                  const int32_t *offsets, const void *x,
                                                   int d, float *dwr) {
   const int e = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= d) return;
   float acc = 0.f;
   for (int p = offsets[e]; p < offsets[e + 1]; ++p)
-    acc += dr[p] * bf16_to_f32(x[static_cast<int64_t>(stok[p]) * d + i]);
+    acc += dr[p] * Elem<AT>::load(x, static_cast<int64_t>(stok[p]) * d + i);
   dwr[static_cast<int64_t>(e) * d + i] = acc;
 }
 
 // Latent layer ("StableLatentMoE and QuantileBalancer", "Return to model
 // width"), one wavefront per token. Forward recompute: R = sum_k Y[inv[t K +
 // k]] (fp32, k in order), rinv = 1 / sqrt(mean(R^2) + eps) (1 without the
-// norm), R' = R rinv gamma as bf16 (gamma = 1 if null).
+// norm), R' = R rinv gamma in the activation type (gamma = 1 if null).
+template <typename AT>
 __global__ __launch_bounds__(256) void latent_fwd_kernel(const float *Y, const int32_t *inv,
                                                          int64_t T, int K, int L, int norm,
                                                          float eps, const float *gamma, float *R,
-                                                         float *rinv, uint16_t *Rp) {
+                                                         float *rinv, void *Rp) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
@@ -287,22 +308,23 @@ __global__ __launch_bounds__(256) void latent_fwd_kernel(const float *Y, const i
   if (lane == 0) rinv[t] = r;
   for (int l = lane; l < L; l += 64) {
     const float gm = (norm && gamma) ? gamma[l] : 1.0f;
-    Rp[t * L + l] = f32_to_bf16(R[t * L + l] * r * gm);
+    Elem<AT>::store(Rp, t * L + l, R[t * L + l] * r * gm);
   }
 }
 
 // RMSNorm backward per token: s = gamma dR' (dR' = W_lat_up^T dy, fp32),
-// dR = rinv s - R rinv^3 <s, R> / L (dR = dR' without the norm), as bf16.
+// dR = rinv s - R rinv^3 <s, R> / L (dR = dR' without the norm), in the
+// activation type.
+template <typename AT>
 __global__ __launch_bounds__(256) void latent_bwd_kernel(const float *dRp, const float *R,
                                                          const float *rinv, const float *gamma,
-                                                         int64_t T, int L, int norm,
-                                                         uint16_t *dR) {
+                                                         int64_t T, int L, int norm, void *dR) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   const int64_t o = t * L;
   if (!norm) {
-    for (int l = lane; l < L; l += 64) dR[o + l] = f32_to_bf16(dRp[o + l]);
+    for (int l = lane; l < L; l += 64) Elem<AT>::store(dR, o + l, dRp[o + l]);
     return;
   }
   float sR = 0.f;
@@ -312,7 +334,7 @@ __global__ __launch_bounds__(256) void latent_bwd_kernel(const float *dRp, const
   const float r = rinv[t];
   const float c = r * r * r * sR / static_cast<float>(L);
   for (int l = lane; l < L; l += 64)
-    dR[o + l] = f32_to_bf16(r * dRp[o + l] * (gamma ? gamma[l] : 1.0f) - R[o + l] * c);
+    Elem<AT>::store(dR, o + l, r * dRp[o + l] * (gamma ? gamma[l] : 1.0f) - R[o + l] * c);
 }
 
 // Column sums sum_t A[t, l] B[t, l] s[t] in two passes (fixed order): per
@@ -351,24 +373,35 @@ hipError_t launch_fill0(void *p, size_t bytes, hipStream_t s) {
 
 hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t C,
                             const int32_t *active, void *dst, int64_t dst_ld, int64_t dst_bstride,
-                            int64_t col0, hipStream_t s) {
+                            int64_t col0, int act_bf16, hipStream_t s) {
   if (batches == 0 || R == 0 || C == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((R + 63) / 64),
             static_cast<unsigned>(batches));
-  transpose_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), R, C, active,
-                                        static_cast<uint16_t *>(dst), dst_ld, dst_bstride, col0);
+  if (act_bf16)
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), R, C,
+                                                    active, static_cast<uint16_t *>(dst), dst_ld,
+                                                    dst_bstride, col0);
+  else
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t *>(src), R, C,
+                                                    active, static_cast<uint32_t *>(dst), dst_ld,
+                                                    dst_bstride, col0);
   return hipGetLastError();
 }
 
 hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
                        const float *row_scale, int64_t R, int64_t C, const int32_t *off,
                        const int32_t *poff, int G, int64_t Q, void *dst, int64_t ldd,
-                       hipStream_t s) {
+                       int act_bf16, hipStream_t s) {
   if (Q == 0 || C == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((Q + 63) / 64));
-  cols_kernel<<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), ld_src, row_index,
-                                   row_scale, R, C, off, poff, G, Q,
-                                   static_cast<uint16_t *>(dst), ldd);
+  if (act_bf16)
+    cols_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(src), ld_src,
+                                               row_index, row_scale, R, C, off, poff, G, Q,
+                                               static_cast<uint16_t *>(dst), ldd);
+  else
+    cols_kernel<uint32_t><<<grid, 256, 0, s>>>(static_cast<const uint32_t *>(src), ld_src,
+                                               row_index, row_scale, R, C, off, poff, G, Q,
+                                               static_cast<uint32_t *>(dst), ldd);
   return hipGetLastError();
 }
 
@@ -379,44 +412,60 @@ hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, i
 }
 
 hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const float *gw,
-                           int64_t R, int f, void *H, void *dAU, float *dg, hipStream_t s) {
+                           int64_t R, int f, void *H, void *dAU, float *dg, int act_bf16,
+                           hipStream_t s) {
   if (R == 0) return hipSuccess;
-  rows_kernel<<<static_cast<unsigned>((R + 3) / 4), 256, 0, s>>>(
-      A, U, D, gw, R, f, static_cast<uint16_t *>(H), static_cast<uint16_t *>(dAU), dg);
+  const unsigned grid = static_cast<unsigned>((R + 3) / 4);
+  if (act_bf16)
+    rows_kernel<bf16_t><<<grid, 256, 0, s>>>(A, U, D, gw, R, f, H, dAU, dg);
+  else
+    rows_kernel<float><<<grid, 256, 0, s>>>(A, U, D, gw, R, f, H, dAU, dg);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
                          const int32_t *inv, const int32_t *idx, const float *dr, const float *wr,
-                         int64_t T, int K, int d, void *dx, hipStream_t s) {
+                         int64_t T, int K, int d, void *dx, int act_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dx_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
-      dXs, dXsh, add2, inv, idx, dr, wr, T, K, d, static_cast<uint16_t *>(dx));
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  if (act_bf16)
+    dx_kernel<bf16_t><<<grid, 256, 0, s>>>(dXs, dXsh, add2, inv, idx, dr, wr, T, K, d, dx);
+  else
+    dx_kernel<float><<<grid, 256, 0, s>>>(dXs, dXsh, add2, inv, idx, dr, wr, T, K, d, dx);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
-                          const void *x, int E, int d, float *dwr, hipStream_t s) {
+                          const void *x, int E, int d, float *dwr, int act_bf16, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E));
-  dwr_kernel<<<grid, 256, 0, s>>>(dr, stok, offsets, static_cast<const uint16_t *>(x), d, dwr);
+  if (act_bf16)
+    dwr_kernel<bf16_t><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, dwr);
+  else
+    dwr_kernel<float><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, dwr);
   return hipGetLastError();
 }
 
 hipError_t launch_latent_fwd(const float *Y, const int32_t *inv, int64_t T, int K, int L,
                              int norm, float eps, const float *gamma, float *R, float *rinv,
-                             void *Rp, hipStream_t s) {
+                             void *Rp, int act_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  latent_fwd_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
-      Y, inv, T, K, L, norm, eps, gamma, R, rinv, static_cast<uint16_t *>(Rp));
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  if (act_bf16)
+    latent_fwd_kernel<bf16_t><<<grid, 256, 0, s>>>(Y, inv, T, K, L, norm, eps, gamma, R, rinv, Rp);
+  else
+    latent_fwd_kernel<float><<<grid, 256, 0, s>>>(Y, inv, T, K, L, norm, eps, gamma, R, rinv, Rp);
   return hipGetLastError();
 }
 
 hipError_t launch_latent_bwd(const float *dRp, const float *R, const float *rinv,
                              const float *gamma, int64_t T, int L, int norm, void *dR,
-                             hipStream_t s) {
+                             int act_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  latent_bwd_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(
-      dRp, R, rinv, gamma, T, L, norm, static_cast<uint16_t *>(dR));
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  if (act_bf16)
+    latent_bwd_kernel<bf16_t><<<grid, 256, 0, s>>>(dRp, R, rinv, gamma, T, L, norm, dR);
+  else
+    latent_bwd_kernel<float><<<grid, 256, 0, s>>>(dRp, R, rinv, gamma, T, L, norm, dR);
   return hipGetLastError();
 }
 

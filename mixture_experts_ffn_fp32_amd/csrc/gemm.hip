@@ -114,6 +114,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     m_end = min<int64_t>(m_begin + BM, p.M);
   }
   const int n_begin = nt * NOUT;
+  // K-grouped: this expert's reduction columns and output block
+  int64_t kbeg = 0;
+  int kseg = p.K;
+  if (p.k_offsets) {
+    kbeg = p.k_offsets[expert];
+    kseg = static_cast<int>(p.k_offsets[expert + 1] - kbeg);
+  }
+  const int64_t obase = p.k_offsets ? expert * p.out_stride : 0;
 
   // ---------------------------------------------------------------- loaders
   const int kc_ld = tid & 7;
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       arow[i] = nullptr;
       if (r < BM && m < m_end) {
         const int64_t src = (!seg && p.a_rows) ? static_cast<int64_t>(p.a_rows[m]) : m;
-        arow[i] = abase + src * lda * ES;
+        arow[i] = abase + (src * lda + (seg ? 0 : kbeg)) * ES;
       }
     }
 #pragma unroll
@@ -149,14 +157,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
           bbase = static_cast<const char *>(up ? p.b1 : p.b0);
           n = n_begin + (up ? r - BN / 2 : r);
           ldb = p.ldb;
-          off = expert * p.b_stride;
+          off = expert * p.b_stride + kbeg;
         }
         if (n < p.N) brow[i] = bbase + (off + static_cast<int64_t>(n) * ldb) * ES;
       }
     }
   };
 
-  const int steps1 = (p.K + BK - 1) / BK;
+  const int steps1 = (kseg + BK - 1) / BK;
   const int steps = steps1 + (p.a2 ? (p.K2 + BK - 1) / BK : 0);
   // this split's stages (single-segment GEMMs only are split)
   const int per_split = (steps + ksplit - 1) / ksplit;
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   auto load = [&](int st) {
     const bool s2 = st >= steps1;
     const int k = (s2 ? st - steps1 : st) * BK + kc_ld * EPC;
-    const bool kin = k < (s2 ? p.K2 : p.K);
+    const bool kin = k < (s2 ? p.K2 : kseg);
     const int64_t kb = static_cast<int64_t>(k) * ES;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
@@ -269,8 +277,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         } else {
           v = acc[fm][fo][r];
         }
-        if (EPI == EPI_STORE_F32)
-          static_cast<float *>(p.out)[split * p.split_stride + m * p.ldo + col] = v;
+        if (EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32))
+          static_cast<float *>(p.out)[obase + split * p.split_stride + m * p.ldo + col] = v;
         else
           Elem<T>::store(p.out, m * p.ldo + col, v);
       }

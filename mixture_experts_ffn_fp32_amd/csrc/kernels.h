@@ -149,9 +149,9 @@ struct GemmArgs {
   int64_t a_extent;          // rows A may address (0: M; required for tile tables)
   int k_split;               // fp32-store only: K split count (0 or 1 = none);
   int64_t split_stride;      // elements between the splits' partial outputs
-  int out_f32;               // SCALE, pipelined kernel: fp32 output instead of act dtype
+  int out_f32;               // SCALE: fp32 output instead of act dtype
   int64_t b2_stride;         // elements between experts' B matrices of the second K segment
-  // K-grouped (pipelined kernel): tile table entries {expert, m_begin, m_end}
+  // K-grouped: tile table entries {expert, m_begin, m_end}
   // over the output rows; expert e reduces over columns [k_offsets[e],
   // k_offsets[e+1]) of A and B (multiples of 64, shared by all experts) and
   // writes its output at out + e * out_stride.
@@ -221,12 +221,12 @@ hipError_t launch_router_backward(const RouterArgs &a, int act_bf16, const int32
                                   const float *dg, float *dr, hipStream_t s);
 // backward.hip
 hipError_t launch_fill0(void *p, size_t bytes, hipStream_t s);
-// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (bf16) for batches
-// b with active[b] != 0 (all if null)
+// dst[b * dst_bstride + c * dst_ld + col0 + r] = src[b][r][c] (act dtype) for
+// batches b with active[b] != 0 (all if null)
 hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t C,
                             const int32_t *active, void *dst, int64_t dst_ld, int64_t dst_bstride,
-                            int64_t col0, hipStream_t s);
-// bf16 rows (gathered by row_index, scaled by row_scale, either optional) as
+                            int64_t col0, int act_bf16, hipStream_t s);
+// rows (act dtype; gathered by row_index, scaled by row_scale, either optional) as
 // columns of dst (ld ldd, a multiple of 8): column q = row q (dense, zeros
 // from R up to Q, a bound of the columns written) or, grouped, the runs
 // [poff[e], poff[e+1]) hold rows [off[e], off[e+1]) then zeros (Q bounds
@@ -234,33 +234,34 @@ hipError_t launch_transpose(const void *src, int64_t batches, int64_t R, int64_t
 hipError_t launch_cols(const void *src, int64_t ld_src, const int32_t *row_index,
                        const float *row_scale, int64_t R, int64_t C, const int32_t *off,
                        const int32_t *poff, int G, int64_t Q, void *dst, int64_t ldd,
-                       hipStream_t s);
+                       int act_bf16, hipStream_t s);
 // padded expert offsets and the K-grouped m-tile tables of heights M1, M2
 hipError_t launch_kgroup(const int32_t *counts, int E, int M1, int M2, int bm, int32_t *poff,
                          int32_t *t1, int32_t *n1, int32_t *t2, int32_t *n2, hipStream_t s);
-// h = SiLU(a) u and [da | du] (bf16 [R, 2f]) from a, u and W_down^T dy (fp32
+// h = SiLU(a) u and [da | du] (act dtype [R, 2f]) from a, u and W_down^T dy (fp32
 // [R, f]) and the row weights gw (1 if null); dg[p] = <W_down^T dy, h> if dg;
 // with D null, h only
 hipError_t launch_bwd_rows(const float *A, const float *U, const float *D, const float *gw,
-                           int64_t R, int f, void *H, void *dAU, float *dg, hipStream_t s);
+                           int64_t R, int f, void *H, void *dAU, float *dg, int act_bf16,
+                           hipStream_t s);
 // dx = sum_k dXs[inv] + dXsh + add2 + sum_k dr W_router rows (terms optional)
 hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
                          const int32_t *inv, const int32_t *idx, const float *dr, const float *wr,
-                         int64_t T, int K, int d, void *dx, hipStream_t s);
+                         int64_t T, int K, int d, void *dx, int act_bf16, hipStream_t s);
 // latent: R = sum_k Y[inv] (fp32), rinv, R' = R rinv gamma (bf16)
 hipError_t launch_latent_fwd(const float *Y, const int32_t *inv, int64_t T, int K, int L,
                              int norm, float eps, const float *gamma, float *R, float *rinv,
-                             void *Rp, hipStream_t s);
+                             void *Rp, int act_bf16, hipStream_t s);
 // latent: RMSNorm backward dR (bf16) from dR' (fp32)
 hipError_t launch_latent_bwd(const float *dRp, const float *R, const float *rinv,
                              const float *gamma, int64_t T, int L, int norm, void *dR,
-                             hipStream_t s);
+                             int act_bf16, hipStream_t s);
 // out[l] = sum_t A[t, l] B[t, l] sc[t] (part: [colsum_blocks(T), L] scratch)
 int64_t colsum_blocks(int64_t T);
 hipError_t launch_colsum(const float *A, const float *B, const float *sc, int64_t T, int L,
                          float *part, float *out, hipStream_t s);
 hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
-                          const void *x, int E, int d, float *dwr, hipStream_t s);
+                          const void *x, int E, int d, float *dwr, int act_bf16, hipStream_t s);
 
 // Bias-based balancer step (balance.hip); nk = tokens x top-k.
 hipError_t launch_balance(int E, int64_t nk, const int32_t *counts, float alpha, float *bias,

@@ -187,8 +187,8 @@ def test_plan_paths_of_the_workloads():
 
 
 def test_backward_checked_before_launch():
-    """moe_backward: bf16 non-latent layers with widths that are multiples of
-    32; NULLs and a short workspace are reported before anything runs."""
+    """moe_backward: widths that are multiples of 32; NULLs and a short
+    workspace are reported before anything runs."""
     fake = C.c_void_p(1 << 20)
     w = moe.MoeWeights(**{k: fake.value for k, _ in moe.MoeWeights._fields_})
     g = moe.MoeGrads()
@@ -196,8 +196,6 @@ def test_backward_checked_before_launch():
     d = _desc(T=64)
     n = moe.moe_backward_workspace_size(d)
     assert n > moe.moe_workspace_size(d)
-    assert L.moe_backward(C.byref(_desc(T=64, act_dtype=0)), C.byref(w), fake, fake, fake,
-                          C.byref(g), fake, 1 << 40, None) == -3
     dl = moe.make_desc(moe_synth.get("latent"))
     dl.latent = 40  # latent widths must be multiples of 32 as well
     assert L.moe_backward(C.byref(dl), C.byref(w), fake, fake, fake, C.byref(g), fake, 1 << 40,

@@ -13,6 +13,7 @@ from _layers import custom, max_abs_rel
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2  # max-abs-rel per gradient tensor: bf16 operands, fp32 accumulation
+TOL_BY_ACT = {"bf16": TOL, "f32": 1e-5}  # fp32: every product in fp32
 
 SHAPES = {"w_router": ("E", "d"), "w_gate": ("E", "d_ff", "de"), "w_up": ("E", "d_ff", "de"),
           "w_down": ("E", "de", "d_ff"), "ws_gate": ("d_shared", "d"),
@@ -34,8 +35,9 @@ def _grad_buffers(w, keys):
 
 
 def _d_out(w, seed):
-    bits = moe_synth.draw_rows(seed, (w.T, w.d), "bf16")
-    return bits, torch.from_numpy(bits).view(torch.bfloat16).cuda()
+    v = moe_synth.draw_rows(seed, (w.T, w.d), w.act)
+    t = torch.from_numpy(v)
+    return v, (t.view(torch.bfloat16) if w.act == "bf16" else t).cuda()
 
 
 def run_backward(w, a, layer, keys, seed=11):
@@ -57,12 +59,13 @@ def oracle_selection(orc, g_idx):
     return use, int(near.sum())
 
 
-def check_all(w, a, layer, keys=None, seed=11, tol=TOL):
+def check_all(w, a, layer, keys=None, seed=11, tol=None):
     keys = _keys(w) if keys is None else keys
+    tol = tol or TOL_BY_ACT[w.act]
     bits, dx, grads, g_idx = run_backward(w, a, layer, keys, seed)
     orc = oracle.Oracle(w, a)
     use, n_near = oracle_selection(orc, g_idx)
-    ref = orc.backward(moe_synth.as_f64(bits, "bf16"), idx_override=use,
+    ref = orc.backward(moe_synth.as_f64(bits, w.act), idx_override=use,
                        shared=bool(w.d_shared))
     errs = {"dx": max_abs_rel(dx, ref["dx"])}
     active = np.bincount(use.ravel(), minlength=w.E) > 0
@@ -84,6 +87,12 @@ def check_all(w, a, layer, keys=None, seed=11, tol=TOL):
 
 LAYERS = {
     "small_256": None,
+    "tiny": None,  # the fp32 workload (generic kernel, fp32 matrix cores)
+    "latent_f32": dict(T=64, d=64, latent=32, d_ff=32, E=4, K=2, act="f32",
+                       route="sigmoid_bias", bias_std=0.1, has_rmsnorm=True, n_shared=1,
+                       d_ff_shared=32, w_std=0.1, router_std=0.1),
+    "f32_ragged": dict(T=300, d=96, d_ff=160, E=6, K=2, act="f32", n_shared=1,
+                       d_ff_shared=64, w_std=0.08, router_std=0.08),
     "topk_e16": dict(T=512, d=256, d_ff=384, E=16, K=4, act="bf16", n_shared=1,
                      d_ff_shared=256, w_std=0.05, router_std=0.05, bias_std=0.01),
     "softmax_first": dict(T=300, d=128, d_ff=160, E=8, K=2, act="bf16", route="softmax_topk",
@@ -118,6 +127,8 @@ def _gpu():
 def test_backward_matches_oracle(name):
     if name == "small_256":
         w = moe_synth.get("small").with_T(256)
+    elif name == "tiny":
+        w = moe_synth.get("tiny")
     else:
         w = custom(name, config_no=950 + sorted(LAYERS).index(name), **LAYERS[name])
     say(f"case backward {name} T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K} route={w.route}")
@@ -155,7 +166,7 @@ def test_backward_medium_sampled():
     bits, dx, grads, g_idx = run_backward(w, a, layer, ["w_gate", "w_up", "w_down"])
     orc = oracle.Oracle(w, a)
     use, n_near = oracle_selection(orc, g_idx)
-    dy = moe_synth.as_f64(bits, "bf16")
+    dy = moe_synth.as_f64(bits, w.act)
     toks = sample_tokens(use, w.E, 256, seed=5)
     ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
                        router=False, shared=False)
@@ -191,7 +202,7 @@ def test_backward_latent_full_size_sampled():
     bits, dx, grads, g_idx = run_backward(w, a, layer, ["w_gate", "w_up", "w_down"])
     orc = oracle.Oracle(w, a)
     use, n_near = oracle_selection(orc, g_idx)
-    dy = moe_synth.as_f64(bits, "bf16")
+    dy = moe_synth.as_f64(bits, w.act)
     toks = sample_tokens(use, w.E, 128, seed=6)
     ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
                        router=False, shared=False, latent=False)
