@@ -114,9 +114,16 @@ def cpu_baseline(w, a, budget_s=12.0):
     t0 = time.perf_counter()
     orc.forward(tokens=toks)
     dt = time.perf_counter() - t0
+    # a whole batch shorter than the budget: repeat it (up to 10 passes)
+    passes = 1
+    while n == w.T and dt < 0.8 * budget_s and passes < 10:
+        orc.forward(tokens=toks)
+        passes += 1
+        dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens (seeded), full layer per token in fp64, "
+    rep = f" x {passes} passes" if passes > 1 else ""
+    return {"value": n * passes / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.T} tokens (seeded){rep}, full layer per token in fp64, "
                       f"{dt:.1f} s"}
 
 
