@@ -414,7 +414,7 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
 struct BwdLayout {
   size_t poff, kt1, kn1, kt2, kn2, tiles, ntiles;
   size_t wguT, wdT, wsguT, wsdT;
-  size_t apre, upre, dhu, h, dau, dg, dr, dxs;
+  size_t apre, upre, dhu, h, dau, dg, dr, dxs, dwr_part;
   size_t apre_s, upre_s, dhu_s, h_s, dau_s, dxsh;
   size_t xsT, dysT, daT, duT, hT, xT, dyT, dashT, dushT, hshT;
   // latent
@@ -457,6 +457,7 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.dg = take(rows * 4);
   B.dr = take(rows * 4);
   B.dxs = take(rows * de * 4);
+  B.dwr_part = take(dwr_part_bytes(static_cast<int>(E), static_cast<int>(dm)));
   B.apre_s = take(T * ds * 4);
   B.upre_s = take(T * ds * 4);
   B.dhu_s = take(T * ds * 4);
@@ -1075,7 +1076,8 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
 
   // 7. weight gradients
   if (gr->w_router)
-    MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, gr->w_router, bf, s));
+    MOE_TRY(launch_bwd_dwr(F(B.dr), stok, offsets, x, static_cast<int>(E), dm, F(B.dwr_part),
+                           gr->w_router, bf, s));
   if (Lt && d->has_rmsnorm && gr->rms_gamma)
     MOE_TRY(launch_colsum(F(B.dRp), F(B.R), F(B.rinv), T, Lt, F(B.gpart), gr->rms_gamma, s));
   const bool want_e = gr->w_gate || gr->w_up || gr->w_down;

@@ -226,8 +226,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const float *A, const float *
 // dx[t] = sum_k dXs[inv[t K + k]] + add1[t] + add2[t]
 //         + sum_k dr[inv[t K + k]] W_router[idx[t K + k]]
 // (each term optional; fp32, k in order, then stored in the activation type);
-// one wavefront
-// per token.
+// one wavefront per token and 256-column block (blockIdx.y).
 template <typename AT>
 __global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *dXsh,
                                                  const float *add2, const int32_t *inv,
@@ -235,51 +234,74 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *dXs, const float *
                                                  const float *wr, int64_t T, int K, int d,
                                                  void *dx) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int lane = threadIdx.x & 63;
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (dXs) {
-      for (int k = 0; k < K; ++k) {
-        const int64_t q = inv[t * K + k];
-        const float4 v = *reinterpret_cast<const float4 *>(dXs + q * d + i);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
-    }
-    if (dXsh) {
-      const float4 v = *reinterpret_cast<const float4 *>(dXsh + t * d + i);
+  const int i = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
+  if (t >= T || i >= d) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (dXs) {
+    for (int k = 0; k < K; ++k) {
+      const int64_t q = inv[t * K + k];
+      const float4 v = *reinterpret_cast<const float4 *>(dXs + q * d + i);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    if (add2) {
-      const float4 v = *reinterpret_cast<const float4 *>(add2 + t * d + i);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (dr) {
-      for (int k = 0; k < K; ++k) {
-        const float c = dr[inv[t * K + k]];
-        const float4 w = *reinterpret_cast<const float4 *>(wr + static_cast<int64_t>(idx[t * K + k]) * d + i);
-        acc.x += c * w.x; acc.y += c * w.y; acc.z += c * w.z; acc.w += c * w.w;
-      }
-    }
-    Elem<AT>::store(dx, t * d + i, acc.x);
-    Elem<AT>::store(dx, t * d + i + 1, acc.y);
-    Elem<AT>::store(dx, t * d + i + 2, acc.z);
-    Elem<AT>::store(dx, t * d + i + 3, acc.w);
   }
+  if (dXsh) {
+    const float4 v = *reinterpret_cast<const float4 *>(dXsh + t * d + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (add2) {
+    const float4 v = *reinterpret_cast<const float4 *>(add2 + t * d + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (dr) {
+    for (int k = 0; k < K; ++k) {
+      const float c = dr[inv[t * K + k]];
+      const float4 w = *reinterpret_cast<const float4 *>(wr + static_cast<int64_t>(idx[t * K + k]) * d + i);
+      acc.x += c * w.x; acc.y += c * w.y; acc.z += c * w.z; acc.w += c * w.w;
+    }
+  }
+  Elem<AT>::store(dx, t * d + i, acc.x);
+  Elem<AT>::store(dx, t * d + i + 1, acc.y);
+  Elem<AT>::store(dx, t * d + i + 2, acc.z);
+  Elem<AT>::store(dx, t * d + i + 3, acc.w);
 }
 
 // dW_router[e, i] = sum over the rows p of expert e (sorted order) of
-// dr[p] x[sorted_token[p], i], fp32 in row order; one thread per (e, i).
+// dr[p] x[sorted_token[p], i], fp32. Block (column block, e, z) of Z sums the
+// rows offsets[e] + z + j Z (j = 0, 1, ...) in order, one thread per column,
+// into part[e, z, i] (Z > 1) or straight into dwr (Z == 1); dwr_final_kernel
+// adds the Z partials in order.
 template <typename AT>
 __global__ __launch_bounds__(256) void dwr_kernel(const float *dr, const int32_t *stok,
-                                                  const int32_t *offsets, const void *x,
-                                                  int d, float *dwr) {
+                                                  const int32_t *offsets, const void *x, int d,
+                                                  int Z, float *part, float *dwr) {
+  const int e = blockIdx.y, z = blockIdx.z;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= d) return;
+  const int p0 = offsets[e] + z, p1 = offsets[e + 1];
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;  // rows j = 0, 1, 2, 3 mod 4
+  int p = p0;
+  for (; p + 3 * Z < p1; p += 4 * Z) {
+    const int64_t r0 = stok[p], r1 = stok[p + Z], r2 = stok[p + 2 * Z], r3 = stok[p + 3 * Z];
+    a0 += dr[p] * Elem<AT>::load(x, r0 * d + i);
+    a1 += dr[p + Z] * Elem<AT>::load(x, r1 * d + i);
+    a2 += dr[p + 2 * Z] * Elem<AT>::load(x, r2 * d + i);
+    a3 += dr[p + 3 * Z] * Elem<AT>::load(x, r3 * d + i);
+  }
+  for (; p < p1; p += Z) a0 += dr[p] * Elem<AT>::load(x, static_cast<int64_t>(stok[p]) * d + i);
+  const float acc = (a0 + a1) + (a2 + a3);
+  if (Z == 1)
+    dwr[static_cast<int64_t>(e) * d + i] = acc;
+  else
+    part[(static_cast<int64_t>(e) * Z + z) * d + i] = acc;
+}
+
+__global__ __launch_bounds__(256) void dwr_final_kernel(const float *part, int d, int Z,
+                                                        float *dwr) {
   const int e = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= d) return;
   float acc = 0.f;
-  for (int p = offsets[e]; p < offsets[e + 1]; ++p)
-    acc += dr[p] * Elem<AT>::load(x, static_cast<int64_t>(stok[p]) * d + i);
+  for (int z = 0; z < Z; ++z) acc += part[(static_cast<int64_t>(e) * Z + z) * d + i];
   dwr[static_cast<int64_t>(e) * d + i] = acc;
 }
 
@@ -427,7 +449,7 @@ hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
                          const int32_t *inv, const int32_t *idx, const float *dr, const float *wr,
                          int64_t T, int K, int d, void *dx, int act_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4), static_cast<unsigned>((d + 255) / 256));
   if (act_bf16)
     dx_kernel<bf16_t><<<grid, 256, 0, s>>>(dXs, dXsh, add2, inv, idx, dr, wr, T, K, d, dx);
   else
@@ -435,13 +457,32 @@ hipError_t launch_bwd_dx(const float *dXs, const float *dXsh, const float *add2,
   return hipGetLastError();
 }
 
+int dwr_splits(int E, int d) {
+  const int blocks = E * ((d + 255) / 256);
+  const int z = (4096 + blocks - 1) / blocks;
+  return z < 1 ? 1 : (z > 64 ? 64 : z);
+}
+
+size_t dwr_part_bytes(int E, int d) {
+  const int z = dwr_splits(E, d);
+  return z > 1 ? static_cast<size_t>(E) * z * d * 4 : 0;
+}
+
 hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
-                          const void *x, int E, int d, float *dwr, int act_bf16, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E));
+                          const void *x, int E, int d, float *part, float *dwr, int act_bf16,
+                          hipStream_t s) {
+  if (E == 0 || d == 0) return hipSuccess;
+  const int Z = dwr_splits(E, d);
+  const dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E),
+                  static_cast<unsigned>(Z));
   if (act_bf16)
-    dwr_kernel<bf16_t><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, dwr);
+    dwr_kernel<bf16_t><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, Z, part, dwr);
   else
-    dwr_kernel<float><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, dwr);
+    dwr_kernel<float><<<grid, 256, 0, s>>>(dr, stok, offsets, x, d, Z, part, dwr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || Z == 1) return e;
+  dwr_final_kernel<<<dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(E)), 256,
+                     0, s>>>(part, d, Z, dwr);
   return hipGetLastError();
 }
 

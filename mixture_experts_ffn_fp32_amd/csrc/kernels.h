@@ -260,8 +260,13 @@ hipError_t launch_latent_bwd(const float *dRp, const float *R, const float *rinv
 int64_t colsum_blocks(int64_t T);
 hipError_t launch_colsum(const float *A, const float *B, const float *sc, int64_t T, int L,
                          float *part, float *out, hipStream_t s);
+// dW_router from the logit gradients dr per sorted row; rows of an expert are
+// split over dwr_splits(E, d) blocks (part: dwr_part_bytes(E, d) scratch)
+int dwr_splits(int E, int d);
+size_t dwr_part_bytes(int E, int d);
 hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *offsets,
-                          const void *x, int E, int d, float *dwr, int act_bf16, hipStream_t s);
+                          const void *x, int E, int d, float *part, float *dwr, int act_bf16,
+                          hipStream_t s);
 
 // Bias-based balancer step (balance.hip); nk = tokens x top-k.
 hipError_t launch_balance(int E, int64_t nk, const int32_t *counts, float alpha, float *bias,
