@@ -83,21 +83,33 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // Exclusive scan over a block of exactly 1024 threads; one value per thread.
-// `tmp` is __shared__ scratch of 1024 ints. Returns the exclusive prefix and
-// writes the block total to *total.
+// `tmp` is __shared__ scratch of at least 16 ints. Returns the exclusive
+// prefix and writes the block total to *total.
 __device__ __forceinline__ int block_exscan_1024(int v, int *tmp, int *total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  // inclusive scan inside each wavefront (shuffles), then of the 16
+  // wavefront totals by wavefront 0; three barriers in all
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  int incl = tmp[t];
-  *total = tmp[1023];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
+  if (w == 0) {
+    int s = lane < 16 ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(s, off);
+      if (lane >= off) s += y;
+    }
+    if (lane < 16) tmp[lane] = s;
+  }
+  __syncthreads();
+  const int incl = x + (w ? tmp[w - 1] : 0);
+  *total = tmp[15];
+  __syncthreads();  // tmp may be rewritten as soon as this returns
   return incl - v;
 }
 

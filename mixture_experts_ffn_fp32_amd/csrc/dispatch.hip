@@ -40,13 +40,15 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
     chunk_hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// Fill the m-tile table of height bm from offsets held in LDS (1024 threads).
-// tile i = {expert, row_begin, row_end, group_first, group_size}; experts
-// with no rows get no tile. A group is a run of at most kTileGroup m-tiles
-// of one expert (the GEMMs schedule a group's tiles together so they share
-// the expert's weight slices in L2).
-__device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
-                            int32_t *tiles, int32_t *n_tiles) {
+// m-tile tables of height bm from offsets held in LDS (1024 threads), in two
+// steps so that callers can put every global write after their last
+// barrier: tile_starts (LDS only: start[e] = first tile of expert e,
+// start[E] = total) and write_tiles (global writes only). Tile i = {expert,
+// row_begin, row_end, group_first, group_size}; experts with no rows get no
+// tile. A group is a run of at most kTileGroup m-tiles of one expert (the
+// GEMMs schedule a group's tiles together so they share the expert's weight
+// slices in L2).
+__device__ void tile_starts(const int *off, int E, int bm, int *start, int *tmp) {
   const int t = threadIdx.x;
   int nt = 0;
   if (t < E) nt = (off[t + 1] - off[t] + bm - 1) / bm;
@@ -54,7 +56,12 @@ __device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
   const int ex = block_exscan_1024(nt, tmp, &total);
   if (t < E) start[t] = ex;
   if (t == 0) start[E] = total;
-  __syncthreads();
+}
+
+__device__ void write_tiles(const int *off, int E, int bm, const int *start, int32_t *tiles,
+                            int32_t *n_tiles) {
+  const int t = threadIdx.x;
+  const int total = start[E];
   for (int i = t; i < total; i += 1024) {
     int lo = 0, hi = E;  // find e with start[e] <= i < start[e+1]
     while (hi - lo > 1) {
@@ -72,6 +79,13 @@ __device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
     ti[4] = min(kTileGroup, start[e + 1] - gfirst);
   }
   if (t == 0) *n_tiles = total;
+}
+
+__device__ void build_tiles(const int *off, int E, int bm, int *start, int *tmp,
+                            int32_t *tiles, int32_t *n_tiles) {
+  tile_starts(off, E, bm, start, tmp);
+  __syncthreads();
+  write_tiles(off, E, bm, start, tiles, n_tiles);
 }
 
 __global__ __launch_bounds__(1024) void scan_kernel(ScanArgs a) {
@@ -203,41 +217,76 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
 // The whole dispatch in one workgroup of 1024 threads, for few slots and
 // experts (a launch per step costs more than the work there). Each thread
 // owns slots t, t + 1024, ... (one per round of 1024): their ids, weights and
-// the router gaps are loaded once, up front. Per round and wavefront, slots
-// of equal id find each other with one ballot per id bit (peer masks), so
-// the LDS histogram takes one atomic per (wavefront, id), and a slot's
-// position is its expert's running base + the slots of that id in earlier
-// wavefronts of the round (per-wavefront peer counts in LDS) + its rank among
-// its wavefront's peers. Scan, m-tile tables and near-tie count as in
-// scan_kernel.
+// router gaps are loaded once, up front. Per round and wavefront, slots of
+// equal id find each other with one ballot per id bit (peer masks), so the
+// LDS histogram takes one atomic per (wavefront, id). One exclusive scan of
+// packed (count, m-tiles, m-tiles of the second height) per expert gives the
+// offsets and both tile tables' starts. A slot's position is its expert's
+// running base + the slots of that id in earlier wavefronts of the round +
+// its rank among its wavefront's peers: per round the wavefronts' peer
+// counts go to LDS and one thread per expert turns them into those bases
+// (two barriers a round, the count tables alternating between two buffers).
+// Everything up to the positions stays in LDS and registers; the global
+// writes all come after the last barrier.
 constexpr int kFusedRounds = static_cast<int>(kFusedMaxSlots / 1024);
 
+__device__ __forceinline__ uint64_t block_exscan64_1024(uint64_t v, uint64_t *tmp,
+                                                        uint64_t *total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t s = lane < 16 ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint64_t y = __shfl_up(s, off);
+      if (lane >= off) s += y;
+    }
+    if (lane < 16) tmp[lane] = s;
+  }
+  __syncthreads();
+  const uint64_t incl = x + (w ? tmp[w - 1] : 0);
+  *total = tmp[15];
+  return incl - v;
+}
+
 __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, ScatterArgs sc) {
-  __shared__ int tmp[1024];
+  __shared__ uint64_t tmp64[16];
   __shared__ int run[kMaxE + 1];
   __shared__ int off[kMaxE + 1];
   __shared__ int start[kMaxE + 1];
-  __shared__ int wcnt[16][kFusedMaxE];
+  __shared__ int start2[kMaxE + 1];
+  __shared__ int wcnt[2][16][kFusedMaxE];
+  __shared__ int ntie_total;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int E = a.E;
-  const int rounds = static_cast<int>((a.slots + 1023) / 1024);
+  const int slots = static_cast<int>(a.slots);
+  const int rounds = (slots + 1023) / 1024;
+  const bool ties = a.gap && a.n_near_ties;
+  const int Tn = ties ? static_cast<int>(a.T) : 0;  // T <= slots
   int ids[kFusedRounds];
-  float gs[kFusedRounds];
+  float gs[kFusedRounds], gap[kFusedRounds];
 #pragma unroll
   for (int r = 0; r < kFusedRounds; ++r) {
-    const int64_t s = static_cast<int64_t>(r) * 1024 + t;
-    ids[r] = (r < rounds && s < a.slots) ? sc.idx[s] : -1;
-    gs[r] = (r < rounds && s < a.slots && sc.sorted_w) ? sc.g[s] : 0.f;
+    const int s = r * 1024 + t;
+    ids[r] = (r < rounds && s < slots) ? sc.idx[s] : -1;
+    gs[r] = (r < rounds && s < slots && sc.sorted_w) ? sc.g[s] : 0.f;
+    gap[r] = (r < rounds && s < Tn) ? a.gap[s] : INFINITY;
   }
-  int ntie = 0;
-  if (a.gap && a.n_near_ties)
-    for (int64_t i = t; i < a.T; i += 1024) ntie += (a.gap[i] < a.tie_eps) ? 1 : 0;
   for (int e = t; e < E; e += 1024) run[e] = 0;
+  if (t == 0) ntie_total = 0;
   int bits = 0;
   while ((1 << bits) < E) ++bits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int rk[kFusedRounds], cn[kFusedRounds];
   __syncthreads();
+  int ntie = 0;
 #pragma unroll
   for (int r = 0; r < kFusedRounds; ++r) {
     rk[r] = 0;
@@ -254,63 +303,85 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, Scatte
       rk[r] = __popcll(peers & lt_mask);
       cn[r] = __popcll(peers);
       if (valid && rk[r] == cn[r] - 1) atomicAdd(&run[e], cn[r]);
+      ntie += gap[r] < a.tie_eps ? 1 : 0;
     }
   }
+  if (ties) {  // near ties: a wavefront sum, one LDS atomic per wavefront
+    int v = ntie;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0 && v) atomicAdd(&ntie_total, v);
+  }
   __syncthreads();
+  // (count, tiles of height bm, tiles of height bm2) per expert, 21 bits each
   const int cnt_t = t < E ? run[t] : 0;
-  int total;
-  const int ex = block_exscan_1024(cnt_t, tmp, &total);
+  const uint64_t nt1 = (t < E && a.tiles) ? (cnt_t + a.bm - 1) / a.bm : 0;
+  const uint64_t nt2 = (t < E && a.tiles2) ? (cnt_t + a.bm2 - 1) / a.bm2 : 0;
+  constexpr uint64_t kM = (1ull << 21) - 1;
+  uint64_t tot;
+  const uint64_t ex = block_exscan64_1024(static_cast<uint64_t>(cnt_t) | (nt1 << 21) | (nt2 << 42),
+                                          tmp64, &tot);
+  const int ex_c = static_cast<int>(ex & kM);
   if (t < E) {
-    off[t] = ex;
-    run[t] = ex;
-    a.counts[t] = cnt_t;
-    a.offsets[t] = ex;
+    off[t] = ex_c;
+    run[t] = ex_c;
+    start[t] = static_cast<int>((ex >> 21) & kM);
+    start2[t] = static_cast<int>(ex >> 42);
   }
   if (t == 0) {
-    off[E] = total;
-    a.offsets[E] = total;
+    off[E] = static_cast<int>(tot & kM);
+    start[E] = static_cast<int>((tot >> 21) & kM);
+    start2[E] = static_cast<int>(tot >> 42);
   }
   __syncthreads();
-  if (a.tiles) build_tiles(off, E, a.bm, start, tmp, a.tiles, a.n_tiles);
-  __syncthreads();
-  if (a.tiles2) build_tiles(off, E, a.bm2, start, tmp, a.tiles2, a.n_tiles2);
-  __syncthreads();
-  if (a.gap && a.n_near_ties) {
-    int tot;
-    block_exscan_1024(ntie, tmp, &tot);
-    if (t == 0) *a.n_near_ties = tot;
+  int pos[kFusedRounds];
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    pos[r] = -1;
+    if (r >= rounds) break;
+    int(*wc)[kFusedMaxE] = wcnt[r & 1];
+    const int e = ids[r];
+    const bool valid = e >= 0 && e < E;
+    for (int i = lane; i < E; i += 64) wc[wave][i] = 0;  // this wave's row (in order)
+    if (valid && rk[r] == cn[r] - 1) wc[wave][e] = cn[r];
+    __syncthreads();
+    if (t < E) {  // expert t: bases of its slots per wavefront, then the running base
+      int v[16];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) v[w] = wc[w][t];
+      int acc = run[t];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        wc[w][t] = acc;
+        acc += v[w];
+      }
+      run[t] = acc;
+    }
+    __syncthreads();
+    if (valid) pos[r] = wc[wave][e] + rk[r];
   }
+
+  // global writes
+  if (t < E) {
+    a.counts[t] = cnt_t;
+    a.offsets[t] = ex_c;
+  }
+  if (t == 0) a.offsets[E] = off[E];
+  if (a.tiles) write_tiles(off, E, a.bm, start, a.tiles, a.n_tiles);
+  if (a.tiles2) write_tiles(off, E, a.bm2, start2, a.tiles2, a.n_tiles2);
+  if (ties && t == 0) *a.n_near_ties = ntie_total;
 #pragma unroll
   for (int r = 0; r < kFusedRounds; ++r) {
     if (r >= rounds) break;
-    const int64_t s = static_cast<int64_t>(r) * 1024 + t;
-    const int e = ids[r];
-    const bool valid = e >= 0 && e < E;
-    for (int i = lane; i < E; i += 64) wcnt[wave][i] = 0;  // this wave's row (in order)
-    if (valid && rk[r] == cn[r] - 1) wcnt[wave][e] = cn[r];
-    __syncthreads();
-    int pos = 0;
-    if (valid) {
-      int pre = 0;
-      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-      pos = run[e] + pre + rk[r];
-    }
-    __syncthreads();  // every read of run[] and wcnt[] of this round is done
-    if (t < E) {
-      int add = 0;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) add += wcnt[w][t];
-      run[t] += add;
-    }
-    if (valid) {
-      sc.perm[pos] = static_cast<int32_t>(s);
-      sc.sorted_token[pos] = static_cast<int32_t>(s / sc.K);
-      sc.inv[s] = pos;
-      if (sc.sorted_w) sc.sorted_w[pos] = gs[r];
-    } else if (s < a.slots) {
+    const int s = r * 1024 + t;
+    if (pos[r] >= 0) {
+      sc.perm[pos[r]] = s;
+      sc.sorted_token[pos[r]] = s / sc.K;
+      sc.inv[s] = pos[r];
+      if (sc.sorted_w) sc.sorted_w[pos[r]] = gs[r];
+    } else if (s < slots) {
       sc.inv[s] = -1;
     }
-    __syncthreads();  // run[] updated before the next round reads it
   }
 }
 

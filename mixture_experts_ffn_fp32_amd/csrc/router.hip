@@ -241,29 +241,45 @@ __global__ __launch_bounds__(256) void router_valu_kernel(RouterArgs a, int sele
       Chunk<T>::unpack(raw4, &xv[c][h * Chunk<T>::N]);
     }
   }
+  // four experts per pass: all their W_router loads are issued before the
+  // FMAs (lanes past d read element 0 and add it times x = 0); per expert the
+  // sum runs over the chunks in order, then a butterfly over the lanes
   float raw = 0.f;  // logit of expert `lane`
-  for (int e = 0; e < a.E; ++e) {
-    const float *w = a.w + static_cast<int64_t>(e) * a.d;
-    float p = 0.f;
+  for (int e0 = 0; e0 < a.E; e0 += 4) {
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-      const int i0 = 512 * c + 8 * lane;
-      if (c < chunks && i0 < a.d) {
-        const float4 w0 = *reinterpret_cast<const float4 *>(w + i0);
-        const float4 w1 = *reinterpret_cast<const float4 *>(w + i0 + 4);
-        p = fmaf(xv[c][0], w0.x, p);
-        p = fmaf(xv[c][1], w0.y, p);
-        p = fmaf(xv[c][2], w0.z, p);
-        p = fmaf(xv[c][3], w0.w, p);
-        p = fmaf(xv[c][4], w1.x, p);
-        p = fmaf(xv[c][5], w1.y, p);
-        p = fmaf(xv[c][6], w1.z, p);
-        p = fmaf(xv[c][7], w1.w, p);
+      if (c < chunks) {
+        const int i0 = 512 * c + 8 * lane;
+        const int ii = i0 < a.d ? i0 : 0;
+        float4 w0[4], w1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = e0 + j < a.E ? e0 + j : a.E - 1;
+          const float *w = a.w + static_cast<int64_t>(e) * a.d + ii;
+          w0[j] = *reinterpret_cast<const float4 *>(w);
+          w1[j] = *reinterpret_cast<const float4 *>(w + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = fmaf(xv[c][0], w0[j].x, p[j]);
+          p[j] = fmaf(xv[c][1], w0[j].y, p[j]);
+          p[j] = fmaf(xv[c][2], w0[j].z, p[j]);
+          p[j] = fmaf(xv[c][3], w0[j].w, p[j]);
+          p[j] = fmaf(xv[c][4], w1[j].x, p[j]);
+          p[j] = fmaf(xv[c][5], w1[j].y, p[j]);
+          p[j] = fmaf(xv[c][6], w1[j].z, p[j]);
+          p[j] = fmaf(xv[c][7], w1[j].w, p[j]);
+        }
       }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-    if (lane == e) raw = p;
+    for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] += __shfl_xor(p[j], off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane == e0 + j) raw = p[j];
   }
   if (lane < a.E) a.logits[t * a.E + lane] = raw;
   if (select) {
