@@ -501,39 +501,56 @@ __global__ __launch_bounds__(256) void loss_partial_kernel(const float *logits, 
 // losses[0] = alpha E sum_e (counts[e] / (T K)) (P_e / T), losses[1] =
 // z_weight (sum lse^2) / T; chunk sums in chunk order, expert terms reduced
 // in a fixed tree, all in fp64.
-__global__ __launch_bounds__(256) void loss_final_kernel(const float *part, int64_t n_chunks,
-                                                         int64_t T, int E, int K,
-                                                         const int32_t *counts, float alpha,
-                                                         float z_weight, float *losses) {
-  __shared__ double sa[256], sz[256];
-  double a = 0.0, zs = 0.0;
-  constexpr int kBatch = 16;  // chunk partials loaded together, added in order
-  for (int e = threadIdx.x; e <= E; e += 256) {
+__global__ __launch_bounds__(1024) void loss_final_kernel(const float *part, int64_t n_chunks,
+                                                          int64_t T, int E, int K,
+                                                          const int32_t *counts, float alpha,
+                                                          float z_weight, float *losses) {
+  // column e of the chunk partials (E + 1 columns: the experts' probability
+  // sums, then the z term) is summed in fp64 by J threads, thread j taking
+  // chunks j, j + J, ... in order (their loads issued kBatch at a time);
+  // then the J sums of each column in order, then the columns by a fixed
+  // tree
+  constexpr int kBatch = 16;
+  __shared__ double ps[kMaxE + 8];
+  __shared__ double sa[1024], sz[1024];
+  const int t = threadIdx.x, E1 = E + 1;
+  const int J = E1 >= 1024 ? 1 : 1024 / E1;
+  for (int i = t; i < E1 * J; i += 1024) {
+    const int e = i % E1, j = i / E1;
     double s = 0.0;
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += kBatch) {
+    for (int64_t c0 = j; c0 < n_chunks; c0 += static_cast<int64_t>(J) * kBatch) {
       float v[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        v[j] = c0 + j < n_chunks ? part[(c0 + j) * (E + 1) + e] : 0.f;
+      for (int b = 0; b < kBatch; ++b) {
+        const int64_t c = c0 + static_cast<int64_t>(b) * J;
+        v[b] = c < n_chunks ? part[c * E1 + e] : 0.f;
+      }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) s += static_cast<double>(v[j]);
+      for (int b = 0; b < kBatch; ++b) s += static_cast<double>(v[b]);
     }
+    ps[i] = s;
+  }
+  __syncthreads();
+  double a = 0.0, zs = 0.0;
+  for (int e = t; e < E1; e += 1024) {
+    double s = 0.0;
+    for (int j = 0; j < J; ++j) s += ps[j * E1 + e];
     if (e < E)
       a += (static_cast<double>(counts[e]) / (static_cast<double>(T) * K)) * (s / static_cast<double>(T));
     else
       zs = s;
   }
-  sa[threadIdx.x] = a;
-  sz[threadIdx.x] = zs;
+  sa[t] = a;
+  sz[t] = zs;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      sa[threadIdx.x] += sa[threadIdx.x + w];
-      sz[threadIdx.x] += sz[threadIdx.x + w];
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) {
+      sa[t] += sa[t + w];
+      sz[t] += sz[t + w];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     losses[0] = static_cast<float>(static_cast<double>(alpha) * E * sa[0]);
     losses[1] = static_cast<float>(static_cast<double>(z_weight) * sz[0] / static_cast<double>(T));
   }
@@ -659,8 +676,8 @@ hipError_t launch_router_losses(const RouterArgs &a, int act_bf16, const int32_t
     loss_partial_kernel<kPerLane><<<grid, 256, 0, s>>>(a.logits, parts, splits, ss, a.T, a.E,
                                                        ct, part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  loss_final_kernel<<<1, 256, 0, s>>>(part, chunks, a.T, a.E, a.K, counts, alpha, z_weight,
-                                      losses);
+  loss_final_kernel<<<1, 1024, 0, s>>>(part, chunks, a.T, a.E, a.K, counts, alpha, z_weight,
+                                       losses);
   return hipGetLastError();
 }
 
