@@ -32,6 +32,7 @@ int64_t grouped_tile_bound(int64_t rows, int64_t E, int bm) {
 }
 
 bool merged_plan(const moe_desc *d);
+bool shared_rows_f32(const moe_desc *d);
 
 Layout layout_of(const moe_desc *d) {
   Layout L{};
@@ -67,7 +68,7 @@ Layout layout_of(const moe_desc *d) {
   L.h = take(rows * d->d_ff * es);
   L.y = take(rows * de * es);
   L.hsh = d->d_shared ? take(T * d->d_shared * es) : 0;
-  L.sh = merged_plan(d) ? take(T * d->d_model * 4) : 0;  // fp32
+  L.sh = shared_rows_f32(d) ? take(T * d->d_model * 4) : 0;  // fp32
   L.r = d->latent ? take(T * d->latent * es) : 0;
   if (d->route_mode == MOE_ROUTE_SIGMOID_BIAS) {
     L.qb_top = take(T * (K + 1) * 4);
@@ -152,6 +153,17 @@ Plan plan_grouped(const moe_desc *d) {
 }
 
 bool merged_plan(const moe_desc *d) { return plan_grouped(d).merged; }
+
+// The shared experts' down projection goes to fp32 rows (sh) that the
+// combine kernel adds to the routed rows — on merged plans, and on the other
+// non-latent bf16 layers with more than 64 tokens, where the pipelined
+// kernel's gather-sum epilogue (K dependent row loads per output chunk, on
+// one workgroup per CU) measured slower than a separate combine pass with a
+// wavefront per token.
+bool shared_rows_f32(const moe_desc *d) {
+  return merged_plan(d) ||
+         (!d->latent && d->d_shared > 0 && d->act_dtype == MOE_BF16 && d->T > 64);
+}
 
 hipError_t run_grouped(const GemmArgs &a, int epi, const GemmPlan &pl, int bf, hipStream_t s) {
   if (!pl.v2) return launch_gemm(a, epi, pl.cfg, bf, s);
@@ -271,13 +283,22 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
       c.K = d->d_shared;
       c.N = dm;
       c.M = T;
-      c.out = out;
-      c.ldo = dm;
-      c.y = y;
-      c.ldy = dm;
-      c.inv = inv;
-      c.topk = d->top_k;
-      MOE_TRY(launch_dense(c, EPI_COMBINE, bf, s));
+      if (shared_rows_f32(d)) {  // fp32 rows, then the combine kernel adds them
+        float *sh = reinterpret_cast<float *>(ws + L.sh);
+        c.out = sh;
+        c.ldo = dm;
+        c.out_f32 = 1;
+        MOE_TRY(launch_dense(c, EPI_SCALE, bf, s));
+        MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, bf, s, sh));
+      } else {
+        c.out = out;
+        c.ldo = dm;
+        c.y = y;
+        c.ldy = dm;
+        c.inv = inv;
+        c.topk = d->top_k;
+        MOE_TRY(launch_dense(c, EPI_COMBINE, bf, s));
+      }
     } else {
       MOE_TRY(launch_combine_sum(y, inv, T, d->top_k, dm, out, bf, s));
     }

@@ -136,22 +136,33 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // then those of p1. Consecutive workgroups go to different XCDs: give each
   // XCD a contiguous range of tiles, in groups of m-tiles that run together
   // over all n-tiles so tiles sharing B or A meet in L2.
+  // Each problem's tiles are dealt over the XCDs separately (a contiguous
+  // range of each per XCD), so two problems of different K balance; the one
+  // with the longer reduction runs first on every XCD.
   const int n_tn0 = (p0.N + NOUT - 1) / NOUT;
   const int64_t n_m0 = p0.tiles ? static_cast<int64_t>(*p0.n_tiles) : p0.max_mtiles;
   const int64_t total0 = n_m0 * n_tn0;
   const int n_tn1 = (p1.N + NOUT - 1) / NOUT;
   const int64_t n_m1 = p1.N <= 0 ? 0 : (p1.tiles ? static_cast<int64_t>(*p1.n_tiles) : p1.max_mtiles);
-  const int64_t total = total0 + n_m1 * n_tn1;
-  const int64_t per = (total + 7) / 8;
-  const int64_t local = blockIdx.x >> 3;
-  if (local >= per) return;
-  int64_t pid = static_cast<int64_t>(blockIdx.x & 7) * per + local;
-  if (pid >= total) return;
-  const bool second = pid >= total0;
+  const int64_t total1 = n_m1 * n_tn1;
+  const int64_t per0 = (total0 + 7) / 8, per1 = (total1 + 7) / 8;
+  const bool p1_first = total1 > 0 && p1.K + (p1.a2 ? p1.K2 : 0) > p0.K + (p0.a2 ? p0.K2 : 0);
+  int64_t local = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  bool second;
+  if (p1_first) {
+    second = local < per1;
+    if (!second) local -= per1;
+  } else {
+    second = local >= per0;
+    if (second) local -= per0;
+  }
+  if (local >= (second ? per1 : per0)) return;
+  int64_t pid = xcd * (second ? per1 : per0) + local;
+  if (pid >= (second ? total1 : total0)) return;
   const GemmArgs &p = second ? p1 : p0;
   const int n_tn = second ? n_tn1 : n_tn0;
   const int64_t n_m = second ? n_m1 : n_m0;
-  if (second) pid -= total0;
   // groups of m-tiles: one expert's (from the table; a group of g m-tiles
   // owns tiles [first n_tn, (first + g) n_tn), so pid / n_tn is one of its
   // m-tiles) or GM consecutive ones (dense); inside a group the m-tile
@@ -437,13 +448,14 @@ hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
     return g.max_mtiles * ((g.N + NOUT - 1) / NOUT);
   };
   GemmArgs b0 = a, b1{};
-  int64_t total = bound(b0);
+  const int64_t t0 = bound(b0);
+  int64_t t1 = 0;
   if (second && second->N > 0) {
     b1 = *second;
-    total += bound(b1);
+    t1 = bound(b1);
   }
-  if (total == 0) return hipSuccess;
-  const int64_t blocks = 8 * ((total + 7) / 8);
+  if (t0 + t1 == 0) return hipSuccess;
+  const int64_t blocks = 8 * ((t0 + 7) / 8 + (t1 + 7) / 8);  // each problem dealt over 8 XCDs
   gemm2_kernel<BM, BN, WGM, WGN, NA, EPI>
       <<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b0, b1);
   return hipGetLastError();
