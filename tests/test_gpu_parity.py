@@ -161,6 +161,8 @@ DISPATCH_CASES = [
     # (T, K, E) ; the page's example first
     (3, 2, 3), (1, 1, 1), (5000, 2, 4), (4096 * 3 // 8 + 37, 8, 64), (700, 3, 1000),
     (2049, 8, 256), (2048, 8, 256), (9000, 2, 16),
+    # one workgroup: every round of 1024 slots, the most experts, ragged ends
+    (16383, 1, 256), (4097, 4, 200), (1025, 1, 2),
 ]
 
 
