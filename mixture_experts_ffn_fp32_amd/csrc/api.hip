@@ -432,6 +432,53 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
 // activations in expert-contiguous, 64-padded columns for the K-grouped
 // weight-gradient GEMMs, and (latent layers) the recomputed routed sum and
 // the projections' buffers. de is the routed width (d_model, or L).
+// Which backward products read the weights in place, K-major on the
+// pipelined kernel (bf16): dh (W_down, the shared W_down, the latent
+// projections) and dX (W_gate and W_up as two K segments: d_ff and d_shared
+// multiples of 64); the others transpose those weights first. In place
+// pays when the products stream the weights (64 rows per expert or fewer:
+// the copies would double the traffic); with more rows the GEMMs are
+// matrix-core bound and the transposing LDS reads (two 8-byte reads per
+// fragment where the row-major operand takes one 16-byte read) measured
+// ~1.5x slower per stage than the copies cost. The shapes restate the
+// products moe_backward runs.
+struct KmajorUse {
+  bool dh, dx;
+};
+KmajorUse kmajor_use(const moe_desc *d) {
+  KmajorUse u{false, false};
+  const int64_t T = d->T, rows = T * d->top_k;
+  if (d->act_dtype != MOE_BF16 || rows > 64 * static_cast<int64_t>(d->n_experts)) return u;
+  const int dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
+  const int de = Lt ? Lt : dm;
+  auto prod = [](int64_t M, int64_t a_extent, int64_t lda, int K, int N, int64_t ldb) {
+    GemmArgs g{};
+    g.M = M;
+    g.a_extent = a_extent;
+    g.lda = lda;
+    g.K = K;
+    g.N = N;
+    g.ldb = ldb;
+    g.ldo = N;
+    g.b_kmajor = 1;
+    return g;
+  };
+  static const char kSegment = 0;
+  auto second = [](GemmArgs g, int64_t lda2, int K2, int64_t ldb2) {
+    g.a2 = &kSegment;  // (only its presence matters here)
+    g.lda2 = lda2;
+    g.K2 = K2;
+    g.ldb2 = ldb2;
+    return g;
+  };
+  auto ok = [](const GemmArgs &g) { return gemm2_applicable(g, EPI_STORE_F32); };
+  u.dh = ok(prod(rows, T, de, de, f, f)) && (!ds || ok(prod(T, T, dm, dm, ds, ds))) &&
+         (!Lt || (ok(prod(T, T, dm, dm, Lt, Lt)) && ok(prod(T, T, Lt, Lt, dm, dm))));
+  u.dx = f % 64 == 0 && ds % 64 == 0 && ok(second(prod(rows, rows, 2 * f, f, de, de), 2 * f, f, de)) &&
+         (!ds || ok(second(prod(T, T, 2 * ds, ds, dm, dm), 2 * ds, ds, dm)));
+  return u;
+}
+
 struct BwdLayout {
   size_t poff, kt1, kn1, kt2, kn2, tiles, ntiles;
   size_t wguT, wdT, wsguT, wsdT;
@@ -466,10 +513,11 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.kn2 = take(4);
   B.tiles = take(static_cast<size_t>(grouped_tile_bound(rows, E, 32)) * kTileInts * 4);
   B.ntiles = take(4);
-  B.wguT = take(E * de * 2 * f * es);  // [E, de, 2 f]: W_gate^T | W_up^T
-  B.wdT = take(E * f * de * es);       // [E, f, de]
-  B.wsguT = take(dm * 2 * ds * es);
-  B.wsdT = take(ds * dm * es);
+  const KmajorUse ku = kmajor_use(d);  // weights read in place need no copy
+  B.wguT = ku.dx ? 0 : take(E * de * 2 * f * es);  // [E, de, 2 f]: W_gate^T | W_up^T
+  B.wdT = ku.dh ? 0 : take(E * f * de * es);       // [E, f, de]
+  B.wsguT = ku.dx ? 0 : take(dm * 2 * ds * es);
+  B.wsdT = ku.dh ? 0 : take(ds * dm * es);
   B.apre = take(rows * f * 4);
   B.upre = take(rows * f * 4);
   B.dhu = take(rows * f * 4);
@@ -496,8 +544,8 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.dushT = take(ds * B.TP * es);
   B.hshT = take(ds * B.TP * es);
   if (Lt) {
-    B.wluT = take(Lt * dm * es);
-    B.wldT = take(dm * Lt * es);
+    B.wluT = ku.dh ? 0 : take(Lt * dm * es);
+    B.wldT = ku.dh ? 0 : take(dm * Lt * es);
     B.yf = take(rows * Lt * 4);
     B.R = take(T * Lt * 4);
     B.rinv = take(T * 4);
@@ -945,21 +993,6 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   MOE_TRY(launch_tiles(offsets, static_cast<int>(E), bm, I(B.tiles), I(B.ntiles), s));
   const int64_t mt_bound = grouped_tile_bound(rows, E, bm);
 
-  // 2. transposed weights of the active experts (and the shared FFN, the
-  //    latent projections)
-  MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, bf, s));
-  MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, bf, s));
-  MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, bf, s));
-  if (ds) {
-    MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, bf, s));
-    MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, bf, s));
-    MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, bf, s));
-  }
-  if (Lt) {
-    MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, bf, s));
-    MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, bf, s));
-  }
-
   auto grouped = [&](const void *a, int64_t lda, const int32_t *a_rows, int64_t a_extent,
                      const void *b, int64_t ldb, int64_t b_stride, int Kd, int N, void *out,
                      int64_t ldo) {
@@ -995,6 +1028,70 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     g.ldo = ldo;
     return g;
   };
+  // 2. the products that read W_down, W_gate, W_up (and the shared FFN's and
+  //    the latent projections) along their first dimension: bf16 layers
+  //    read those weights in place, K-major on the pipelined kernel (the
+  //    input gradient as two K segments, gate then up, which needs d_ff and
+  //    d_shared to be multiples of 64); otherwise the active experts'
+  //    weights are transposed first.
+  const int64_t fe = static_cast<int64_t>(f) * de;
+  auto kmajor = [&](GemmArgs g, const void *b, int64_t ldb, int64_t b_stride) {
+    g.b0 = b;
+    g.ldb = ldb;
+    g.b_stride = b_stride;
+    g.b_kmajor = 1;
+    return g;
+  };
+  auto two_seg = [&](GemmArgs g, const char *a2, int64_t lda2, int K2, const void *b2,
+                     int64_t ldb2, int64_t b2_stride) {
+    g.a2 = a2;
+    g.lda2 = lda2;
+    g.K2 = K2;
+    g.b2 = b2;
+    g.ldb2 = ldb2;
+    g.b2_stride = b2_stride;
+    return g;
+  };
+  // dh = dy W_down per row (W_down [de, f]), shared dh = dy Ws_down ([d, ds])
+  const GemmArgs gd_k = kmajor(grouped(nullptr, de, stok, T, nullptr, 0, 0, de, f, F(B.dhu), f),
+                               w->w_down, f, fe);
+  const GemmArgs sd_k = kmajor(dense(d_out, dm, nullptr, 0, dm, ds, T, F(B.dhu_s), ds),
+                               w->ws_down, ds, 0);
+  // dX = da W_gate + du W_up per row (W_gate, W_up [f, de]); shared alike
+  const GemmArgs gx_k =
+      two_seg(kmajor(grouped(wsb + B.dau, 2 * f, nullptr, rows, nullptr, 0, 0, f, de, F(B.dxs),
+                             de),
+                     w->w_gate, de, fe),
+              wsb + B.dau + static_cast<size_t>(f) * es, 2 * f, f, w->w_up, de, fe);
+  const GemmArgs sx_k =
+      two_seg(kmajor(dense(wsb + B.dau_s, 2 * ds, nullptr, 0, ds, dm, T, F(B.dxsh), dm),
+                     w->ws_gate, dm, 0),
+              wsb + B.dau_s + static_cast<size_t>(ds) * es, 2 * ds, ds, w->ws_up, dm, 0);
+  // latent: dR' = dy W_lat_up ([d, L]), dx_lat = dz W_lat_down ([L, d])
+  const GemmArgs gp_k = kmajor(dense(d_out, dm, nullptr, 0, dm, Lt, T, F(B.dRp), Lt),
+                               w->w_lat_up, Lt, 0);
+  const GemmArgs gl_k = kmajor(dense(wsb + B.dz, Lt, nullptr, 0, Lt, dm, T, F(B.dxl), dm),
+                               w->w_lat_down, dm, 0);
+  const KmajorUse ku = kmajor_use(d);
+  const bool km_dh = ku.dh, km_dx = ku.dx;
+  if (!km_dx) {
+    MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, bf, s));
+    MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, bf, s));
+    if (ds) {
+      MOE_TRY(launch_transpose(w->ws_gate, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, 0, bf, s));
+      MOE_TRY(launch_transpose(w->ws_up, 1, ds, dm, nullptr, wsb + B.wsguT, 2 * ds, 0, ds, bf, s));
+    }
+  }
+  if (!km_dh) {
+    MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, bf, s));
+    if (ds)
+      MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, bf, s));
+    if (Lt) {
+      MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, bf, s));
+      MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, bf, s));
+    }
+  }
+
   auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c, int epi = EPI_STORE_F32) {
     if (!bf) {  // generic kernel, one problem per launch
       if (launch_gemm(a, epi, TILE_LARGE, 0, s) != hipSuccess) return MOE_ERR_HIP;
@@ -1042,7 +1139,8 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     if ((rc = gemm(gy, nullptr, cfg, EPI_SCALE))) return rc;
     MOE_TRY(launch_latent_fwd(F(B.yf), inv, T, static_cast<int>(K), Lt, d->has_rmsnorm,
                               d->rms_eps, w->rms_gamma, F(B.R), F(B.rinv), wsb + B.Rp, bf, s));
-    const GemmArgs gp = dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
+    const GemmArgs gp =
+        km_dh ? gp_k : dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
     if ((rc = gemm(gp, nullptr, pick_dense(T, dm, Lt)))) return rc;
     MOE_TRY(launch_latent_bwd(F(B.dRp), F(B.R), F(B.rinv), w->rms_gamma, T, Lt,
                               d->has_rmsnorm, wsb + B.dR, bf, s));
@@ -1051,10 +1149,12 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
 
   // 4. W_down^T dy per sorted row (unscaled) and per token for the shared FFN
   {
-    const GemmArgs gd = grouped(rdy, de, stok, T, wsb + B.wdT, de, static_cast<int64_t>(f) * de,
-                                de, f, F(B.dhu), f);
+    GemmArgs gd = km_dh ? gd_k : grouped(nullptr, de, stok, T, wsb + B.wdT, de, fe, de, f,
+                                         F(B.dhu), f);
+    gd.a = rdy;
     if (ds) {
-      const GemmArgs sd = dense(d_out, dm, wsb + B.wsdT, dm, dm, ds, T, F(B.dhu_s), ds);
+      const GemmArgs sd =
+          km_dh ? sd_k : dense(d_out, dm, wsb + B.wsdT, dm, dm, ds, T, F(B.dhu_s), ds);
       if ((rc = gemm(gd, &sd, cfg))) return rc;
     } else if ((rc = gemm(gd, nullptr, cfg))) {
       return rc;
@@ -1072,11 +1172,13 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   //    and through W_lat_down), shared, router
   const bool need_dz = d_x || (Lt && gr->w_lat_down);
   if (need_dz) {
-    const GemmArgs gx = grouped(wsb + B.dau, 2 * f, nullptr, rows, wsb + B.wguT, 2 * f,
-                                static_cast<int64_t>(de) * 2 * f, 2 * f, de, F(B.dxs), de);
+    const GemmArgs gx = km_dx ? gx_k
+                              : grouped(wsb + B.dau, 2 * f, nullptr, rows, wsb + B.wguT, 2 * f,
+                                        static_cast<int64_t>(de) * 2 * f, 2 * f, de, F(B.dxs), de);
     if (ds) {
-      const GemmArgs sx = dense(wsb + B.dau_s, 2 * ds, wsb + B.wsguT, 2 * ds, 2 * ds, dm, T,
-                                F(B.dxsh), dm);
+      const GemmArgs sx = km_dx ? sx_k
+                                : dense(wsb + B.dau_s, 2 * ds, wsb + B.wsguT, 2 * ds, 2 * ds, dm,
+                                        T, F(B.dxsh), dm);
       if ((rc = gemm(gx, &sx, cfg))) return rc;
     } else if ((rc = gemm(gx, nullptr, cfg))) {
       return rc;
@@ -1086,7 +1188,8 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     MOE_TRY(launch_bwd_dx(F(B.dxs), nullptr, nullptr, inv, idx, nullptr, nullptr, T,
                           static_cast<int>(K), Lt, wsb + B.dz, bf, s));
     if (d_x) {
-      const GemmArgs gl = dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
+      const GemmArgs gl =
+          km_dh ? gl_k : dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
       if ((rc = gemm(gl, nullptr, pick_dense(T, Lt, dm)))) return rc;
     }
   }

@@ -84,6 +84,28 @@ __device__ __forceinline__ void barrier() {
 // physical 16-byte chunk of logical chunk c in row r (rows of 8 chunks)
 __device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 
+// K-major B stage buffers: XOR applied to a k-row's chunk-pair index (pairs
+// per row a power of two): rows 0-3 and 8-11, 16-19, 24-27 of a k-step (the
+// rows one transposing read touches) get distinct values
+__device__ __forceinline__ int bkm_swz(int kr, int pairs) {
+  return ((kr & 3) | (((kr >> 3) & 3) << 2)) & (pairs - 1);
+}
+
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16 lanes, lane l receives element l % 4 of
+// the 8-byte pieces lanes 4 e + l / 4 point at, e = 0..3 (a 4 x 4 transpose
+// of 16-bit elements). (Device-pass only.)
+__device__ __forceinline__ v4s16 ds_read_tr16(const char *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s16 *)(const_cast<char *>(lds)));
+#else
+  (void)lds;
+  return v4s16{0, 0, 0, 0};
+#endif
+}
+
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
@@ -108,7 +130,7 @@ struct G2Shape {
   static constexpr int MIN_WAVES = (NW == 4 && LDS16 * 16 <= 80 * 1024) ? 2 : 1;
 };
 
-template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM>
 __global__ __launch_bounds__(64 * WGM * WGN, (G2Shape<BM, BN, WGM, WGN, NA, EPI>::MIN_WAVES))
 void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   using Sh = G2Shape<BM, BN, WGM, WGN, NA, EPI>;
@@ -126,6 +148,15 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   static_assert(!GLU || (BN / 2) % ROWS == 0, "gate and up rows in separate loads");
   static_assert(!GLU || FN % 2 == 0, "paired gate/up fragments");
   static_assert(FM >= 1 && FN >= 1, "at least one fragment per wave");
+  static_assert(!(BKM && GLU), "K-major B: no gate/up pairs");
+  // K-major B (BKM): B is [K, N] row-major; a stage buffer holds 64 k-rows of
+  // BN columns, 16-byte chunks of 8 columns, chunk pairs XOR-swizzled by the
+  // k-row so that the 16 rows one transposing read touches fall in distinct
+  // banks; fragments are read with ds_read_b64_tr_b16 (4 k-rows x 4 columns
+  // per 16 lanes, transposed so each lane holds 4 consecutive k of one
+  // column), two reads per 8-k fragment.
+  constexpr int KROWB = BN * 2;       // bytes per k-row (BKM)
+  constexpr int KPAIRS = BN / 16;     // chunk pairs per k-row (BKM)
   __shared__ __attribute__((aligned(1024))) u32x4 g2_lds[Sh::LDS16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -223,8 +254,28 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       aoff[j] = static_cast<uint32_t>((src * lda + (seg ? 0 : kbeg) + lchunk * 8) * 2);
     }
   };
+  uint32_t bkoff[B_LD];  // BKM: each B load's lane offset (stage 0)
+  uint32_t bkstage = 0;  // BKM: bytes per stage (64 k-rows)
   auto setup_b = [&](int seg) {
     if (seg && !p.a2) return;
+    if constexpr (BKM) {
+      const int64_t ldb = seg ? p.ldb2 : p.ldb;
+      const int64_t kseg_b = seg ? p.K2 : kseg;
+      const int64_t bytes = kseg_b * ldb * 2;
+      const int64_t eoff = expert * (seg ? p.b2_stride : p.b_stride) * 2;
+      br0 = br1 = rsrc(static_cast<const char *>(seg ? p.b2 : p.b0) + eoff, bytes);
+#pragma unroll
+      for (int j = 0; j < B_LD; ++j) {
+        // byte o of the stage buffer: k-row o / KROWB, physical chunk
+        // (o % KROWB) / 16, holding logical chunk pair (pc / 2) ^ swizzle
+        const int o = (NW * j + wave) * 1024 + lane * 16;
+        const int kr = o / KROWB, pc = (o % KROWB) / 16;
+        const int lc = (((pc >> 1) ^ bkm_swz(kr, KPAIRS)) << 1) | (pc & 1);
+        bkoff[j] = static_cast<uint32_t>((kr * ldb + n_begin + lc * 8) * 2);
+      }
+      bkstage = static_cast<uint32_t>(64 * ldb * 2);
+      return;
+    }
     const int64_t ldb = seg ? p.ldb2 : p.ldb, bytes = static_cast<int64_t>(p.N) * ldb * 2;
     if (seg) {
       br0 = br1 = rsrc(static_cast<const char *>(p.b2) + expert * p.b2_stride * 2, bytes);
@@ -252,6 +303,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     load_lds16(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j], kbytes(st));
   };
   auto load_b = [&](u32x4 *bb, int st, int j) {
+    if constexpr (BKM) {
+      const int sl = st >= steps1 ? st - steps1 : st;
+      load_lds16(br0, bb + (NW * j + wave) * 64, bkoff[j],
+                 __builtin_amdgcn_readfirstlane(sl * bkstage));
+      return;
+    }
     const bool up = GLU && j >= B_LD / 2;  // gate rows first, then up rows
     load_lds16(up ? br1 : br0, bb + (ROWS * j + 8 * wave) * 8,
                boff0 + (up ? j - B_LD / 2 : j) * bstep, kbytes(st));
@@ -282,9 +339,27 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
   auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
     const int kc = 4 * ks + fc;
-    if (i < FN)
-      xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(i) + fr, kc)]);
-    else
+    if (i < FN) {
+      if constexpr (BKM) {
+        // lane (g = lane / 16, r = (lane % 16) / 4, q = lane % 4) points at
+        // k-row 32 ks + 8 g + 4 h + r, columns brow + 4 q .. + 3; the
+        // transposing read hands lane l the 4 k of column brow + l % 16
+        const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+        const int lc = (brow_of(i) >> 3) + (q >> 1);
+        const char *base = reinterpret_cast<const char *>(bb);
+        v4s16 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kr = 32 * ks + 8 * g + 4 * h + r;
+          const int pc = (((lc >> 1) ^ bkm_swz(kr, KPAIRS)) << 1) | (lc & 1);
+          h2[h] = ds_read_tr16(base + kr * KROWB + pc * 16 + (q & 1) * 8);
+        }
+        xb[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5,
+                                                                   6, 7));
+      } else {
+        xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(i) + fr, kc)]);
+      }
+    } else
       xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
   };
   auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
@@ -440,7 +515,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NA, int EPI>
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM = false>
 hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   auto bound = [&](GemmArgs &g) {  // m-tile bound (grid size) of one problem
@@ -456,13 +531,18 @@ hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   }
   if (t0 + t1 == 0) return hipSuccess;
   const int64_t blocks = 8 * ((t0 + 7) / 8 + (t1 + 7) / 8);  // each problem dealt over 8 XCDs
-  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI>
+  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI, BKM>
       <<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b0, b1);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, int NA = 2>
 hipError_t dispatch2(const GemmArgs &a, const GemmArgs *b, int epi, hipStream_t s) {
+  if (a.b_kmajor) {  // K-major B: fp32 store only (backward products)
+    if (epi != EPI_STORE_F32 || (b && b->N > 0 && !b->b_kmajor)) return hipErrorInvalidValue;
+    return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32, true>(a, b, s);
+  }
+  if (b && b->N > 0 && b->b_kmajor) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_SWIGLU: return run2<BM, BN, WGM, WGN, NA, EPI_SWIGLU>(a, b, s);
     case EPI_SCALE: return run2<BM, BN, WGM, WGN, NA, EPI_SCALE>(a, b, s);
@@ -481,9 +561,16 @@ bool gemm2_applicable(const GemmArgs &a, int epi) {
   // (B offsets run up to one tile past N)
   constexpr int64_t kLim = int64_t(1) << 32;
   const int64_t a_rows = a.a_extent ? a.a_extent : (a.tiles ? 0 : a.M);
-  if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim || (a.N + 256LL) * a.ldb * 2 >= kLim)
+  if (a_rows <= 0 || a_rows * a.lda * 2 >= kLim) return false;
+  if (a.b_kmajor) {  // [K, N] B: stage offsets run up to 64 rows past K
+    if (epi != EPI_STORE_F32 || a.k_offsets || a.ldb % 8 || (a.K + 64LL) * a.ldb * 2 >= kLim)
+      return false;
+    if (a.a2 && (a.ldb2 % 8 || (a.K2 + 64LL) * a.ldb2 * 2 >= kLim)) return false;
+  } else if ((a.N + 256LL) * a.ldb * 2 >= kLim ||
+             (a.a2 && (a.N + 256LL) * a.ldb2 * 2 >= kLim)) {
     return false;
-  if (a.a2 && (a.M * a.lda2 * 2 >= kLim || (a.N + 256LL) * a.ldb2 * 2 >= kLim)) return false;
+  }
+  if (a.a2 && a.M * a.lda2 * 2 >= kLim) return false;
   // K a multiple of 32 (64 for the first of two segments)
   if (!a.k_offsets && (a.K % 32 || (a.a2 && (a.K % 64 || a.K2 % 32)))) return false;
   if (a.k_offsets && (!a.tiles || a.a2 || a.a_rows)) return false;

@@ -157,6 +157,9 @@ struct GemmArgs {
   // writes its output at out + e * out_stride.
   const int32_t *k_offsets;
   int64_t out_stride;
+  // B (and b2) stored K-major, [K, N] row-major with leading dimension ldb
+  // (pipelined kernel, fp32-store epilogue, no gate/up pair)
+  int b_kmajor;
 };
 
 // Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,

@@ -93,6 +93,15 @@ LAYERS = {
                        d_ff_shared=32, w_std=0.1, router_std=0.1),
     "f32_ragged": dict(T=300, d=96, d_ff=160, E=6, K=2, act="f32", n_shared=1,
                        d_ff_shared=64, w_std=0.08, router_std=0.08),
+    # few rows per expert: the products read W_down, W_gate, W_up (and the
+    # shared / latent projections) in place, K-major
+    "decode_like": dict(T=64, d=256, d_ff=384, E=32, K=4, act="bf16", n_shared=1,
+                        d_ff_shared=128, w_std=0.05, router_std=0.05, bias_std=0.01),
+    "decode_dff_mod32": dict(T=48, d=128, d_ff=160, E=16, K=2, act="bf16", n_shared=1,
+                             d_ff_shared=96, w_std=0.08, router_std=0.08),
+    "decode_latent": dict(T=32, d=128, latent=64, d_ff=64, E=8, K=2, act="bf16",
+                          route="sigmoid_bias", bias_std=0.05, has_rmsnorm=True, n_shared=1,
+                          d_ff_shared=64, w_std=0.08, router_std=0.08),
     "topk_e16": dict(T=512, d=256, d_ff=384, E=16, K=4, act="bf16", n_shared=1,
                      d_ff_shared=256, w_std=0.05, router_std=0.05, bias_std=0.01),
     "softmax_first": dict(T=300, d=128, d_ff=160, E=8, K=2, act="bf16", route="softmax_topk",
@@ -185,6 +194,44 @@ def test_backward_medium_sampled():
     for v in errs.values():
         assert v <= TOL
     del layer, a
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_backward_large_decode_full_size_sampled():
+    """Full-size decode layer (64 tokens over 256 experts, weights read in
+    place): input gradients on a seeded token sample and the weight
+    gradients of the smallest non-empty expert over its tokens."""
+    w = moe_synth.get("large_decode")
+    say("case backward large_decode: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    bits, d_out = _d_out(w, 11)
+    dev = _grad_buffers(w, ["w_gate", "w_up", "w_down"])  # 45 GB: copied back per expert
+    dx = f64(layer.backward(layer.dev["x"], d_out, grads=dev))
+    torch.cuda.synchronize()
+    g_idx = gpu_route(layer)[0]
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    dy = moe_synth.as_f64(bits, w.act)
+    toks = sample_tokens(use, w.E, 12, seed=7)
+    ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
+                       router=False, shared=False)
+    err = max_abs_rel(dx[toks], ref["dx"])
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    nz = np.nonzero(counts)[0]
+    e = int(nz[np.argmin(counts[nz])])
+    mine = np.nonzero((use == e).any(1))[0]
+    one = orc.backward(dy[mine], tokens=mine, idx_override=use[mine], experts=e, router=False,
+                       shared=False)
+    errs = {k: max_abs_rel(dev[k][e].cpu().numpy().astype(np.float64), one[k][0])
+            for k in ("w_gate", "w_up", "w_down")}
+    say(f"  large_decode: near-ties={n_near} dx(sample {len(toks)})={err:.2e} expert {e} "
+        f"({counts[e]} rows): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert err <= TOL
+    for v in errs.values():
+        assert v <= TOL
+    del layer, a, dev
     torch.cuda.empty_cache()
 
 
