@@ -433,24 +433,27 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
 // weight-gradient GEMMs, and (latent layers) the recomputed routed sum and
 // the projections' buffers. de is the routed width (d_model, or L).
 // Which backward products read the weights in place, K-major on the
-// pipelined kernel (bf16): dh (W_down, the shared W_down, the latent
-// projections) and dX (W_gate and W_up as two K segments: d_ff and d_shared
-// multiples of 64); the others transpose those weights first. In place
-// pays when the products stream the weights (64 rows per expert or fewer:
-// the copies would double the traffic); with more rows the GEMMs are
-// matrix-core bound and the transposing LDS reads (two 8-byte reads per
-// fragment where the row-major operand takes one 16-byte read) measured
-// ~1.5x slower per stage than the copies cost. The shapes restate the
-// products moe_backward runs.
+// pipelined kernel (bf16), instead of transposed copies: dh (W_down and the
+// shared W_down), dX (W_gate and W_up as two K segments: d_ff and d_shared
+// multiples of 64) and the latent projections. The transposing LDS reads
+// (two 8-byte reads per fragment where the row-major operand takes one
+// 16-byte read) make those GEMMs ~1.5x slower per stage, so in place pays
+// only where the copies cost more: layers that stream their weights (64 rows
+// per expert or fewer), and, for the expert weights, large experts
+// (d_e x d_ff >= 2^23) with 512 rows per expert or fewer (measured: the
+// large prefill layer 61.0 -> 58.7 ms; the medium and latent layers slower).
+// The shapes restate the products moe_backward runs.
 struct KmajorUse {
-  bool dh, dx;
+  bool dh, dx, lat;
 };
 KmajorUse kmajor_use(const moe_desc *d) {
-  KmajorUse u{false, false};
-  const int64_t T = d->T, rows = T * d->top_k;
-  if (d->act_dtype != MOE_BF16 || rows > 64 * static_cast<int64_t>(d->n_experts)) return u;
+  KmajorUse u{false, false, false};
+  if (d->act_dtype != MOE_BF16) return u;
+  const int64_t T = d->T, rows = T * d->top_k, E = d->n_experts;
   const int dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
   const int de = Lt ? Lt : dm;
+  const bool stream = rows <= 64 * E;
+  const bool experts = stream || (rows <= 512 * E && static_cast<int64_t>(de) * f >= (1 << 23));
   auto prod = [](int64_t M, int64_t a_extent, int64_t lda, int K, int N, int64_t ldb) {
     GemmArgs g{};
     g.M = M;
@@ -472,10 +475,11 @@ KmajorUse kmajor_use(const moe_desc *d) {
     return g;
   };
   auto ok = [](const GemmArgs &g) { return gemm2_applicable(g, EPI_STORE_F32); };
-  u.dh = ok(prod(rows, T, de, de, f, f)) && (!ds || ok(prod(T, T, dm, dm, ds, ds))) &&
-         (!Lt || (ok(prod(T, T, dm, dm, Lt, Lt)) && ok(prod(T, T, Lt, Lt, dm, dm))));
-  u.dx = f % 64 == 0 && ds % 64 == 0 && ok(second(prod(rows, rows, 2 * f, f, de, de), 2 * f, f, de)) &&
+  u.dh = experts && ok(prod(rows, T, de, de, f, f)) && (!ds || ok(prod(T, T, dm, dm, ds, ds)));
+  u.dx = experts && f % 64 == 0 && ds % 64 == 0 &&
+         ok(second(prod(rows, rows, 2 * f, f, de, de), 2 * f, f, de)) &&
          (!ds || ok(second(prod(T, T, 2 * ds, ds, dm, dm), 2 * ds, ds, dm)));
+  u.lat = Lt && stream && ok(prod(T, T, dm, dm, Lt, Lt)) && ok(prod(T, T, Lt, Lt, dm, dm));
   return u;
 }
 
@@ -544,8 +548,8 @@ BwdLayout bwd_layout_of(const moe_desc *d) {
   B.dushT = take(ds * B.TP * es);
   B.hshT = take(ds * B.TP * es);
   if (Lt) {
-    B.wluT = ku.dh ? 0 : take(Lt * dm * es);
-    B.wldT = ku.dh ? 0 : take(dm * Lt * es);
+    B.wluT = ku.lat ? 0 : take(Lt * dm * es);
+    B.wldT = ku.lat ? 0 : take(dm * Lt * es);
     B.yf = take(rows * Lt * 4);
     B.R = take(T * Lt * 4);
     B.rinv = take(T * 4);
@@ -1073,7 +1077,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   const GemmArgs gl_k = kmajor(dense(wsb + B.dz, Lt, nullptr, 0, Lt, dm, T, F(B.dxl), dm),
                                w->w_lat_down, dm, 0);
   const KmajorUse ku = kmajor_use(d);
-  const bool km_dh = ku.dh, km_dx = ku.dx;
+  const bool km_dh = ku.dh, km_dx = ku.dx, km_lat = ku.lat;
   if (!km_dx) {
     MOE_TRY(launch_transpose(w->w_gate, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, 0, bf, s));
     MOE_TRY(launch_transpose(w->w_up, E, f, de, counts, wsb + B.wguT, 2 * f, de * 2 * f, f, bf, s));
@@ -1086,19 +1090,22 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     MOE_TRY(launch_transpose(w->w_down, E, de, f, counts, wsb + B.wdT, de, f * de, 0, bf, s));
     if (ds)
       MOE_TRY(launch_transpose(w->ws_down, 1, dm, ds, nullptr, wsb + B.wsdT, dm, 0, 0, bf, s));
-    if (Lt) {
-      MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, bf, s));
-      MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, bf, s));
-    }
+  }
+  if (Lt && !km_lat) {
+    MOE_TRY(launch_transpose(w->w_lat_up, 1, dm, Lt, nullptr, wsb + B.wluT, dm, 0, 0, bf, s));
+    MOE_TRY(launch_transpose(w->w_lat_down, 1, Lt, dm, nullptr, wsb + B.wldT, Lt, 0, 0, bf, s));
   }
 
-  auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c, int epi = EPI_STORE_F32) {
+  auto gemm = [&](const GemmArgs &a, const GemmArgs *b, int c, int epi = EPI_STORE_F32) -> int {
     if (!bf) {  // generic kernel, one problem per launch
       if (launch_gemm(a, epi, TILE_LARGE, 0, s) != hipSuccess) return MOE_ERR_HIP;
       if (b && launch_gemm(*b, epi, TILE_LARGE, 0, s) != hipSuccess) return MOE_ERR_HIP;
       return MOE_OK;
     }
     if (!gemm2_applicable(a, epi) || (b && !gemm2_applicable(*b, epi))) return MOE_ERR_SHAPE;
+    // K-major B: the 2x4-wavefront 256x256 tile (four B fragments per
+    // wavefront instead of eight) loses less to the transposing reads
+    if (a.b_kmajor && c == TILE2_256x256_TALLW) c = TILE2_256x256;
     return launch_gemm2(a, epi, c, s, b) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   };
   auto pick_dense = [&](int64_t M, int Kd, int N) { return gemm2_pick(M, 0, Kd, N, 0); };
@@ -1140,7 +1147,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     MOE_TRY(launch_latent_fwd(F(B.yf), inv, T, static_cast<int>(K), Lt, d->has_rmsnorm,
                               d->rms_eps, w->rms_gamma, F(B.R), F(B.rinv), wsb + B.Rp, bf, s));
     const GemmArgs gp =
-        km_dh ? gp_k : dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
+        km_lat ? gp_k : dense(d_out, dm, wsb + B.wluT, dm, dm, Lt, T, F(B.dRp), Lt);
     if ((rc = gemm(gp, nullptr, pick_dense(T, dm, Lt)))) return rc;
     MOE_TRY(launch_latent_bwd(F(B.dRp), F(B.R), F(B.rinv), w->rms_gamma, T, Lt,
                               d->has_rmsnorm, wsb + B.dR, bf, s));
@@ -1189,7 +1196,7 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
                           static_cast<int>(K), Lt, wsb + B.dz, bf, s));
     if (d_x) {
       const GemmArgs gl =
-          km_dh ? gl_k : dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
+          km_lat ? gl_k : dense(wsb + B.dz, Lt, wsb + B.wldT, Lt, Lt, dm, T, F(B.dxl), dm);
       if ((rc = gemm(gl, nullptr, pick_dense(T, Lt, dm)))) return rc;
     }
   }
