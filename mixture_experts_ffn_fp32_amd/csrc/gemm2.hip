@@ -40,6 +40,11 @@
 // time and writes the output with 16-byte stores along rows; the combine
 // epilogue adds the token's K routed rows with 16-byte loads.
 //
+// K-major B (template flag BKM, fp32-store epilogue only): B given as
+// [K, N] row-major, as the backward's products read W_down, W_gate and W_up
+// in place. A stage buffer then holds 64 k-rows of the tile's columns and
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16).
+//
 // K must be a multiple of 32 (the first of two K segments, of 64); the host
 // uses gemm.hip otherwise.
 #include "common.h"
