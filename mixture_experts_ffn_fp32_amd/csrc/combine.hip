@@ -17,18 +17,20 @@ namespace moe {
 
 namespace {
 
-// out[t] = sum_k y[inv[t*K+k]] (+ add[t], fp32): one wavefront per token,
-// 16-byte chunks, the K rows summed in k order in fp32, then add.
+// out[t] = sum_k y[inv[t*K+k]] (+ add[t], fp32): one wavefront per token and
+// span of 64 * cstep chunks (blockIdx.y), 16-byte chunks, the K rows summed
+// in k order in fp32, then add.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_sum_kernel(const uint4 *__restrict__ y,
                                                           const int32_t *__restrict__ inv, int K,
                                                           int chunks, int64_t n_tok,
                                                           const float *__restrict__ add,
-                                                          uint4 *__restrict__ out) {
+                                                          uint4 *__restrict__ out, int cspan) {
   constexpr int N = Chunk<T>::N;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= n_tok) return;
-  for (int c = threadIdx.x & 63; c < chunks; c += 64) {
+  const int c_end = min(chunks, static_cast<int>(blockIdx.y + 1) * cspan);
+  for (int c = blockIdx.y * cspan + (threadIdx.x & 63); c < c_end; c += 64) {
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
@@ -112,13 +114,19 @@ hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int 
                               void *out, int act_bf16, hipStream_t s, const float *add) {
   if (T == 0) return hipSuccess;
   const int chunks = width / (act_bf16 ? 8 : 4);
-  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  // few tokens: split each row over column spans (multiples of 64 chunks) so
+  // that the launch has about 1024 wavefronts
+  const int64_t waves_per_tok = (1024 + T - 1) / T;
+  int64_t span = (chunks + waves_per_tok - 1) / waves_per_tok;
+  span = (span + 63) / 64 * 64;
+  const int cspan = static_cast<int>(span < chunks ? span : chunks);
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4), static_cast<unsigned>((chunks + cspan - 1) / cspan));
   if (act_bf16)
     combine_sum_kernel<bf16_t><<<grid, 256, 0, s>>>(static_cast<const uint4 *>(y), inv, K, chunks,
-                                                    T, add, static_cast<uint4 *>(out));
+                                                    T, add, static_cast<uint4 *>(out), cspan);
   else
     combine_sum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const uint4 *>(y), inv, K, chunks,
-                                                   T, add, static_cast<uint4 *>(out));
+                                                   T, add, static_cast<uint4 *>(out), cspan);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
 // K splits of the router GEMM: few tokens (decode) cannot fill the chip
 // with output tiles alone, so the reduction over d is split and the
 // partial logits are summed in fixed order by the selection kernel.
-inline int router_splits(int64_t T, int64_t d) {
+inline int router_splits(int64_t T, int64_t d) {  // at most 8 (the selection's bound)
   if (T > 256) return 1;
   const int64_t s = d / 512;
   return s < 1 ? 1 : (s > 8 ? 8 : static_cast<int>(s));

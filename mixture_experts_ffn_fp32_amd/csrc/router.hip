@@ -43,17 +43,28 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf
 // with split stride ss): each plane's K-split partials summed in split
 // order, then the planes high + mid + low. Every consumer of the logits
 // calls this, so they all see the same fp32 value.
+// (All of a logit's partials are loaded before they are added, split by
+// split in order: at most kMaxRouterSplits splits.)
+constexpr int kMaxRouterSplits = 8;
 __device__ __forceinline__ float logit_of(const float *lg, int e, int E, int parts, int splits,
                                           int64_t ss) {
-  float pl[3] = {0.f, 0.f, 0.f};
-  for (int q = 0; q < splits; ++q) {
+  float v[3][kMaxRouterSplits];
+#pragma unroll
+  for (int q = 0; q < kMaxRouterSplits; ++q) {
     const float *ls = lg + q * ss;
-    pl[0] += ls[e];
-    if (parts == 3) {
-      pl[1] += ls[E + e];
-      pl[2] += ls[2 * E + e];
-    }
+    const bool on = q < splits;
+    v[0][q] = on ? ls[e] : 0.f;
+    v[1][q] = on && parts == 3 ? ls[E + e] : 0.f;
+    v[2][q] = on && parts == 3 ? ls[2 * E + e] : 0.f;
   }
+  float pl[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < kMaxRouterSplits; ++q)
+    if (q < splits) {
+      pl[0] += v[0][q];
+      pl[1] += v[1][q];
+      pl[2] += v[2][q];
+    }
   return parts == 3 ? (pl[0] + pl[1]) + pl[2] : pl[0];
 }
 
