@@ -100,7 +100,7 @@ def calibrate_copy(mib: int, reps: int = 5):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, a, budget_s=12.0):
+def cpu_baseline(w, a, budget_s=15.0):
     """Time the CPU oracle (as it stands) on a seeded token sample."""
     import oracle
     orc = oracle.Oracle(w, a)
@@ -130,8 +130,8 @@ def cpu_baseline(w, a, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
