@@ -178,10 +178,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // with the longer reduction runs first on every XCD.
   const int n_tn0 = (p0.N + NOUT - 1) / NOUT;
   const int64_t n_m0 = p0.tiles ? static_cast<int64_t>(*p0.n_tiles) : p0.max_mtiles;
-  const int64_t total0 = n_m0 * n_tn0;
+  // (a K-split fp32 store: each tile once per split)
+  const int ks0 = p0.k_split > 1 ? p0.k_split : 1, ks1 = p1.k_split > 1 ? p1.k_split : 1;
+  const int64_t total0 = n_m0 * n_tn0 * ks0;
   const int n_tn1 = (p1.N + NOUT - 1) / NOUT;
   const int64_t n_m1 = p1.N <= 0 ? 0 : (p1.tiles ? static_cast<int64_t>(*p1.n_tiles) : p1.max_mtiles);
-  const int64_t total1 = n_m1 * n_tn1;
+  const int64_t total1 = n_m1 * n_tn1 * ks1;
   const int64_t per0 = (total0 + 7) / 8, per1 = (total1 + 7) / 8;
   const bool p1_first = total1 > 0 && p1.K + (p1.a2 ? p1.K2 : 0) > p0.K + (p0.a2 ? p0.K2 : 0);
   int64_t local = blockIdx.x >> 3;
@@ -200,6 +202,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   const GemmArgs &p = second ? p1 : p0;
   const int n_tn = second ? n_tn1 : n_tn0;
   const int64_t n_m = second ? n_m1 : n_m0;
+  int split = 0;
+  if ((second ? ks1 : ks0) > 1) {  // split-major: all tiles of split 0 first
+    const int64_t t2 = n_m * n_tn;
+    split = static_cast<int>(pid / t2);
+    pid -= split * t2;
+  }
   // groups of m-tiles: one expert's (from the table; a group of g m-tiles
   // owns tiles [first n_tn, (first + g) n_tn), so pid / n_tn is one of its
   // m-tiles) or GM consecutive ones (dense); inside a group the m-tile
@@ -230,11 +238,17 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   const int n_begin = nt * NOUT;
   // K-grouped: this expert's reduction columns and output block
   int64_t kbeg = 0, kseg = p.K;
+  int64_t obase = 0;
   if (p.k_offsets) {
     kbeg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert]);
     kseg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert + 1]) - kbeg;
+    obase = expert * p.out_stride;
+  } else if (p.k_split > 1) {  // split s reduces K columns [s kps, (s + 1) kps), kps whole stages
+    const int64_t kps = ((p.K + 63) / 64 + p.k_split - 1) / p.k_split * 64;
+    kbeg = split * kps;
+    kseg = min<int64_t>(kps, p.K - kbeg);
+    obase = split * p.split_stride;
   }
-  const int64_t obase = p.k_offsets ? expert * p.out_stride : 0;
 
   // ------------------------------------------------------------ loads
   // load j of a thread: tile row ROWS j + lrow, in the 1 KB block starting at
@@ -551,7 +565,7 @@ hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   auto bound = [&](GemmArgs &g) {  // m-tile bound (grid size) of one problem
     g.max_mtiles = g.tiles ? g.max_mtiles : (g.M + BM - 1) / BM;
-    return g.max_mtiles * ((g.N + NOUT - 1) / NOUT);
+    return g.max_mtiles * ((g.N + NOUT - 1) / NOUT) * (g.k_split > 1 ? g.k_split : 1);
   };
   GemmArgs b0 = a, b1{};
   const int64_t t0 = bound(b0);
@@ -587,7 +601,13 @@ hipError_t dispatch2(const GemmArgs &a, const GemmArgs *b, int epi, hipStream_t 
 }  // namespace
 
 bool gemm2_applicable(const GemmArgs &a, int epi) {
-  if (a.k_split > 1) return false;
+  // K split: fp32 store of one problem, each split whole stages of K and
+  // every split holding some
+  if (a.k_split > 1) {
+    if (epi != EPI_STORE_F32 || a.a2 || a.k_offsets || a.b_kmajor) return false;
+    const int64_t stages = (a.K + 63) / 64, kps = (stages + a.k_split - 1) / a.k_split * 64;
+    if ((a.k_split - 1) * kps >= a.K) return false;
+  }
   // 32-bit load offsets: A (rows it may address), each B slice, below 4 GiB
   // (B offsets run up to one tile past N)
   constexpr int64_t kLim = int64_t(1) << 32;

@@ -43,16 +43,24 @@ int64_t router_loss_chunks(int64_t T);
 inline size_t router_split_bytes(int64_t E, int64_t d, int act_bf16) {
   return act_bf16 ? static_cast<size_t>(3 * E * d * 2) : 0;
 }
-// K splits of the router GEMM: few tokens (decode) cannot fill the chip
-// with output tiles alone, so the reduction over d is split and the
-// partial logits are summed in fixed order by the selection kernel.
-inline int router_splits(int64_t T, int64_t d) {  // at most 8 (the selection's bound)
-  if (T > 256) return 1;
-  const int64_t s = d / 512;
-  return s < 1 ? 1 : (s > 8 ? 8 : static_cast<int>(s));
+// K splits of the router GEMM: when the output tiles alone cannot fill the
+// chip (few tokens, or few experts: E x 3 planes is a narrow output), the
+// reduction over d is split and the partial logits are summed in fixed
+// order by the selection kernel. At most 8 (the selection's bound) and d /
+// 512. T <= 256: the generic kernel; bf16 planes with more tokens: the
+// pipelined kernel's 128x128 tile, splits enough for ~384 workgroups (two
+// per CU).
+inline int router_splits(int64_t T, int64_t d, int64_t E, int act_bf16) {
+  const int64_t smax = d / 512 < 1 ? 1 : (d / 512 > 8 ? 8 : d / 512);
+  if (T <= 256) return static_cast<int>(smax);
+  if (!act_bf16) return 1;
+  const int64_t tiles = ((T + 127) / 128) * ((3 * E + 127) / 128);
+  const int64_t s = (384 + tiles - 1) / tiles;
+  return static_cast<int>(s < 1 ? 1 : (s > smax ? smax : s));
 }
 inline size_t router_logit_bytes(int64_t T, int64_t E, int64_t d, int act_bf16) {
-  return static_cast<size_t>(T * E * (act_bf16 ? 3 : 1) * 4 * router_splits(T, d));
+  return static_cast<size_t>(T * E * (act_bf16 ? 3 : 1) * 4 *
+                             router_splits(T, d, E, act_bf16));
 }
 
 // ------------------------------------------------------------------ dispatch

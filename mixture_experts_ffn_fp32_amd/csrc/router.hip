@@ -583,7 +583,7 @@ void logit_layout(const RouterArgs &a, int act_bf16, int *parts, int *splits) {
     *splits = 1;
   } else {
     *parts = act_bf16 ? 3 : 1;
-    *splits = router_splits(a.T, a.d);
+    *splits = router_splits(a.T, a.d, a.E, act_bf16);
   }
 }
 
@@ -611,7 +611,7 @@ hipError_t launch_router_logits(const RouterArgs &a, int act_bf16, hipStream_t s
   const int parts = act_bf16 ? 3 : 1;
   g.N = parts * a.E;
   g.ldo = g.N;
-  const int splits = router_splits(a.T, a.d);
+  const int splits = router_splits(a.T, a.d, a.E, act_bf16);
   g.k_split = splits;
   g.split_stride = a.T * g.N;
   if (act_bf16) {
@@ -625,6 +625,8 @@ hipError_t launch_router_logits(const RouterArgs &a, int act_bf16, hipStream_t s
   } else {
     g.b0 = a.w;
   }
+  if (act_bf16 && a.T > 256 && splits > 1 && gemm2_applicable(g, EPI_STORE_F32))
+    return launch_gemm2(g, EPI_STORE_F32, TILE2_128x128, s);
   return launch_dense(g, EPI_STORE_F32, act_bf16, s);
 }
 
