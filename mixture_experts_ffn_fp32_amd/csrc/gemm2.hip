@@ -136,7 +136,7 @@ struct G2Shape {
   static constexpr int MIN_WAVES = (NW == 4 && LDS16 * 16 <= 80 * 1024) ? 2 : 1;
 };
 
-template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM>
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM, bool KS>
 __global__ __launch_bounds__(64 * WGM * WGN, (G2Shape<BM, BN, WGM, WGN, NA, EPI>::MIN_WAVES))
 void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   using Sh = G2Shape<BM, BN, WGM, WGN, NA, EPI>;
@@ -178,8 +178,9 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // with the longer reduction runs first on every XCD.
   const int n_tn0 = (p0.N + NOUT - 1) / NOUT;
   const int64_t n_m0 = p0.tiles ? static_cast<int64_t>(*p0.n_tiles) : p0.max_mtiles;
-  // (a K-split fp32 store: each tile once per split)
-  const int ks0 = p0.k_split > 1 ? p0.k_split : 1, ks1 = p1.k_split > 1 ? p1.k_split : 1;
+  // (KS, a K-split fp32 store: each tile once per split)
+  const int ks0 = KS && p0.k_split > 1 ? p0.k_split : 1;
+  const int ks1 = KS && p1.k_split > 1 ? p1.k_split : 1;
   const int64_t total0 = n_m0 * n_tn0 * ks0;
   const int n_tn1 = (p1.N + NOUT - 1) / NOUT;
   const int64_t n_m1 = p1.N <= 0 ? 0 : (p1.tiles ? static_cast<int64_t>(*p1.n_tiles) : p1.max_mtiles);
@@ -203,7 +204,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   const int n_tn = second ? n_tn1 : n_tn0;
   const int64_t n_m = second ? n_m1 : n_m0;
   int split = 0;
-  if ((second ? ks1 : ks0) > 1) {  // split-major: all tiles of split 0 first
+  if (KS && (second ? ks1 : ks0) > 1) {  // split-major: all tiles of split 0 first
     const int64_t t2 = n_m * n_tn;
     split = static_cast<int>(pid / t2);
     pid -= split * t2;
@@ -243,7 +244,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     kbeg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert]);
     kseg = __builtin_amdgcn_readfirstlane(p.k_offsets[expert + 1]) - kbeg;
     obase = expert * p.out_stride;
-  } else if (p.k_split > 1) {  // split s reduces K columns [s kps, (s + 1) kps), kps whole stages
+  } else if (KS && p.k_split > 1) {  // split s: K columns [s kps, (s + 1) kps), whole stages
     const int64_t kps = ((p.K + 63) / 64 + p.k_split - 1) / p.k_split * 64;
     kbeg = split * kps;
     kseg = min<int64_t>(kps, p.K - kbeg);
@@ -560,12 +561,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM = false>
+template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM = false, bool KS = false>
 hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   auto bound = [&](GemmArgs &g) {  // m-tile bound (grid size) of one problem
     g.max_mtiles = g.tiles ? g.max_mtiles : (g.M + BM - 1) / BM;
-    return g.max_mtiles * ((g.N + NOUT - 1) / NOUT) * (g.k_split > 1 ? g.k_split : 1);
+    return g.max_mtiles * ((g.N + NOUT - 1) / NOUT) * (KS && g.k_split > 1 ? g.k_split : 1);
   };
   GemmArgs b0 = a, b1{};
   const int64_t t0 = bound(b0);
@@ -576,13 +577,18 @@ hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   }
   if (t0 + t1 == 0) return hipSuccess;
   const int64_t blocks = 8 * ((t0 + 7) / 8 + (t1 + 7) / 8);  // each problem dealt over 8 XCDs
-  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI, BKM>
+  gemm2_kernel<BM, BN, WGM, WGN, NA, EPI, BKM, KS>
       <<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b0, b1);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WGM, int WGN, int NA = 2>
 hipError_t dispatch2(const GemmArgs &a, const GemmArgs *b, int epi, hipStream_t s) {
+  if (a.k_split > 1 || (b && b->N > 0 && b->k_split > 1)) {  // K split: fp32 store only
+    if (epi != EPI_STORE_F32 || a.b_kmajor || (b && b->N > 0 && b->b_kmajor))
+      return hipErrorInvalidValue;
+    return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32, false, true>(a, b, s);
+  }
   if (a.b_kmajor) {  // K-major B: fp32 store only (backward products)
     if (epi != EPI_STORE_F32 || (b && b->N > 0 && !b->b_kmajor)) return hipErrorInvalidValue;
     return run2<BM, BN, WGM, WGN, NA, EPI_STORE_F32, true>(a, b, s);

@@ -163,6 +163,8 @@ DISPATCH_CASES = [
     (2049, 8, 256), (2048, 8, 256), (9000, 2, 16),
     # one workgroup: every round of 1024 slots, the most experts, ragged ends
     (16383, 1, 256), (4097, 4, 200), (1025, 1, 2),
+    # one workgroup, few rounds of 1024 slots, few and many experts
+    (700, 2, 128), (2048, 2, 64), (3000, 1, 5), (64, 8, 256),
 ]
 
 
