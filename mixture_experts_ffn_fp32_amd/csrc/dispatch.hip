@@ -385,6 +385,119 @@ __global__ __launch_bounds__(1024) void dispatch_fused_kernel(ScanArgs a, Scatte
   }
 }
 
+// Few experts (E <= 4), one workgroup: thread t owns the R = ceil(slots /
+// 1024) consecutive slots [R t, R t + R). Its per-expert counts, 16 bits
+// each in one 64-bit word, go through a single block exclusive scan, whose
+// result is, per expert, the number of that expert's slots before the
+// thread's first one, and whose total holds the per-expert counts; every
+// thread then derives the offsets and tile starts of the (at most 4) experts
+// itself. Two barriers in all, against two per round of 1024 slots in
+// dispatch_fused_kernel.
+constexpr int kFewE = 4;
+
+// v[i] for i in [0, kFewE] without a dynamically indexed register array
+__device__ __forceinline__ int pick_few(const int (&v)[kFewE + 1], int i) {
+  int r = v[0];
+#pragma unroll
+  for (int j = 1; j <= kFewE; ++j) r = i == j ? v[j] : r;
+  return r;
+}
+
+__device__ void write_tiles_few(const int (&off)[kFewE + 1], const int (&st)[kFewE + 1], int E,
+                                int bm, int32_t *tiles, int32_t *n_tiles) {
+  const int total = pick_few(st, E);
+  for (int i = threadIdx.x; i < total; i += 1024) {
+    int e = 0;
+#pragma unroll
+    for (int j = 1; j < kFewE; ++j) e += (j < E && st[j] <= i) ? 1 : 0;
+    const int se = pick_few(st, e), se1 = pick_few(st, e + 1);
+    const int r0 = pick_few(off, e) + (i - se) * bm;
+    const int gfirst = se + (i - se) / kTileGroup * kTileGroup;
+    int32_t *ti = tiles + kTileInts * static_cast<int64_t>(i);
+    ti[0] = e;
+    ti[1] = r0;
+    ti[2] = min(r0 + bm, pick_few(off, e + 1));
+    ti[3] = gfirst;
+    ti[4] = min(kTileGroup, se1 - gfirst);
+  }
+  if (threadIdx.x == 0) *n_tiles = total;
+}
+
+__global__ __launch_bounds__(1024) void dispatch_few_kernel(ScanArgs a, ScatterArgs sc) {
+  __shared__ uint64_t tmp64[16];
+  __shared__ int wave_ties[16];
+  const int t = threadIdx.x, lane = t & 63;
+  const int E = a.E;
+  const int slots = static_cast<int>(a.slots);
+  const int R = (slots + 1023) / 1024;
+  const int s0 = R * t;
+  int ids[kFusedRounds];
+  float gs[kFusedRounds];
+  uint64_t mine = 0;
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int s = s0 + r;
+    const bool in = r < R && s < slots;
+    ids[r] = in ? sc.idx[s] : -1;
+    gs[r] = (in && sc.sorted_w) ? sc.g[s] : 0.f;
+  }
+  const bool ties = a.gap && a.n_near_ties;
+  if (ties) {  // near ties: per wavefront sums, added up after the scan's barriers
+    int n = 0;
+    for (int64_t i = t; i < a.T; i += 1024) n += a.gap[i] < a.tie_eps ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    if (lane == 0) wave_ties[t >> 6] = n;
+  }
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) mine += 1ull << (16 * e);
+  }
+  uint64_t tot;
+  uint64_t run = block_exscan64_1024(mine, tmp64, &tot);
+  int off[kFewE + 1], st1[kFewE + 1], st2[kFewE + 1];
+  off[0] = st1[0] = st2[0] = 0;
+#pragma unroll
+  for (int e = 0; e < kFewE; ++e) {
+    const int c = e < E ? static_cast<int>((tot >> (16 * e)) & 0xffff) : 0;
+    off[e + 1] = off[e] + c;
+    st1[e + 1] = st1[e] + (a.tiles ? (c + a.bm - 1) / a.bm : 0);
+    st2[e + 1] = st2[e] + (a.tiles2 ? (c + a.bm2 - 1) / a.bm2 : 0);
+  }
+#pragma unroll
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int s = s0 + r;
+    if (r >= R || s >= slots) break;
+    const int e = ids[r];
+    if (e >= 0 && e < E) {
+      const int pos = pick_few(off, e) + static_cast<int>((run >> (16 * e)) & 0xffff);
+      run += 1ull << (16 * e);
+      sc.perm[pos] = s;
+      sc.sorted_token[pos] = s / sc.K;
+      sc.inv[s] = pos;
+      if (sc.sorted_w) sc.sorted_w[pos] = gs[r];
+    } else {
+      sc.inv[s] = -1;
+    }
+  }
+  if (t < E) {
+    a.counts[t] = pick_few(off, t + 1) - pick_few(off, t);
+    a.offsets[t] = pick_few(off, t);
+  }
+  if (t == 0) {
+    a.offsets[E] = pick_few(off, E);
+    if (ties) {
+      int n = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) n += wave_ties[w];
+      *a.n_near_ties = n;
+    }
+  }
+  if (a.tiles) write_tiles_few(off, st1, E, a.bm, a.tiles, a.n_tiles);
+  if (a.tiles2) write_tiles_few(off, st2, E, a.bm2, a.tiles2, a.n_tiles2);
+}
+
 // One wavefront per sorted row: out[p, :] = rows[sorted_token[p], :].
 __global__ __launch_bounds__(256) void gather_kernel(const uint4 *__restrict__ rows,
                                                      const int32_t *__restrict__ sorted_token,
@@ -424,7 +537,10 @@ bool dispatch_fused_ok(int64_t slots, int E) {
 
 hipError_t launch_dispatch_fused(const ScanArgs &a, const ScatterArgs &sc, hipStream_t s) {
   if (!dispatch_fused_ok(a.slots, a.E)) return hipErrorInvalidValue;
-  dispatch_fused_kernel<<<1, 1024, 0, s>>>(a, sc);
+  if (a.E <= kFewE)
+    dispatch_few_kernel<<<1, 1024, 0, s>>>(a, sc);
+  else
+    dispatch_fused_kernel<<<1, 1024, 0, s>>>(a, sc);
   return hipGetLastError();
 }
 

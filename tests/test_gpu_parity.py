@@ -165,6 +165,8 @@ DISPATCH_CASES = [
     (16383, 1, 256), (4097, 4, 200), (1025, 1, 2),
     # one workgroup, few rounds of 1024 slots, few and many experts
     (700, 2, 128), (2048, 2, 64), (3000, 1, 5), (64, 8, 256),
+    # one workgroup, at most 4 experts (one packed scan): up to 16384 slots
+    (16384, 1, 4), (8192, 2, 3), (2048, 2, 4), (1, 2, 2), (333, 4, 4), (5461, 3, 4),
 ]
 
 
