@@ -19,8 +19,9 @@
 // per 32 (bf16) or 4 (fp32) products instead of once per product.
 //
 // Selection: one wavefront per token. Each lane holds E/64 scores; K+1
-// rounds of a butterfly (value, lower id) max-reduction over the 64 lanes
-// pick the experts in descending order, ties to the lower id.
+// rounds of a (value, lower id) max-reduction over the 64 lanes (DPP moves
+// inside rows of 16 lanes, readlane across the rows) pick the experts in
+// descending order, ties to the lower id.
 #include <math.h>
 
 #include "common.h"
@@ -84,6 +85,50 @@ __global__ __launch_bounds__(256) void split_kernel(const float *__restrict__ w,
   }
 }
 
+// Wavefront maximum of a 64-bit key, returned to every lane: inside each row
+// of 16 lanes by DPP moves (swaps within quads, then the half-row and the
+// row mirror, each pairing a lane with one whose partial maximum covers the
+// lanes it lacks), then the four row maxima through readlane.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t k) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(k)), CTRL, 0xF, 0xF,
+                                  false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF,
+                                  0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > k ? o : k;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t k, int l) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(k)), l));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(k >> 32)), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = dpp_max_u64<0xB1>(k);   // quad_perm [1, 0, 3, 2]
+  k = dpp_max_u64<0x4E>(k);   // quad_perm [2, 3, 0, 1]
+  k = dpp_max_u64<0x141>(k);  // row_half_mirror
+  k = dpp_max_u64<0x140>(k);  // row_mirror
+  const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
+  const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// Ranking key of (score, expert id): larger score first, then lower id. The
+// score's bits are mapped to an unsigned order (negative values inverted)
+// after -0 is made +0, so equal scores compare equal as floats do.
+__device__ __forceinline__ uint64_t rank_key(float v, int id) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t o = (u >> 31) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(id));
+}
+
 // Selection of token t by one wavefront from its logits: lane l holds the
 // logits of experts l + 64 j (j < PL, PL * 64 >= E) in raw[j]. Writes idx, g
 // and the optional gap / top scores.
@@ -136,19 +181,12 @@ __device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int 
           br = raw[j];
           bi = lane + 64 * j;
         }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const float orw = __shfl_xor(br, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          br = orw;
-          bi = oi;
-        }
-      }
-      sv[r] = bv;
-      sraw[r] = br;
+      // the winner's lane holds its score and logit as its own best
+      const uint64_t win = wave_max_u64(rank_key(bv, bi));
+      bi = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
+      const int wl = __builtin_amdgcn_readfirstlane(bi & 63);
+      sv[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), wl));
+      sraw[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(br), wl));
       si[r] = bi;
 #pragma unroll
       for (int j = 0; j < PL; ++j)
