@@ -431,14 +431,17 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + a_nxt * A16;
     u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
     wait_lgkm0();  // set 0 has landed
+    // per fragment row: the LDS reads for the next k-step go out before the
+    // row's MFMAs, so the last reads' latency overlaps the last MFMAs
+    // (measured: small -1.3%, latent -0.8%, large prefill -0.8%)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      if (fm < live) mrow(fm, xa0, xb0);
 #pragma unroll
       for (int q = 0; q < RD_PER; ++q) {
         const int i = fm * RD_PER + q;
         if (i < NRD) rd(ac, bc, 1, i, xa1, xb1);
       }
+      if (fm < live) mrow(fm, xa0, xb0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // A and B of st + 1 have landed (the loads issued after them: the B
@@ -451,17 +454,17 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     const int live1 = (half_last && st == last) ? 0 : live;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+      for (int q = 0; q < RD_PER; ++q) {
+        const int i = fm * RD_PER + q;
+        if (i < NRD) rd(an, bn, 0, i, xa0, xb0);
+      }
       if (fm < live1) mrow(fm, xa1, xb1);
 #pragma unroll
       for (int q = 0; q < LD_PER; ++q) {
         const int j = fm * LD_PER + q;
         if (j < A_LD) load_a(ac, sa, j);
         else if (j < A_LD + B_LD) load_b(bc, sb, j - A_LD);
-      }
-#pragma unroll
-      for (int q = 0; q < RD_PER; ++q) {
-        const int i = fm * RD_PER + q;
-        if (i < NRD) rd(an, bn, 0, i, xa0, xb0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
