@@ -120,6 +120,27 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   return a > b ? a : b;
 }
 
+// Wavefront sum of one float per lane, the same in every lane: DPP adds
+// inside each row of 16 lanes (the pairings of wave_max_u64), then the four
+// row sums, (row 0 + row 1) + (row 2 + row 3). A fixed order: the result
+// depends only on the 64 inputs.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Ranking key of (score, expert id): larger score first, then lower id. The
 // score's bits are mapped to an unsigned order (negative values inverted)
 // after -0 is made +0, so equal scores compare equal as floats do.
@@ -266,7 +287,7 @@ __global__ __launch_bounds__(256) void select_kernel(RouterArgs a, int parts, in
 // Router for few experts and a narrow model, one wavefront per token: lane l
 // holds elements [512 c + 8 l, 512 c + 8 l + 8) of x for every 512-column
 // chunk c; per expert its fp32 partial dot product (fused multiply-adds in
-// column order) is summed over the 64 lanes by a fixed xor butterfly, so
+// column order) is summed over the 64 lanes in a fixed order (wave_sum_f32), so
 // every lane holds the logit; the logits go to a.logits [T, E] (one plane,
 // one split) and, if `select`, straight into the selection.
 template <typename T>
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(256) void router_valu_kernel(RouterArgs a, int sele
   }
   // four experts per pass: all their W_router loads are issued before the
   // FMAs (lanes past d read element 0 and add it times x = 0); per expert the
-  // sum runs over the chunks in order, then a butterfly over the lanes
+  // sum runs over the chunks in order, then a fixed-order sum over the lanes
   float raw = 0.f;  // logit of expert `lane`
   for (int e0 = 0; e0 < a.E; e0 += 4) {
     float p[4] = {0.f, 0.f, 0.f, 0.f};
@@ -323,9 +344,7 @@ __global__ __launch_bounds__(256) void router_valu_kernel(RouterArgs a, int sele
       }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] += __shfl_xor(p[j], off);
+    for (int j = 0; j < 4; ++j) p[j] = wave_sum_f32(p[j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (lane == e0 + j) raw = p[j];

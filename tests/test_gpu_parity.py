@@ -167,6 +167,8 @@ DISPATCH_CASES = [
     (700, 2, 128), (2048, 2, 64), (3000, 1, 5), (64, 8, 256),
     # one workgroup, at most 4 experts (one packed scan): up to 16384 slots
     (16384, 1, 4), (8192, 2, 3), (2048, 2, 4), (1, 2, 2), (333, 4, 4), (5461, 3, 4),
+    # just past one workgroup, few experts: the three-launch path
+    (8193, 2, 4),
 ]
 
 
