@@ -214,8 +214,9 @@ __device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int 
         if (lane + 64 * j == bi) v[j] = -INFINITY;
     }
   }
-  if (lane != 0) return;
-
+  // the selection is the same in every lane: each lane computes the weights
+  // and stores its own slot (lane k < K: idx and g of slot k, lane r <= K:
+  // the r-th top score), so a token's stores are one instruction each
   float gk[kMaxK];
   float z = 0.f;
   if (sig) {
@@ -241,17 +242,23 @@ __device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int 
     for (int k = 0; k < kMaxK; ++k)
       if (k < K) gk[k] = gk[k] / z;
   }
+  int my_i = 0;
+  float my_g = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k)
-    if (k < K) {
-      a.idx[t * K + k] = si[k];
-      a.g[t * K + k] = gk[k] * a.routed_scale;
+    if (k < K && lane == k) {
+      my_i = si[k];
+      my_g = gk[k];
     }
+  if (lane < K) {
+    a.idx[t * K + lane] = my_i;
+    a.g[t * K + lane] = my_g * a.routed_scale;
+  }
   float rs[kMaxK + 1];  // scores in the ranked space
 #pragma unroll
   for (int r = 0; r <= kMaxK; ++r)
     rs[r] = (a.mode == 1 && r < nsel) ? expf(sv[r] - vmax) / zall : sv[r];
-  if (a.gap) {
+  if (a.gap && lane == 0) {
     float gp = INFINITY;
 #pragma unroll
     for (int r = 1; r <= kMaxK; ++r)
@@ -259,9 +266,11 @@ __device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int 
     a.gap[t] = gp;
   }
   if (a.top) {
+    float my_top = -INFINITY;
 #pragma unroll
     for (int r = 0; r <= kMaxK; ++r)
-      if (r <= K) a.top[t * (K + 1) + r] = r < nsel ? rs[r] : -INFINITY;
+      if (r <= K && lane == r) my_top = r < nsel ? rs[r] : -INFINITY;
+    if (lane <= K) a.top[t * (K + 1) + lane] = my_top;
   }
 }
 
