@@ -9,7 +9,8 @@
 //   hist    - per chunk of 4096 slots, an LDS histogram of expert ids;
 //   scan    - one workgroup: counts, exclusive offsets, the absolute base of
 //             every (chunk, expert) pair, the grouped-GEMM m-tile table and
-//             the near-tie count of the router gaps;
+//             the near-tie count of the router gaps (below 2^21 slots with
+//             one packed 64-bit scan: scan_packed_kernel);
 //   scatter - per chunk, rank of each slot among earlier slots of the same
 //             expert (64-lane peer masks from one ballot per id bit, waves
 //             of the workgroup taking turns on an LDS running count), then
@@ -498,6 +499,111 @@ __global__ __launch_bounds__(1024) void dispatch_few_kernel(ScanArgs a, ScatterA
   if (a.tiles2) write_tiles_few(off, st2, E, a.bm2, a.tiles2, a.n_tiles2);
 }
 
+// The scan step for fewer than 2^21 slots: per expert its count and its
+// m-tile counts for both tile heights, 21 bits each, in one 64-bit block
+// scan (the near-tie gaps requested first, so their latency overlaps the
+// chunk counts'; the first 16 chunk counts kept in registers for the bases).
+// One workgroup of 1024 threads, three barriers against seventeen in
+// scan_kernel.
+__global__ __launch_bounds__(1024) void scan_packed_kernel(ScanArgs a) {
+  __shared__ uint64_t tmp64[16];
+  __shared__ int off[kMaxE + 1];
+  __shared__ int start[kMaxE + 1];
+  __shared__ int start2[kMaxE + 1];
+  __shared__ int wave_ties[16];
+  const int t = threadIdx.x, lane = t & 63;
+  const int E = a.E;
+  const int64_t nch = n_chunks(a.slots);
+  constexpr int kBatch = 16;
+  const bool ties = a.gap && a.n_near_ties;
+  float gv[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) {
+    const int64_t i = t + 1024 * j;
+    gv[j] = (ties && i < a.T) ? a.gap[i] : INFINITY;
+  }
+  int v0[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) v0[j] = (t < E && j < nch) ? a.chunk_hist[j * E + t] : 0;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) cnt += v0[j];
+  for (int64_t c0 = kBatch; t < E && c0 < nch; c0 += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * E + t] : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) cnt += v[j];
+  }
+  if (ties) {  // per wavefront sums, added after the scan's barriers
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) n += gv[j] < a.tie_eps ? 1 : 0;
+    for (int64_t i0 = t + 1024 * kBatch; i0 < a.T; i0 += 1024 * kBatch) {
+      float g[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t i = i0 + 1024 * j;
+        g[j] = i < a.T ? a.gap[i] : INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) n += g[j] < a.tie_eps ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    if (lane == 0) wave_ties[t >> 6] = n;
+  }
+  const uint64_t nt1 = (t < E && a.tiles) ? (cnt + a.bm - 1) / a.bm : 0;
+  const uint64_t nt2 = (t < E && a.tiles2) ? (cnt + a.bm2 - 1) / a.bm2 : 0;
+  constexpr uint64_t kM = (1ull << 21) - 1;
+  uint64_t tot;
+  const uint64_t ex = block_exscan64_1024(
+      static_cast<uint64_t>(t < E ? cnt : 0) | (nt1 << 21) | (nt2 << 42), tmp64, &tot);
+  if (t < E) {
+    const int ex_c = static_cast<int>(ex & kM);
+    off[t] = ex_c;
+    start[t] = static_cast<int>((ex >> 21) & kM);
+    start2[t] = static_cast<int>(ex >> 42);
+    a.counts[t] = cnt;
+    a.offsets[t] = ex_c;
+    // absolute base of every (chunk, expert) pair (chunk_base may alias
+    // chunk_hist: this thread reads each of its elements before writing it)
+    int run = ex_c;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (j < nch) {
+        a.chunk_base[j * E + t] = run;
+        run += v0[j];
+      }
+    for (int64_t c0 = kBatch; c0 < nch; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * E + t] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (c0 + j < nch) {
+          a.chunk_base[(c0 + j) * E + t] = run;
+          run += v[j];
+        }
+    }
+  }
+  if (t == 0) {
+    off[E] = static_cast<int>(tot & kM);
+    start[E] = static_cast<int>((tot >> 21) & kM);
+    start2[E] = static_cast<int>(tot >> 42);
+    a.offsets[E] = static_cast<int>(tot & kM);
+  }
+  __syncthreads();
+  if (a.tiles) write_tiles(off, E, a.bm, start, a.tiles, a.n_tiles);
+  if (a.tiles2) write_tiles(off, E, a.bm2, start2, a.tiles2, a.n_tiles2);
+  if (ties && t == 0) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) n += wave_ties[w];
+    *a.n_near_ties = n;
+  }
+}
+
 // One wavefront per sorted row: out[p, :] = rows[sorted_token[p], :].
 __global__ __launch_bounds__(256) void gather_kernel(const uint4 *__restrict__ rows,
                                                      const int32_t *__restrict__ sorted_token,
@@ -521,7 +627,10 @@ hipError_t launch_hist(const int32_t *idx, int64_t slots, int E, int32_t *chunk_
 }
 
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(a);
+  if (a.slots < (int64_t(1) << 21))
+    scan_packed_kernel<<<1, 1024, 0, s>>>(a);
+  else
+    scan_kernel<<<1, 1024, 0, s>>>(a);
   return hipGetLastError();
 }
 
