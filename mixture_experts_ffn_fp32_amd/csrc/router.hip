@@ -18,10 +18,11 @@
 // v_mfma_f32_16x16x4_f32 directly. Either way the accumulation rounds once
 // per 32 (bf16) or 4 (fp32) products instead of once per product.
 //
-// Selection: one wavefront per token. Each lane holds E/64 scores; K+1
-// rounds of a (value, lower id) max-reduction over the 64 lanes (DPP moves
-// inside rows of 16 lanes, readlane across the rows) pick the experts in
-// descending order, ties to the lower id.
+// Selection: one wavefront per token. Each lane holds E/64 scores. Up to 64
+// experts, every lane ranks its expert against all the others at once;
+// otherwise K+1 rounds of a (value, lower id) max-reduction over the 64
+// lanes (DPP moves inside rows of 16 lanes, readlane across the rows) pick
+// the experts in descending order. Ties go to the lower id either way.
 #include <math.h>
 
 #include "common.h"
@@ -183,6 +184,49 @@ __device__ __forceinline__ void select_from(const RouterArgs &a, int64_t t, int 
       if (lane + 64 * j < E) zall += expf(v[j] - vmax);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) zall += __shfl_xor(zall, off);
+  }
+
+  if constexpr (PL == 1) {
+    // at most 64 experts, one per lane: each lane's rank among them, counted
+    // against every other lane's key (the same order as the rounds below:
+    // larger score first, ties to the lower id); rank r < K is slot r.
+    // Lanes without an expert hold key 0 and rank 64.
+    const bool valid = lane < E;
+    const uint64_t key = valid ? rank_key(v[0], lane) : 0;
+    int rk[4] = {0, 0, 0, 0};
+    const int e4 = (E + 3) & ~3;
+    for (int l0 = 0; l0 < e4; l0 += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rk[q] += readlane_u64(key, l0 + q) > key ? 1 : 0;
+    }
+    const int rank = valid ? (rk[0] + rk[1]) + (rk[2] + rk[3]) : 64;
+    auto lane_of = [&](int r) {  // the lane holding rank r (uniform)
+      const uint64_t b = __ballot(rank == r);
+      return b ? static_cast<int>(__builtin_ctzll(b)) : 0;
+    };
+    auto at = [&](float x, int l) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+    };
+    const bool chosen = rank < K;
+    const float top0 = at(v[0], lane_of(0));  // the largest ranking score
+    const float w = !chosen ? 0.f : (sig ? sigmoidf_(raw[0]) : expf(v[0] - top0));
+    const float z = wave_sum_f32(w);
+    const float gw = (sig && !a.renormalize) ? w : w / z;
+    if (chosen) {
+      a.idx[t * K + rank] = lane;
+      a.g[t * K + rank] = gw * a.routed_scale;
+    }
+    // scores in the ranked space
+    const float rsv = a.mode == 1 ? expf(v[0] - vmax) / zall : v[0];
+    if (a.gap) {
+      const float gp = K < E ? at(rsv, lane_of(K - 1)) - at(rsv, lane_of(K)) : INFINITY;
+      if (lane == 0) a.gap[t] = gp;
+    }
+    if (a.top) {
+      if (rank <= K) a.top[t * (K + 1) + rank] = rsv;
+      if (K >= E && lane == 0) a.top[t * (K + 1) + K] = -INFINITY;  // no expert of rank K
+    }
+    return;
   }
 
   float sv[kMaxK + 1], sraw[kMaxK + 1];
