@@ -64,45 +64,63 @@ __global__ __launch_bounds__(256) void combine_latent_kernel(const uint4 *__rest
                                                              int has_rmsnorm, float eps,
                                                              const float *__restrict__ gamma,
                                                              uint4 *__restrict__ r) {
+  // one workgroup per token, a thread per 16-byte chunk of the row (the
+  // workgroup is as wide as the row, in whole wavefronts, up to 256
+  // threads; wider rows loop and keep their sums in LDS). Each chunk's K
+  // rows are all requested before they are added, in slot order.
   constexpr int N = Chunk<T>::N;
-  extern __shared__ float row[];  // [L]
+  constexpr int kMaxSlots = 16;
+  extern __shared__ float row[];  // [L], for rows wider than the workgroup
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
+  const int nthr = blockDim.x;
+  const bool one = chunks <= nthr;  // one chunk per thread: sums stay in registers
+  int q[kMaxSlots];
+#pragma unroll
+  for (int k = 0; k < kMaxSlots; ++k) q[k] = k < K ? inv[t * K + k] : -1;
+  float keep[N];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
+  for (int c = threadIdx.x; c < chunks; c += nthr) {
+    uint4 raw[kMaxSlots];
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k)
+      raw[k] = q[k] >= 0 ? y[static_cast<int64_t>(q[k]) * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int q = inv[t * K + k];
-      if (q < 0) continue;
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k) {
+      if (q[k] < 0) continue;
       float v[N];
-      Chunk<T>::unpack(y[static_cast<int64_t>(q) * chunks + c], v);
+      Chunk<T>::unpack(raw[k], v);
 #pragma unroll
       for (int i = 0; i < N; ++i) acc[i] += v[i];
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      row[c * N + i] = acc[i];
+      keep[i] = acc[i];
+      if (!one) row[c * N + i] = acc[i];
       ss += acc[i] * acc[i];
     }
   }
   float scale = 1.0f;
-  if (has_rmsnorm) {
+  if (has_rmsnorm) {  // per wavefront, then the wavefronts in order
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
+    float tot = 0.f;
+    for (int w = 0; w < nthr / 64; ++w) tot += red[w];
     scale = 1.0f / sqrtf(tot / static_cast<float>(L) + eps);
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < chunks; c += 256) {
+  if (!one) __syncthreads();
+  for (int c = threadIdx.x; c < chunks; c += nthr) {
     float v[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int l = c * N + i;
-      v[i] = has_rmsnorm ? row[l] * scale * (gamma ? gamma[l] : 1.0f) : row[l];
+      const float x = one ? keep[i] : row[l];
+      v[i] = has_rmsnorm ? x * scale * (gamma ? gamma[l] : 1.0f) : x;
     }
     r[t * chunks + c] = Chunk<T>::pack(v);
   }
@@ -134,14 +152,16 @@ hipError_t launch_combine_latent(const void *y, const int32_t *inv, int64_t T, i
                                  int has_rmsnorm, float eps, const float *gamma, void *r,
                                  int act_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (K > 16) return hipErrorInvalidValue;
   const int chunks = L / (act_bf16 ? 8 : 4);
-  const size_t shm = static_cast<size_t>(L) * sizeof(float);
+  const int nthr = chunks >= 256 ? 256 : (chunks + 63) / 64 * 64;
+  const size_t shm = chunks > nthr ? static_cast<size_t>(L) * sizeof(float) : 0;
   if (act_bf16)
-    combine_latent_kernel<bf16_t><<<static_cast<unsigned>(T), 256, shm, s>>>(
+    combine_latent_kernel<bf16_t><<<static_cast<unsigned>(T), nthr, shm, s>>>(
         static_cast<const uint4 *>(y), inv, K, chunks, L, has_rmsnorm, eps, gamma,
         static_cast<uint4 *>(r));
   else
-    combine_latent_kernel<float><<<static_cast<unsigned>(T), 256, shm, s>>>(
+    combine_latent_kernel<float><<<static_cast<unsigned>(T), nthr, shm, s>>>(
         static_cast<const uint4 *>(y), inv, K, chunks, L, has_rmsnorm, eps, gamma,
         static_cast<uint4 *>(r));
   return hipGetLastError();
