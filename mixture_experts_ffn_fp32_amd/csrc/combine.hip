@@ -30,15 +30,23 @@ __global__ __launch_bounds__(256) void combine_sum_kernel(const uint4 *__restric
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= n_tok) return;
   const int c_end = min(chunks, static_cast<int>(blockIdx.y + 1) * cspan);
+  constexpr int kMaxSlots = 16;
+  int q[kMaxSlots];  // the token's sorted rows, read once
+#pragma unroll
+  for (int k = 0; k < kMaxSlots; ++k) q[k] = k < K ? inv[t * K + k] : -1;
   for (int c = blockIdx.y * cspan + (threadIdx.x & 63); c < c_end; c += 64) {
+    uint4 raw[kMaxSlots];  // all K rows requested before they are added
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k)
+      raw[k] = q[k] >= 0 ? y[static_cast<int64_t>(q[k]) * chunks + c] : make_uint4(0u, 0u, 0u, 0u);
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int q = inv[t * K + k];
-      if (q < 0) continue;
+#pragma unroll
+    for (int k = 0; k < kMaxSlots; ++k) {
+      if (q[k] < 0) continue;
       float v[N];
-      Chunk<T>::unpack(y[static_cast<int64_t>(q) * chunks + c], v);
+      Chunk<T>::unpack(raw[k], v);
 #pragma unroll
       for (int i = 0; i < N; ++i) acc[i] += v[i];
     }
@@ -131,6 +139,7 @@ __global__ __launch_bounds__(256) void combine_latent_kernel(const uint4 *__rest
 hipError_t launch_combine_sum(const void *y, const int32_t *inv, int64_t T, int K, int width,
                               void *out, int act_bf16, hipStream_t s, const float *add) {
   if (T == 0) return hipSuccess;
+  if (K > 16) return hipErrorInvalidValue;
   const int chunks = width / (act_bf16 ? 8 : 4);
   // few tokens: split each row over column spans (multiples of 64 chunks) so
   // that the launch has about 1024 wavefronts
