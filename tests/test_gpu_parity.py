@@ -115,25 +115,30 @@ def test_all_tokens_to_one_expert():
     assert counts.cpu().tolist() == [0, 0, 0, 300, 0, 0]
 
 
-def test_exact_ties_take_lower_id():
-    """Experts 2 and 5 have identical router rows: equal logits, the lower id
+@pytest.mark.parametrize("E,K,lo,hi,kw", [
+    (8, 3, 2, 5, {}),                                    # wavefront router, rank selection
+    (64, 8, 3, 60, dict(act="bf16", d=2560, d_ff=64)),   # split-plane GEMM, rank selection
+    (128, 8, 5, 69, {}),                                 # GEMM router, selection rounds; same lane
+])
+def test_exact_ties_take_lower_id(E, K, lo, hi, kw):
+    """Experts lo and hi have identical router rows: equal logits, the lower id
     ranks first on both sides."""
-    w = custom(name="ties", T=120, E=8, K=3, bias_std=0.0)
+    w = custom(name="ties", T=120, E=E, K=K, bias_std=0.0, **kw)
     a = moe_synth.generate(w)
-    a["w_router"][5] = a["w_router"][2]
+    a["w_router"][hi] = a["w_router"][lo]
     a["bias"] = None
     layer = layer_of(w, a)
-    say("case exact ties")
+    say(f"case exact ties E={E} K={K} ids {lo}/{hi}")
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
     g = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
     moe.moe_route(layer.desc, layer.weights, layer.dev["x"], idx, g, ws=layer.ws)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     o_idx, _, _, _ = oracle.Oracle(w, a).route()
-    both = (gi == 2).any(1) & (gi == 5).any(1)
+    both = (gi == lo).any(1) & (gi == hi).any(1)
     assert np.array_equal(gi, o_idx)
-    one = ((gi == 2) | (gi == 5)).sum(1) == 1
-    assert np.all((gi[one] == 2).any(1))
+    one = ((gi == lo) | (gi == hi)).sum(1) == 1
+    assert np.all((gi[one] == lo).any(1))
     assert both.sum() + one.sum() > 0
 
 
