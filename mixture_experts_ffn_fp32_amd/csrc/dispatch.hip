@@ -179,10 +179,19 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   const int64_t s0 = c * kChunkSlots;
   const int64_t s1 = min<int64_t>(s0 + kChunkSlots, a.slots);
   const int32_t *base = a.chunk_base + c * a.E;
-  for (int64_t r0 = s0; r0 < s1; r0 += 256) {
-    const int64_t s = r0 + tid;
-    int e = -1;
-    if (s < s1) e = a.idx[s];
+  constexpr int kRounds = kChunkSlots / 256;
+  int ids[kRounds];  // the chunk's ids and weights, all requested up front
+  float gs[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t s = s0 + 256 * r + tid;
+    ids[r] = s < s1 ? a.idx[s] : -1;
+    gs[r] = (s < s1 && a.sorted_w) ? a.g[s] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t s = s0 + 256 * r + tid;
+    const int e = ids[r];
     const bool valid = e >= 0 && e < a.E;
     const uint64_t active = ballot(valid);
     uint64_t peers = active;
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
       a.perm[pos] = static_cast<int32_t>(s);
       a.sorted_token[pos] = static_cast<int32_t>(s / a.K);
       a.inv[s] = pos;
-      if (a.sorted_w) a.sorted_w[pos] = a.g[s];
+      if (a.sorted_w) a.sorted_w[pos] = gs[r];
     } else if (s < s1) {
       a.inv[s] = -1;
     }
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(1024) void dispatch_few_kernel(ScanArgs a, ScatterA
 // The scan step for fewer than 2^21 slots: per expert its count and its
 // m-tile counts for both tile heights, 21 bits each, in one 64-bit block
 // scan (the near-tie gaps requested first, so their latency overlaps the
-// chunk counts'; the first 16 chunk counts kept in registers for the bases).
+// chunk counts'; the first 64 chunk counts kept in registers for the bases).
 // One workgroup of 1024 threads, three barriers against seventeen in
 // scan_kernel.
 __global__ __launch_bounds__(1024) void scan_packed_kernel(ScanArgs a) {
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(1024) void scan_packed_kernel(ScanArgs a) {
   const int t = threadIdx.x, lane = t & 63;
   const int E = a.E;
   const int64_t nch = n_chunks(a.slots);
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 16, kFirst = 64;  // the first 64 chunk counts stay in registers
   const bool ties = a.gap && a.n_near_ties;
   float gv[kBatch];
 #pragma unroll
@@ -522,13 +531,13 @@ __global__ __launch_bounds__(1024) void scan_packed_kernel(ScanArgs a) {
     const int64_t i = t + 1024 * j;
     gv[j] = (ties && i < a.T) ? a.gap[i] : INFINITY;
   }
-  int v0[kBatch];
+  int v0[kFirst];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) v0[j] = (t < E && j < nch) ? a.chunk_hist[j * E + t] : 0;
+  for (int j = 0; j < kFirst; ++j) v0[j] = (t < E && j < nch) ? a.chunk_hist[j * E + t] : 0;
   int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) cnt += v0[j];
-  for (int64_t c0 = kBatch; t < E && c0 < nch; c0 += kBatch) {
+  for (int j = 0; j < kFirst; ++j) cnt += v0[j];
+  for (int64_t c0 = kFirst; t < E && c0 < nch; c0 += kBatch) {
     int v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * E + t] : 0;
@@ -570,12 +579,12 @@ __global__ __launch_bounds__(1024) void scan_packed_kernel(ScanArgs a) {
     // chunk_hist: this thread reads each of its elements before writing it)
     int run = ex_c;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
+    for (int j = 0; j < kFirst; ++j)
       if (j < nch) {
         a.chunk_base[j * E + t] = run;
         run += v0[j];
       }
-    for (int64_t c0 = kBatch; c0 < nch; c0 += kBatch) {
+    for (int64_t c0 = kFirst; c0 < nch; c0 += kBatch) {
       int v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < nch ? a.chunk_hist[(c0 + j) * E + t] : 0;
