@@ -32,10 +32,16 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
   __syncthreads();
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kChunkSlots;
   const int64_t s1 = min<int64_t>(s0 + kChunkSlots, slots);
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) {
-    const int e = idx[s];
-    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  constexpr int kRounds = kChunkSlots / 256;
+  int ids[kRounds];  // all of the chunk's ids requested before the first atomic
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t s = s0 + 256 * r + threadIdx.x;
+    ids[r] = s < s1 ? idx[s] : -1;
   }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    if (ids[r] >= 0 && ids[r] < E) atomicAdd(&h[ids[r]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256)
     chunk_hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
