@@ -1,23 +1,33 @@
 """Benchmark of the MoE SwiGLU feed-forward forward pass on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+python bench.py --peak            (peak-rate microbenchmarks only)
+python bench.py --calibrate-copy MiB   (plain device copy, counter calibration)
 
 One step = one moe_forward over one batch of synthetic tokens (router,
 dispatch, grouped expert SwiGLU, shared experts, combine), inputs resident
 in HBM. Prints ONE JSON line on stdout; details go to stderr.
 
-The timed steps are plain forwards. After them, the dominant kernel (the
-grouped gate/up GEMM) is timed with HIP events recorded by the library on the
-launch stream: around that launch in single forwards, and around 20
-back-to-back passes of it (which removes the events' own overhead from short
-launches); its algorithmic flops (or bytes, for weight-streaming batches) per
-launch divided by the mean duration of one pass gives roofline.achieved.
+The default workload is the largest single-GPU configuration, the large
+layer (E=256, K=8, d=7168, d_ff=2048, 2 shared) at T=16384 tokens; the same
+resident weights are then also timed at the decode batch of T=64 tokens
+(the `decode` object of the line).
 
-cpu_baseline: the CPU oracle timed on a bounded sample of the same tokens.
+The timed steps are plain forwards (each also bracketed by HIP events on the
+launch stream for the median / min figures). After them, each GEMM stage of
+the layer is timed with HIP events the library records on its launch stream,
+around 20 back-to-back passes of the stage (removing the events' own
+overhead); the dominant kernel (the grouped gate/up GEMM) gives
+roofline.achieved = its algorithmic flops (or bytes, for weight-streaming
+batches) per launch / the mean duration of one pass.
+
+cpu_baseline: the CPU oracle timed on a bounded sample of the same tokens
+(all host cores, then one core), plus its routing and dispatch over all T.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -29,9 +39,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec and achieved fraction of MFMA/HBM roofline, 1 GPU"
-PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X)
-HBM_GBS = 8000.0                        # HBM3E GB/s (MI355X)
-DEFAULT_WORKLOAD = "small"              # the second configuration of the layer
+PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X datasheet, 2.4 GHz)
+HBM_GBS = 8000.0                        # HBM3E GB/s (MI355X datasheet)
+DEFAULT_WORKLOAD = "large_prefill"      # the largest configuration that fits one GPU
+DECODE_OF = {"large_prefill": "large_decode"}  # same layer at the decode batch
+CU_COUNT = 256
+MFMA_FLOP_PER_CLK_CU = 4096             # dense bf16: 2.5 PFLOP/s / (256 CUs x 2.4 GHz)
 
 
 def log(*a):
@@ -39,8 +52,8 @@ def log(*a):
 
 
 def algorithmic(w, counts, merged=False):
-    """Per-step algorithmic work of the layer and of the gate/up launch
-    (merged: the shared experts' gate/up GEMM runs in the same launch)."""
+    """Per-step algorithmic work of the layer and of each GEMM launch
+    (merged: the shared experts' GEMMs run in the grouped launches)."""
     es = 2 if w.act == "bf16" else 4
     de, f, rows = w.d_e, w.d_ff, w.T * w.K
     touched = int((counts > 0).sum())
@@ -54,11 +67,19 @@ def algorithmic(w, counts, merged=False):
     gu_flops = 4.0 * rows * de * f
     # gate/up launch: touched experts' gate+up weights, gathered rows in, h out
     gu_bytes = touched * 2 * f * de * es + rows * de * es + rows * f * es
-    if merged:  # + shared gate/up: its weights, x in, its h out
-        gu_flops += 4.0 * w.T * w.d * w.d_shared
-        gu_bytes += 2 * w.d_shared * w.d * es + w.T * w.d * es + w.T * w.d_shared * es
+    # down launch: touched experts' down weights, h in, y out
+    dn_flops = 2.0 * rows * de * f
+    dn_bytes = touched * f * de * es + rows * f * es + rows * de * es
+    sh_gu_flops = 4.0 * w.T * w.d * w.d_shared
+    sh_gu_bytes = 2 * w.d_shared * w.d * es + w.T * w.d * es + w.T * w.d_shared * es
+    if merged:
+        gu_flops += sh_gu_flops
+        gu_bytes += sh_gu_bytes
+        dn_flops += 2.0 * w.T * w.d * w.d_shared
+        dn_bytes += w.d_shared * w.d * es + w.T * w.d_shared * es + w.T * w.d * 4
     return dict(flops=fl_router + fl_routed + fl_shared + fl_latent, bytes=bytes_w + bytes_act,
-                gu_flops=gu_flops, gu_bytes=gu_bytes, touched=touched)
+                gu_flops=gu_flops, gu_bytes=gu_bytes, dn_flops=dn_flops, dn_bytes=dn_bytes,
+                sh_gu_flops=sh_gu_flops, sh_gu_bytes=sh_gu_bytes, touched=touched)
 
 
 def kernel_source_hash() -> str:
@@ -100,11 +121,188 @@ def calibrate_copy(mib: int, reps: int = 5):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
 
 
-def cpu_baseline(w, a, budget_s=15.0):
-    """Time the CPU oracle (as it stands) on a seeded token sample."""
-    import oracle
-    orc = oracle.Oracle(w, a)
-    rng = np.random.default_rng(7)
+# ------------------------------------------------------------ peak rates
+
+PEAK_MODES = {0: "mfma_16x16x32_bf16", 1: "mfma_32x32x16_bf16", 2: "lds_read_16B",
+              3: "mfma_16x16x32_bf16+lds(3 reads/8 mfma)", 4: "mfma_32x32x16_bf16+lds(3 reads/4 mfma)",
+              5: "mfma_16x16x32_bf16+lds(2 reads/8 mfma)", 6: "mfma_32x32x16_bf16+lds(2 reads/4 mfma)"}
+
+
+def peak_rates(modes=tuple(PEAK_MODES), threads=(256, 512), iters=4000, rounds=4):
+    """Peak-rate microbenchmarks (moe_peak): per mode and wavefronts per SIMD,
+    the rate over the whole launch (HIP events) and per CU at the running
+    shader clock (from each workgroup's s_memtime / s_memrealtime)."""
+    import torch
+    import mixture_experts_ffn_fp32_amd as moe
+    groups = CU_COUNT * rounds
+    out = []
+    for mode in modes:
+        for th in threads:
+            clk = torch.zeros(2 * groups, dtype=torch.int64, device="cuda")
+            sink = torch.zeros(groups * th, dtype=torch.int32, device="cuda")
+            moe.moe_peak(mode, th, groups, 200, clk, sink)  # warm-up
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record()
+            moe.moe_peak(mode, th, groups, iters, clk, sink)
+            e.record()
+            torch.cuda.synchronize()
+            ms = b.elapsed_time(e)
+            c = clk.cpu().numpy().reshape(groups, 2).astype(np.float64)
+            cycles, ticks = np.median(c[:, 0]), np.median(c[:, 1])
+            ghz = cycles / (ticks / 100e6) / 1e9
+            waves = th // 64
+            rec = {"mode": PEAK_MODES[mode], "waves_per_simd": waves // 4,
+                   "clock_ghz": round(ghz, 3), "launch_ms": round(ms, 4)}
+            if mode == 2:
+                by = 8 * 1024 * 2 * iters * waves  # bytes per workgroup (= per CU)
+                rec["lds_bytes_per_clk_cu"] = round(by / cycles, 1)
+                rec["lds_tbs"] = round(by * groups / (ms / 1e3) / 1e12, 2)
+            else:
+                fl = 131072.0 * 2 * iters * waves
+                rec["tflops"] = round(fl * groups / (ms / 1e3) / 1e12, 1)
+                rec["frac_of_clock_peak"] = round(fl / cycles / MFMA_FLOP_PER_CLK_CU, 4)
+                rec["frac_of_datasheet"] = round(rec["tflops"] / PEAK["bf16"], 4)
+            out.append(rec)
+            log(f"peak {rec}")
+    return out
+
+
+# ------------------------------------------------------------ timing
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def timed_steps(layer, x, out, counts, steps, warmup):
+    """Wall time of `steps` plain forwards (synchronised on both sides), and
+    each step's duration between HIP events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward(x, out, counts=counts)
+    evs = _events(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for b, e in evs:
+        b.record(stream)
+        layer.forward(x, out, counts=counts)
+        e.record(stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    per = np.array([b.elapsed_time(e) for b, e in evs])
+    return dt / steps * 1e3, {"mean": round(float(per.mean()), 5),
+                              "median": round(float(np.median(per)), 5),
+                              "min": round(float(per.min()), 5),
+                              "max": round(float(per.max()), 5)}
+
+
+def stage_ms(layer, x, out, counts, stage, reps, passes=5):
+    """Mean duration of one pass of a stage: `passes` forwards whose stage is
+    bracketed by HIP events the library records on its launch stream, the
+    GEMM stages enqueued `reps` times back to back between them."""
+    import torch
+    import mixture_experts_ffn_fp32_amd as moe
+    stream = torch.cuda.current_stream()
+    evs = _events(passes)
+    for b, e in evs:  # materialise the events on the launch stream
+        b.record(stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    for b, e in evs:
+        layer.forward(x, out, counts=counts,
+                      probe=moe.MoeProbe(stage=moe.STAGES[stage], repeat=reps,
+                                         ev_begin=b.cuda_event, ev_end=e.cuda_event))
+    torch.cuda.synchronize()
+    return float(np.mean([b.elapsed_time(e) for b, e in evs])) / reps
+
+
+REPEATABLE = ("latent_down", "expert_gate_up", "expert_down", "shared_gate_up")
+
+
+def stages_of(layer, x, out, counts, w, alg, plan, peak_tf):
+    """Per-stage times; the GEMM stages with their algorithmic rate."""
+    st = {}
+    for name in ("route", "dispatch", "latent_down", "expert_gate_up", "expert_down",
+                 "shared_gate_up", "combine"):
+        if name == "latent_down" and not w.latent:
+            continue
+        if name == "shared_gate_up" and (not w.d_shared or plan["merged_shared"]):
+            continue
+        reps = 20 if name in REPEATABLE else 1
+        ms = stage_ms(layer, x, out, counts, name, reps)
+        rec = {"ms": round(ms, 4)}
+        fl = {"expert_gate_up": alg["gu_flops"], "expert_down": alg["dn_flops"],
+              "shared_gate_up": alg["sh_gu_flops"],
+              "latent_down": 2.0 * w.T * w.d * w.latent}.get(name)
+        by = {"expert_gate_up": alg["gu_bytes"], "expert_down": alg["dn_bytes"],
+              "shared_gate_up": alg["sh_gu_bytes"]}.get(name)
+        if fl:
+            rec["tflops"] = round(fl / (ms / 1e3) / 1e12, 1)
+            rec["frac_of_mfma_peak"] = round(fl / (ms / 1e3) / 1e12 / peak_tf, 4)
+        if by:
+            rec["gbs"] = round(by / (ms / 1e3) / 1e9, 1)
+        st[name] = rec
+    return st
+
+
+def roofline_of(alg, gu_ms, peak_tf, name, plan):
+    intensity = alg["gu_flops"] / alg["gu_bytes"]
+    ridge = peak_tf * 1e12 / (HBM_GBS * 1e9)
+    if intensity >= ridge:
+        ach = alg["gu_flops"] / (gu_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(ach / peak_tf, 4), "traffic": None}
+    else:
+        ach = alg["gu_bytes"] / (gu_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_GBS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(name)
+    roof["kernel"] = "grouped gate/up GEMM + SiLU*up" + (
+        " (+ the shared experts' gate/up GEMM in the same launch)" if plan["merged_shared"] else "")
+    roof["tile"] = f"{plan['gate_up_tile_m']}x{plan['gate_up_tile_n']}"
+    roof["kernel_ms"] = round(gu_ms, 4)
+    roof["algorithmic"] = (f"{alg['gu_flops'] / 1e12:.4f} TFLOP, {alg['gu_bytes'] / 1e9:.4f} GB "
+                           "per launch")
+    roof["timing"] = ("mean of 5 x 20 back-to-back launches between HIP events on the launch "
+                      "stream, after the timed steps")
+    return roof
+
+
+def layer_rates(alg, ms, peak_tf):
+    return {"algorithmic_tflop": round(alg["flops"] / 1e12, 5),
+            "tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
+            "frac_of_mfma_peak": round(alg["flops"] / (ms / 1e3) / 1e12 / peak_tf, 4),
+            "algorithmic_gb": round(alg["bytes"] / 1e9, 4),
+            "gbs": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg["bytes"] / (ms / 1e3) / 1e9 / HBM_GBS, 4),
+            "experts_touched": alg["touched"]}
+
+
+# ------------------------------------------------------------ CPU oracle
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _omp_threads(n):
+    """Thread count of the oracle's OpenMP loops (its runtime is libgomp)."""
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        return True
+    except OSError:
+        return False
+
+
+def _time_sample(orc, w, rng, budget_s):
     probe = rng.choice(w.T, size=min(w.T, 8), replace=False)
     t0 = time.perf_counter()
     orc.forward(tokens=probe)
@@ -114,38 +312,97 @@ def cpu_baseline(w, a, budget_s=15.0):
     t0 = time.perf_counter()
     orc.forward(tokens=toks)
     dt = time.perf_counter() - t0
-    # a whole batch shorter than the budget: repeat it (up to 10 passes)
-    passes = 1
+    passes = 1  # a whole batch shorter than the budget: repeat it (up to 10 passes)
     while n == w.T and dt < 0.8 * budget_s and passes < 10:
         orc.forward(tokens=toks)
         passes += 1
         dt = time.perf_counter() - t0
+    return n, passes, dt
+
+
+def cpu_baseline(w, a, budget_s=12.0, budget_1_s=6.0):
+    """Time the CPU oracle (as it stands) on seeded token samples: all host
+    cores, then one core; and its routing + dispatch over all T tokens."""
+    import oracle
+    orc = oracle.Oracle(w, a)
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    _omp_threads(cores)
+    n, passes, dt = _time_sample(orc, w, np.random.default_rng(7), budget_s)
     rep = f" x {passes} passes" if passes > 1 else ""
-    return {"value": n * passes / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens (seeded){rep}, full layer per token in fp64, "
-                      f"{dt:.1f} s"}
+    res = {"value": n * passes / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n} of {w.T} tokens (seeded){rep}, full layer per token in fp64 "
+                     f"(per-token cost is independent of the other tokens), {dt:.1f} s",
+           "cpu_model": _cpu_model()}
+    if _omp_threads(1):
+        n1, p1, dt1 = _time_sample(orc, w, np.random.default_rng(8), budget_1_s)
+        res["one_core"] = {"value": n1 * p1 / dt1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} tokens x {p1} passes, {dt1:.1f} s"}
+        _omp_threads(cores)
+    t0 = time.perf_counter()
+    idx, g, _, _ = orc.route()
+    t1 = time.perf_counter()
+    oracle.dispatch(idx, g.astype(np.float32), w.E)
+    t2 = time.perf_counter()
+    res["route_dispatch_all_tokens"] = {"tokens": w.T, "route_s": round(t1 - t0, 3),
+                                        "dispatch_s": round(t2 - t1, 3), "cores": cores,
+                                        "tokens_per_s": round(w.T / (t2 - t0), 1)}
+    return res
+
+
+# ------------------------------------------------------------ main
+
+def run_workload(w, a_dev, steps, warmup, probe_stages=True):
+    """Time one workload on resident device tensors; returns the pieces of
+    its bench record."""
+    import torch
+    import mixture_experts_ffn_fp32_amd as moe
+    dev = torch.device("cuda:0")
+    layer = moe.Layer(w, a_dev, device=dev)
+    x = layer.dev["x"]
+    out = torch.empty((w.T, w.d), dtype=layer.act, device=dev)
+    counts = torch.zeros(w.E, dtype=torch.int32, device=dev)
+    ms, step_ms = timed_steps(layer, x, out, counts, steps, warmup)
+    gu_ms = stage_ms(layer, x, out, counts, "expert_gate_up", 20)
+    cnt = counts.cpu().numpy()
+    plan = moe.moe_plan(layer.desc)
+    alg = algorithmic(w, cnt, merged=bool(plan["merged_shared"]))
+    peak_tf = PEAK[w.act]
+    rec = {"ms": ms, "step_ms": step_ms, "alg": alg, "plan": plan, "counts": cnt,
+           "roofline": roofline_of(alg, gu_ms, peak_tf, w.name, plan),
+           "layer": layer_rates(alg, ms, peak_tf),
+           "layer_obj": layer, "x": x, "out": out, "counts_t": counts}
+    if probe_stages:
+        rec["stages"] = stages_of(layer, x, out, counts, w, alg, plan, peak_tf)
+    return rec
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass timing")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-batch timing of the same layer")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
+    ap.add_argument("--peak", action="store_true",
+                    help="only run the peak-rate microbenchmarks (MFMA issue, LDS reads)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is not part of this build", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.peak:
+        print(json.dumps({"peak_rates": peak_rates()}), flush=True)
+        return
 
     import torch
 
@@ -160,64 +417,21 @@ def main():
     log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layer = moe.Layer(w, moe.to_device(a, dev), device=dev)
-    x = layer.dev["x"]
-    out = torch.empty((w.T, w.d), dtype=layer.act, device=dev)
-    counts = torch.zeros(w.E, dtype=torch.int32, device=dev)
+    a_dev = moe.to_device(a, dev)
     stream = torch.cuda.current_stream()
+    r = run_workload(w, a_dev, args.steps, args.warmup, probe_stages=not args.no_stages)
+    layer, x, out, counts = r["layer_obj"], r["x"], r["out"], r["counts_t"]
+    ms, alg, cnt = r["ms"], r["alg"], r["counts"]
+    peak_tf = PEAK[w.act]
+    log(f"step {ms:.4f} ms (events: {r['step_ms']}), {w.T / (ms / 1e3):.4g} tokens/s; "
+        f"gate/up kernel {r['roofline']['kernel_ms']:.4f} ms; experts touched "
+        f"{alg['touched']}/{w.E}; loads max {cnt.max()} min {cnt.min()}")
+    if "stages" in r:
+        log(f"stages: {r['stages']}")
 
-    for _ in range(args.warmup):
-        layer.forward(x, out, counts=counts)
-    torch.cuda.synchronize()
-
-    # the timed steps: plain forwards (no timing events inside the layer)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        layer.forward(x, out, counts=counts)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms = dt / args.steps * 1e3
-
-    # after them: the gate/up launch bracketed by HIP events that the library
-    # records on the launch stream, once per forward (the events' own cost
-    # included) ...
-    stage = moe.STAGES["expert_gate_up"]
-    n_ev = min(args.steps, 20)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for b, e in evs:  # materialise the events on the launch stream
-        b.record(stream)
-        e.record(stream)
-    torch.cuda.synchronize()
-    for b, e in evs:
-        layer.forward(x, out, counts=counts,
-                      probe=moe.MoeProbe(stage=stage, repeat=1, ev_begin=b.cuda_event,
-                                         ev_end=e.cuda_event))
-    torch.cuda.synchronize()
-    gu_ms_event = float(np.mean([b.elapsed_time(e) for b, e in evs]))
-
-    # ... and without the events' own overhead (a few us, which matters for
-    # short launches): forwards whose gate/up stage enqueues the launch REPS
-    # times back to back between the two events (each pass recomputes the
-    # same rows); one launch = elapsed / REPS.
-    REPS, PASSES = 20, 5
-    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(PASSES)]
-    for b, e in rev:
-        b.record(stream)
-        e.record(stream)
-    torch.cuda.synchronize()
-    for b, e in rev:
-        layer.forward(x, out, counts=counts,
-                      probe=moe.MoeProbe(stage=stage, repeat=REPS, ev_begin=b.cuda_event,
-                                         ev_end=e.cuda_event))
-    torch.cuda.synchronize()
-    gu_ms = float(np.mean([b.elapsed_time(e) for b, e in rev])) / REPS
-
-    cnt = counts.cpu().numpy()
-    plan = moe.moe_plan(layer.desc)
-    alg = algorithmic(w, cnt, merged=bool(plan["merged_shared"]))
+    # measured MFMA peak of this part (two wavefronts per SIMD), for the
+    # fraction against the running clock beside the datasheet's
+    meas = peak_rates(modes=(0,), threads=(512,), iters=2000)[0]
 
     # bias-based balancer step on this step's loads (a scratch bias, so the
     # layer's routing is untouched)
@@ -293,42 +507,44 @@ def main():
         del grads, d_x, dy
         layer.ws_bwd = None
         torch.cuda.empty_cache()
-    tok_s = w.T / (ms / 1e3)
-    peak_tf = PEAK[w.act]
-    intensity = alg["gu_flops"] / alg["gu_bytes"]
-    ridge = peak_tf * 1e12 / (HBM_GBS * 1e9)
-    if intensity >= ridge:
-        ach = alg["gu_flops"] / (gu_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tf,
-                "unit": "TFLOP/s", "frac": round(ach / peak_tf, 4), "traffic": None}
-    else:
-        ach = alg["gu_bytes"] / (gu_ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_GBS, 4), "traffic": None}
-    roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "grouped gate/up GEMM + SiLU*up" + (
-        " (+ the shared experts' gate/up GEMM in the same launch)" if plan["merged_shared"] else "")
-    roof["tile"] = f"{plan['gate_up_tile_m']}x{plan['gate_up_tile_n']}"
-    roof["kernel_ms"] = round(gu_ms, 4)
-    roof["timing"] = (f"mean of {PASSES} x {REPS} back-to-back launches between HIP events on "
-                      f"the launch stream; a single launch bracketed by events, after the timed steps: "
-                      f"{gu_ms_event:.4f} ms (includes the events' own overhead)")
-    log(f"step {ms:.4f} ms, {tok_s:.4g} tokens/s; gate/up kernel {gu_ms:.4f} ms; "
-        f"experts touched {alg['touched']}/{w.E}; loads max {cnt.max()} min {cnt.min()}")
+
+    # the same resident weights at the decode batch
+    decode = None
+    if w.name in DECODE_OF and not args.no_decode:
+        wd = moe_synth.get(DECODE_OF[w.name])
+        ad = moe_synth.generate(wd, experts=False)
+        assert np.array_equal(ad["w_router"], a["w_router"]), "decode layer differs"
+        dd = dict(a_dev)
+        dd["x"] = moe.to_device({"x": ad["x"]}, dev)["x"]
+        rd = run_workload(wd, dd, max(args.steps, 100), max(args.warmup, 20), probe_stages=False)
+        decode = {"workload": wd.name, "tokens": wd.T,
+                  "value": round(wd.T / (rd["ms"] / 1e3), 1),
+                  "unit": "tokens/s", "ms_per_step": round(rd["ms"], 5),
+                  "step_ms": rd["step_ms"], "layer": rd["layer"], "roofline": rd["roofline"],
+                  "note": "same weights as the prefill layer, own tokens; the layer's bound is "
+                          "HBM: layer.frac_of_hbm_peak = touched expert + shared + router "
+                          "weight bytes / mean step"}
+        log(f"decode: {decode}")
+        del rd
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, a)
         log(f"cpu baseline: {cpu}")
 
+    roof = r["roofline"]
+    if roof["bound"] == "mfma":
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / meas["tflops"], 4)
     line = {
         "metric": METRIC,
-        "value": round(tok_s, 1),
+        "value": round(w.T / (ms / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "step_ms": r["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -337,13 +553,11 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.d, "d_ff": w.d_ff,
                    "experts": w.E, "top_k": w.K, "shared_width": w.d_shared,
                    "latent": w.latent, "route": w.route, "parallelism": "single-gpu"},
-        "layer": {"algorithmic_tflop": round(alg["flops"] / 1e12, 5),
-                  "tflops": round(alg["flops"] / (ms / 1e3) / 1e12, 2),
-                  "frac_of_mfma_peak": round(alg["flops"] / (ms / 1e3) / 1e12 / peak_tf, 4),
-                  "algorithmic_gb": round(alg["bytes"] / 1e9, 4),
-                  "gbs": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
-                  "experts_touched": alg["touched"]},
+        "layer": r["layer"],
         "roofline": roof,
+        "stages": r.get("stages"),
+        "decode": decode,
+        "measured_mfma_peak": meas,
         "balance_bias": {"us_per_call": round(balance_us, 2), "experts": w.E,
                          "note": "one bias-based balancer step, back-to-back launches"},
         "quantile_balance": qb,

@@ -170,6 +170,12 @@ typedef struct moe_plan_info {
                                      fp32 logits (few experts, narrow model);
                                      0: matrix-core router GEMM             */
   int32_t dispatch_one_workgroup; /* 1: the whole dispatch in one workgroup  */
+  int32_t backward_in_place;      /* moe_backward's products that read the
+                                     weights in place (K-major) instead of
+                                     transposed copies: bit 0 the W_down
+                                     products, bit 1 the input gradient
+                                     (W_gate, W_up), bit 2 the latent
+                                     projections                           */
 } moe_plan_info;
 
 /* Text of a status code (static storage). */
@@ -366,6 +372,25 @@ MOE_API int moe_router_losses(const moe_desc *desc, const moe_weights *w, const 
  * finite), MOE_ERR_HIP (launch failure). */
 MOE_API int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens,
                              const int32_t *counts, float alpha, float *bias, void *stream);
+
+/* Measurement helper, not a step of the layer: peak-rate microbenchmarks of
+ * the part, so that fractions of peak can be stated against measured rates as
+ * well as the datasheet's. Each of `groups` workgroups of `threads` (256: one
+ * wavefront per SIMD, 512: two) holds 96 KB of LDS (one workgroup per CU)
+ * and runs `iters` iterations of two halves; a half issues, per wavefront:
+ *   mode 0: 8 independent v_mfma_f32_16x16x32_bf16 (131072 flops);
+ *   mode 1: 4 independent v_mfma_f32_32x32x16_bf16 (131072 flops);
+ *   mode 2: 8 conflict-free 16-byte LDS reads per lane (8 KB per wavefront);
+ *   mode 3 / 4: mode 0 / 1 plus 3 16-byte LDS reads per lane whose data are
+ *     the next half's MFMA operands (the read-to-MFMA ratio of a 64 x 128
+ *     wavefront tile); mode 5 / 6: the same with 2 reads (a 128 x 128 tile).
+ * clk: int64 [2 * groups] device array, per workgroup the shader clock cycles
+ * (s_memtime) and the 100 MHz constant clock ticks (s_memrealtime) its loop
+ * took. sink: uint32 [groups * threads] device array (results kept live).
+ * Enqueued on stream. Errors: MOE_ERR_SHAPE (mode outside 0..6, threads not
+ * 256 or 512, groups outside 1..2^20, iters < 1), MOE_ERR_NULL, MOE_ERR_HIP. */
+MOE_API int moe_peak(int32_t mode, int32_t threads, int32_t groups, int32_t iters, int64_t *clk,
+                     uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

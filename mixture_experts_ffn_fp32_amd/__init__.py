@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
            "moe_balance_bias", "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
-           "moe_backward")
+           "moe_backward", "moe_peak")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -49,7 +49,7 @@ class MoePlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "merged_shared", "gate_up_pipelined", "gate_up_tile_m", "gate_up_tile_n",
         "down_pipelined", "down_tile_m", "down_tile_n", "router_per_token",
-        "dispatch_one_workgroup")]
+        "dispatch_one_workgroup", "backward_in_place")]
 
 
 class MoeGrads(C.Structure):
@@ -91,10 +91,11 @@ def lib():
         L.moe_plan.argtypes = [P, P]
         L.moe_backward_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
         L.moe_backward.argtypes = [P, P, P, P, P, P, P, S, P]
+        L.moe_peak.argtypes = [C.c_int32] * 4 + [P, P, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                   "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance",
                   "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
-                  "moe_backward"):
+                  "moe_backward", "moe_peak"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -228,6 +229,12 @@ def moe_forward(desc, weights, x, out, counts=None, n_near_ties=None, ws=None, p
                           0 if ws is None else ws.numel() * ws.element_size(),
                           None if probe is None else C.byref(probe), _stream(stream)),
         "moe_forward")
+
+
+def moe_peak(mode, threads, groups, iters, clk, sink, stream=None):
+    """Peak-rate microbenchmark launch (measurement helper; see include/moe.h)."""
+    _ok(lib().moe_peak(int(mode), int(threads), int(groups), int(iters), _ptr(clk), _ptr(sink),
+                       _stream(stream)), "moe_peak")
 
 
 # ----------------------------------------------------------------- plumbing

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["router.hip", "dispatch.hip", "gemm.hip", "gemm2.hip", "combine.hip", "balance.hip",
-           "backward.hip", "api.hip"]
+           "backward.hip", "peak.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

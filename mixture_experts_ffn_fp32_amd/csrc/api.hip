@@ -1331,6 +1331,8 @@ int moe_plan(const moe_desc *d, moe_plan_info *info) {
   info->down_tile_n = pl.dn.v2 ? gemm2_bn(pl.dn.cfg) : tile_bn(pl.dn.cfg);
   info->router_per_token = router_valu(ra) ? 1 : 0;
   info->dispatch_one_workgroup = dispatch_fused_ok(d->T * d->top_k, d->n_experts) ? 1 : 0;
+  const KmajorUse ku = kmajor_use(d);
+  info->backward_in_place = (ku.dh ? 1 : 0) | (ku.dx ? 2 : 0) | (ku.lat ? 4 : 0);
   return MOE_OK;
 }
 
@@ -1344,6 +1346,16 @@ int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens, const i
   if (n_tokens == 0) return MOE_OK;
   MOE_TRY(launch_balance(n_experts, n_tokens * top_k, counts, alpha, bias,
                          static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_peak(int32_t mode, int32_t threads, int32_t groups, int32_t iters, int64_t *clk,
+             uint32_t *sink, void *stream) {
+  if (mode < 0 || mode > 6 || (threads != 256 && threads != 512) || groups < 1 ||
+      groups > (1 << 20) || iters < 1)
+    return MOE_ERR_SHAPE;
+  if (!clk || !sink) return MOE_ERR_NULL;
+  MOE_TRY(launch_peak(mode, threads, groups, iters, clk, sink, static_cast<hipStream_t>(stream)));
   return MOE_OK;
 }
 

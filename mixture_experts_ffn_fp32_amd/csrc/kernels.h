@@ -283,4 +283,11 @@ hipError_t launch_bwd_dwr(const float *dr, const int32_t *stok, const int32_t *o
 hipError_t launch_balance(int E, int64_t nk, const int32_t *counts, float alpha, float *bias,
                           hipStream_t s);
 
+// Peak-rate microbenchmarks (peak.hip): mode 0/1 MFMA 16x16x32 / 32x32x16
+// bf16, 2 LDS 16-byte reads, 3/4 MFMAs with 3 reads per 131072 flops, 5/6
+// with 2; clk: int64 [2 groups] (shader cycles, 100 MHz ticks); sink:
+// uint32 [groups x threads].
+hipError_t launch_peak(int mode, int threads, int groups, int iters, int64_t *clk,
+                       uint32_t *sink, hipStream_t s);
+
 }  // namespace moe

@@ -124,7 +124,18 @@ LAYERS = {
     "latent_nonorm_topk": dict(T=200, d=96, latent=64, d_ff=64, E=6, K=2, act="bf16",
                                has_rmsnorm=False, n_shared=0, d_ff_shared=0, w_std=0.1,
                                router_std=0.1),
+    # large experts (d x d_ff = 2^23) with ~256 rows each: the products read
+    # W_down, W_gate and W_up in place on the 2x4-wavefront tile, with
+    # partial m-tiles; every gradient compared in full
+    "kmajor_large_expert": dict(T=512, d=4096, d_ff=2048, E=4, K=2, act="bf16", n_shared=1,
+                                d_ff_shared=512, w_std=0.02, router_std=0.02, bias_std=0.01),
 }
+
+# layers whose backward must take the in-place (K-major) weight products
+IN_PLACE = {"kmajor_large_expert": 3, "decode_like": 3}
+# seeds: layers added later take their own, so the others keep theirs
+SEED_OF = {"kmajor_large_expert": 980}
+_SEEDED = sorted(n for n in LAYERS if n not in SEED_OF)
 
 
 @pytest.fixture(autouse=True)
@@ -139,8 +150,11 @@ def test_backward_matches_oracle(name):
     elif name == "tiny":
         w = moe_synth.get("tiny")
     else:
-        w = custom(name, config_no=950 + sorted(LAYERS).index(name), **LAYERS[name])
+        cfg = SEED_OF.get(name) or 950 + _SEEDED.index(name)
+        w = custom(name, config_no=cfg, **LAYERS[name])
     say(f"case backward {name} T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K} route={w.route}")
+    if name in IN_PLACE:
+        assert moe.moe_plan(moe.make_desc(w))["backward_in_place"] == IN_PLACE[name]
     a = moe_synth.generate(w)
     layer = layer_of(w, a)
     check_all(w, a, layer)
@@ -202,10 +216,9 @@ def test_backward_medium_sampled():
 def test_backward_large_full_size_sampled(name):
     """Full-size large layers (decode: 64 tokens over 256 experts; prefill:
     16384 tokens; both read the expert weights in place, K-major): input
-    gradients on a seeded token sample, and (decode) the weight gradients of
-    the smallest non-empty expert over its tokens. (At the prefill size that
-    expert has ~440 tokens, minutes of fp64 oracle work; its weight
-    gradients use the same K-grouped kernels the medium layer checks.)"""
+    gradients on a seeded sample of 256 tokens, and (decode) the weight
+    gradients of the smallest non-empty expert over its tokens. (The prefill
+    layer's weight gradients: the masked test below.)"""
     w = moe_synth.get(name)
     say(f"case backward {name}: generating inputs")
     a = moe_synth.generate(w)
@@ -220,7 +233,7 @@ def test_backward_large_full_size_sampled(name):
     say(f"  {name}: oracle routing")
     use, n_near = oracle_selection(orc, g_idx)
     dy = moe_synth.as_f64(bits, w.act)
-    toks = np.sort(np.random.default_rng(7).choice(w.T, size=min(w.T, 12), replace=False))
+    toks = np.sort(np.random.default_rng(7).choice(w.T, size=min(w.T, 256), replace=False))
     say(f"  {name}: oracle input gradients of {len(toks)} tokens")
     ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
                        router=False, shared=False)
@@ -276,5 +289,62 @@ def test_backward_latent_full_size_sampled():
     assert err <= TOL
     for v in errs.values():
         assert v <= TOL
+    del layer, a
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_backward_large_prefill_masked_output_gradient():
+    """Full-size large prefill layer (16384 tokens, the launch configuration
+    the benchmark times) with an output gradient that is zero outside a token
+    set S: S = every token of one expert holding 257-511 rows (a full and a
+    partial 256-row m-tile on the in-place weight products) plus a seeded
+    sample of 256 others. Each token's gradient terms are independent of the
+    other tokens, so every weight gradient is then the oracle's sum over S:
+    router, shared gate/up/down and that expert's gate/up/down are compared
+    element by element; dx matches on S and is exactly zero elsewhere."""
+    w = moe_synth.get("large_prefill")
+    say("case backward large_prefill masked: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    assert moe.moe_plan(layer.desc)["backward_in_place"] == 3
+    g_idx = gpu_route(layer)[0]
+    orc = oracle.Oracle(w, a)
+    say("  large_prefill masked: oracle routing")
+    use, n_near = oracle_selection(orc, g_idx)
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    mid = np.nonzero((counts > 256) & (counts < 512))[0]
+    assert len(mid), "no expert with a partial second m-tile"
+    e = int(mid[np.argmin(counts[mid])])
+    mine = np.nonzero((use == e).any(1))[0]
+    rng = np.random.default_rng(13)
+    others = rng.choice(np.setdiff1d(np.arange(w.T), mine), size=256, replace=False)
+    S = np.sort(np.union1d(mine, others))
+    bits = moe_synth.draw_rows(17, (w.T, w.d), w.act)
+    mask = np.zeros(w.T, bool)
+    mask[S] = True
+    bits[~mask] = 0  # +0.0 in bf16
+    dy_dev = torch.from_numpy(bits).view(torch.bfloat16).cuda()
+    keys = _keys(w)
+    grads = _grad_buffers(w, keys)
+    say(f"  large_prefill masked: backward (expert {e}: {counts[e]} rows, |S| = {len(S)})")
+    dx = f64(layer.backward(layer.dev["x"], dy_dev, grads=grads))
+    torch.cuda.synchronize()
+    got = {k: (grads[k][e].cpu().numpy() if k in ("w_gate", "w_up", "w_down")
+               else grads[k].cpu().numpy()).astype(np.float64) for k in keys}
+    del grads
+    torch.cuda.empty_cache()
+    dy = moe_synth.as_f64(bits, w.act)
+    say(f"  large_prefill masked: oracle backward over {len(S)} tokens")
+    ref = orc.backward(dy[S], tokens=S, idx_override=use[S], experts=e, router=True,
+                       shared=True)
+    errs = {"dx": max_abs_rel(dx[S], ref["dx"])}
+    for k in keys:
+        errs[k] = max_abs_rel(got[k], ref[k][0] if k in ("w_gate", "w_up", "w_down") else ref[k])
+    say(f"  large_prefill masked: near-ties={n_near} "
+        + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert np.all(dx[~mask] == 0)
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
     del layer, a
     torch.cuda.empty_cache()

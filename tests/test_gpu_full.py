@@ -11,7 +11,7 @@ from _gpu import check_forward, check_route, layer_of, need_gpu, sample_tokens, 
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
-SAMPLE = {"medium": 1024, "latent": 512, "large_decode": None, "large_prefill": 256}
+SAMPLE = {"medium": 1024, "latent": 1024, "large_decode": None, "large_prefill": 1024}
 
 
 @pytest.mark.parametrize("name", ["medium", "latent", "large_decode", "large_prefill"])

@@ -174,6 +174,8 @@ DISPATCH_CASES = [
     (16384, 1, 4), (8192, 2, 3), (2048, 2, 4), (1, 2, 2), (333, 4, 4), (5461, 3, 4),
     # just past one workgroup, few experts: the three-launch path
     (8193, 2, 4),
+    # 2^21 slots and more: the scan over unpacked counts (scan_kernel)
+    (262144, 8, 64), (262147, 8, 64), (1 << 21, 1, 256),
 ]
 
 
@@ -186,6 +188,10 @@ def test_dispatch_matches_counting_sort(T, K, E):
     rng = np.random.default_rng(T + 7 * E)
     if (T, K, E) == (3, 2, 3):
         idx = np.array([[2, 0], [0, 2], [2, 1]], np.int32)
+    elif T * K >= 1 << 20 and K == 1:
+        idx = rng.integers(0, E, size=(T, 1), dtype=np.int32)
+    elif T * K >= 1 << 20:  # K distinct experts per token, drawn in one pass
+        idx = np.argsort(rng.random((T, E), dtype=np.float32), axis=1)[:, :K].astype(np.int32)
     else:
         idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
     g = rng.random((T, K)).astype(np.float32)
