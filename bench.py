@@ -125,7 +125,10 @@ def calibrate_copy(mib: int, reps: int = 5):
 
 PEAK_MODES = {0: "mfma_16x16x32_bf16", 1: "mfma_32x32x16_bf16", 2: "lds_read_16B",
               3: "mfma_16x16x32_bf16+lds(3 reads/8 mfma)", 4: "mfma_32x32x16_bf16+lds(3 reads/4 mfma)",
-              5: "mfma_16x16x32_bf16+lds(2 reads/8 mfma)", 6: "mfma_32x32x16_bf16+lds(2 reads/4 mfma)"}
+              5: "mfma_16x16x32_bf16+lds(2 reads/8 mfma)", 6: "mfma_32x32x16_bf16+lds(2 reads/4 mfma)",
+              7: "lds_frag16_swz_row", 8: "lds_frag16_swz_row_half", 9: "lds_frag32_swz_row",
+              10: "lds_frag32_swz_row_half"}
+LDS_MODES = (2, 7, 8, 9, 10)
 
 
 def peak_rates(modes=tuple(PEAK_MODES), threads=(256, 512), iters=4000, rounds=4):
@@ -153,7 +156,7 @@ def peak_rates(modes=tuple(PEAK_MODES), threads=(256, 512), iters=4000, rounds=4
             waves = th // 64
             rec = {"mode": PEAK_MODES[mode], "waves_per_simd": waves // 4,
                    "clock_ghz": round(ghz, 3), "launch_ms": round(ms, 4)}
-            if mode == 2:
+            if mode in LDS_MODES:
                 by = 8 * 1024 * 2 * iters * waves  # bytes per workgroup (= per CU)
                 rec["lds_bytes_per_clk_cu"] = round(by / cycles, 1)
                 rec["lds_tbs"] = round(by * groups / (ms / 1e3) / 1e12, 2)

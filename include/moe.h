@@ -383,11 +383,15 @@ MOE_API int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens,
  *   mode 2: 8 conflict-free 16-byte LDS reads per lane (8 KB per wavefront);
  *   mode 3 / 4: mode 0 / 1 plus 3 16-byte LDS reads per lane whose data are
  *     the next half's MFMA operands (the read-to-MFMA ratio of a 64 x 128
- *     wavefront tile); mode 5 / 6: the same with 2 reads (a 128 x 128 tile).
+ *     wavefront tile); mode 5 / 6: the same with 2 reads (a 128 x 128 tile);
+ *   mode 7 .. 10: as mode 2, each read a GEMM operand fragment from stage
+ *     rows of 128 bytes whose 16-byte units are XOR-swizzled: 7 / 8 the
+ *     16x16x32 operand (16 rows per read) swizzled by row & 7 / by
+ *     (row >> 1) & 7; 9 / 10 the 32x32x16 operand (32 rows), the same two.
  * clk: int64 [2 * groups] device array, per workgroup the shader clock cycles
  * (s_memtime) and the 100 MHz constant clock ticks (s_memrealtime) its loop
  * took. sink: uint32 [groups * threads] device array (results kept live).
- * Enqueued on stream. Errors: MOE_ERR_SHAPE (mode outside 0..6, threads not
+ * Enqueued on stream. Errors: MOE_ERR_SHAPE (mode outside 0..10, threads not
  * 256 or 512, groups outside 1..2^20, iters < 1), MOE_ERR_NULL, MOE_ERR_HIP. */
 MOE_API int moe_peak(int32_t mode, int32_t threads, int32_t groups, int32_t iters, int64_t *clk,
                      uint32_t *sink, void *stream);

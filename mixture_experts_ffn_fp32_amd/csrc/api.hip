@@ -1351,7 +1351,7 @@ int moe_balance_bias(int32_t n_experts, int32_t top_k, int64_t n_tokens, const i
 
 int moe_peak(int32_t mode, int32_t threads, int32_t groups, int32_t iters, int64_t *clk,
              uint32_t *sink, void *stream) {
-  if (mode < 0 || mode > 6 || (threads != 256 && threads != 512) || groups < 1 ||
+  if (mode < 0 || mode > 10 || (threads != 256 && threads != 512) || groups < 1 ||
       groups > (1 << 20) || iters < 1)
     return MOE_ERR_SHAPE;
   if (!clk || !sink) return MOE_ERR_NULL;

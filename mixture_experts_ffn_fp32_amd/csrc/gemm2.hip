@@ -87,8 +87,13 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-// physical 16-byte chunk of logical chunk c in row r (rows of 8 chunks)
-__device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+#ifndef MOE_G2_SWZ
+#define MOE_G2_SWZ 0
+#endif
+// XOR key of a stage row's 16-byte chunks (rows of 8 chunks)
+__device__ __forceinline__ int swz_key(int r) { return MOE_G2_SWZ ? ((r >> 1) & 7) : (r & 7); }
+// physical 16-byte chunk of logical chunk c in row r
+__device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ swz_key(r)); }
 
 // K-major B stage buffers: XOR applied to a k-row's chunk-pair index (pairs
 // per row a power of two): rows 0-3 and 8-11, 16-19, 24-27 of a k-step (the
@@ -98,6 +103,22 @@ __device__ __forceinline__ int bkm_swz(int kr, int pairs) {
 }
 
 typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#ifndef MOE_G2_MF
+#define MOE_G2_MF 16
+#endif
+template <int MF> struct AccOf;
+template <> struct AccOf<16> { typedef f32x4 T; static constexpr int N = 4; };
+template <> struct AccOf<32> { typedef f32x16 T; static constexpr int N = 16; };
+
+// row (within a fragment) of accumulator element i of lane `lane`:
+// 16 x 16: lane (fr, fc) holds rows 4 fc + i of column fr; 32 x 32: lane
+// (c = lane % 32, h = lane / 32) holds rows 8 (i / 4) + 4 h + i % 4 of column c
+template <int MF>
+__device__ __forceinline__ int acc_row(int lane, int i) {
+  return MF == 16 ? 4 * (lane >> 4) + i : 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
 
 // ds_read_b64_tr_b16: within each 16 lanes, lane l receives element l % 4 of
 // the 8-byte pieces lanes 4 e + l / 4 point at, e = 0..3 (a 4 x 4 transpose
@@ -144,7 +165,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   static_assert(NA >= 2, "at least double-buffered");
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
+  // fragment edge: 32 x 32 (v_mfma_f32_32x32x16_bf16) where the wavefront
+  // tile holds whole 32 x 32 fragments (K-major B reads 16 x 16 fragments)
+  constexpr int MF = (MOE_G2_MF == 32 && !BKM && WTM % 32 == 0 &&
+                      WTN % (EPI == EPI_SWIGLU ? 64 : 32) == 0) ? 32 : 16;
+  using Acc = typename AccOf<MF>::T;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr bool GLU = EPI == EPI_SWIGLU;
   constexpr int NOUT = GLU ? BN / 2 : BN;
   constexpr int ROWS = THREADS / 8;                 // rows covered by one load of every thread
@@ -256,7 +282,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // row ROWS j + 8 wave; the slot of lane (lrow, lchunk) holds logical chunk
   // lchunk ^ (lrow & 7)
   const int lrow = tid >> 3;
-  const int lchunk = (tid & 7) ^ (lrow & 7);
+  const int lchunk = (tid & 7) ^ swz_key(lrow);
   __amdgpu_buffer_rsrc_t ar, br0, br1;
   uint32_t aoff[A_LD];
   uint32_t boff0 = 0, bstep = 0;  // B: row lrow's offset; ROWS rows further (uniform)
@@ -340,25 +366,40 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   auto brow_of = [&](int fn) {  // B row (within the tile) of fragment fn
     if (GLU) {
       constexpr int half = FN / 2;
-      return fn < half ? wn * (WTN / 2) + fn * 16 : BN / 2 + wn * (WTN / 2) + (fn - half) * 16;
+      return fn < half ? wn * (WTN / 2) + fn * MF : BN / 2 + wn * (WTN / 2) + (fn - half) * MF;
     }
-    return wn * WTN + fn * 16;
+    return wn * WTN + fn * MF;
   };
   // this wave's 16-row fragments that hold rows of the tile
   const int64_t rows_left = m_end - (m_begin + wm * WTM);
-  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + 15) / 16));
+  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + MF - 1) / MF));
   const int live = __builtin_amdgcn_readfirstlane(fm_live);
 
-  f32x4 acc[FM][FN];
+  Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < AccOf<MF>::N; ++e) acc[i][j][e] = 0.f;
 
   u32x4 *const abuf = g2_lds;             // A: NA x A16
   u32x4 *const bbuf = g2_lds + NA * A16;  // B: NB x B16
-  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
+  // per 32-k step a 16 x 16 fragment takes one 16-byte read per lane (lane
+  // (fr, fc): row fr, 8 k at 8 fc); a 32 x 32 fragment two, one per 16-k half
+  // (lane (c, h): row c, 8 k at 16 kk + 8 h)
+  constexpr int KK = MF == 32 ? 2 : 1;
+  bf16x8 xa0[FM * KK], xb0[FN * KK], xa1[FM * KK], xb1[FN * KK];
   auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
+    if constexpr (MF == 32) {
+      const int r = lane & 31, kk = i & 1, f = i >> 1;
+      const int kc = 4 * ks + 2 * kk + (lane >> 5);
+      if (f < FN)
+        xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(f) + r, kc)]);
+      else
+        xa[i - 2 * FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (f - FN) * 32 + r, kc)]);
+      return;
+    }
     const int kc = 4 * ks + fc;
     if (i < FN) {
       if constexpr (BKM) {
@@ -384,11 +425,20 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
   };
   auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
+    if constexpr (MF == 32) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[2 * fm + kk], xb[2 * fn + kk],
+                                                                acc[fm][fn], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
+    }
   };
-  constexpr int NRD = FM + FN;                         // fragment reads per set
+  constexpr int NRD = (FM + FN) * KK;                  // fragment reads per set
   constexpr int RD_PER = (NRD + FM - 1) / FM;          // ... per MFMA row
   constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;  // loads per MFMA row
 
@@ -487,10 +537,10 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       if (fm >= live) break;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int col = n_begin + wn * WTN + fn * 16 + fr;
+        const int col = n_begin + wn * WTN + fn * MF + (lane % MF);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m_begin + wm * WTM + fm * 16 + 4 * fc + i;
+        for (int i = 0; i < AccOf<MF>::N; ++i) {
+          const int64_t m = m_begin + wm * WTM + fm * MF + acc_row<MF>(lane, i);
           if (m < m_end && col < p.N) o[m * p.ldo + col] = acc[fm][fn][i];
         }
       }
@@ -504,16 +554,22 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   float *stg = reinterpret_cast<float *>(g2_lds) + wave * 16 * PITCH;
   const int col0 = n_begin + (GLU ? wn * (WTN / 2) : wn * WTN);
   constexpr int ITEMS = 16 * OUTW / 8;        // (row, 8-column) items per 16 rows
+  // 16 rows per pass: a 16 x 16 fragment row, or half of a 32 x 32 one
+  // (its accumulator elements 8 q .. 8 q + 7 hold rows 16 q .. 16 q + 15)
+  constexpr int PASSES = MF / 16;
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+  for (int fq = 0; fq < FM * PASSES; ++fq) {
+    const int fm = fq / PASSES, q = fq % PASSES;
     if (fm >= live) break;  // unrolled: acc is indexed statically and stays in registers
 #pragma unroll
     for (int fo = 0; fo < FO; ++fo)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = acc[fm][fo][i];
-        if (GLU) v = silu_f(v) * acc[fm][fo + FO][i];
-        stg[(4 * fc + i) * PITCH + fo * 16 + fr] = v;
+      for (int i = 0; i < 4 * (MF / 16); ++i) {
+        const int e = 8 * q * (MF / 32) + i;  // accumulator element (MF 32: 8 per pass)
+        if (MF == 32 && i >= 8) break;
+        float v = acc[fm][fo][e];
+        if (GLU) v = silu_f(v) * acc[fm][fo + FO][e];
+        stg[(acc_row<MF>(lane, e) - 16 * q) * PITCH + fo * MF + (lane % MF)] = v;
       }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
@@ -522,7 +578,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       const int item = it * 64 + lane;
       if (item >= ITEMS) break;
       const int r = item / (OUTW / 8), c8 = (item % (OUTW / 8)) * 8;
-      const int64_t m = m_begin + wm * WTM + fm * 16 + r;
+      const int64_t m = m_begin + wm * WTM + fm * MF + 16 * q + r;
       const int col = col0 + c8;
       if (m >= m_end || col >= p.N) continue;
       float v[8];

@@ -21,10 +21,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPeakLds16 = 96 * 1024 / 16;  // 16-byte units of LDS per workgroup
 constexpr int kReadMask = 4096 - 1;         // reads cycle through the first 64 KB
 
+// 16-byte unit read by `lane` for read number q of a wavefront under the
+// fragment pattern PAT (LDS rows of 128 bytes, 8 units each, as a GEMM
+// stage buffer holds 64 bf16 of k per row): 0 contiguous (lane i reads unit
+// i); 1 / 2 the 16x16x32 operand (16 rows, lanes 16 apart take the next
+// 8-k unit) with units XOR-swizzled by row & 7 / by (row >> 1) & 7; 3 / 4
+// the 32x32x16 operand (32 rows, lanes 32 apart take the next unit), same
+// two swizzles.
+template <int PAT>
+__device__ __forceinline__ int frag_unit(int wave, int lane, int q) {
+  if (PAT == 0) return (wave * 512 + q * 64 + lane) & kReadMask;
+  const int rows = PAT <= 2 ? 16 : 32;
+  const int r = lane % rows, u = lane / rows;
+  // successive reads step 24 / 40 rows (not a power of two: the addresses
+  // repeat only after 64 reads, so no read is loop-invariant)
+  const int row = (wave * 64 + q * (rows + 8) + r) & 511;
+  const int kc = ((q & 1) * 4 + u) & 7;
+  const int sw = (PAT == 1 || PAT == 3) ? (row & 7) : ((row >> 1) & 7);
+  return row * 8 + (kc ^ sw);
+}
+
 // KIND 0: v_mfma_f32_16x16x32_bf16, 8 per half-iteration; KIND 1:
 // v_mfma_f32_32x32x16_bf16, 4 per half-iteration (131072 flops either way);
-// KIND 2: LDS reads only. RD: 16-byte LDS reads per half-iteration.
-template <int KIND, int RD>
+// KIND 2: LDS reads only. RD: 16-byte LDS reads per half-iteration. PAT:
+// the read pattern (frag_unit).
+template <int KIND, int RD, int PAT = 0>
 __global__ __launch_bounds__(512) void peak_kernel(int iters, int64_t *clk, uint32_t *sink) {
   __shared__ __attribute__((aligned(1024))) uint4 lds[kPeakLds16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -51,7 +72,6 @@ __global__ __launch_bounds__(512) void peak_kernel(int iters, int64_t *clk, uint
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc16[j][e] = 0.f;
   uint4 x = make_uint4(0, 0, 0, 0);
-  const int base = wave * 512 + lane;
 
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -59,7 +79,7 @@ __global__ __launch_bounds__(512) void peak_kernel(int iters, int64_t *clk, uint
       // this half's reads (operands of the next half's MFMAs)
 #pragma unroll
       for (int r = 0; r < RD; ++r) {
-        const uint4 v = lds[(base + ((2 * it + h) * RD + r) * 64) & kReadMask];
+        const uint4 v = lds[frag_unit<PAT>(wave, lane, (2 * it + h) * RD + r)];
         if (KIND == 2) {
           x.x ^= v.x;
           x.y ^= v.y;
@@ -99,10 +119,10 @@ __global__ __launch_bounds__(512) void peak_kernel(int iters, int64_t *clk, uint
   }
 }
 
-template <int KIND, int RD>
+template <int KIND, int RD, int PAT = 0>
 hipError_t run_peak(int threads, int groups, int iters, int64_t *clk, uint32_t *sink,
                     hipStream_t s) {
-  peak_kernel<KIND, RD><<<groups, threads, 0, s>>>(iters, clk, sink);
+  peak_kernel<KIND, RD, PAT><<<groups, threads, 0, s>>>(iters, clk, sink);
   return hipGetLastError();
 }
 
@@ -118,6 +138,10 @@ hipError_t launch_peak(int mode, int threads, int groups, int iters, int64_t *cl
     case 4: return run_peak<1, 3>(threads, groups, iters, clk, sink, s);
     case 5: return run_peak<0, 2>(threads, groups, iters, clk, sink, s);
     case 6: return run_peak<1, 2>(threads, groups, iters, clk, sink, s);
+    case 7: return run_peak<2, 8, 1>(threads, groups, iters, clk, sink, s);
+    case 8: return run_peak<2, 8, 2>(threads, groups, iters, clk, sink, s);
+    case 9: return run_peak<2, 8, 3>(threads, groups, iters, clk, sink, s);
+    case 10: return run_peak<2, 8, 4>(threads, groups, iters, clk, sink, s);
   }
   return hipErrorInvalidValue;
 }

@@ -271,6 +271,34 @@ def test_sigmoid_topk_plus_one_drop_last():
     assert np.allclose(gr, g / g.sum(1, keepdims=True), atol=1e-15)
 
 
+@pytest.mark.parametrize("renorm,scale", [(False, 1.0), (True, 1.0), (False, 2.5)])
+def test_sigmoid_zero_router_closed_form(renorm, scale):
+    """StableLatentMoE, closed form: with a zero router weight every raw
+    score is sigmoid(0) = 1/2 exactly, so the selection is the top-K of the
+    bias alone (ties to the lower id), each weight is routed_scale / 2 (or
+    routed_scale / K when renormalised), and the routed output of a token is
+    that weight times the sum of its K experts' SwiGLU (computed here by
+    numpy matmuls)."""
+    w = custom(T=40, d=12, d_ff=10, E=9, K=3, route="sigmoid_bias", bias_std=0.3,
+               renormalize=renorm, routed_scale=scale, n_shared=0, d_ff_shared=0)
+    a = moe_synth.generate(w)
+    a["w_router"] = np.zeros_like(a["w_router"])
+    orc = oracle.Oracle(w, a)
+    idx, g, gap, top = orc.route()
+    want_idx = np.argsort(-a["bias"].astype(np.float64), kind="stable")[:w.K]
+    assert np.array_equal(idx, np.broadcast_to(want_idx, idx.shape))
+    gw = scale / w.K if renorm else scale * 0.5
+    assert np.all(g == gw)
+    out, _, _, _ = orc.forward()
+    x = f64(a["x"])
+    ref = np.zeros((w.T, w.d))
+    for e in want_idx:
+        ag = x @ f64(a["w_gate"][e]).T
+        au = x @ f64(a["w_up"][e]).T
+        ref += gw * ((ag / (1.0 + np.exp(-ag))) * au) @ f64(a["w_down"][e]).T
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 @pytest.mark.parametrize("route", ["topk_softmax", "softmax_topk", "sigmoid_bias"])
 def test_selection_maximises_score_sum(route):
     """Brute force over all C(E, K) subsets: the selected set has the largest
