@@ -35,8 +35,9 @@
  *    cost nothing (APEX-1 docs "10 - Mixture of Experts", BUG-08: an expert
  *    may get 0, 1 or many tokens).
  *  - Inputs must be finite; NaN / Inf behaviour is unspecified.
- *  - The library has no mutable global state; calls on different streams
- *    with disjoint outputs and workspaces may run concurrently.
+ *  - The library has no mutable global state apart from moe_forward_noalloc's
+ *    per-device scratch (below); calls on different streams with disjoint
+ *    outputs and workspaces may run concurrently.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -63,8 +64,14 @@ typedef enum moe_status {
   MOE_ERR_MODE = -3,      /* unknown dtype / route mode, or a mode
                              combination this layer does not define         */
   MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_workspace_size()     */
-  MOE_ERR_HIP = -5        /* a kernel launch failed                          */
+  MOE_ERR_HIP = -5,       /* a kernel launch failed                          */
+  MOE_ERR_SCRATCH = -6    /* moe_forward_noalloc: the layer needs more than
+                             the library's static scratch (MOE_SCRATCH_BYTES),
+                             or the stream is not on the current device     */
 } moe_status;
+
+/* Size of the static device scratch moe_forward_noalloc runs in. */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -263,6 +270,26 @@ MOE_API int moe_combine(const moe_desc *desc, const moe_weights *w, const void *
 MOE_API int moe_forward(const moe_desc *desc, const moe_weights *w, const void *x, void *out,
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream);
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops such as decode, harnesses that
+ * forbid hipMalloc): the same kernels and results as moe_forward, with its
+ * workspace taken from a static device array of MOE_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends. The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library call);
+ * on its first call on a device it looks up that device's copy of the array
+ * (hipGetSymbolAddress). The caller passes inputs and outputs as for
+ * moe_forward. `stream` must belong to the current device.
+ * Every call on one GPU shares that GPU's scratch, which keeps the previous
+ * call's contents (nothing in the forward depends on them): calls that may
+ * overlap on one GPU (different streams, or different host threads) race
+ * and must be serialised by the caller.
+ * Errors: as moe_forward, and MOE_ERR_SCRATCH when moe_workspace_size() of
+ * the layer exceeds MOE_SCRATCH_BYTES (e.g. the d=7168, E=256, K=8 layer
+ * fits up to 256 tokens, the d=512, E=4 layer up to ~4000) or the stream is
+ * on another device; nothing is launched then. */
+MOE_API int moe_forward_noalloc(const moe_desc *desc, const moe_weights *w, const void *x,
+                                void *out, int32_t *counts, int32_t *n_near_ties, void *stream);
 
 /* Gradients of the layer's parameters (fp32 DEVICE arrays, caller-owned; a
  * NULL member is not computed). Shapes as in moe_weights. */

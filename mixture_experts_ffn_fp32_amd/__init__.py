@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 EXPORTS = ("moe_strerror", "moe_stage_name", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_quantile_balance",
            "moe_balance_bias", "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
-           "moe_backward", "moe_peak")
+           "moe_backward", "moe_peak", "moe_forward_noalloc")
 
 MOE_F32, MOE_BF16 = 0, 1
 ROUTE_MODES = {"topk_softmax": 0, "softmax_topk": 1, "sigmoid_bias": 2}
@@ -92,10 +92,11 @@ def lib():
         L.moe_backward_workspace_size.argtypes = [P, C.POINTER(C.c_size_t)]
         L.moe_backward.argtypes = [P, P, P, P, P, P, P, S, P]
         L.moe_peak.argtypes = [C.c_int32] * 4 + [P, P, P]
+        L.moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
         for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
                   "moe_combine", "moe_forward", "moe_balance_bias", "moe_quantile_balance",
                   "moe_router_losses", "moe_plan", "moe_backward_workspace_size",
-                  "moe_backward", "moe_peak"):
+                  "moe_backward", "moe_peak", "moe_forward_noalloc"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -235,6 +236,16 @@ def moe_peak(mode, threads, groups, iters, clk, sink, stream=None):
     """Peak-rate microbenchmark launch (measurement helper; see include/moe.h)."""
     _ok(lib().moe_peak(int(mode), int(threads), int(groups), int(iters), _ptr(clk), _ptr(sink),
                        _stream(stream)), "moe_peak")
+
+
+def moe_forward_noalloc(desc, weights, x, out, counts=None, n_near_ties=None, stream=None):
+    """moe_forward in the library's static device scratch (allocates nothing)."""
+    _ok(lib().moe_forward_noalloc(C.byref(desc), C.byref(weights), _ptr(x), _ptr(out),
+                                  _ptr(counts), _ptr(n_near_ties), _stream(stream)),
+        "moe_forward_noalloc")
+
+
+SCRATCH_BYTES = 64 << 20  # MOE_SCRATCH_BYTES
 
 
 # ----------------------------------------------------------------- plumbing

@@ -4,8 +4,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "moe.h"
+
+// Workspace of moe_forward_noalloc: a file-scope device array, one copy on
+// each GPU the library runs on. In host code `scratch` names a host-side
+// stand-in, not a device address: the address of the current device's copy
+// comes from hipGetSymbolAddress (taken once per device, below) and only
+// that pointer is ever handed to kernels.
+static __device__ __align__(256) char scratch[MOE_SCRATCH_BYTES];
 
 namespace {
 
@@ -607,6 +616,9 @@ const char *moe_strerror(int status) {
     case MOE_ERR_MODE: return "invalid dtype or mode combination";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "layer needs more than the static scratch (MOE_SCRATCH_BYTES), or the stream is "
+             "on another device";
   }
   return "unknown status";
 }
@@ -806,9 +818,65 @@ int moe_combine(const moe_desc *d, const moe_weights *w, const void *x, const vo
   return shared_combine(d, w, x, y_sorted, inv, out, static_cast<char *>(ws), L, pr, s);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Per-device address of `scratch` (set once per device, under the lock).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
+
+int scratch_of(hipStream_t s, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  if (s) {  // the stream's device must be the current one (whose copy is looked up)
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(s, &sd) != hipSuccess) return MOE_ERR_HIP;
+    if (sd != dev) return MOE_ERR_SCRATCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *out,
+                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
+                 const moe_probe *probe, void *stream);
+
+}  // namespace
+
+extern "C" {
+
 int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *out,
                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                 const moe_probe *probe, void *stream) {
+  return forward_impl(d, w, x, out, counts, n_near_ties, ws, ws_bytes, probe, stream);
+}
+
+int moe_forward_noalloc(const moe_desc *d, const moe_weights *w, const void *x, void *out,
+                        int32_t *counts, int32_t *n_near_ties, void *stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (layout_of(d).total > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  if (!w || !w->w_router || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  void *ws = nullptr;
+  if ((rc = scratch_of(static_cast<hipStream_t>(stream), &ws))) return rc;
+  return forward_impl(d, w, x, out, counts, n_near_ties, ws, MOE_SCRATCH_BYTES, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *out,
+                 int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
+                 const moe_probe *probe, void *stream) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (!w || !w->w_router) return MOE_ERR_NULL;
@@ -919,6 +987,10 @@ int moe_forward(const moe_desc *d, const moe_weights *w, const void *x, void *ou
     return rc;
   return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
 }
+
+}  // namespace
+
+extern "C" {
 
 int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes) {
   const int rc = check_backward(desc);

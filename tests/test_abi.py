@@ -215,3 +215,19 @@ def test_backward_checked_before_launch():
     d0 = _desc(T=0)
     assert L.moe_backward(C.byref(d0), C.byref(w), None, None, None, C.byref(g), fake,
                           moe.moe_backward_workspace_size(d0), None) == 0
+
+
+def test_noalloc_rejects_layers_beyond_the_static_scratch():
+    """moe_forward_noalloc checks the layer's workspace against the static
+    scratch on the host, before touching any device."""
+    fake = C.c_void_p(1 << 20)
+    w = moe.MoeWeights(**{k: fake.value for k, _ in moe.MoeWeights._fields_})
+    for name in ("medium", "large_prefill", "latent"):
+        d = moe.make_desc(moe_synth.get(name))
+        assert moe.moe_workspace_size(d) > moe.SCRATCH_BYTES
+        assert moe.lib().moe_forward_noalloc(C.byref(d), C.byref(w), fake, fake, None, None,
+                                             None) == -6
+    for name, T in (("small", 2048), ("large_decode", 256), ("tiny", 128)):
+        d = moe.make_desc(moe_synth.get(name).with_T(T))
+        assert moe.moe_workspace_size(d) <= moe.SCRATCH_BYTES
+    assert "static scratch" in moe.strerror(-6)
