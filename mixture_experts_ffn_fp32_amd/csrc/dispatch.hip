@@ -47,14 +47,32 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
     chunk_hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// m-tile tables of height bm from offsets held in LDS (1024 threads), in two
-// steps so that callers can put every global write after their last
-// barrier: tile_starts (LDS only: start[e] = first tile of expert e,
-// start[E] = total) and write_tiles (global writes only). Tile i = {expert,
-// row_begin, row_end, group_first, group_size}; experts with no rows get no
-// tile. A group is a run of at most kTileGroup m-tiles of one expert (the
-// GEMMs schedule a group's tiles together so they share the expert's weight
-// slices in L2).
+#ifndef MOE_TILE_EVEN
+#define MOE_TILE_EVEN 1
+#endif
+// Rows [begin, end) of m-tile j of n over an expert's R rows starting at
+// row0: n = ceil(R / bm) tiles of R / n rows each (the first R % n one row
+// more), so an expert just past a multiple of bm rows does not end in a
+// tile of a few rows that costs nearly a full one.
+__device__ __forceinline__ void tile_rows(int row0, int R, int n, int j, int bm, int *begin,
+                                          int *end) {
+  if (MOE_TILE_EVEN) {
+    *begin = row0 + static_cast<int>(static_cast<int64_t>(j) * R / n);
+    *end = row0 + static_cast<int>(static_cast<int64_t>(j + 1) * R / n);
+  } else {
+    *begin = row0 + j * bm;
+    *end = min(*begin + bm, row0 + R);
+  }
+}
+
+// m-tile tables of height at most bm from offsets held in LDS (1024
+// threads), in two steps so that callers can put every global write after
+// their last barrier: tile_starts (LDS only: start[e] = first tile of expert
+// e, start[E] = total) and write_tiles (global writes only). Tile i =
+// {expert, row_begin, row_end, group_first, group_size}; experts with no rows
+// get no tile. A group is a run of at most kTileGroup m-tiles of one expert
+// (the GEMMs schedule a group's tiles together so they share the expert's
+// weight slices in L2).
 __device__ void tile_starts(const int *off, int E, int bm, int *start, int *tmp) {
   const int t = threadIdx.x;
   int nt = 0;
@@ -76,12 +94,13 @@ __device__ void write_tiles(const int *off, int E, int bm, const int *start, int
       if (start[mid] <= i) lo = mid; else hi = mid;
     }
     const int e = lo;
-    const int r0 = off[e] + (i - start[e]) * bm;
+    int r0, r1;
+    tile_rows(off[e], off[e + 1] - off[e], start[e + 1] - start[e], i - start[e], bm, &r0, &r1);
     const int gfirst = start[e] + (i - start[e]) / kTileGroup * kTileGroup;
     int32_t *ti = tiles + kTileInts * static_cast<int64_t>(i);
     ti[0] = e;
     ti[1] = r0;
-    ti[2] = min(r0 + bm, off[e + 1]);
+    ti[2] = r1;
     ti[3] = gfirst;
     ti[4] = min(kTileGroup, start[e + 1] - gfirst);
   }
@@ -427,12 +446,14 @@ __device__ void write_tiles_few(const int (&off)[kFewE + 1], const int (&st)[kFe
 #pragma unroll
     for (int j = 1; j < kFewE; ++j) e += (j < E && st[j] <= i) ? 1 : 0;
     const int se = pick_few(st, e), se1 = pick_few(st, e + 1);
-    const int r0 = pick_few(off, e) + (i - se) * bm;
+    const int o0 = pick_few(off, e);
+    int r0, r1;
+    tile_rows(o0, pick_few(off, e + 1) - o0, se1 - se, i - se, bm, &r0, &r1);
     const int gfirst = se + (i - se) / kTileGroup * kTileGroup;
     int32_t *ti = tiles + kTileInts * static_cast<int64_t>(i);
     ti[0] = e;
     ti[1] = r0;
-    ti[2] = min(r0 + bm, pick_few(off, e + 1));
+    ti[2] = r1;
     ti[3] = gfirst;
     ti[4] = min(kTileGroup, se1 - gfirst);
   }

@@ -90,6 +90,9 @@ __device__ __forceinline__ void barrier() {
 #ifndef MOE_G2_SWZ
 #define MOE_G2_SWZ 0
 #endif
+#ifndef MOE_G2_ILV
+#define MOE_G2_ILV 1
+#endif
 // XOR key of a stage row's 16-byte chunks (rows of 8 chunks)
 __device__ __forceinline__ int swz_key(int r) { return MOE_G2_SWZ ? ((r >> 1) & 7) : (r & 7); }
 // physical 16-byte chunk of logical chunk c in row r
@@ -371,8 +374,20 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     return wn * WTN + fn * MF;
   };
   // this wave's 16-row fragments that hold rows of the tile
-  const int64_t rows_left = m_end - (m_begin + wm * WTM);
-  const int fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + MF - 1) / MF));
+  // fragment row fm of wavefront row wm holds tile rows frow(fm) .. + MF - 1:
+  // interleaved over the wavefront rows (fm WGM + wm), so that a tile with
+  // fewer rows than BM spreads its MFMAs over all four SIMDs (two wavefront
+  // rows share a SIMD) instead of leaving the SIMDs of the last rows idle
+  auto frow = [&](int fm) { return MOE_G2_ILV ? (fm * WGM + wm) * MF : wm * WTM + fm * MF; };
+  const int64_t rows_in = m_end - m_begin;
+  int fm_live;
+  if (MOE_G2_ILV) {
+    const int64_t n_frag = (rows_in + MF - 1) / MF;  // fragment rows holding tile rows
+    fm_live = static_cast<int>(min<int64_t>(FM, max<int64_t>(0, (n_frag - wm + WGM - 1) / WGM)));
+  } else {
+    const int64_t rows_left = rows_in - wm * WTM;
+    fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + MF - 1) / MF));
+  }
   const int live = __builtin_amdgcn_readfirstlane(fm_live);
 
   Acc acc[FM][FN];
@@ -397,7 +412,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       if (f < FN)
         xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(f) + r, kc)]);
       else
-        xa[i - 2 * FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (f - FN) * 32 + r, kc)]);
+        xa[i - 2 * FN] = __builtin_bit_cast(bf16x8, ab[sw8(frow(f - FN) + r, kc)]);
       return;
     }
     const int kc = 4 * ks + fc;
@@ -422,7 +437,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
         xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(i) + fr, kc)]);
       }
     } else
-      xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(wm * WTM + (i - FN) * 16 + fr, kc)]);
+      xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(frow(i - FN) + fr, kc)]);
   };
   auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
     if constexpr (MF == 32) {
@@ -540,7 +555,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
         const int col = n_begin + wn * WTN + fn * MF + (lane % MF);
 #pragma unroll
         for (int i = 0; i < AccOf<MF>::N; ++i) {
-          const int64_t m = m_begin + wm * WTM + fm * MF + acc_row<MF>(lane, i);
+          const int64_t m = m_begin + frow(fm) + acc_row<MF>(lane, i);
           if (m < m_end && col < p.N) o[m * p.ldo + col] = acc[fm][fn][i];
         }
       }
@@ -578,7 +593,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       const int item = it * 64 + lane;
       if (item >= ITEMS) break;
       const int r = item / (OUTW / 8), c8 = (item % (OUTW / 8)) * 8;
-      const int64_t m = m_begin + wm * WTM + fm * MF + 16 * q + r;
+      const int64_t m = m_begin + frow(fm) + 16 * q + r;
       const int col = col0 + c8;
       if (m >= m_end || col >= p.N) continue;
       float v[8];
