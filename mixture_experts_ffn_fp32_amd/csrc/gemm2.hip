@@ -156,7 +156,8 @@ struct G2Shape {
   static constexpr int PITCH = OUTW + 4;            // floats per staged row
   static constexpr int STAGE16 = (NA * BM + (NA + 1) * BN) * 8;
   static constexpr int STG16 = NW * 16 * PITCH / 4;
-  static constexpr int LDS16 = STAGE16 > STG16 ? STAGE16 : STG16;
+  static constexpr int SCL16 = EPI == EPI_SCALE ? BM / 4 : 0;  // row scales after the staging rows
+  static constexpr int LDS16 = STAGE16 > STG16 + SCL16 ? STAGE16 : STG16 + SCL16;
   static constexpr int MIN_WAVES = (NW == 4 && LDS16 * 16 <= 80 * 1024) ? 2 : 1;
 };
 
@@ -266,6 +267,17 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     m_end = min<int64_t>(m_begin + BM, p.M);
   }
   const int n_begin = nt * NOUT;
+  // the row-scale epilogue's routing weights, one per tile row: requested
+  // before the prologue (loads complete in order, so the stage waits still
+  // count right) and parked in LDS after the main loop — a global load per
+  // output chunk inside the epilogue cost a dependent load latency in each
+  // of its 16-row passes
+  float row_w = 1.f;
+  if constexpr (EPI == EPI_SCALE) {
+    static_assert(64 * WGM * WGN >= BM, "a thread per tile row");
+    if (p.row_scale && threadIdx.x < BM && m_begin + threadIdx.x < m_end)
+      row_w = p.row_scale[m_begin + threadIdx.x];
+  }
   // K-grouped: this expert's reduction columns and output block
   int64_t kbeg = 0, kseg = p.K;
   int64_t obase = 0;
@@ -539,6 +551,11 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   __builtin_amdgcn_s_setprio(0);
   wait_vm_lgkm0<0>();
   barrier();  // the epilogue reuses the stage buffers
+  float *const row_scale_lds = reinterpret_cast<float *>(g2_lds) + Sh::STG16 * 4;
+  if constexpr (EPI == EPI_SCALE) {
+    if (tid < BM) row_scale_lds[tid] = row_w;
+    barrier();
+  }
 
   // ------------------------------------------------------------ epilogue
   if constexpr (EPI == EPI_STORE_F32) {
@@ -602,7 +619,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
       v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
       if (EPI == EPI_SCALE && p.row_scale) {
-        const float s = p.row_scale[m];
+        const float s = row_scale_lds[m - m_begin];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] *= s;
       }
