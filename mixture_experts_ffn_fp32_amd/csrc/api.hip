@@ -256,11 +256,9 @@ int expert_gemms(const moe_desc *d, const moe_weights *w, const void *rows,
   return MOE_OK;
 }
 
-// Shared experts + combine (+ latent RMSNorm and up-projection) into out.
-int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const void *y,
-                   const int32_t *inv, void *out, char *ws, const Layout &L, const Probe &pr,
-                   hipStream_t s) {
-  const int64_t T = d->T;
+// The shared experts' first GEMM: H_shared = SiLU(x Ws_gate^T) * (x Ws_up^T).
+int shared_gate_up(const moe_desc *d, const moe_weights *w, const void *x, char *ws,
+                   const Layout &L, const Probe &pr, hipStream_t s) {
   const int bf = d->act_dtype == MOE_BF16;
   const int dm = d->d_model;
   void *hsh = ws + L.hsh;
@@ -273,13 +271,29 @@ int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const
     a.ldb = dm;
     a.K = dm;
     a.N = d->d_shared;
-    a.M = T;
+    a.M = d->T;
     a.out = hsh;
     a.ldo = d->d_shared;
     pr.begin(MOE_STAGE_SHARED_GATE_UP);
     for (int r = 0; r < pr.reps(MOE_STAGE_SHARED_GATE_UP); ++r)
       MOE_TRY(launch_dense(a, EPI_SWIGLU, bf, s));
     pr.end(MOE_STAGE_SHARED_GATE_UP);
+  }
+  return MOE_OK;
+}
+
+// Shared experts + combine (+ latent RMSNorm and up-projection) into out;
+// with have_hsh the shared experts' first GEMM has already run.
+int shared_combine(const moe_desc *d, const moe_weights *w, const void *x, const void *y,
+                   const int32_t *inv, void *out, char *ws, const Layout &L, const Probe &pr,
+                   hipStream_t s, bool have_hsh = false) {
+  const int64_t T = d->T;
+  const int bf = d->act_dtype == MOE_BF16;
+  const int dm = d->d_model;
+  void *hsh = ws + L.hsh;
+  if (!have_hsh) {
+    const int rc = shared_gate_up(d, w, x, ws, L, pr, s);
+    if (rc) return rc;
   }
   pr.begin(MOE_STAGE_COMBINE);
   if (!d->latent) {
@@ -849,6 +863,43 @@ int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *o
                  int32_t *counts, int32_t *n_near_ties, void *ws, size_t ws_bytes,
                  const moe_probe *probe, void *stream);
 
+// A second stream per device (default priority) and three events, created on
+// the first forward that overlaps there and kept until the process ends:
+// the shared experts' first GEMM (and the latent down-projection) depend on x
+// alone, so they run beside the routing, dispatch and routed GEMMs, which use
+// few CUs at a time (router, dispatch) or leave CUs idle in their tails.
+// The lock is held while a forward enqueues, so each event's record and the
+// waits on it come from one call.
+struct Side {
+  hipStream_t s2 = nullptr;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+};
+std::mutex g_side_mu;
+Side g_side[kMaxDevices];
+
+int side_of(hipStream_t s, Side **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  if (s) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(s, &sd) != hipSuccess || sd != dev) return MOE_ERR_HIP;
+  }
+  Side &sd = g_side[dev];
+  if (!sd.s2) {
+    if (hipStreamCreateWithFlags(&sd.s2, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+    for (hipEvent_t &e : sd.ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return MOE_ERR_HIP;
+  }
+  *out = &sd;
+  return MOE_OK;
+}
+
+// Run the shared experts' first GEMM on the side stream: large bf16 layers
+// whose shared GEMMs are separate launches, not under a timing probe.
+bool overlap_shared(const moe_desc *d, bool merged, const moe_probe *probe) {
+  return !probe && !merged && d->d_shared > 0 && d->act_dtype == MOE_BF16 && d->T >= 1024;
+}
+
 }  // namespace
 
 extern "C" {
@@ -902,6 +953,34 @@ int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *o
   float *sw = reinterpret_cast<float *>(wsb + L.sw);
   const Plan pl = plan_grouped(d);
   const Tables tb = tables_of(wsb, L, pl);
+
+  // 0. fork: the shared experts' first GEMM (latent: after the latent
+  // down-projection, which the routed rows wait for) on the side stream
+  const bool side = d->T > 0 && overlap_shared(d, pl.merged, probe);
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  Side *sd = nullptr;
+  if (side) {
+    side_lock.lock();
+    if ((rc = side_of(s, &sd))) return rc;
+    MOE_TRY(hipEventRecord(sd->ev[0], s));
+    MOE_TRY(hipStreamWaitEvent(sd->s2, sd->ev[0], 0));
+    if (d->latent) {
+      GemmArgs a{};
+      a.a = x;
+      a.lda = d->d_model;
+      a.b0 = w->w_lat_down;
+      a.ldb = d->d_model;
+      a.K = d->d_model;
+      a.N = d->latent;
+      a.M = T;
+      a.out = wsb + L.z;
+      a.ldo = d->latent;
+      MOE_TRY(launch_dense(a, EPI_STORE, bf, sd->s2));
+      MOE_TRY(hipEventRecord(sd->ev[1], sd->s2));
+    }
+    if ((rc = shared_gate_up(d, w, x, wsb, L, Probe{nullptr, sd->s2}, sd->s2))) return rc;
+    MOE_TRY(hipEventRecord(sd->ev[2], sd->s2));
+  }
 
   // 1. router
   RouterArgs ra{};
@@ -962,7 +1041,10 @@ int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *o
 
   // 3. latent down-projection (routed rows are z = x W_lat_down^T)
   const void *rsrc = x;
-  if (d->latent) {
+  if (d->latent && side) {
+    MOE_TRY(hipStreamWaitEvent(s, sd->ev[1], 0));
+    rsrc = wsb + L.z;
+  } else if (d->latent) {
     GemmArgs a{};
     a.a = x;
     a.lda = d->d_model;
@@ -985,7 +1067,8 @@ int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *o
   if (pl.merged) return merged_gemms(d, w, x, rsrc, stok, tb, pl, sw, inv, out, wsb, L, pr, s);
   if ((rc = expert_gemms(d, w, rsrc, stok, tb, pl, sw, wsb + L.h, wsb + L.y, pr, s)))
     return rc;
-  return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s);
+  if (side) MOE_TRY(hipStreamWaitEvent(s, sd->ev[2], 0));  // join
+  return shared_combine(d, w, x, wsb + L.y, inv, out, wsb, L, pr, s, side);
 }
 
 }  // namespace
