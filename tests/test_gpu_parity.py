@@ -298,6 +298,29 @@ def test_forward_is_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_side_stream_forward_matches_single_stream():
+    """A layer large enough for 256x256 tiles with shared experts runs the
+    shared gate/up GEMM on a second stream beside routing and the routed
+    GEMMs; with a timing probe everything runs on the caller's stream. Both
+    must give the same bytes, repeatably, and match the oracle."""
+    w = custom(name="side", config_no=931, T=4096, d=1024, d_ff=1024, E=8, K=2, act="bf16",
+               n_shared=1, d_ff_shared=1024, w_std=0.03, router_std=0.03, bias_std=0.01)
+    plan = moe.moe_plan(moe.make_desc(w))
+    assert plan["merged_shared"] == 0 and plan["gate_up_tile_m"] == 256
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    say("case side stream")
+    x = layer.dev["x"]
+    o1 = layer.forward(x).clone()
+    o2 = layer.forward(x).clone()
+    probe = moe.MoeProbe(stage=-1, repeat=1, ev_begin=None, ev_end=None)
+    o3 = layer.forward(x, probe=probe).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    check_forward(w, a, layer, tokens=np.arange(0, w.T, 7))
+
+
 def test_probe_records_stage_events():
     w = moe_synth.get("tiny")
     a = moe_synth.generate(w)
