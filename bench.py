@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import os
 import sys
@@ -379,6 +380,96 @@ def run_workload(w, a_dev, steps, warmup, probe_stages=True):
     return rec
 
 
+def expert_shard(spec: str, workload: str, reps: int = 10):
+    """One GPU's share of an expert-parallel layer of G GPUs (experts
+    [g E/G, (g+1) E/G) on this GPU): the grouped expert SwiGLU on the rows
+    routed to those experts (their true count, from the whole batch's routing
+    and dispatch), plus routing, dispatch, shared experts and combine for this
+    GPU's T/G tokens. The all-to-all exchanges between them are not part of a
+    one-GPU run; they are left out of the sum, which says so."""
+    import torch
+
+    import mixture_experts_ffn_fp32_amd as moe
+    import moe_synth
+    g, G = (int(v) for v in spec.split("/"))
+    w = moe_synth.get(workload)
+    if not (0 <= g < G and w.E % G == 0 and w.T % G == 0) or w.latent:
+        raise SystemExit(f"--expert-shard {spec}: need 0 <= g < G, G dividing E={w.E} and T={w.T}, "
+                         "and a layer without latent projections")
+    a = moe_synth.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d_all = moe.to_device(a, dev)
+    layer = moe.Layer(w, d_all, device=dev)
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    T, K, E = w.T, w.K, w.E
+    idx, gw = i32((T, K)), torch.empty((T, K), dtype=torch.float32, device=dev)
+    moe.moe_route(layer.desc, layer.weights, d_all["x"], idx, gw, ws=layer.ws)
+    counts, offsets, perm, st, inv = i32(E), i32(E + 1), i32(T * K), i32(T * K), i32(T * K)
+    sw = torch.empty(T * K, dtype=torch.float32, device=dev)
+    moe.moe_dispatch(layer.desc, idx, gw, None, counts, offsets, perm, st, inv, sw, None, layer.ws)
+    torch.cuda.synchronize()
+    e0, e1 = g * E // G, (g + 1) * E // G
+    off = offsets.cpu().numpy()
+    lo, hi = int(off[e0]), int(off[e1])
+    # the shard: E/G experts, their rows [lo, hi) of the sorted order
+    ws_ = dataclasses.replace(w, E=E // G)
+    desc_s = moe.make_desc(ws_)
+    shard_w = {k: d_all[k][e0:e1] for k in ("w_gate", "w_up", "w_down")}
+    shard_w["w_router"] = d_all["w_router"][e0:e1]
+    weights_s = moe.make_weights(shard_w)
+    offs_s = (offsets[e0:e1 + 1] - lo).contiguous()
+    y = torch.empty((T * K, w.d_e), dtype=layer.act, device=dev)
+    ws_s = torch.empty(moe.moe_workspace_size(desc_s), dtype=torch.uint8, device=dev)
+    row_idx, row_w = st[lo:hi], sw[lo:hi]
+
+    def ffn():
+        moe.moe_expert_ffn(desc_s, weights_s, d_all["x"], row_idx, offs_s, row_w, y, ws_s)
+
+    def timed(fn):
+        fn()
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return b.elapsed_time(e) / reps
+
+    ffn_ms = timed(ffn)
+    rows = hi - lo
+    fl = 6.0 * rows * w.d_e * w.d_ff
+    # this GPU's T/G tokens: routing + dispatch, shared experts + combine
+    wt = w.with_T(T // G)
+    lt = moe.Layer(wt, {**d_all, "x": d_all["x"][: T // G]}, device=dev)
+    idx_t, g_t = i32((wt.T, K)), torch.empty((wt.T, K), dtype=torch.float32, device=dev)
+    c_t, o_t, p_t, s_t, v_t = i32(E), i32(E + 1), i32(wt.T * K), i32(wt.T * K), i32(wt.T * K)
+    w_t = torch.empty(wt.T * K, dtype=torch.float32, device=dev)
+    y_t = torch.zeros((wt.T * K, w.d_e), dtype=layer.act, device=dev)
+    out_t = torch.empty((wt.T, w.d), dtype=layer.act, device=dev)
+
+    def route_dispatch():
+        moe.moe_route(lt.desc, lt.weights, lt.dev["x"], idx_t, g_t, ws=lt.ws)
+        moe.moe_dispatch(lt.desc, idx_t, g_t, None, c_t, o_t, p_t, s_t, v_t, w_t, None, lt.ws)
+
+    def combine():
+        moe.moe_combine(lt.desc, lt.weights, lt.dev["x"], y_t, v_t, out_t, lt.ws)
+
+    rd_ms = timed(route_dispatch)
+    cb_ms = timed(combine)
+    loads = counts.cpu().numpy()
+    per_gpu = [int(loads[k * E // G:(k + 1) * E // G].sum()) for k in range(G)]
+    rec = {"expert_shard": spec, "workload": workload, "experts": [e0, e1], "rows": rows,
+           "rows_per_gpu_min_max": [min(per_gpu), max(per_gpu)],
+           "expert_ffn_ms": round(ffn_ms, 4), "expert_ffn_tflops": round(fl / ffn_ms / 1e9, 1),
+           "route_dispatch_ms_tokens_of_this_gpu": round(rd_ms, 4),
+           "shared_and_combine_ms_tokens_of_this_gpu": round(cb_ms, 4),
+           "sum_ms_without_all_to_all": round(ffn_ms + rd_ms + cb_ms, 4),
+           "note": "one GPU's share of an expert-parallel layer; the two all-to-all exchanges "
+                   "(rows to the expert owners and back) are not measured"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +486,9 @@ def main():
                     help="only run the peak-rate microbenchmarks (MFMA issue, LDS reads)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MiB", default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--expert-shard", metavar="g/G", default=None,
+                    help="only time one GPU's share (experts g E/G .. (g+1) E/G) of an "
+                         "expert-parallel layer over G GPUs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
@@ -405,6 +499,9 @@ def main():
         return
     if args.peak:
         print(json.dumps({"peak_rates": peak_rates()}), flush=True)
+        return
+    if args.expert_shard:
+        expert_shard(args.expert_shard, args.workload)
         return
 
     import torch
