@@ -18,11 +18,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -69,12 +73,8 @@ template <> struct Chunk<bf16_t> {
     }
   }
   static __device__ __forceinline__ uint4 pack(const float *v) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]),
+                      f32x2_to_bf16x2(v[4], v[5]), f32x2_to_bf16x2(v[6], v[7]));
   }
 };
 

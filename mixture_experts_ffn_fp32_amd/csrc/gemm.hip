@@ -60,7 +60,11 @@ template <> struct Mfma<float> {
   }
 };
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware reciprocal (1 ulp) in place of an IEEE division:
+// the product is rounded to bf16 or kept in fp32 within the layer's tolerance
+__device__ __forceinline__ float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 template <typename T, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {

@@ -136,7 +136,11 @@ __device__ __forceinline__ v4s16 ds_read_tr16(const char *lds) {
 #endif
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware reciprocal (1 ulp) in place of an IEEE division:
+// the product is rounded to bf16 or kept in fp32 within the layer's tolerance
+__device__ __forceinline__ float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
@@ -585,7 +589,20 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   constexpr int PITCH = Sh::PITCH;
   float *stg = reinterpret_cast<float *>(g2_lds) + wave * 16 * PITCH;
   const int col0 = n_begin + (GLU ? wn * (WTN / 2) : wn * WTN);
-  constexpr int ITEMS = 16 * OUTW / 8;        // (row, 8-column) items per 16 rows
+  // each lane stores one 8-column chunk of rows r0, r0 + RSTEP, ... of a
+  // 16-row pass: its column (and column bound) is fixed, its output address
+  // steps one uniform row stride per item
+  constexpr int CPR8 = OUTW / 8;  // 8-column chunks per staged row
+  static_assert(64 % CPR8 == 0, "whole rows per 64 lanes");
+  constexpr int RSTEP = 64 / CPR8, NIT = (16 + RSTEP - 1) / RSTEP;
+  const int c8 = (lane % CPR8) * 8, r0 = lane / CPR8;
+  const int col = col0 + c8;
+  const bool col_ok = col < p.N;
+  const int rows32 = static_cast<int>(rows_in);
+  const bool f32o = EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32);
+  const int64_t esz = f32o ? 4 : 2;
+  char *const obytes = static_cast<char *>(p.out) + (obase + m_begin * p.ldo + col) * esz;
+  const int64_t rstride = p.ldo * esz;
   // 16 rows per pass: a 16 x 16 fragment row, or half of a 32 x 32 one
   // (its accumulator elements 8 q .. 8 q + 7 hold rows 16 q .. 16 q + 15)
   constexpr int PASSES = MF / 16;
@@ -605,25 +622,23 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
+    const int rel0 = frow(fm) + 16 * q + r0;  // tile row of item 0
 #pragma unroll
-    for (int it = 0; it < (ITEMS + 63) / 64; ++it) {
-      const int item = it * 64 + lane;
-      if (item >= ITEMS) break;
-      const int r = item / (OUTW / 8), c8 = (item % (OUTW / 8)) * 8;
-      const int64_t m = m_begin + frow(fm) + 16 * q + r;
-      const int col = col0 + c8;
-      if (m >= m_end || col >= p.N) continue;
+    for (int it = 0; it < NIT; ++it) {
+      const int r = r0 + it * RSTEP, rel = rel0 + it * RSTEP;
+      if ((RSTEP > 16 && r >= 16) || !col_ok || rel >= rows32) continue;
       float v[8];
       const float4 lo = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8);
       const float4 hi = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8 + 4);
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
       v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
       if (EPI == EPI_SCALE && p.row_scale) {
-        const float s = row_scale_lds[m - m_begin];
+        const float s = row_scale_lds[rel];
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] *= s;
       }
       if (EPI == EPI_COMBINE) {
+        const int64_t m = m_begin + rel;
         float rs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int k = 0; k < p.topk; ++k) {
           const int q = p.inv[m * p.topk + k];
@@ -638,13 +653,12 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += rs[e];
       }
-      if (EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32)) {
-        float *o = static_cast<float *>(p.out) + obase + m * p.ldo + col;
-        *reinterpret_cast<float4 *>(o) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4 *>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      char *const o = obytes + rel * rstride;
+      if (f32o) {
+        reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
       } else {
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + obase + m * p.ldo + col) =
-            Chunk<bf16_t>::pack(v);
+        *reinterpret_cast<uint4 *>(o) = Chunk<bf16_t>::pack(v);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0): reads done before rewrite
@@ -729,19 +743,17 @@ bool gemm2_applicable(const GemmArgs &a, int epi) {
 
 int gemm2_bm(int cfg) {
   switch (cfg) {
-    case TILE2_128x256: case TILE2_128x128: case TILE2_128x64: case TILE2_128x128_D4:
-    case TILE2_128x128_W8D4: case TILE2_128x256_W8: return 128;
-    case TILE2_64x128: case TILE2_64x128_D4: return 64;
-    case TILE2_32x256_D3: case TILE2_32x256_D2: return 32;
+    case TILE2_128x128: case TILE2_128x128_W8D4: return 128;
+    case TILE2_64x128: return 64;
+    case TILE2_32x256_D2: return 32;
   }
   return 256;
 }
 
 int gemm2_bn(int cfg) {
   switch (cfg) {
-    case TILE2_256x128: case TILE2_128x128: case TILE2_64x128: case TILE2_128x128_D4:
-    case TILE2_128x128_W8D4: case TILE2_256x128_W8D3: case TILE2_64x128_D4: return 128;
-    case TILE2_128x64: return 64;
+    case TILE2_128x128: case TILE2_64x128: case TILE2_128x128_W8D4: case TILE2_256x128_W8D3:
+      return 128;
   }
   return 256;
 }
@@ -796,18 +808,10 @@ hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, cons
   switch (cfg) {
     case TILE2_256x256: return dispatch2<256, 256, 2, 4>(a, b, epi, s);
     case TILE2_256x256_TALLW: return dispatch2<256, 256, 4, 2>(a, b, epi, s);
-    case TILE2_256x256_W4: return dispatch2<256, 256, 2, 2>(a, b, epi, s);
-    case TILE2_256x128: return dispatch2<256, 128, 2, 2>(a, b, epi, s);
-    case TILE2_128x256: return dispatch2<128, 256, 2, 2>(a, b, epi, s);
     case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, b, epi, s);
     case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, b, epi, s);
-    case TILE2_128x64: return dispatch2<128, 64, 2, 2>(a, b, epi, s);
-    case TILE2_128x128_D4: return dispatch2<128, 128, 2, 2, 4>(a, b, epi, s);
     case TILE2_128x128_W8D4: return dispatch2<128, 128, 4, 2, 4>(a, b, epi, s);
     case TILE2_256x128_W8D3: return dispatch2<256, 128, 4, 2, 3>(a, b, epi, s);
-    case TILE2_128x256_W8: return dispatch2<128, 256, 2, 4>(a, b, epi, s);
-    case TILE2_64x128_D4: return dispatch2<64, 128, 2, 2, 4>(a, b, epi, s);
-    case TILE2_32x256_D3: return dispatch2<32, 256, 1, 4, 3>(a, b, epi, s);
     case TILE2_32x256_D2: return dispatch2<32, 256, 1, 4, 2>(a, b, epi, s);
   }
   return hipErrorInvalidValue;

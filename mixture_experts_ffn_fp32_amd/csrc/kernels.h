@@ -186,17 +186,13 @@ hipError_t launch_gemm(const GemmArgs &a, int epi, int cfg, int act_bf16, hipStr
 
 // Pipelined bf16 GEMM (gemm2.hip): direct-to-LDS loads.
 // (256x256: 8 wavefronts as 2 x 4 of 128x64 blocks; _TALLW: 4 x 2 of 64x128;
-// _W4 and the others: 4 wavefronts, 2 x 2;
-// 128x128, 64x128 and 128x64 run 4 wavefronts (2 x 2) in at most 80 KB of LDS,
-// so two workgroups can share a CU.)
+// 128x128 and 64x128 run 4 wavefronts (2 x 2) in at most 80 KB of LDS, so
+// two workgroups can share a CU; _W8D4 / _W8D3: 8 wavefronts (4 x 2) with A
+// 4 / 3 stages ahead; 32x256: 4 wavefronts (1 x 4) streaming the weights for
+// few rows per expert.)
 enum Tile2Cfg {
-  TILE2_256x256 = 0, TILE2_256x128 = 1, TILE2_128x256 = 2, TILE2_256x256_W4 = 3,
-  TILE2_256x256_TALLW = 4, TILE2_128x128 = 5, TILE2_64x128 = 6, TILE2_128x64 = 7,
-  // deeper look-ahead (A NA stages ahead, B NA + 1) for tiles that leave LDS room:
-  TILE2_128x128_D4 = 8, TILE2_128x128_W8D4 = 9, TILE2_256x128_W8D3 = 10, TILE2_128x256_W8 = 11,
-  TILE2_64x128_D4 = 12,
-  // few rows per expert (weight streaming): 32 rows x 256 weight rows, 4 wavefronts
-  TILE2_32x256_D3 = 13, TILE2_32x256_D2 = 14
+  TILE2_256x256 = 0, TILE2_256x256_TALLW = 4, TILE2_128x128 = 5, TILE2_64x128 = 6,
+  TILE2_128x128_W8D4 = 9, TILE2_256x128_W8D3 = 10, TILE2_32x256_D2 = 14
 };
 bool gemm2_applicable(const GemmArgs &a, int epi);
 int gemm2_bm(int cfg);
