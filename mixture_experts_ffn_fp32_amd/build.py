@@ -23,20 +23,20 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj_dir: str = OBJ, defines=()) -> str:
+def _compile(src: str, obj_dir: str = OBJ) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, obj_dir: str = OBJ, defines=()) -> str:
-    """Compile and link libmoe.so; `defines` are extra -D macros (variant builds)."""
+def build(verbose: bool = False, out: str = LIB, obj_dir: str = OBJ) -> str:
+    """Compile and link libmoe.so (into `out`, objects under `obj_dir`)."""
     os.makedirs(obj_dir, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -57,9 +57,8 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef MOE_G2_GM
-#define MOE_G2_GM 4
-#endif
+// dense launches: m-tiles per tile group (the group runs over all n-tiles)
+constexpr int kGroupM = 4;
 
 // bytes of one operand row per stage (64 bf16)
 constexpr int kRowBytes = 128;
@@ -87,14 +86,8 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-#ifndef MOE_G2_SWZ
-#define MOE_G2_SWZ 0
-#endif
-#ifndef MOE_G2_ILV
-#define MOE_G2_ILV 1
-#endif
 // XOR key of a stage row's 16-byte chunks (rows of 8 chunks)
-__device__ __forceinline__ int swz_key(int r) { return MOE_G2_SWZ ? ((r >> 1) & 7) : (r & 7); }
+__device__ __forceinline__ int swz_key(int r) { return r & 7; }
 // physical 16-byte chunk of logical chunk c in row r
 __device__ __forceinline__ int sw8(int r, int c) { return r * 8 + (c ^ swz_key(r)); }
 
@@ -106,22 +99,10 @@ __device__ __forceinline__ int bkm_swz(int kr, int pairs) {
 }
 
 typedef short v4s16 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-#ifndef MOE_G2_MF
-#define MOE_G2_MF 16
-#endif
-template <int MF> struct AccOf;
-template <> struct AccOf<16> { typedef f32x4 T; static constexpr int N = 4; };
-template <> struct AccOf<32> { typedef f32x16 T; static constexpr int N = 16; };
-
-// row (within a fragment) of accumulator element i of lane `lane`:
-// 16 x 16: lane (fr, fc) holds rows 4 fc + i of column fr; 32 x 32: lane
-// (c = lane % 32, h = lane / 32) holds rows 8 (i / 4) + 4 h + i % 4 of column c
-template <int MF>
-__device__ __forceinline__ int acc_row(int lane, int i) {
-  return MF == 16 ? 4 * (lane >> 4) + i : 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-}
+// row (within a 16 x 16 fragment) of accumulator element i of lane `lane`:
+// lane (fr, fc) holds rows 4 fc + i of column fr
+__device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4) + i; }
 
 // ds_read_b64_tr_b16: within each 16 lanes, lane l receives element l % 4 of
 // the 8-byte pieces lanes 4 e + l / 4 point at, e = 0..3 (a 4 x 4 transpose
@@ -173,11 +154,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   static_assert(NA >= 2, "at least double-buffered");
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  // fragment edge: 32 x 32 (v_mfma_f32_32x32x16_bf16) where the wavefront
-  // tile holds whole 32 x 32 fragments (K-major B reads 16 x 16 fragments)
-  constexpr int MF = (MOE_G2_MF == 32 && !BKM && WTM % 32 == 0 &&
-                      WTN % (EPI == EPI_SWIGLU ? 64 : 32) == 0) ? 32 : 16;
-  using Acc = typename AccOf<MF>::T;
+  constexpr int MF = 16;  // fragment edge (v_mfma_f32_16x16x32_bf16)
   constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr bool GLU = EPI == EPI_SWIGLU;
   constexpr int NOUT = GLU ? BN / 2 : BN;
@@ -247,7 +224,7 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // owns tiles [first n_tn, (first + g) n_tn), so pid / n_tn is one of its
   // m-tiles) or GM consecutive ones (dense); inside a group the m-tile
   // index runs fastest
-  constexpr int GM = MOE_G2_GM;
+  constexpr int GM = kGroupM;
   int64_t first_m;
   int gsz;
   if (p.tiles) {
@@ -394,43 +371,24 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   // interleaved over the wavefront rows (fm WGM + wm), so that a tile with
   // fewer rows than BM spreads its MFMAs over all four SIMDs (two wavefront
   // rows share a SIMD) instead of leaving the SIMDs of the last rows idle
-  auto frow = [&](int fm) { return MOE_G2_ILV ? (fm * WGM + wm) * MF : wm * WTM + fm * MF; };
+  auto frow = [&](int fm) { return (fm * WGM + wm) * MF; };
   const int64_t rows_in = m_end - m_begin;
-  int fm_live;
-  if (MOE_G2_ILV) {
-    const int64_t n_frag = (rows_in + MF - 1) / MF;  // fragment rows holding tile rows
-    fm_live = static_cast<int>(min<int64_t>(FM, max<int64_t>(0, (n_frag - wm + WGM - 1) / WGM)));
-  } else {
-    const int64_t rows_left = rows_in - wm * WTM;
-    fm_live = rows_left <= 0 ? 0 : (rows_left >= WTM ? FM : static_cast<int>((rows_left + MF - 1) / MF));
-  }
-  const int live = __builtin_amdgcn_readfirstlane(fm_live);
+  const int64_t n_frag = (rows_in + MF - 1) / MF;  // fragment rows holding tile rows
+  const int live = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(min<int64_t>(FM, max<int64_t>(0, (n_frag - wm + WGM - 1) / WGM))));
 
-  Acc acc[FM][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < AccOf<MF>::N; ++e) acc[i][j][e] = 0.f;
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 *const abuf = g2_lds;             // A: NA x A16
   u32x4 *const bbuf = g2_lds + NA * A16;  // B: NB x B16
-  // per 32-k step a 16 x 16 fragment takes one 16-byte read per lane (lane
-  // (fr, fc): row fr, 8 k at 8 fc); a 32 x 32 fragment two, one per 16-k half
-  // (lane (c, h): row c, 8 k at 16 kk + 8 h)
-  constexpr int KK = MF == 32 ? 2 : 1;
-  bf16x8 xa0[FM * KK], xb0[FN * KK], xa1[FM * KK], xb1[FN * KK];
+  // per 32-k step a fragment takes one 16-byte read per lane (lane (fr, fc):
+  // row fr, 8 k at 8 fc)
+  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
   auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
-    if constexpr (MF == 32) {
-      const int r = lane & 31, kk = i & 1, f = i >> 1;
-      const int kc = 4 * ks + 2 * kk + (lane >> 5);
-      if (f < FN)
-        xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(f) + r, kc)]);
-      else
-        xa[i - 2 * FN] = __builtin_bit_cast(bf16x8, ab[sw8(frow(f - FN) + r, kc)]);
-      return;
-    }
     const int kc = 4 * ks + fc;
     if (i < FN) {
       if constexpr (BKM) {
@@ -456,20 +414,11 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(frow(i - FN) + fr, kc)]);
   };
   auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
-    if constexpr (MF == 32) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[2 * fm + kk], xb[2 * fn + kk],
-                                                                acc[fm][fn], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
-    }
+    for (int fn = 0; fn < FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
   };
-  constexpr int NRD = (FM + FN) * KK;                  // fragment reads per set
+  constexpr int NRD = FM + FN;                         // fragment reads per set
   constexpr int RD_PER = (NRD + FM - 1) / FM;          // ... per MFMA row
   constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;  // loads per MFMA row
 
@@ -575,8 +524,8 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
       for (int fn = 0; fn < FN; ++fn) {
         const int col = n_begin + wn * WTN + fn * MF + (lane % MF);
 #pragma unroll
-        for (int i = 0; i < AccOf<MF>::N; ++i) {
-          const int64_t m = m_begin + frow(fm) + acc_row<MF>(lane, i);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m_begin + frow(fm) + acc_row(lane, i);
           if (m < m_end && col < p.N) o[m * p.ldo + col] = acc[fm][fn][i];
         }
       }
@@ -603,26 +552,21 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   const int64_t esz = f32o ? 4 : 2;
   char *const obytes = static_cast<char *>(p.out) + (obase + m_begin * p.ldo + col) * esz;
   const int64_t rstride = p.ldo * esz;
-  // 16 rows per pass: a 16 x 16 fragment row, or half of a 32 x 32 one
-  // (its accumulator elements 8 q .. 8 q + 7 hold rows 16 q .. 16 q + 15)
-  constexpr int PASSES = MF / 16;
+  // one pass per fragment row (16 rows)
 #pragma unroll
-  for (int fq = 0; fq < FM * PASSES; ++fq) {
-    const int fm = fq / PASSES, q = fq % PASSES;
+  for (int fm = 0; fm < FM; ++fm) {
     if (fm >= live) break;  // unrolled: acc is indexed statically and stays in registers
 #pragma unroll
     for (int fo = 0; fo < FO; ++fo)
 #pragma unroll
-      for (int i = 0; i < 4 * (MF / 16); ++i) {
-        const int e = 8 * q * (MF / 32) + i;  // accumulator element (MF 32: 8 per pass)
-        if (MF == 32 && i >= 8) break;
-        float v = acc[fm][fo][e];
-        if (GLU) v = silu_f(v) * acc[fm][fo + FO][e];
-        stg[(acc_row<MF>(lane, e) - 16 * q) * PITCH + fo * MF + (lane % MF)] = v;
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[fm][fo][i];
+        if (GLU) v = silu_f(v) * acc[fm][fo + FO][i];
+        stg[acc_row(lane, i) * PITCH + fo * MF + (lane % MF)] = v;
       }
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
-    const int rel0 = frow(fm) + 16 * q + r0;  // tile row of item 0
+    const int rel0 = frow(fm) + r0;  // tile row of item 0
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int r = r0 + it * RSTEP, rel = rel0 + it * RSTEP;
