@@ -73,11 +73,29 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 // 16-byte direct-to-LDS load: lane i's data lands at lds + 16 i (lds is
 // wave-uniform). (Device-pass only: the host pass does not know the builtin.)
+//
+// UNTRACKED: the same load issued from inline asm, which the compiler does
+// not see as an LDS write. It cannot tell the transposing LDS reads
+// (ds_read_b64_tr_b16) from the loads' destinations, and before each such
+// read it would wait for every load in flight (vmcnt(0)), which undoes the
+// stage pipeline; the kernel's own vmcnt waits cover these loads as they do
+// the builtin's. Wait states: s_nop 4 in case a VALU instruction has just
+// written an SGPR the load reads (5 needed), s_nop 0 after writing M0 (1).
+template <bool UNTRACKED = false>
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, u32x4 *lds, uint32_t voff,
                                            int soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                           voff, soff, 0, 0);
+  if constexpr (UNTRACKED) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void *)lds)));
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "m0");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             voff, soff, 0, 0);
+  }
 #endif
 }
 
@@ -343,17 +361,17 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     return __builtin_amdgcn_readfirstlane((st >= steps1 ? st - steps1 : st) * kRowBytes);
   };
   auto load_a = [&](u32x4 *ab, int st, int j) {
-    load_lds16(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j], kbytes(st));
+    load_lds16<BKM>(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j], kbytes(st));
   };
   auto load_b = [&](u32x4 *bb, int st, int j) {
     if constexpr (BKM) {
       const int sl = st >= steps1 ? st - steps1 : st;
-      load_lds16(br0, bb + (NW * j + wave) * 64, bkoff[j],
+      load_lds16<BKM>(br0, bb + (NW * j + wave) * 64, bkoff[j],
                  __builtin_amdgcn_readfirstlane(sl * bkstage));
       return;
     }
     const bool up = GLU && j >= B_LD / 2;  // gate rows first, then up rows
-    load_lds16(up ? br1 : br0, bb + (ROWS * j + 8 * wave) * 8,
+    load_lds16<BKM>(up ? br1 : br0, bb + (ROWS * j + 8 * wave) * 8,
                boff0 + (up ? j - B_LD / 2 : j) * bstep, kbytes(st));
   };
 
