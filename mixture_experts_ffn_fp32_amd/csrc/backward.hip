@@ -37,12 +37,18 @@ __global__ __launch_bounds__(256) void fill0_kernel(uint4 *p, int64_t n16) {
 // LDS with 16-byte global accesses on both sides: tile row i holds 64
 // consecutive columns of one source row; a destination row takes EPC tile
 // rows of one column per 16-byte chunk. Widths and offsets are multiples of
-// 8 elements.
+// 8 elements. The 16-byte chunks of row r sit XOR-swizzled by (r / EPC) so
+// that a wavefront's column reads (EPC-row groups x a few columns) fall in
+// distinct LDS banks, as its row writes do.
 template <typename E>
 struct TileOf {
   static constexpr int EPC = 16 / static_cast<int>(sizeof(E));  // elements per chunk
   static constexpr int CPR = 64 / EPC;                           // chunks per tile row
-  static constexpr int P = 64 + EPC;                             // pitch: rows stay 16-byte aligned
+  static constexpr int P = 64;                                   // pitch (elements)
+  // element offset in row r of logical column c
+  static __device__ __forceinline__ int col(int r, int c) {
+    return (((c / EPC) ^ ((r / EPC) & (CPR - 1))) * EPC) + c % EPC;
+  }
 };
 template <typename E> struct ChunkT;
 template <> struct ChunkT<uint16_t> { using C = Chunk<bf16_t>; };
@@ -61,7 +67,7 @@ __device__ __forceinline__ void tile_store_cols(const E (*tile)[TileOf<E>::P], i
       E e[EPC];
     } u;
 #pragma unroll
-    for (int j = 0; j < EPC; ++j) u.e[j] = tile[EPC * qc + j][c];
+    for (int j = 0; j < EPC; ++j) u.e[j] = tile[EPC * qc + j][TileOf<E>::col(EPC * qc + j, c)];
     *reinterpret_cast<uint4 *>(dst + (c0 + c) * dst_ld + q0 + EPC * qc) = u.v;
   }
 }
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *src, int64_t R,
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int r = i / CPR, cc = i % CPR;
     if (r0 + r < R && c0 + EPC * cc < C)
-      *reinterpret_cast<uint4 *>(&tile[r][EPC * cc]) =
+      *reinterpret_cast<uint4 *>(&tile[r][TileOf<E>::col(r, EPC * cc)]) =
           *reinterpret_cast<const uint4 *>(s + (r0 + r) * C + c0 + EPC * cc);
   }
   __syncthreads();
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(256) void cols_kernel(const E *src, int64_t ld_src,
         v = CK::pack(f);
       }
     }
-    *reinterpret_cast<uint4 *>(&tile[qi][EPC * cc]) = v;
+    *reinterpret_cast<uint4 *>(&tile[qi][TileOf<E>::col(qi, EPC * cc)]) = v;
   }
   __syncthreads();
   tile_store_cols<E>(tile, c0, C, q0, qend, dst, ldd);
