@@ -533,19 +533,35 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     // fp32 out straight from the accumulators: lane (fr, fc) holds rows
     // 4 fc + i, column fr of each 16x16 fragment, so each store writes four
     // 64-byte row pieces (measured 1-2% faster on the backward's fp32
-    // products than staging through LDS)
-    float *o = static_cast<float *>(p.out) + obase;
+    // products than staging through LDS). One row address per (fragment
+    // row, i); the fragments of a row are immediate offsets from it. Tiles
+    // wholly inside the output store without per-element checks.
+    const int64_t ldo = p.ldo;
+    const int col_l = wn * WTN + (lane % MF);  // this lane's column within the tile
+    float *const o_l = static_cast<float *>(p.out) + obase + (m_begin + acc_row(lane, 0)) * ldo +
+                       n_begin + col_l;
+    if (rows_in >= BM && n_begin + BN <= p.N) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float *const orow = o_l + static_cast<int64_t>(frow(fm) + i) * ldo;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) orow[fn * MF] = acc[fm][fn][i];
+        }
+      return;
+    }
+    const int rows32 = static_cast<int>(rows_in), cols_in = p.N - n_begin - col_l;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (fm >= live) break;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = n_begin + wn * WTN + fn * MF + (lane % MF);
+      for (int i = 0; i < 4; ++i) {
+        if (frow(fm) + acc_row(lane, i) >= rows32) continue;
+        float *const orow = o_l + static_cast<int64_t>(frow(fm) + i) * ldo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m_begin + frow(fm) + acc_row(lane, i);
-          if (m < m_end && col < p.N) o[m * p.ldo + col] = acc[fm][fn][i];
-        }
+        for (int fn = 0; fn < FN; ++fn)
+          if (fn * MF < cols_in) orow[fn * MF] = acc[fm][fn][i];
       }
     }
     return;
