@@ -48,6 +48,8 @@
 //
 // K must be a multiple of 32 (the first of two K segments, of 64); the host
 // uses gemm.hip otherwise.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -601,44 +603,60 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     const int rel0 = frow(fm) + r0;  // tile row of item 0
+    // the pass's LDS reads all go out first (a row past the 16 staged ones
+    // reads row 15 and is never stored), then the items are scaled,
+    // converted and stored (the row weights are 1 where none are given, so
+    // the scaling needs no branch)
+    float v[NIT][8], sc[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = r0 + it * RSTEP, rel = rel0 + it * RSTEP;
-      if ((RSTEP > 16 && r >= 16) || !col_ok || rel >= rows32) continue;
-      float v[8];
+      const int r = min(r0 + it * RSTEP, 15);
       const float4 lo = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8);
       const float4 hi = *reinterpret_cast<const float4 *>(stg + r * PITCH + c8 + 4);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      if (EPI == EPI_SCALE && p.row_scale) {
-        const float s = row_scale_lds[rel];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] *= s;
-      }
-      if (EPI == EPI_COMBINE) {
-        const int64_t m = m_begin + rel;
-        float rs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < p.topk; ++k) {
-          const int q = p.inv[m * p.topk + k];
-          if (q < 0) continue;
-          float y[8];
-          Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4 *>(
-                                    static_cast<const uint16_t *>(p.y) + static_cast<int64_t>(q) * p.ldy + col),
-                                y);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rs[e] += y[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += rs[e];
-      }
-      char *const o = obytes + rel * rstride;
-      if (f32o) {
-        reinterpret_cast<float4 *>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4 *>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        *reinterpret_cast<uint4 *>(o) = Chunk<bf16_t>::pack(v);
-      }
+      v[it][0] = lo.x; v[it][1] = lo.y; v[it][2] = lo.z; v[it][3] = lo.w;
+      v[it][4] = hi.x; v[it][5] = hi.y; v[it][6] = hi.z; v[it][7] = hi.w;
+      sc[it] = EPI == EPI_SCALE ? row_scale_lds[min(rel0 + it * RSTEP, BM - 1)] : 1.f;
     }
+    auto store_items = [&](auto f32_c) {
+      constexpr bool F32 = decltype(f32_c)::value;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int r = r0 + it * RSTEP, rel = rel0 + it * RSTEP;
+        if ((RSTEP > 16 && r >= 16) || !col_ok || rel >= rows32) continue;
+        float *const w = v[it];
+        if (EPI == EPI_SCALE) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) w[q] *= sc[it];
+        }
+        if (EPI == EPI_COMBINE) {
+          const int64_t m = m_begin + rel;
+          float rs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          for (int k = 0; k < p.topk; ++k) {
+            const int q = p.inv[m * p.topk + k];
+            if (q < 0) continue;
+            float y[8];
+            Chunk<bf16_t>::unpack(*reinterpret_cast<const uint4 *>(
+                                      static_cast<const uint16_t *>(p.y) + static_cast<int64_t>(q) * p.ldy + col),
+                                  y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rs[e] += y[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] += rs[e];
+        }
+        char *const o = obytes + rel * rstride;
+        if constexpr (F32) {
+          reinterpret_cast<float4 *>(o)[0] = make_float4(w[0], w[1], w[2], w[3]);
+          reinterpret_cast<float4 *>(o)[1] = make_float4(w[4], w[5], w[6], w[7]);
+        } else {
+          *reinterpret_cast<uint4 *>(o) = Chunk<bf16_t>::pack(w);
+        }
+      }
+    };
+    if (f32o)
+      store_items(std::true_type{});
+    else
+      store_items(std::false_type{});
     __builtin_amdgcn_s_waitcnt(0xC07F & ~0x0F00);  // lgkmcnt(0): reads done before rewrite
     asm volatile("" ::: "memory");
   }
