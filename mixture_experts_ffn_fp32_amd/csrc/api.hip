@@ -458,14 +458,14 @@ int merged_gemms(const moe_desc *d, const moe_weights *w, const void *x, const v
 // Which backward products read the weights in place, K-major on the
 // pipelined kernel (bf16), instead of transposed copies: dh (W_down and the
 // shared W_down), dX (W_gate and W_up as two K segments: d_ff and d_shared
-// multiples of 64) and the latent projections. The transposing LDS reads
-// (two 8-byte reads per fragment where the row-major operand takes one
-// 16-byte read) make those GEMMs ~1.5x slower per stage, so in place pays
-// only where the copies cost more: layers that stream their weights (64 rows
-// per expert or fewer), and, for the expert weights, large experts
-// (d_e x d_ff >= 2^23) with 512 rows per expert or fewer (measured: the
-// large prefill layer 61.0 -> 58.7 ms; the medium and latent layers slower).
-// The shapes restate the products moe_backward runs.
+// multiples of 64) and the latent projections. The expert weights are read
+// in place wherever the kernel applies: with its stage loads out of the
+// compiler's LDS tracking, the transposing reads cost little per stage and
+// the copies cost more on every layer measured (medium 5.96 -> 5.62 ms,
+// latent 3.93 -> 3.82, small 0.384 -> 0.377, large prefill level); the
+// latent projections only when the layer streams its weights (64 rows per
+// expert or fewer; elsewhere level). The shapes restate the products
+// moe_backward runs.
 struct KmajorUse {
   bool dh, dx, lat;
 };
@@ -476,7 +476,6 @@ KmajorUse kmajor_use(const moe_desc *d) {
   const int dm = d->d_model, f = d->d_ff, ds = d->d_shared, Lt = d->latent;
   const int de = Lt ? Lt : dm;
   const bool stream = rows <= 64 * E;
-  const bool experts = stream || (rows <= 512 * E && static_cast<int64_t>(de) * f >= (1 << 23));
   auto prod = [](int64_t M, int64_t a_extent, int64_t lda, int K, int N, int64_t ldb) {
     GemmArgs g{};
     g.M = M;
@@ -498,8 +497,8 @@ KmajorUse kmajor_use(const moe_desc *d) {
     return g;
   };
   auto ok = [](const GemmArgs &g) { return gemm2_applicable(g, EPI_STORE_F32); };
-  u.dh = experts && ok(prod(rows, T, de, de, f, f)) && (!ds || ok(prod(T, T, dm, dm, ds, ds)));
-  u.dx = experts && f % 64 == 0 && ds % 64 == 0 &&
+  u.dh = ok(prod(rows, T, de, de, f, f)) && (!ds || ok(prod(T, T, dm, dm, ds, ds)));
+  u.dx = f % 64 == 0 && ds % 64 == 0 &&
          ok(second(prod(rows, rows, 2 * f, f, de, de), 2 * f, f, de)) &&
          (!ds || ok(second(prod(T, T, 2 * ds, ds, dm, dm), 2 * ds, ds, dm)));
   u.lat = Lt && stream && ok(prod(T, T, dm, dm, Lt, Lt)) && ok(prod(T, T, Lt, Lt, dm, dm));
