@@ -31,6 +31,10 @@
  *  - Return value: MOE_OK, or a negative moe_status. Arguments are checked
  *    on the host before anything is launched; a failed check launches
  *    nothing. MOE_ERR_HIP reports a launch failure.
+ *  - Device arrays of activations, weights, routed rows, outputs, gradients
+ *    and workspaces must be 16-byte aligned (the kernels move 16-byte
+ *    chunks; torch's allocations are); index and count arrays need only
+ *    their element's alignment.
  *  - T = 0 is valid and launches nothing. Experts that receive no tokens
  *    cost nothing (APEX-1 docs "10 - Mixture of Experts", BUG-08: an expert
  *    may get 0, 1 or many tokens).
@@ -59,8 +63,9 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL = -1,      /* a required pointer is NULL                      */
   MOE_ERR_SHAPE = -2,     /* T < 0, a width <= 0 or not a multiple of 8,
-                             K < 1, K > E, K > 16, E > 1024, or a size that
-                             overflows the 32-bit row indices               */
+                             K < 1, K > E, K > 16, E > 1024, a size that
+                             overflows the 32-bit row indices, or a device
+                             array that is not 16-byte aligned            */
   MOE_ERR_MODE = -3,      /* unknown dtype / route mode, or a mode
                              combination this layer does not define         */
   MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_workspace_size()     */

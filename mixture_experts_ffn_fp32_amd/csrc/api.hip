@@ -4,6 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "kernels.h"
@@ -605,6 +606,19 @@ int check_backward(const moe_desc *d) {
   return MOE_OK;
 }
 
+// Device arrays the kernels move in 16-byte chunks (activations, weights,
+// routed rows, outputs, gradients, workspaces) must be 16-byte aligned, as
+// torch's allocations are. NULL passes (presence is checked separately).
+bool aligned16(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
+bool weights_aligned(const moe_weights *w) {
+  return aligned16({w->w_router, w->bias, w->rms_gamma, w->w_gate, w->w_up, w->w_down,
+                    w->ws_gate, w->ws_up, w->ws_down, w->w_lat_down, w->w_lat_up});
+}
+
 int check_expert_weights(const moe_desc *d, const moe_weights *w) {
   if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
   return MOE_OK;
@@ -656,6 +670,7 @@ int moe_route(const moe_desc *d, const moe_weights *w, const void *x, int32_t *i
   int rc = check_desc(d);
   if (rc) return rc;
   if (!w || !w->w_router || !idx || !g || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  if (!aligned16({x, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   RouterArgs a{};
@@ -687,6 +702,7 @@ int moe_quantile_balance(const moe_desc *d, const moe_weights *w, const void *x,
   if (d->route_mode != MOE_ROUTE_SIGMOID_BIAS) return MOE_ERR_MODE;
   if (d->top_k >= d->n_experts) return MOE_ERR_SHAPE;
   if (!w || !w->w_router || !new_bias || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  if (!aligned16({x, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -721,6 +737,7 @@ int moe_router_losses(const moe_desc *d, const moe_weights *w, const void *x,
   int rc = check_desc(d);
   if (rc) return rc;
   if (!w || !w->w_router || !counts || !losses || !ws || (!x && d->T > 0)) return MOE_ERR_NULL;
+  if (!aligned16({x, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   if (!(alpha == alpha) || alpha > 3.4e38f || alpha < -3.4e38f || !(z_weight == z_weight) ||
       z_weight > 3.4e38f || z_weight < -3.4e38f)
     return MOE_ERR_MODE;
@@ -752,6 +769,7 @@ int moe_dispatch(const moe_desc *d, const int32_t *idx, const float *g, const vo
   if (rc) return rc;
   if (!counts || !offsets || !perm || !sorted_token || !inv || !ws) return MOE_ERR_NULL;
   if ((!idx && d->T > 0) || (sorted_w && !g) || (rows_sorted && !rows)) return MOE_ERR_NULL;
+  if (!aligned16({rows, rows_sorted, ws})) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -800,6 +818,7 @@ int moe_expert_ffn(const moe_desc *d, const moe_weights *w, const void *rows,
   if (rc) return rc;
   if ((rc = check_expert_weights(d, w))) return rc;
   if (!offsets || !y_sorted || !ws || (!rows && d->T > 0)) return MOE_ERR_NULL;
+  if (!aligned16({rows, y_sorted, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -823,6 +842,7 @@ int moe_combine(const moe_desc *d, const moe_weights *w, const void *x, const vo
   if ((rc = check_combine_weights(d, w))) return rc;
   if (d->T > 0 && (!y_sorted || !inv || !out || (d->d_shared && !x))) return MOE_ERR_NULL;
   if (!ws) return MOE_ERR_NULL;
+  if (!aligned16({x, y_sorted, out, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;
@@ -915,6 +935,7 @@ int moe_forward_noalloc(const moe_desc *d, const moe_weights *w, const void *x, 
   if (rc) return rc;
   if (layout_of(d).total > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
   if (!w || !w->w_router || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  if (!aligned16({x, out}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   void *ws = nullptr;
   if ((rc = scratch_of(static_cast<hipStream_t>(stream), &ws))) return rc;
   return forward_impl(d, w, x, out, counts, n_near_ties, ws, MOE_SCRATCH_BYTES, nullptr, stream);
@@ -933,6 +954,7 @@ int forward_impl(const moe_desc *d, const moe_weights *w, const void *x, void *o
   if ((rc = check_expert_weights(d, w)) || (rc = check_combine_weights(d, w))) return rc;
   if (d->latent && !w->w_lat_down) return MOE_ERR_NULL;
   if (!ws || (d->T > 0 && (!x || !out))) return MOE_ERR_NULL;
+  if (!aligned16({x, out, ws}) || !weights_aligned(w)) return MOE_ERR_SHAPE;
   const Layout L = layout_of(d);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1090,6 +1112,10 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
   if ((rc = check_expert_weights(d, w)) || (rc = check_combine_weights(d, w))) return rc;
   if (d->latent && !w->w_lat_down) return MOE_ERR_NULL;
   if (!ws || (d->T > 0 && (!x || !d_out))) return MOE_ERR_NULL;
+  if (!aligned16({x, d_out, d_x, ws, gr->w_router, gr->w_gate, gr->w_up, gr->w_down, gr->ws_gate,
+                  gr->ws_up, gr->ws_down, gr->w_lat_down, gr->w_lat_up, gr->rms_gamma}) ||
+      !weights_aligned(w))
+    return MOE_ERR_SHAPE;
   const BwdLayout B = bwd_layout_of(d);
   if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
   if (d->T == 0) return MOE_OK;

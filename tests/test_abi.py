@@ -93,6 +93,30 @@ def test_null_pointers_rejected_before_launch():
     assert rc == -1
 
 
+def test_misaligned_arrays_rejected_before_launch():
+    """Activations, weights, outputs, gradients and workspaces must be 16-byte
+    aligned; a misaligned one is a shape error found on the host (the fake
+    addresses are never dereferenced)."""
+    d = _desc(T=16)
+    a, bad = 1 << 20, (1 << 20) + 8
+    w = moe.MoeWeights(w_router=a, w_gate=a, w_up=a, w_down=a, ws_gate=a, ws_up=a, ws_down=a)
+    big = 1 << 40
+    rc = moe.lib().moe_route(C.byref(d), C.byref(w), bad, a, a, None, None, a, big, None)
+    assert rc == -2
+    rc = moe.lib().moe_forward(C.byref(d), C.byref(w), a, bad, None, None, a, big, None, None)
+    assert rc == -2
+    w_bad = moe.MoeWeights(w_router=a, w_gate=a, w_up=bad, w_down=a, ws_gate=a, ws_up=a,
+                           ws_down=a)
+    rc = moe.lib().moe_forward(C.byref(d), C.byref(w_bad), a, a, None, None, a, big, None, None)
+    assert rc == -2
+    g = moe.MoeGrads(w_gate=bad)
+    rc = moe.lib().moe_backward(C.byref(d), C.byref(w), a, a, a, C.byref(g), a, big, None)
+    assert rc == -2
+    # aligned: past these checks, to the workspace size check
+    rc = moe.lib().moe_route(C.byref(d), C.byref(w), a, a, a, None, None, a, 16, None)
+    assert rc == -4
+
+
 def test_workspace_too_small_rejected():
     d = _desc(T=16)
     fake = 1 << 20  # never dereferenced: the size check fails first
