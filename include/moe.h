@@ -188,6 +188,10 @@ typedef struct moe_plan_info {
                                      products, bit 1 the input gradient
                                      (W_gate, W_up), bit 2 the latent
                                      projections                           */
+  int32_t persistent;             /* grouped GEMMs on the persistent kernel
+                                     (one workgroup per CU over a fixed list
+                                     of 256x256 tiles): bit 0 gate/up, bit 1
+                                     down                                  */
 } moe_plan_info;
 
 /* Text of a status code (static storage). */

@@ -49,7 +49,7 @@ class MoePlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "merged_shared", "gate_up_pipelined", "gate_up_tile_m", "gate_up_tile_n",
         "down_pipelined", "down_tile_m", "down_tile_n", "router_per_token",
-        "dispatch_one_workgroup", "backward_in_place")]
+        "dispatch_one_workgroup", "backward_in_place", "persistent")]
 
 
 class MoeGrads(C.Structure):

@@ -1513,6 +1513,25 @@ int moe_plan(const moe_desc *d, moe_plan_info *info) {
   info->dispatch_one_workgroup = dispatch_fused_ok(d->T * d->top_k, d->n_experts) ? 1 : 0;
   const KmajorUse ku = kmajor_use(d);
   info->backward_in_place = (ku.dh ? 1 : 0) | (ku.dx ? 2 : 0) | (ku.lat ? 4 : 0);
+  // the grouped launches as expert_gemms makes them (a second, dense problem
+  // when the shared experts are merged in)
+  if (pl.gu.v2 && pl.dn.v2) {
+    const int64_t rows_n = d->T * d->top_k;
+    const int de = d->latent ? d->latent : d->d_model;
+    static const int32_t kTable = 0;  // (only its presence matters here)
+    GemmArgs a{}, b{}, sec{};
+    a.tiles = b.tiles = &kTable;
+    a.K = de;
+    a.N = d->d_ff;
+    a.ldo = d->d_ff;
+    a.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.gu.bm());
+    b.K = d->d_ff;
+    b.N = b.ldo = de;
+    b.max_mtiles = grouped_tile_bound(rows_n, d->n_experts, pl.dn.bm());
+    sec.N = pl.merged ? 1 : 0;
+    info->persistent = (gemm2_persistent(a, EPI_SWIGLU, pl.gu.cfg, &sec) ? 1 : 0) |
+                       (gemm2_persistent(b, EPI_SCALE, pl.dn.cfg, &sec) ? 2 : 0);
+  }
   return MOE_OK;
 }
 

@@ -48,6 +48,8 @@
 //
 // K must be a multiple of 32 (the first of two K segments, of 64); the host
 // uses gemm.hip otherwise.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -662,6 +664,392 @@ void gemm2_kernel(GemmArgs p0, GemmArgs p1) {
   }
 }
 
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Value of lane 16 (l / 16) + I for each lane l (within each 16-lane row:
+// its lane I), by a bit-mode swizzle (source lane (l & 16) | I of each 32).
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x10 | (I << 5)));
+}
+
+// ------------------------------------------------------------------ persistent
+// Persistent form of the 256x256 tile (4 x 2 wavefronts of 64x128, A two
+// stages ahead) for one problem with a fixed reduction (no second K segment,
+// no K grouping or split) and an epilogue that writes from the accumulators:
+// SwiGLU, row scale, fp32 store. Each workgroup runs a fixed list of tiles:
+// the tiles are dealt over the XCDs in contiguous ranges as in gemm2_kernel,
+// and workgroup w of an XCD takes tiles w, w + G, w + 2 G, ... of its range
+// (G workgroups per XCD), so that at any time an XCD works on G consecutive
+// tiles and tiles sharing operands still meet in L2.
+//
+// The stage pipeline runs on across tiles: the loads a tile's last stages
+// would spend on repeats of its last stage fetch the next tile's first
+// stages instead (B from three stages before the end, A from two), and the
+// fragment reads at the end of a tile's last stage are the next tile's
+// first. The epilogue then needs no LDS (every stage buffer holds the next
+// tile's data): B rows are loaded in an order that gives each lane a run of
+// adjacent output columns, RUN = 8 (4 for SwiGLU, whose gate and up
+// fragments pair up), so it stores straight from its accumulators, one
+// 16-byte (8-byte) piece per row. The next tile is decoded during the first
+// stages of the current one (tile table reads two stages apart, so their
+// latency overlaps MFMAs), its A row gather is requested a stage later and
+// consumed one stage before its first A load. The epilogue's stores are
+// waited for by the next tile's first stage wait.
+//
+// Lane (fr, fc) holds rows 4 fc + i of column fr of each 16 x 16 fragment.
+// Stage buffer row R of B holds, within each 128-row block (64 for each of
+// SwiGLU's gate and up halves) of fragments f = (R % 128) / 16, lanes
+// fr = R % 16, the weight row of output column RUN fr + f of the block.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
+  constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2, NA = 2, NB = NA + 1;
+  constexpr int NW = WGM * WGN, THREADS = 64 * NW;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MF = 16, FM = WTM / MF, FN = WTN / MF;
+  constexpr bool GLU = EPI == EPI_SWIGLU;
+  constexpr int NOUT = GLU ? BN / 2 : BN;
+  constexpr int ROWS = THREADS / 8, A_LD = BM / ROWS, B_LD = BN / ROWS;
+  constexpr int A16 = BM * 8, B16 = BN * 8;
+  constexpr int RUN = GLU ? FN / 2 : FN;  // adjacent output columns per lane
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_SCALE || EPI == EPI_STORE_F32,
+                "epilogues that store from the accumulators");
+  static_assert(A_LD == 4 && B_LD == 4 && FM == 4 && FN == 8, "tile geometry");
+  __shared__ __attribute__((aligned(1024))) u32x4 g2p_lds[(NA * BM + NB * BN) * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar arithmetic)
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int fr = lane & 15, fc = lane >> 4;
+
+  // ------------------------------------------------------------ tile list
+  // (tile counts, rows and columns fit 32 bits: the host bounds the
+  // operands' byte extents below 4 GiB)
+  const int n_tn = (p.N + NOUT - 1) / NOUT;
+  const int n_m = p.tiles ? *p.n_tiles : static_cast<int>(p.max_mtiles);
+  const int total = n_m * n_tn, per = (total + 7) / 8;
+  const int xcd = blockIdx.x & 7, gstride = gridDim.x >> 3;
+  const int t_end = min(total, (xcd + 1) * per);
+  int pid = xcd * per + (blockIdx.x >> 3);
+  if (pid >= t_end) return;
+
+  // tile decode in two steps (its group of m-tiles; then its table entry),
+  // so that the dependent table reads can sit half a stage apart
+  constexpr int GM = kGroupM;
+  // (read as constant memory: scalar loads, which the stage waits do not count)
+  const __attribute__((address_space(4))) int32_t *const tt =
+      (const __attribute__((address_space(4))) int32_t *)p.tiles;
+  auto group_of = [&](int q, int &first_m, int &gsz) {
+    if (p.tiles) {
+      const int j = q / n_tn;
+      first_m = __builtin_amdgcn_readfirstlane(tt[kTileInts * j + 3]);
+      gsz = __builtin_amdgcn_readfirstlane(tt[kTileInts * j + 4]);
+    } else {
+      first_m = q / (GM * n_tn) * GM;
+      gsz = min(n_m - first_m, GM);
+    }
+  };
+  auto tile_of = [&](int q, int first_m, int gsz, int &expert, int &m_begin, int &m_end,
+                     int &n_begin) {
+    const int in_g = q - first_m * n_tn;
+    const int mt = first_m + in_g % gsz;
+    n_begin = (in_g / gsz) * NOUT;
+    if (p.tiles) {
+      expert = __builtin_amdgcn_readfirstlane(tt[kTileInts * mt]);
+      m_begin = __builtin_amdgcn_readfirstlane(tt[kTileInts * mt + 1]);
+      m_end = __builtin_amdgcn_readfirstlane(tt[kTileInts * mt + 2]);
+    } else {
+      expert = 0;
+      m_begin = mt * BM;
+      m_end = static_cast<int>(min<int64_t>(m_begin + BM, p.M));
+    }
+  };
+  // fragment row fm of wavefront row wm holds tile rows frow(fm) .. + 15
+  // (interleaved over the wavefront rows as in gemm2_kernel); live: the
+  // fragment rows that hold tile rows
+  auto frow = [&](int fm) { return (fm * WGM + wm) * MF; };
+  auto live_of = [&](int rows_in) {
+    const int n_frag = (rows_in + MF - 1) / MF;
+    return __builtin_amdgcn_readfirstlane(min(FM, max(0, (n_frag - wm + WGM - 1) / WGM)));
+  };
+
+  // ------------------------------------------------------------ loads
+  // load j of a thread: stage row ROWS j + lrow (A: tile row; B: see above),
+  // in the 1 KB block at row ROWS j + 8 wave, logical chunk lchunk
+  const int lrow = tid >> 3;
+  const int lchunk = (tid & 7) ^ swz_key(lrow);
+  const uint32_t arow_bytes = static_cast<uint32_t>(p.lda * 2);
+  const uint32_t brow_bytes = static_cast<uint32_t>(p.ldb * 2);
+  const int64_t a_rows_ext = p.a_extent ? p.a_extent : p.M;
+  const __amdgpu_buffer_rsrc_t ar = rsrc(p.a, a_rows_ext * p.lda * 2);
+  // B: the weight row of stage row ROWS j + lrow is n_begin + bperm + bj(j)
+  const int bperm = GLU ? (lrow % 16) * 4 + lrow / 16 : (lrow % 16) * 8 + lrow / 16;
+  auto bj = [&](int j) { return GLU ? (j % 2) * 64 : (j / 2) * 128 + (j % 2) * 4; };
+  const int64_t b_bytes = static_cast<int64_t>(p.N) * p.ldb * 2;
+  __amdgpu_buffer_rsrc_t br0, br1;
+  uint32_t boff = 0;
+  auto b_setup = [&](int expert, int n_begin) {
+    const int64_t eoff = static_cast<int64_t>(expert) * p.b_stride * 2;
+    br0 = rsrc(static_cast<const char *>(p.b0) + eoff, b_bytes);
+    br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, b_bytes) : br0;
+    boff = static_cast<uint32_t>(n_begin + bperm) * brow_bytes + lchunk * 16;
+  };
+  // A rows of the tile's loads (gathered rows when given; rows past the
+  // tile's end repeat its first row), then, in place, their offsets
+  // (the gather through a buffer resource: 32-bit lane offsets; every
+  // index read is below m_end)
+  uint32_t aoff[A_LD];
+  const __amdgpu_buffer_rsrc_t gr = rsrc(p.a_rows, p.a_rows ? 0xFFFFFFFFll : 0);
+  auto a_gather = [&](int m_begin, int m_end) {
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+      int m = m_begin + ROWS * j + lrow;
+      if (m >= m_end) m = m_begin;
+      aoff[j] = p.a_rows ? __builtin_amdgcn_raw_buffer_load_b32(gr, m * 4, 0, 0)
+                         : static_cast<uint32_t>(m);
+    }
+  };
+  auto a_offsets = [&]() {
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) aoff[j] = aoff[j] * arow_bytes + lchunk * 16;
+  };
+  auto load_a = [&](u32x4 *ab, int st, int j) {
+    load_lds16(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j],
+               __builtin_amdgcn_readfirstlane(st * kRowBytes));
+  };
+  auto load_b = [&](u32x4 *bb, int st, int j) {
+    const bool up = GLU && j >= B_LD / 2;
+    load_lds16(up ? br1 : br0, bb + (ROWS * j + 8 * wave) * 8, boff + bj(j) * brow_bytes,
+               __builtin_amdgcn_readfirstlane(st * kRowBytes));
+  };
+
+  // ------------------------------------------------------------ fragments
+  auto brow_of = [&](int fn) {  // B stage row (within the tile) of fragment fn
+    if (GLU) {
+      constexpr int half = FN / 2;
+      return fn < half ? wn * (WTN / 2) + fn * MF : BN / 2 + wn * (WTN / 2) + (fn - half) * MF;
+    }
+    return wn * WTN + fn * MF;
+  };
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 *const abuf = g2p_lds;
+  u32x4 *const bbuf = g2p_lds + NA * A16;
+  bf16x8 xa0[FM], xb0[FN], xa1[FM], xb1[FN];
+  auto rd = [&](const u32x4 *ab, const u32x4 *bb, int ks, int i, bf16x8 *xa, bf16x8 *xb) {
+    const int kc = 4 * ks + fc;
+    if (i < FN)
+      xb[i] = __builtin_bit_cast(bf16x8, bb[sw8(brow_of(i) + fr, kc)]);
+    else
+      xa[i - FN] = __builtin_bit_cast(bf16x8, ab[sw8(frow(i - FN) + fr, kc)]);
+  };
+  auto mrow = [&](int fm, const bf16x8 *xa, const bf16x8 *xb) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[fm], xb[fn], acc[fm][fn], 0, 0, 0);
+  };
+  constexpr int NRD = FM + FN;
+  constexpr int RD_PER = (NRD + FM - 1) / FM;
+  constexpr int LD_PER = (A_LD + B_LD + FM - 1) / FM;
+
+  // ------------------------------------------------------------ epilogue
+  // row scales: lane (r, c) of 16-lane row c holds the weight of tile row
+  // frow(fm) + 4 c + (r & 3); row_bcast hands each lane the one of its row
+  const __amdgpu_buffer_rsrc_t sr =
+      rsrc(p.row_scale, (EPI == EPI_SCALE && p.row_scale ? a_rows_ext : 0) * 4);
+  float wsc[FM];
+  auto scale_load = [&](int m_begin) {
+    if constexpr (EPI == EPI_SCALE) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = m_begin + frow(fm) + 4 * fc + (fr & 3);
+        wsc[fm] = p.row_scale ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                             sr, r * 4, 0, 0))
+                              : 1.f;
+      }
+    }
+  };
+  // stores through a buffer resource at the tile's first row: one lane
+  // offset (its rows 4 fc, its run's column), a uniform row offset per
+  // fragment row and element
+  auto epilogue = [&](int m_begin, int rows_in, int n_begin, int live) {
+    // (N is a multiple of 8: a lane's run is wholly in or out)
+    const int col = n_begin + wn * (WTN / (GLU ? 2 : 1)) + fr * RUN;
+    const bool col_ok = col < p.N;
+    const bool f32o = EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32);
+    const int esz = f32o ? 4 : 2;
+    // (opaque here, so that the row offsets and row checks below are formed
+    // per tile, not held across the K loop)
+    uint32_t rbytes = static_cast<uint32_t>(p.ldo) * esz;
+    int lane_row = 4 * fc;
+    asm volatile("" : "+s"(rbytes));
+    asm volatile("" : "+v"(lane_row));
+    const __amdgpu_buffer_rsrc_t orr =
+        rsrc(static_cast<char *>(p.out) + static_cast<int64_t>(m_begin) * p.ldo * esz,
+             static_cast<int64_t>(rows_in) * rbytes);
+    const int voff = static_cast<int>(lane_row * rbytes + col * esz);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm >= live) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = frow(fm) + i;  // + lane_row
+        float v[RUN];
+        if constexpr (GLU) {
+#pragma unroll
+          for (int q = 0; q < RUN; ++q) v[q] = silu_f(acc[fm][q][i]) * acc[fm][q + RUN][i];
+        } else {
+#pragma unroll
+          for (int q = 0; q < RUN; ++q) v[q] = acc[fm][q][i];
+        }
+        if constexpr (EPI == EPI_SCALE) {
+          const float w = i == 0 ? row_bcast<0>(wsc[fm])
+                        : i == 1 ? row_bcast<1>(wsc[fm])
+                        : i == 2 ? row_bcast<2>(wsc[fm])
+                                 : row_bcast<3>(wsc[fm]);
+#pragma unroll
+          for (int q = 0; q < RUN; ++q) v[q] *= w;
+        }
+        // (after the swizzle: every lane takes part in it)
+        if (!col_ok || lane_row >= rows_in - r) continue;
+        const int so = __builtin_amdgcn_readfirstlane(r * static_cast<int>(rbytes));
+        if constexpr (GLU) {
+          const v2i32 d = {static_cast<int>(f32x2_to_bf16x2(v[0], v[1])),
+                           static_cast<int>(f32x2_to_bf16x2(v[2], v[3]))};
+          __builtin_amdgcn_raw_buffer_store_b64(d, orr, voff, so, 0);
+        } else if (f32o) {
+          const v4i32 d0 = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                            __float_as_int(v[3])};
+          const v4i32 d1 = {__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]),
+                            __float_as_int(v[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(d0, orr, voff, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(d1, orr, voff + 16, so, 0);
+        } else {
+          const uint4 c = Chunk<bf16_t>::pack(v);
+          const v4i32 d = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z),
+                           static_cast<int>(c.w)};
+          __builtin_amdgcn_raw_buffer_store_b128(d, orr, voff, so, 0);
+        }
+        // one row at a time: the next tile's first fragments stay live
+        // across the epilogue, which leaves it few registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------ first tile
+  const int steps = (p.K + 63) / 64, last = steps - 1;  // (at least 4: host check)
+  const bool half_last = (p.K & 63) != 0;
+  int c_mb, c_me, c_nb;
+  {
+    int first_m, gsz, expert;
+    group_of(pid, first_m, gsz);
+    tile_of(pid, first_m, gsz, expert, c_mb, c_me, c_nb);
+    b_setup(expert, c_nb);
+  }
+  int c_live = live_of(c_me - c_mb);
+  a_gather(c_mb, c_me);
+  a_offsets();
+#pragma unroll
+  for (int s0 = 0; s0 < NB; ++s0) {
+    if (s0 < NA) {
+#pragma unroll
+      for (int j = 0; j < A_LD; ++j) load_a(abuf + s0 * A16, s0, j);
+    }
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) load_b(bbuf + s0 * B16, s0, j);
+  }
+  wait_vm_lgkm0<(NA - 1) * A_LD + (NB - 1) * B_LD>();
+  barrier();
+#pragma unroll
+  for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
+
+  // ------------------------------------------------------------ tiles
+  __builtin_amdgcn_s_setprio(1);
+  int a_cur = 0, b_cur = 0;
+  while (true) {
+    const int n_pid = pid + gstride;
+    const bool n_ok = n_pid < t_end;  // there is a next tile
+    int n_first = 0, n_gsz = 1, n_exp = 0, n_mb = 0, n_me = 0, n_nb = 0;
+    for (int st = 0; st < steps; ++st) {
+      const int a_nxt = a_cur == NA - 1 ? 0 : a_cur + 1;
+      const int b_nxt = b_cur == NB - 1 ? 0 : b_cur + 1;
+      u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + a_nxt * A16;
+      u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
+      wait_lgkm0();
+      if (st == 0 && n_ok) group_of(n_pid, n_first, n_gsz);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int q = 0; q < RD_PER; ++q) {
+          const int i = fm * RD_PER + q;
+          if (i < NRD) rd(ac, bc, 1, i, xa1, xb1);
+        }
+        if (fm < c_live) mrow(fm, xa0, xb0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vm_lgkm0<(NA - 2) * A_LD + (NB - 2) * B_LD>();
+      barrier();
+      if (st == 0) {
+        if (n_ok) tile_of(n_pid, n_first, n_gsz, n_exp, n_mb, n_me, n_nb);
+        scale_load(c_mb);
+      }
+      // this tile's stages, then the next tile's (B from three stages before
+      // the end, A from two), or repeats of the last stage
+      int sa = st + NA, sb = st + NB;
+      if (sb > last) {
+        if (n_ok && sb == last + 1) b_setup(n_exp, n_nb);
+        sb = n_ok ? sb - steps : last;
+      }
+      if (sa > last) {
+        if (n_ok && sa == last + 1) a_offsets();
+        sa = n_ok ? sa - steps : last;
+      }
+      const int live1 = (half_last && st == last) ? 0 : c_live;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int q = 0; q < RD_PER; ++q) {
+          const int i = fm * RD_PER + q;
+          if (i < NRD) rd(an, bn, 0, i, xa0, xb0);
+        }
+        if (fm < live1) mrow(fm, xa1, xb1);
+#pragma unroll
+        for (int q = 0; q < LD_PER; ++q) {
+          const int j = fm * LD_PER + q;
+          if (j < A_LD) load_a(ac, sa, j);
+          else if (j < A_LD + B_LD) load_b(bc, sb, j - A_LD);
+        }
+        // the next tile's A rows, requested once this tile's last A loads
+        // are out (before the stage's B loads, so the next stage's wait
+        // covers them) and turned into offsets a stage later
+        if (fm == (A_LD - 1) / LD_PER && st == last - NA && n_ok) a_gather(n_mb, n_me);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      a_cur = a_nxt;
+      b_cur = b_nxt;
+    }
+    epilogue(c_mb, c_me - c_mb, c_nb, c_live);
+    if (!n_ok) break;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pid = n_pid;
+    c_mb = n_mb;
+    c_me = n_me;
+    c_nb = n_nb;
+    c_live = live_of(c_me - c_mb);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  wait_vm_lgkm0<0>();  // the repeated loads land before the workgroup's LDS is released
+}
+
 template <int BM, int BN, int WGM, int WGN, int NA, int EPI, bool BKM = false, bool KS = false>
 hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   constexpr int NOUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
@@ -681,6 +1069,48 @@ hipError_t run2(const GemmArgs &a, const GemmArgs *second, hipStream_t s) {
   gemm2_kernel<BM, BN, WGM, WGN, NA, EPI, BKM, KS>
       <<<static_cast<unsigned>(blocks), 64 * WGM * WGN, 0, s>>>(b0, b1);
   return hipGetLastError();
+}
+
+// Compute units of the current device, read once per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Persistent 256x256 launch: one workgroup per CU (a multiple of 8: whole
+// XCDs), none past the tile bound.
+template <int EPI>
+hipError_t run2p(const GemmArgs &a, hipStream_t s) {
+  constexpr int NOUT = EPI == EPI_SWIGLU ? 128 : 256;
+  GemmArgs b = a;
+  b.max_mtiles = b.tiles ? b.max_mtiles : (b.M + 255) / 256;
+  const int64_t bound = b.max_mtiles * ((b.N + NOUT - 1) / NOUT);
+  if (bound == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(8 * ((bound + 7) / 8), 8 * (cu_count() / 8));
+  gemm2p_kernel<EPI><<<static_cast<unsigned>(blocks), 512, 0, s>>>(b);
+  return hipGetLastError();
+}
+
+// The persistent form applies to one problem with a fixed reduction of at
+// least 4 stages and a register epilogue, with at least kMinRounds tiles per
+// workgroup (below that the hardware's dynamic dispatch balances better than
+// a fixed list), and output rows of at most 4 MiB (32-bit store offsets).
+constexpr int64_t kMinRounds = 2;
+bool persistent_ok(const GemmArgs &a, const GemmArgs *b, int epi) {
+  if ((b && b->N > 0) || a.a2 || a.k_split > 1 || a.k_offsets || a.b_kmajor) return false;
+  if (epi != EPI_SWIGLU && epi != EPI_SCALE && epi != EPI_STORE_F32) return false;
+  if ((a.K + 63) / 64 < 4 || a.ldo * 4 * 256 >= (int64_t(1) << 32)) return false;
+  const int64_t mt = a.tiles ? a.max_mtiles : (a.M + 255) / 256;
+  const int64_t nout = epi == EPI_SWIGLU ? 128 : 256;
+  return mt * ((a.N + nout - 1) / nout) >= kMinRounds * cu_count();
 }
 
 template <int BM, int BN, int WGM, int WGN, int NA = 2>
@@ -800,10 +1230,22 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
   return launch_gemm(a, epi, TILE_SMALL_N64, act_bf16, s);
 }
 
+bool gemm2_persistent(const GemmArgs &a, int epi, int cfg, const GemmArgs *b) {
+  return cfg == TILE2_256x256_TALLW && persistent_ok(a, b, epi);
+}
+
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, const GemmArgs *b) {
   switch (cfg) {
     case TILE2_256x256: return dispatch2<256, 256, 2, 4>(a, b, epi, s);
-    case TILE2_256x256_TALLW: return dispatch2<256, 256, 4, 2>(a, b, epi, s);
+    case TILE2_256x256_TALLW:
+      if (gemm2_persistent(a, epi, cfg, b)) {
+        switch (epi) {
+          case EPI_SWIGLU: return run2p<EPI_SWIGLU>(a, s);
+          case EPI_SCALE: return run2p<EPI_SCALE>(a, s);
+          case EPI_STORE_F32: return run2p<EPI_STORE_F32>(a, s);
+        }
+      }
+      return dispatch2<256, 256, 4, 2>(a, b, epi, s);
     case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, b, epi, s);
     case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, b, epi, s);
     case TILE2_128x128_W8D4: return dispatch2<128, 128, 4, 2, 4>(a, b, epi, s);

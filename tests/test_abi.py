@@ -213,6 +213,11 @@ def test_plan_paths_of_the_workloads():
         assert P[n]["backward_in_place"] == 3, n
     assert P["small"]["backward_in_place"] == 1  # d_ff = 1376: dX from copies
     assert P["tiny"]["backward_in_place"] == 0
+    # grouped GEMMs on the persistent kernel: 256x256 tiles, two or more per CU
+    for n in ("medium", "large_prefill", "latent"):
+        assert P[n]["persistent"] == 3, n
+    for n in ("tiny", "small", "large_decode"):
+        assert P[n]["persistent"] == 0, n
     with pytest.raises(moe.MoeError):
         moe.moe_plan(_desc(T=-1))
 

@@ -91,6 +91,28 @@ def test_pipelined_gemm_k_tail(name):
     assert (plan["merged_shared"], plan["gate_up_tile_m"]) == want
 
 
+def test_persistent_grouped_gemms():
+    """Both grouped GEMMs on the persistent kernel: reductions ending 32
+    columns into a stage (2080 and 1056), a partial last n-tile in each
+    (1056 = 8 x 128 + 32 SwiGLU columns, 2080 = 8 x 256 + 32), expert loads
+    skewed by the router bias (partial m-tiles of many heights)."""
+    w = custom(name="persist", config_no=640, T=8192, d=2080, d_ff=1056, E=8, K=4, act="bf16",
+               n_shared=1, d_ff_shared=1056, route="sigmoid_bias", bias_std=1.0, w_std=0.03,
+               router_std=0.03)
+    say(f"case persistent T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K}")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    plan = moe.moe_plan(layer.desc)
+    say(f"  plan {plan}")
+    assert plan["persistent"] == 3
+    orc = oracle.Oracle(w, a)
+    r = check_route(w, a, layer, orc)
+    counts = np.bincount(r[0].ravel(), minlength=w.E)
+    say(f"  expert loads {counts.tolist()}")
+    toks = sample_tokens(r[0], w.E, 384, seed=w.config_no)
+    check_forward(w, a, layer, tokens=toks, orc=orc, o_route=r)
+
+
 @pytest.mark.parametrize("name", sorted(EDGE))
 def test_edge_layer(name):
     w = custom(name=name, config_no=500 + sorted(EDGE).index(name), **EDGE[name])
