@@ -677,9 +677,9 @@ __device__ __forceinline__ float row_bcast(float v) {
 
 // ------------------------------------------------------------------ persistent
 // Persistent form of the 256x256 tile (4 x 2 wavefronts of 64x128, A two
-// stages ahead) for one problem with a fixed reduction (no second K segment,
-// no K grouping or split) and an epilogue that writes from the accumulators:
-// SwiGLU, row scale, fp32 store. Each workgroup runs a fixed list of tiles:
+// stages ahead) for one problem (no second K segment or K split; K-grouped
+// allowed) and an epilogue that writes from the accumulators: SwiGLU, row
+// scale, fp32 store. Each workgroup runs a fixed list of tiles:
 // the tiles are dealt over the XCDs in contiguous ranges as in gemm2_kernel,
 // and workgroup w of an XCD takes tiles w, w + G, w + 2 G, ... of its range
 // (G workgroups per XCD), so that at any time an XCD works on G consecutive
@@ -693,11 +693,15 @@ __device__ __forceinline__ float row_bcast(float v) {
 // tile's data): B rows are loaded in an order that gives each lane a run of
 // adjacent output columns, RUN = 8 (4 for SwiGLU, whose gate and up
 // fragments pair up), so it stores straight from its accumulators, one
-// 16-byte (8-byte) piece per row. The next tile is decoded during the first
-// stages of the current one (tile table reads two stages apart, so their
-// latency overlaps MFMAs), its A row gather is requested a stage later and
-// consumed one stage before its first A load. The epilogue's stores are
-// waited for by the next tile's first stage wait.
+// 16-byte (8-byte) piece per row. The next tile is decoded during the
+// current one's first stages (the tile table, then the expert's reduction
+// range: dependent reads a stage apart, their latency under MFMAs); its A
+// rows are gathered once the current tile's last A loads are out and become
+// offsets a stage later. The epilogue's stores are waited for by the next
+// tile's first stage wait. A tile of fewer than 5 stages, or followed by one
+// of fewer than 3, drains its loads instead, and the next tile starts with
+// a prologue of its own (a K-grouped expert without reduction columns runs
+// no stages: its output is zeros).
 //
 // Lane (fr, fc) holds rows 4 fc + i of column fr of each 16 x 16 fragment.
 // Stage buffer row R of B holds, within each 128-row block (64 for each of
@@ -721,6 +725,13 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: scalar arithmetic)
+  // the thread index, opaque: lane-dependent values used once per tile are
+  // formed from it where they are used, not held across the K loop
+  auto tid_o = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
   const int wm = wave / WGN, wn = wave % WGN;
   const int fr = lane & 15, fc = lane >> 4;
 
@@ -766,6 +777,19 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
       m_end = static_cast<int>(min<int64_t>(m_begin + BM, p.M));
     }
   };
+  // K-grouped: the expert's reduction columns [kbeg, kbeg + kseg) (a
+  // multiple of 64; 0 for an expert with no rows: its output is zeros)
+  const __attribute__((address_space(4))) int32_t *const ko =
+      (const __attribute__((address_space(4))) int32_t *)p.k_offsets;
+  auto k_of = [&](int expert, int &kbeg, int &kseg) {
+    if (p.k_offsets) {
+      kbeg = __builtin_amdgcn_readfirstlane(ko[expert]);
+      kseg = __builtin_amdgcn_readfirstlane(ko[expert + 1]) - kbeg;
+    } else {
+      kbeg = 0;
+      kseg = p.K;
+    }
+  };
   // fragment row fm of wavefront row wm holds tile rows frow(fm) .. + 15
   // (interleaved over the wavefront rows as in gemm2_kernel); live: the
   // fragment rows that hold tile rows
@@ -778,23 +802,27 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
   // ------------------------------------------------------------ loads
   // load j of a thread: stage row ROWS j + lrow (A: tile row; B: see above),
   // in the 1 KB block at row ROWS j + 8 wave, logical chunk lchunk
-  const int lrow = tid >> 3;
-  const int lchunk = (tid & 7) ^ swz_key(lrow);
+  auto lrow_of = [&](int t) { return t >> 3; };
+  auto lchunk_of = [&](int t) { return (t & 7) ^ swz_key(t >> 3); };
   const uint32_t arow_bytes = static_cast<uint32_t>(p.lda * 2);
   const uint32_t brow_bytes = static_cast<uint32_t>(p.ldb * 2);
   const int64_t a_rows_ext = p.a_extent ? p.a_extent : p.M;
   const __amdgpu_buffer_rsrc_t ar = rsrc(p.a, a_rows_ext * p.lda * 2);
   // B: the weight row of stage row ROWS j + lrow is n_begin + bperm + bj(j)
-  const int bperm = GLU ? (lrow % 16) * 4 + lrow / 16 : (lrow % 16) * 8 + lrow / 16;
+  auto bperm_of = [&](int lrow) {
+    return GLU ? (lrow % 16) * 4 + lrow / 16 : (lrow % 16) * 8 + lrow / 16;
+  };
   auto bj = [&](int j) { return GLU ? (j % 2) * 64 : (j / 2) * 128 + (j % 2) * 4; };
   const int64_t b_bytes = static_cast<int64_t>(p.N) * p.ldb * 2;
   __amdgpu_buffer_rsrc_t br0, br1;
   uint32_t boff = 0;
-  auto b_setup = [&](int expert, int n_begin) {
+  auto b_setup = [&](int expert, int n_begin, int kbeg) {
     const int64_t eoff = static_cast<int64_t>(expert) * p.b_stride * 2;
     br0 = rsrc(static_cast<const char *>(p.b0) + eoff, b_bytes);
     br1 = GLU ? rsrc(static_cast<const char *>(p.b1) + eoff, b_bytes) : br0;
-    boff = static_cast<uint32_t>(n_begin + bperm) * brow_bytes + lchunk * 16;
+    const int t = tid_o();
+    boff = static_cast<uint32_t>(n_begin + bperm_of(lrow_of(t))) * brow_bytes +
+           (kbeg + lchunk_of(t) * 8) * 2;
   };
   // A rows of the tile's loads (gathered rows when given; rows past the
   // tile's end repeat its first row), then, in place, their offsets
@@ -805,15 +833,16 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
   auto a_gather = [&](int m_begin, int m_end) {
 #pragma unroll
     for (int j = 0; j < A_LD; ++j) {
-      int m = m_begin + ROWS * j + lrow;
+      int m = m_begin + ROWS * j + lrow_of(tid_o());
       if (m >= m_end) m = m_begin;
       aoff[j] = p.a_rows ? __builtin_amdgcn_raw_buffer_load_b32(gr, m * 4, 0, 0)
                          : static_cast<uint32_t>(m);
     }
   };
-  auto a_offsets = [&]() {
+  auto a_offsets = [&](int kbeg) {
 #pragma unroll
-    for (int j = 0; j < A_LD; ++j) aoff[j] = aoff[j] * arow_bytes + lchunk * 16;
+    for (int j = 0; j < A_LD; ++j)
+      aoff[j] = aoff[j] * arow_bytes + (kbeg + lchunk_of(tid_o()) * 8) * 2;
   };
   auto load_a = [&](u32x4 *ab, int st, int j) {
     load_lds16(ar, ab + (ROWS * j + 8 * wave) * 8, aoff[j],
@@ -867,7 +896,8 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
     if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        const int r = m_begin + frow(fm) + 4 * fc + (fr & 3);
+        const int t = tid_o();
+        const int r = m_begin + frow(fm) + 4 * ((t & 63) >> 4) + (t & 3);
         wsc[fm] = p.row_scale ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                              sr, r * 4, 0, 0))
                               : 1.f;
@@ -877,20 +907,22 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
   // stores through a buffer resource at the tile's first row: one lane
   // offset (its rows 4 fc, its run's column), a uniform row offset per
   // fragment row and element
-  auto epilogue = [&](int m_begin, int rows_in, int n_begin, int live) {
+  auto epilogue = [&](int m_begin, int rows_in, int n_begin, int expert, int live) {
     // (N is a multiple of 8: a lane's run is wholly in or out)
-    const int col = n_begin + wn * (WTN / (GLU ? 2 : 1)) + fr * RUN;
+    const int t = tid_o();
+    const int col = n_begin + wn * (WTN / (GLU ? 2 : 1)) + (t & 15) * RUN;
     const bool col_ok = col < p.N;
     const bool f32o = EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32);
     const int esz = f32o ? 4 : 2;
     // (opaque here, so that the row offsets and row checks below are formed
     // per tile, not held across the K loop)
     uint32_t rbytes = static_cast<uint32_t>(p.ldo) * esz;
-    int lane_row = 4 * fc;
+    int lane_row = 4 * ((t & 63) >> 4);
     asm volatile("" : "+s"(rbytes));
     asm volatile("" : "+v"(lane_row));
+    const int64_t obase = p.k_offsets ? static_cast<int64_t>(expert) * p.out_stride : 0;
     const __amdgpu_buffer_rsrc_t orr =
-        rsrc(static_cast<char *>(p.out) + static_cast<int64_t>(m_begin) * p.ldo * esz,
+        rsrc(static_cast<char *>(p.out) + (obase + static_cast<int64_t>(m_begin) * p.ldo) * esz,
              static_cast<int64_t>(rows_in) * rbytes);
     const int voff = static_cast<int>(lane_row * rbytes + col * esz);
 #pragma unroll
@@ -942,47 +974,61 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
     }
   };
 
-  // ------------------------------------------------------------ first tile
-  const int steps = (p.K + 63) / 64, last = steps - 1;  // (at least 4: host check)
-  const bool half_last = (p.K & 63) != 0;
-  int c_mb, c_me, c_nb;
-  {
-    int first_m, gsz, expert;
-    group_of(pid, first_m, gsz);
-    tile_of(pid, first_m, gsz, expert, c_mb, c_me, c_nb);
-    b_setup(expert, c_nb);
-  }
-  int c_live = live_of(c_me - c_mb);
-  a_gather(c_mb, c_me);
-  a_offsets();
-#pragma unroll
-  for (int s0 = 0; s0 < NB; ++s0) {
-    if (s0 < NA) {
-#pragma unroll
-      for (int j = 0; j < A_LD; ++j) load_a(abuf + s0 * A16, s0, j);
-    }
-#pragma unroll
-    for (int j = 0; j < B_LD; ++j) load_b(bbuf + s0 * B16, s0, j);
-  }
-  wait_vm_lgkm0<(NA - 1) * A_LD + (NB - 1) * B_LD>();
-  barrier();
-#pragma unroll
-  for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
-
   // ------------------------------------------------------------ tiles
-  __builtin_amdgcn_s_setprio(1);
+  // A tile whose next one has at least NB stages, and which itself has at
+  // least 5 (its stages 0 - 2 decode the next tile), fetches the next tile's
+  // first stages in its own last ones ("primes" it); any other tile drains
+  // its loads and the next one starts with a prologue of its own.
+  auto n_stages = [&](int kseg) { return (kseg + 63) / 64; };
+  int c_mb, c_me, c_nb, c_exp, c_kb = 0, c_ks = p.K;
+  {
+    int first_m, gsz;
+    group_of(pid, first_m, gsz);
+    tile_of(pid, first_m, gsz, c_exp, c_mb, c_me, c_nb);
+    k_of(c_exp, c_kb, c_ks);
+  }
+  bool primed = false;
   int a_cur = 0, b_cur = 0;
   while (true) {
+    const int steps = n_stages(c_ks), last = steps - 1;
+    const bool half_last = (c_ks & 63) != 0;
+    const int c_live = live_of(c_me - c_mb);
+    if (!primed) {
+      // the previous tile's loads have landed and its reads are done
+      wait_vm_lgkm0<0>();
+      barrier();
+      a_cur = b_cur = 0;
+      if (steps > 0) {
+        b_setup(c_exp, c_nb, c_kb);
+        a_gather(c_mb, c_me);
+        a_offsets(c_kb);
+#pragma unroll
+        for (int s0 = 0; s0 < NB; ++s0) {
+          if (s0 < NA) {
+#pragma unroll
+            for (int j = 0; j < A_LD; ++j) load_a(abuf + s0 * A16, min(s0, last), j);
+          }
+#pragma unroll
+          for (int j = 0; j < B_LD; ++j) load_b(bbuf + s0 * B16, min(s0, last), j);
+        }
+        wait_vm_lgkm0<(NA - 1) * A_LD + (NB - 1) * B_LD>();
+        barrier();
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) rd(abuf, bbuf, 0, i, xa0, xb0);
+      }
+    }
     const int n_pid = pid + gstride;
     const bool n_ok = n_pid < t_end;  // there is a next tile
-    int n_first = 0, n_gsz = 1, n_exp = 0, n_mb = 0, n_me = 0, n_nb = 0;
+    int n_first = 0, n_gsz = 1, n_exp = 0, n_mb = 0, n_me = 0, n_nb = 0, n_kb = 0, n_ks = p.K;
+    bool pf = false;  // this tile primes the next
+    __builtin_amdgcn_s_setprio(1);
     for (int st = 0; st < steps; ++st) {
       const int a_nxt = a_cur == NA - 1 ? 0 : a_cur + 1;
       const int b_nxt = b_cur == NB - 1 ? 0 : b_cur + 1;
       u32x4 *const ac = abuf + a_cur * A16, *const an = abuf + a_nxt * A16;
       u32x4 *const bc = bbuf + b_cur * B16, *const bn = bbuf + b_nxt * B16;
       wait_lgkm0();
-      if (st == 0 && n_ok) group_of(n_pid, n_first, n_gsz);
+      if (st == 0 && n_ok && steps >= 5) group_of(n_pid, n_first, n_gsz);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -996,19 +1042,21 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
       wait_vm_lgkm0<(NA - 2) * A_LD + (NB - 2) * B_LD>();
       barrier();
       if (st == 0) {
-        if (n_ok) tile_of(n_pid, n_first, n_gsz, n_exp, n_mb, n_me, n_nb);
+        if (n_ok && steps >= 5) tile_of(n_pid, n_first, n_gsz, n_exp, n_mb, n_me, n_nb);
         scale_load(c_mb);
       }
+      if (st == 1 && n_ok && steps >= 5) k_of(n_exp, n_kb, n_ks);
+      if (st == 2) pf = n_ok && steps >= 5 && n_stages(n_ks) >= NB;
       // this tile's stages, then the next tile's (B from three stages before
       // the end, A from two), or repeats of the last stage
       int sa = st + NA, sb = st + NB;
       if (sb > last) {
-        if (n_ok && sb == last + 1) b_setup(n_exp, n_nb);
-        sb = n_ok ? sb - steps : last;
+        if (pf && sb == last + 1) b_setup(n_exp, n_nb, n_kb);
+        sb = pf ? sb - steps : last;
       }
       if (sa > last) {
-        if (n_ok && sa == last + 1) a_offsets();
-        sa = n_ok ? sa - steps : last;
+        if (pf && sa == last + 1) a_offsets(n_kb);
+        sa = pf ? sa - steps : last;
       }
       const int live1 = (half_last && st == last) ? 0 : c_live;
 #pragma unroll
@@ -1028,14 +1076,20 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
         // the next tile's A rows, requested once this tile's last A loads
         // are out (before the stage's B loads, so the next stage's wait
         // covers them) and turned into offsets a stage later
-        if (fm == (A_LD - 1) / LD_PER && st == last - NA && n_ok) a_gather(n_mb, n_me);
+        if (fm == (A_LD - 1) / LD_PER && st == last - NA && pf) a_gather(n_mb, n_me);
         __builtin_amdgcn_sched_barrier(0);
       }
       a_cur = a_nxt;
       b_cur = b_nxt;
     }
-    epilogue(c_mb, c_me - c_mb, c_nb, c_live);
+    __builtin_amdgcn_s_setprio(0);
+    epilogue(c_mb, c_me - c_mb, c_nb, c_exp, c_live);
     if (!n_ok) break;
+    if (!pf) {  // (decoded here when the tile was too short to do it on the way)
+      group_of(n_pid, n_first, n_gsz);
+      tile_of(n_pid, n_first, n_gsz, n_exp, n_mb, n_me, n_nb);
+      k_of(n_exp, n_kb, n_ks);
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1044,9 +1098,11 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
     c_mb = n_mb;
     c_me = n_me;
     c_nb = n_nb;
-    c_live = live_of(c_me - c_mb);
+    c_exp = n_exp;
+    c_kb = n_kb;
+    c_ks = n_ks;
+    primed = pf;
   }
-  __builtin_amdgcn_s_setprio(0);
   wait_vm_lgkm0<0>();  // the repeated loads land before the workgroup's LDS is released
 }
 
@@ -1099,15 +1155,18 @@ hipError_t run2p(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The persistent form applies to one problem with a fixed reduction of at
-// least 4 stages and a register epilogue, with at least kMinRounds tiles per
+// A problem for the persistent form: a register epilogue (K-grouped: the
+// fp32 store), a reduction of at least 5 stages (K-grouped: any, a short
+// expert's tile starting with a prologue of its own), output rows of at
+// most 4 MiB (32-bit store offsets), and at least kMinRounds tiles per
 // workgroup (below that the hardware's dynamic dispatch balances better than
-// a fixed list), and output rows of at most 4 MiB (32-bit store offsets).
+// a fixed list).
 constexpr int64_t kMinRounds = 2;
-bool persistent_ok(const GemmArgs &a, const GemmArgs *b, int epi) {
-  if ((b && b->N > 0) || a.a2 || a.k_split > 1 || a.k_offsets || a.b_kmajor) return false;
+bool persistent_one(const GemmArgs &a, int epi) {
+  if (a.a2 || a.k_split > 1 || a.b_kmajor) return false;
   if (epi != EPI_SWIGLU && epi != EPI_SCALE && epi != EPI_STORE_F32) return false;
-  if ((a.K + 63) / 64 < 4 || a.ldo * 4 * 256 >= (int64_t(1) << 32)) return false;
+  if (a.k_offsets ? epi != EPI_STORE_F32 : (a.K + 63) / 64 < 5) return false;
+  if (a.ldo * 4 * 256 >= (int64_t(1) << 32)) return false;
   const int64_t mt = a.tiles ? a.max_mtiles : (a.M + 255) / 256;
   const int64_t nout = epi == EPI_SWIGLU ? 128 : 256;
   return mt * ((a.N + nout - 1) / nout) >= kMinRounds * cu_count();
@@ -1231,7 +1290,7 @@ hipError_t launch_dense(const GemmArgs &a, int epi, int act_bf16, hipStream_t s)
 }
 
 bool gemm2_persistent(const GemmArgs &a, int epi, int cfg, const GemmArgs *b) {
-  return cfg == TILE2_256x256_TALLW && persistent_ok(a, b, epi);
+  return cfg == TILE2_256x256_TALLW && (!b || b->N <= 0) && persistent_one(a, epi);
 }
 
 hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, const GemmArgs *b) {
