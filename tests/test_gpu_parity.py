@@ -95,9 +95,11 @@ def test_persistent_grouped_gemms():
     """Both grouped GEMMs on the persistent kernel: reductions ending 32
     columns into a stage (2080 and 1056), a partial last n-tile in each
     (1056 = 8 x 128 + 32 SwiGLU columns, 2080 = 8 x 256 + 32), expert loads
-    skewed by the router bias (partial m-tiles of many heights)."""
-    w = custom(name="persist", config_no=640, T=8192, d=2080, d_ff=1056, E=8, K=4, act="bf16",
-               n_shared=1, d_ff_shared=1056, route="sigmoid_bias", bias_std=1.0, w_std=0.03,
+    skewed by the router bias (partial m-tiles of many heights); the shared
+    experts' dense gate/up (33 x 16 tiles) on it too, its last m-tile
+    partial (8229 = 32 x 256 + 37 tokens)."""
+    w = custom(name="persist", config_no=640, T=8229, d=2080, d_ff=1056, E=8, K=4, act="bf16",
+               n_shared=1, d_ff_shared=2048, route="sigmoid_bias", bias_std=1.0, w_std=0.03,
                router_std=0.03)
     say(f"case persistent T={w.T} d={w.d} d_ff={w.d_ff} E={w.E} K={w.K}")
     a = moe_synth.generate(w)
