@@ -949,7 +949,8 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
         }
         // (after the swizzle: every lane takes part in it)
         if (!col_ok || lane_row >= rows_in - r) continue;
-        const int so = __builtin_amdgcn_readfirstlane(r * static_cast<int>(rbytes));
+        const int so =
+            __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(r) * rbytes));
         if constexpr (GLU) {
           const v2i32 d = {static_cast<int>(f32x2_to_bf16x2(v[0], v[1])),
                            static_cast<int>(f32x2_to_bf16x2(v[2], v[3]))};
@@ -1090,9 +1091,7 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
       tile_of(n_pid, n_first, n_gsz, n_exp, n_mb, n_me, n_nb);
       k_of(n_exp, n_kb, n_ks);
     }
-#pragma unroll
     for (int i = 0; i < FM; ++i)
-#pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     pid = n_pid;
     c_mb = n_mb;
