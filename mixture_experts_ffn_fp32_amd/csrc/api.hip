@@ -1299,17 +1299,27 @@ int moe_backward(const moe_desc *d, const moe_weights *w, const void *x, const v
     rin = wsb + L.z;
   }
 
-  // 3. pre-activations a, u (fp32), routed and shared
+  // 3. pre-activations a, u (fp32), routed and shared: as one gate/up tile
+  //    (the forward's, both halves stored in fp32) on the persistent kernel
+  //    where it takes the launch, else as two problems of one launch
+  auto gate_up_f32 = [&](GemmArgs ga, GemmArgs gu, int c) -> int {
+    GemmArgs g = ga;
+    g.b1 = gu.b0;
+    g.out2 = gu.out;
+    if (bf && gemm2_applicable(g, EPI_GLU_F32) && gemm2_persistent(g, EPI_GLU_F32, c))
+      return launch_gemm2(g, EPI_GLU_F32, c, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return gemm(ga, &gu, c);
+  };
   {
     const GemmArgs ga = grouped(rin, de, stok, T, w->w_gate, de, static_cast<int64_t>(f) * de, de,
                                 f, F(B.apre), f);
     const GemmArgs gu = grouped(rin, de, stok, T, w->w_up, de, static_cast<int64_t>(f) * de, de,
                                 f, F(B.upre), f);
-    if ((rc = gemm(ga, &gu, cfg))) return rc;
+    if ((rc = gate_up_f32(ga, gu, cfg))) return rc;
     if (ds) {
       const GemmArgs sa2 = dense(x, dm, w->ws_gate, dm, dm, ds, T, F(B.apre_s), ds);
       const GemmArgs su = dense(x, dm, w->ws_up, dm, dm, ds, T, F(B.upre_s), ds);
-      if ((rc = gemm(sa2, &su, cfg_s))) return rc;
+      if ((rc = gate_up_f32(sa2, su, cfg_s))) return rc;
     }
   }
 

@@ -713,12 +713,13 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
   constexpr int NW = WGM * WGN, THREADS = 64 * NW;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MF = 16, FM = WTM / MF, FN = WTN / MF;
-  constexpr bool GLU = EPI == EPI_SWIGLU;
+  constexpr bool GLU = EPI == EPI_SWIGLU || EPI == EPI_GLU_F32;  // gate and up halves
   constexpr int NOUT = GLU ? BN / 2 : BN;
   constexpr int ROWS = THREADS / 8, A_LD = BM / ROWS, B_LD = BN / ROWS;
   constexpr int A16 = BM * 8, B16 = BN * 8;
   constexpr int RUN = GLU ? FN / 2 : FN;  // adjacent output columns per lane
-  static_assert(EPI == EPI_SWIGLU || EPI == EPI_SCALE || EPI == EPI_STORE_F32,
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_SCALE || EPI == EPI_STORE_F32 ||
+                    EPI == EPI_GLU_F32,
                 "epilogues that store from the accumulators");
   static_assert(A_LD == 4 && B_LD == 4 && FM == 4 && FN == 8, "tile geometry");
   __shared__ __attribute__((aligned(1024))) u32x4 g2p_lds[(NA * BM + NB * BN) * 8];
@@ -912,7 +913,8 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
     const int t = tid_o();
     const int col = n_begin + wn * (WTN / (GLU ? 2 : 1)) + (t & 15) * RUN;
     const bool col_ok = col < p.N;
-    const bool f32o = EPI == EPI_STORE_F32 || (EPI == EPI_SCALE && p.out_f32);
+    const bool f32o =
+        EPI == EPI_STORE_F32 || EPI == EPI_GLU_F32 || (EPI == EPI_SCALE && p.out_f32);
     const int esz = f32o ? 4 : 2;
     // (opaque here, so that the row offsets and row checks below are formed
     // per tile, not held across the K loop)
@@ -924,6 +926,11 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t orr =
         rsrc(static_cast<char *>(p.out) + (obase + static_cast<int64_t>(m_begin) * p.ldo) * esz,
              static_cast<int64_t>(rows_in) * rbytes);
+    const __amdgpu_buffer_rsrc_t orr2 =
+        EPI == EPI_GLU_F32
+            ? rsrc(static_cast<char *>(p.out2) + static_cast<int64_t>(m_begin) * p.ldo * esz,
+                   static_cast<int64_t>(rows_in) * rbytes)
+            : orr;
     const int voff = static_cast<int>(lane_row * rbytes + col * esz);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -932,7 +939,10 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
       for (int i = 0; i < 4; ++i) {
         const int r = frow(fm) + i;  // + lane_row
         float v[RUN];
-        if constexpr (GLU) {
+        if constexpr (EPI == EPI_GLU_F32) {
+#pragma unroll
+          for (int q = 0; q < RUN; ++q) v[q] = acc[fm][q][i];
+        } else if constexpr (GLU) {
 #pragma unroll
           for (int q = 0; q < RUN; ++q) v[q] = silu_f(acc[fm][q][i]) * acc[fm][q + RUN][i];
         } else {
@@ -951,7 +961,15 @@ __global__ __launch_bounds__(512, 1) void gemm2p_kernel(GemmArgs p) {
         if (!col_ok || lane_row >= rows_in - r) continue;
         const int so =
             __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(r) * rbytes));
-        if constexpr (GLU) {
+        if constexpr (EPI == EPI_GLU_F32) {
+          const v4i32 dg = {__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                            __float_as_int(v[3])};
+          const v4i32 du = {__float_as_int(acc[fm][RUN][i]), __float_as_int(acc[fm][RUN + 1][i]),
+                            __float_as_int(acc[fm][RUN + 2][i]),
+                            __float_as_int(acc[fm][RUN + 3][i])};
+          __builtin_amdgcn_raw_buffer_store_b128(dg, orr, voff, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(du, orr2, voff, so, 0);
+        } else if constexpr (GLU) {
           const v2i32 d = {static_cast<int>(f32x2_to_bf16x2(v[0], v[1])),
                            static_cast<int>(f32x2_to_bf16x2(v[2], v[3]))};
           __builtin_amdgcn_raw_buffer_store_b64(d, orr, voff, so, 0);
@@ -1133,7 +1151,8 @@ int cu_count() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 8)
       n = 256;
     cache[dev].store(n, std::memory_order_relaxed);
   }
@@ -1144,7 +1163,7 @@ int cu_count() {
 // XCDs), none past the tile bound.
 template <int EPI>
 hipError_t run2p(const GemmArgs &a, hipStream_t s) {
-  constexpr int NOUT = EPI == EPI_SWIGLU ? 128 : 256;
+  constexpr int NOUT = EPI == EPI_SWIGLU || EPI == EPI_GLU_F32 ? 128 : 256;
   GemmArgs b = a;
   b.max_mtiles = b.tiles ? b.max_mtiles : (b.M + 255) / 256;
   const int64_t bound = b.max_mtiles * ((b.N + NOUT - 1) / NOUT);
@@ -1163,11 +1182,12 @@ hipError_t run2p(const GemmArgs &a, hipStream_t s) {
 constexpr int64_t kMinRounds = 2;
 bool persistent_one(const GemmArgs &a, int epi) {
   if (a.a2 || a.k_split > 1 || a.b_kmajor) return false;
-  if (epi != EPI_SWIGLU && epi != EPI_SCALE && epi != EPI_STORE_F32) return false;
+  if (epi != EPI_SWIGLU && epi != EPI_SCALE && epi != EPI_STORE_F32 && epi != EPI_GLU_F32)
+    return false;
   if (a.k_offsets ? epi != EPI_STORE_F32 : (a.K + 63) / 64 < 5) return false;
-  if (a.ldo * 4 * 256 >= (int64_t(1) << 32)) return false;
+  if (a.ldo * 4 * 256 >= (int64_t(1) << 32) || (epi == EPI_GLU_F32 && !a.out2)) return false;
   const int64_t mt = a.tiles ? a.max_mtiles : (a.M + 255) / 256;
-  const int64_t nout = epi == EPI_SWIGLU ? 128 : 256;
+  const int64_t nout = epi == EPI_SWIGLU || epi == EPI_GLU_F32 ? 128 : 256;
   return mt * ((a.N + nout - 1) / nout) >= kMinRounds * cu_count();
 }
 
@@ -1301,8 +1321,10 @@ hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s, cons
           case EPI_SWIGLU: return run2p<EPI_SWIGLU>(a, s);
           case EPI_SCALE: return run2p<EPI_SCALE>(a, s);
           case EPI_STORE_F32: return run2p<EPI_STORE_F32>(a, s);
+          case EPI_GLU_F32: return run2p<EPI_GLU_F32>(a, s);
         }
       }
+      if (epi == EPI_GLU_F32) return hipErrorInvalidValue;  // (persistent kernel only)
       return dispatch2<256, 256, 4, 2>(a, b, epi, s);
     case TILE2_128x128: return dispatch2<128, 128, 2, 2>(a, b, epi, s);
     case TILE2_64x128: return dispatch2<64, 128, 2, 2>(a, b, epi, s);

@@ -123,7 +123,12 @@ hipError_t launch_gather(const void *rows, const int32_t *sorted_token, int64_t 
                          int64_t row_bytes, void *out, hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM
-enum Epilogue { EPI_SWIGLU = 0, EPI_SCALE = 1, EPI_STORE = 2, EPI_COMBINE = 3, EPI_STORE_F32 = 4 };
+// (EPI_GLU_F32, the persistent kernel only: the gate and up products of a
+// SwiGLU tile stored in fp32, gate to out, up to out2)
+enum Epilogue {
+  EPI_SWIGLU = 0, EPI_SCALE = 1, EPI_STORE = 2, EPI_COMBINE = 3, EPI_STORE_F32 = 4,
+  EPI_GLU_F32 = 5
+};
 
 // C = A B^T over one or two K segments, A [M, K] row-major (optionally row
 // gathered), B [N, K] row-major ("out x in" weights), grouped by expert via a
@@ -168,6 +173,7 @@ struct GemmArgs {
   // B (and b2) stored K-major, [K, N] row-major with leading dimension ldb
   // (pipelined kernel, fp32-store epilogue, no gate/up pair)
   int b_kmajor;
+  void *out2;                // GLU_F32: the up products (out: the gate products)
 };
 
 // Tile shapes (rows x B-rows per workgroup): SMALL_M 16x256, LARGE 128x128,
