@@ -679,7 +679,9 @@ __device__ __forceinline__ float row_bcast(float v) {
 // Persistent form of the 256x256 tile (4 x 2 wavefronts of 64x128, A two
 // stages ahead) for one problem (no second K segment or K split; K-grouped
 // allowed) and an epilogue that writes from the accumulators: SwiGLU, row
-// scale, fp32 store. Each workgroup runs a fixed list of tiles:
+// scale, fp32 store, or the gate and up halves of a SwiGLU tile each stored
+// in fp32 (the backward's recomputed pre-activations). Each workgroup runs a
+// fixed list of tiles:
 // the tiles are dealt over the XCDs in contiguous ranges as in gemm2_kernel,
 // and workgroup w of an XCD takes tiles w, w + G, w + 2 G, ... of its range
 // (G workgroups per XCD), so that at any time an XCD works on G consecutive
