@@ -180,6 +180,50 @@ def test_backward_is_deterministic_and_partial_requests():
 
 
 @pytest.mark.timeout(900)
+def test_backward_persistent_edges():
+    """The recomputed gate/up pre-activations on the persistent kernel's fp32
+    gate/up epilogue at its edges: reduction ending 32 columns into a stage
+    (d = 2080), a partial last n-tile (d_ff = 1056 = 8 x 128 + 32), skewed
+    experts (0, 1 and all tokens) and a partial last dense m-tile in the
+    shared recompute (T = 8229): input gradients on a token sample, and the
+    weight gradients of the smallest non-empty expert (one row)."""
+    w = custom(name="persist_bwd", config_no=640, T=8229, d=2080, d_ff=1056, E=8, K=4,
+               act="bf16", n_shared=1, d_ff_shared=2048, route="sigmoid_bias", bias_std=1.0,
+               w_std=0.03, router_std=0.03)
+    say("case backward persistent edges: generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    bits, dx, grads, g_idx = run_backward(w, a, layer, ["w_gate", "w_up", "w_down"])
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    dy = moe_synth.as_f64(bits, w.act)
+    # the last 37 tokens fill the shared recompute's partial last m-tile; each
+    # expert's last 16 tokens sit in its own last m-tile
+    tails = [np.nonzero((use == e).any(1))[0][-16:] for e in range(w.E)]
+    toks = np.union1d(sample_tokens(use, w.E, 256, seed=7),
+                      np.concatenate([np.arange(w.T - 37, w.T)] + tails))
+    ref = orc.backward(dy[toks], tokens=toks, idx_override=use[toks], experts=None,
+                       router=False, shared=False)
+    err = max_abs_rel(dx[toks], ref["dx"])
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    nz = np.nonzero(counts)[0]
+    e = int(nz[np.argmin(counts[nz])])
+    mine = np.nonzero((use == e).any(1))[0]
+    one = orc.backward(dy[mine], tokens=mine, idx_override=use[mine], experts=e, router=False,
+                       shared=False)
+    errs = {k: max_abs_rel(grads[k][e], one[k][0]) for k in ("w_gate", "w_up", "w_down")}
+    assert np.all(np.isnan(grads["w_gate"][counts == 0]))
+    say(f"  persistent edges: loads {counts.tolist()} near-ties={n_near} "
+        f"dx(sample {len(toks)})={err:.2e} expert {e} ({counts[e]} rows): "
+        + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert err <= TOL
+    for v in errs.values():
+        assert v <= TOL
+    del layer, a
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
 def test_backward_medium_sampled():
     """Full-size medium layer (skewed loads, empty experts): input gradients on
     a seeded token sample, and the weight gradients of the smallest non-empty
