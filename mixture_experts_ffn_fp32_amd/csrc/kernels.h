@@ -209,8 +209,8 @@ hipError_t launch_gemm2(const GemmArgs &a, int epi, int cfg, hipStream_t s,
                         const GemmArgs *b = nullptr);
 // Whether launch_gemm2 runs the launch on the persistent 256x256 kernel (one
 // workgroup per CU, each over a fixed list of tiles): one problem, a SwiGLU,
-// row-scale or fp32-store epilogue, a reduction of at least 5 stages
-// (K-grouped fp32 stores: any), at least two tiles per CU.
+// row-scale, fp32-store or fp32 gate/up epilogue, a reduction of at least 5
+// stages (K-grouped fp32 stores: any), at least two tiles per CU.
 bool gemm2_persistent(const GemmArgs &a, int epi, int cfg, const GemmArgs *b = nullptr);
 // Pipelined tile for rows x n_out over K (grouped over `groups` experts, or
 // dense with groups = 0), with an optional dense rows2 x n_out2 problem in
