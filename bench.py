@@ -491,8 +491,9 @@ def main():
                          "expert-parallel layer over G GPUs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's "
-              "multi-GPU sharding is not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding the "
+              "layer over several GPUs is not implemented (--expert-shard g/G times one "
+              "GPU's share of an expert-parallel layer)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
