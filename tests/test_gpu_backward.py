@@ -61,14 +61,37 @@ def oracle_selection(orc, g_idx):
     return use, int(near.sum())
 
 
+def oracle_backward_chunked(orc, dy, use, tokens, n_chunks, **kw):
+    """The oracle's backward over `tokens` as n_chunks calls run side by side
+    (its weight-gradient path is serial within a call): dx rows in token
+    order, weight gradients the chunks' sums added in chunk order (every
+    gradient is a sum of per-token terms)."""
+    parts = [p for p in np.array_split(np.asarray(tokens), n_chunks) if len(p)]
+
+    def one(part):
+        return orc.backward(dy[part], tokens=part, idx_override=use[part], **kw)
+
+    ref = None
+    with ThreadPoolExecutor(min(16, len(parts))) as ex:
+        for r in ex.map(one, parts):
+            if ref is None:
+                ref = r
+                continue
+            ref["dx"] = np.concatenate([ref["dx"], r["dx"]])
+            for k in r:
+                if k != "dx":
+                    ref[k] += r[k]
+    return ref
+
+
 def check_all(w, a, layer, keys=None, seed=11, tol=None):
     keys = _keys(w) if keys is None else keys
     tol = tol or TOL_BY_ACT[w.act]
     bits, dx, grads, g_idx = run_backward(w, a, layer, keys, seed)
     orc = oracle.Oracle(w, a)
     use, n_near = oracle_selection(orc, g_idx)
-    ref = orc.backward(moe_synth.as_f64(bits, w.act), idx_override=use,
-                       shared=bool(w.d_shared))
+    ref = oracle_backward_chunked(orc, moe_synth.as_f64(bits, w.act), use, np.arange(w.T),
+                                  max(1, min(16, w.T // 32)), shared=bool(w.d_shared))
     errs = {"dx": max_abs_rel(dx, ref["dx"])}
     active = np.bincount(use.ravel(), minlength=w.E) > 0
     for k in keys:
