@@ -332,8 +332,7 @@ def test_backward_latent_full_size_sampled():
     """Full-size latent layer (sigmoid routing, RMSNorm in L): input gradients
     on a seeded token sample and the weight gradients of the smallest
     non-empty expert over its tokens. (The projections' and the gain's
-    gradients, sums over all tokens, are checked element by element on the
-    small latent layers above.)"""
+    gradients: the masked test below.)"""
     w = moe_synth.get("latent")
     say("case backward latent: generating inputs")
     a = moe_synth.generate(w)
@@ -362,24 +361,24 @@ def test_backward_latent_full_size_sampled():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.timeout(900)
-def test_backward_large_prefill_masked_output_gradient():
-    """Full-size large prefill layer (16384 tokens, the launch configuration
-    the benchmark times) with an output gradient that is zero outside a token
-    set S: S = every token of one expert holding 257-511 rows (a full and a
-    partial 256-row m-tile on the in-place weight products) plus a seeded
-    sample of 32 others. Each token's gradient terms are independent of the
-    other tokens, so every weight gradient is then the oracle's sum over S:
-    router, shared gate/up/down and that expert's gate/up/down are compared
-    element by element; dx matches on S and is exactly zero elsewhere."""
-    w = moe_synth.get("large_prefill")
-    say("case backward large_prefill masked: generating inputs")
+def _masked_backward(name, in_place=None):
+    """The full-size layer `name` with an output gradient that is zero
+    outside a token set S: S = every token of one expert holding 257-511
+    rows (a full and a partial 256-row m-tile) plus a seeded sample of 32
+    others. Each token's gradient terms are independent of the other tokens,
+    so every weight gradient is then the oracle's sum over S: router, shared
+    (and latent projections and RMSNorm gain) gradients and that expert's
+    gate/up/down are compared element by element; dx matches on S and is
+    exactly zero elsewhere."""
+    w = moe_synth.get(name)
+    say(f"case backward {name} masked: generating inputs")
     a = moe_synth.generate(w)
     layer = layer_of(w, a)
-    assert moe.moe_plan(layer.desc)["backward_in_place"] == 3
+    if in_place is not None:
+        assert moe.moe_plan(layer.desc)["backward_in_place"] == in_place
     g_idx = gpu_route(layer)[0]
     orc = oracle.Oracle(w, a)
-    say("  large_prefill masked: oracle routing")
+    say(f"  {name} masked: oracle routing")
     use, n_near = oracle_selection(orc, g_idx)
     counts = np.bincount(use.ravel(), minlength=w.E)
     mid = np.nonzero((counts > 256) & (counts < 512))[0]
@@ -396,7 +395,7 @@ def test_backward_large_prefill_masked_output_gradient():
     dy_dev = torch.from_numpy(bits).view(torch.bfloat16).cuda()
     keys = _keys(w)
     grads = _grad_buffers(w, keys)
-    say(f"  large_prefill masked: backward (expert {e}: {counts[e]} rows, |S| = {len(S)})")
+    say(f"  {name} masked: backward (expert {e}: {counts[e]} rows, |S| = {len(S)})")
     dx = f64(layer.backward(layer.dev["x"], dy_dev, grads=grads))
     torch.cuda.synchronize()
     got = {k: (grads[k][e].cpu().numpy() if k in ("w_gate", "w_up", "w_down")
@@ -404,33 +403,32 @@ def test_backward_large_prefill_masked_output_gradient():
     del grads
     torch.cuda.empty_cache()
     dy = moe_synth.as_f64(bits, w.act)
-    # the oracle over S in chunks run side by side (its weight-gradient path
-    # is serial within a call); weight gradients: the chunks' sums added
-    parts = np.array_split(S, 32)
-    say(f"  large_prefill masked: oracle backward over {len(S)} tokens in {len(parts)} chunks")
-
-    def one(part):
-        return orc.backward(dy[part], tokens=part, idx_override=use[part], experts=e,
-                            router=True, shared=True)
-
-    ref = None
-    with ThreadPoolExecutor(16) as ex:
-        for i, r in enumerate(ex.map(one, parts)):
-            if ref is None:
-                ref = r
-            else:
-                ref["dx"] = np.concatenate([ref["dx"], r["dx"]])
-                for k in r:
-                    if k != "dx":
-                        ref[k] += r[k]
-            say(f"  large_prefill masked: oracle chunk {i + 1}/{len(parts)}")
+    say(f"  {name} masked: oracle backward over {len(S)} tokens in 32 chunks")
+    ref = oracle_backward_chunked(orc, dy, use, S, 32, experts=e, router=True, shared=True)
     errs = {"dx": max_abs_rel(dx[S], ref["dx"])}
     for k in keys:
         errs[k] = max_abs_rel(got[k], ref[k][0] if k in ("w_gate", "w_up", "w_down") else ref[k])
-    say(f"  large_prefill masked: near-ties={n_near} "
+    say(f"  {name} masked: near-ties={n_near} "
         + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert np.all(dx[~mask] == 0)
     for k, v in errs.items():
         assert v <= TOL, (k, v)
     del layer, a
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_backward_large_prefill_masked_output_gradient():
+    """Full-size large prefill layer (16384 tokens, the launch configuration
+    the benchmark times; expert weights read in place) under a masked output
+    gradient: router, shared and one expert's weight gradients element by
+    element."""
+    _masked_backward("large_prefill", in_place=3)
+
+
+@pytest.mark.timeout(900)
+def test_backward_latent_masked_output_gradient():
+    """Full-size latent layer (sigmoid routing, RMSNorm in L) under a masked
+    output gradient: the latent down- and up-projection, RMSNorm gain,
+    router, shared and one expert's weight gradients element by element."""
+    _masked_backward("latent")
