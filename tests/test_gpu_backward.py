@@ -427,6 +427,14 @@ def test_backward_large_prefill_masked_output_gradient():
 
 
 @pytest.mark.timeout(900)
+def test_backward_medium_masked_output_gradient():
+    """Full-size medium layer (skewed loads, empty experts, two shared
+    experts) under a masked output gradient: router, shared and one expert's
+    weight gradients element by element."""
+    _masked_backward("medium")
+
+
+@pytest.mark.timeout(900)
 def test_backward_latent_masked_output_gradient():
     """Full-size latent layer (sigmoid routing, RMSNorm in L) under a masked
     output gradient: the latent down- and up-projection, RMSNorm gain,
