@@ -361,6 +361,43 @@ def test_backward_latent_full_size_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(900)
+def test_backward_large_decode_router_shared_and_expert():
+    """Full-size decode layer (64 tokens over 256 experts; every weight read
+    in place): router and shared weight gradients over all tokens, and the
+    most loaded expert's weight gradients, element by element."""
+    w = moe_synth.get("large_decode")
+    say("case backward large_decode (router, shared, expert): generating inputs")
+    a = moe_synth.generate(w)
+    layer = layer_of(w, a)
+    keys = ["w_router", "ws_gate", "ws_up", "ws_down", "w_gate", "w_up", "w_down"]
+    bits, d_out = _d_out(w, 19)
+    dev = _grad_buffers(w, keys)  # expert buffers up to 45 GB: copied back for one expert
+    dx = f64(layer.backward(layer.dev["x"], d_out, grads=dev))
+    torch.cuda.synchronize()
+    g_idx = gpu_route(layer)[0]
+    orc = oracle.Oracle(w, a)
+    use, n_near = oracle_selection(orc, g_idx)
+    counts = np.bincount(use.ravel(), minlength=w.E)
+    e = int(np.argmax(counts))
+    got = {k: (dev[k][e] if k in ("w_gate", "w_up", "w_down") else dev[k]).cpu().numpy()
+           .astype(np.float64) for k in keys}
+    del dev
+    torch.cuda.empty_cache()
+    dy = moe_synth.as_f64(bits, w.act)
+    say(f"  large_decode: oracle backward over {w.T} tokens (expert {e}: {counts[e]} rows)")
+    ref = oracle_backward_chunked(orc, dy, use, np.arange(w.T), 16, experts=e, router=True,
+                                  shared=True)
+    errs = {"dx": max_abs_rel(dx, ref["dx"])}
+    for k in keys:
+        errs[k] = max_abs_rel(got[k], ref[k][0] if k in ("w_gate", "w_up", "w_down") else ref[k])
+    say(f"  large_decode: near-ties={n_near} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    del layer, a
+    torch.cuda.empty_cache()
+
+
 def _masked_backward(name, in_place=None):
     """The full-size layer `name` with an output gradient that is zero
     outside a token set S: S = every token of one expert holding 257-511
