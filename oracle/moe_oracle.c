@@ -42,6 +42,11 @@
  * derivable part of the section 12.5 worked example, the router example of
  * section 13.5, the dispatch example of the StableLatentMoE page, closed-form
  * identities and a dense, masked brute force on tiny inputs.
+ *
+ * Parity unpinned: the RMSNorm formula is pinned only by its properties
+ * (invariance to scaling of the routed sum, unit mean square at gamma = 1,
+ * gamma applied per element), and the latent workload's eps (1e-6), gamma
+ * (ones) and routed scale (1.0) are readings with no value on the pages.
  */
 #include <math.h>
 #include <stdint.h>
