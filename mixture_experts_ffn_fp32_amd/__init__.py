@@ -111,7 +111,18 @@ def stage_name(stage: int) -> str:
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor for an array argument of the C ABI (all of
+    them are device memory); None is the null pointer. Host tensors and
+    non-contiguous views are refused here, before anything is launched."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"libmoe takes device tensors; got a host tensor {tuple(t.shape)} "
+                         f"{t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"libmoe takes contiguous tensors; got a strided view "
+                         f"{tuple(t.shape)} {t.dtype}")
+    return t.data_ptr()
 
 
 def _stream(stream):

@@ -93,6 +93,28 @@ def test_null_pointers_rejected_before_launch():
     assert rc == -1
 
 
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding passes device addresses only: a host tensor or a strided
+    view is refused before the library is called."""
+    import torch
+    d = _desc(T=16)
+    w = moe.MoeWeights()
+    with pytest.raises(ValueError, match="device tensors"):
+        moe.moe_route(d, w, torch.zeros(16, 64), None, None, stream=0)
+    assert moe._ptr(None) is None
+
+    class _View:  # stands in for a device tensor whose view is strided
+        is_cuda = True
+
+        @staticmethod
+        def is_contiguous():
+            return False
+
+        shape, dtype = (16, 64), torch.bfloat16
+    with pytest.raises(ValueError, match="contiguous"):
+        moe._ptr(_View())
+
+
 def test_misaligned_arrays_rejected_before_launch():
     """Activations, weights, outputs, gradients and workspaces must be 16-byte
     aligned; a misaligned one is a shape error found on the host (the fake
