@@ -244,6 +244,23 @@ def test_plan_paths_of_the_workloads():
         moe.moe_plan(_desc(T=-1))
 
 
+@pytest.mark.parametrize("kw, want", [
+    # both grouped GEMMs: 256x256 tiles, >= 5 stages, >= 2 tiles per CU
+    (dict(T=8229, d=2080, d_ff=1056, E=8, K=4, n_shared=1, d_ff_shared=2048), 3),
+    # gate/up reduction of 4 stages (d = 256): only the down GEMM
+    (dict(T=65536, d=256, d_ff=2048, E=8, K=2, n_shared=0, d_ff_shared=0), 2),
+    # 256x256 gate/up tiles, but fewer than two per CU: neither
+    (dict(T=1024, d=2048, d_ff=2048, E=8, K=4, n_shared=0, d_ff_shared=0), 0),
+])
+def test_plan_persistent_thresholds(kw, want):
+    """Host-side plan: which grouped GEMMs take the persistent kernel at the
+    edges of its conditions."""
+    from _layers import custom
+    p = moe.moe_plan(moe.make_desc(custom(name="plan", act="bf16", **kw)))
+    assert (p["gate_up_tile_m"], p["gate_up_tile_n"]) == (256, 256)
+    assert p["persistent"] == want
+
+
 def test_backward_checked_before_launch():
     """moe_backward: widths that are multiples of 32; NULLs and a short
     workspace are reported before anything runs."""
